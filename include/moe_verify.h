@@ -1,0 +1,148 @@
+/* moe_verify.h -- C ABI of the MoE verify-block library (gfx950 / CDNA4).
+ *
+ * The target model of a speculative decoder checks a whole draft block in one pass and keeps
+ * only the tokens it would itself have produced ("Speculating on a Strix Halo", section
+ * "Speculative decoding"). In a mixture-of-experts target each block token routes to its own
+ * experts, so the block wakes the union of its tokens' experts plus the always-on shared expert
+ * ("Speculating on a Strix Halo", sections "What the pieces cost" and "Spoilers"); the expert
+ * work is grouped by expert, one grouped launch per projection ("Speculating on a Strix Halo",
+ * section "The verify's own cost"). The verify cost tracks the expert bytes streamed
+ * ("Speculating on a Strix Halo (part 2)", section "The verification cog").
+ *
+ * Two calls cover that pass:
+ *   moe_verify_block -- one MoE layer over a block of k <= 16 tokens: fp32 router logits,
+ *                       top-K with softmax renormalised over the K, woken-expert union, grouped
+ *                       SwiGLU experts (bf16 or mxfp4 weights), weighted combine with the shared
+ *                       expert, optional RMSNorm pre-norm and residual add;
+ *   accept_prefix    -- per-position target argmax and greedy longest-prefix acceptance.
+ *
+ * Conventions (all calls):
+ *   - Pointers are DEVICE memory owned by the caller unless stated otherwise; the library never
+ *     allocates, frees or synchronises. Work is enqueued on `hip_stream` (a hipStream_t; NULL is
+ *     the default stream) and the call returns; results are valid after the stream completes.
+ *   - Only host-visible arguments are validated, all before any HIP call, so a failing status
+ *     leaves the stream untouched. Device contents (ids, codes) are not validated.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Results are deterministic: fixed reduction orders, no floating-point atomics.
+ *   - Calls that share a workspace must not overlap in time (same stream is always safe).
+ */
+#ifndef MOE_VERIFY_H
+#define MOE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,      /* a required pointer is NULL                                     */
+  MOE_ERR_SHAPE = -2,     /* a size is outside the supported range (see each call)           */
+  MOE_ERR_DTYPE = -3,     /* unknown weight format, or mxfp4 without its scale arrays        */
+  MOE_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned                         */
+  MOE_ERR_WORKSPACE = -5, /* workspace smaller than the matching *_workspace_size()          */
+  MOE_ERR_ALIAS = -6,     /* output overlaps an input it must not overlap                    */
+  MOE_ERR_HIP = -7,       /* a kernel launch failed (device faults surface at the next sync) */
+  MOE_ERR_ARG = -8        /* unknown flag bits or a bad scalar argument                      */
+};
+
+/* Routed-expert weight formats. The shared expert is always bf16. */
+enum {
+  MOE_W_BF16 = 0,  /* bf16 bit patterns                                                       */
+  MOE_W_MXFP4 = 1  /* OCP MX FP4: E2M1 codes, two per byte (element 2j in the low nibble of
+                      byte j), one e8m0 scale byte 2^(s-127) per 32 consecutive values along the
+                      reduction dimension. Target weights in mxfp4 cut the verify's HBM bytes
+                      (DFlash-on-MI355X article, allbreaknews.com/?p=4397, section "Why Quantize
+                      the Target Model on Top?"). Scale bytes 1..254 are supported; 0 only on a
+                      block whose codes are all zero; 255 (NaN) is not supported. */
+};
+
+/* moe_verify_block flags: y = [x +] MoE([RMSNorm](x)). */
+enum {
+  MOE_PRE_RMSNORM = 1u, /* x_hat = x / sqrt(mean(x^2) + rms_eps) (unit gain) before the router
+                           and the experts, as in a pre-norm stack of MoE layers              */
+  MOE_RESIDUAL = 2u     /* add the un-normalised input x to the MoE output                    */
+};
+
+/* One MoE layer (a host struct, read only during the call; the arrays are device memory).
+ * Shapes (row-major):
+ *   router_w  fp32 [E][H]
+ *   w_gate, w_up   bf16 [E][I][H]    | mxfp4 codes [E][I][H/2],  s_gate, s_up  [E][I][H/32]
+ *   w_down         bf16 [E][H][I]    | mxfp4 codes [E][H][I/2],  s_down        [E][H][I/32]
+ *   sh_gate, sh_up bf16 [Is][H];  sh_down bf16 [H][Is]    (NULL when shared_inter == 0)
+ * Expert FFN: y_e = W_down (silu(W_gate x) * (W_up x)), silu(z) = z / (1 + e^-z).
+ * Supported sizes: H a multiple of 128 in [128, 1024] or of 256 in [1280, 2048] (mxfp4: a
+ * multiple of 256); I in {128, 256, 512, 1024}; Is = I, or 0 for no shared expert;
+ * 1 <= top_k <= min(E, 16); E <= 512. */
+typedef struct moe_layer {
+  int32_t hidden;       /* H */
+  int32_t n_experts;    /* E */
+  int32_t top_k;        /* K experts routed per token */
+  int32_t inter;        /* I, routed expert intermediate size */
+  int32_t shared_inter; /* Is, shared expert intermediate size; 0 = no shared expert */
+  int32_t wdtype;       /* MOE_W_BF16 | MOE_W_MXFP4 */
+  float rms_eps;        /* used with MOE_PRE_RMSNORM; must be finite and >= 0 */
+  const float* router_w;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const uint8_t* s_gate; /* mxfp4 scales; NULL for bf16 */
+  const uint8_t* s_up;
+  const uint8_t* s_down;
+  const void* sh_gate;
+  const void* sh_up;
+  const void* sh_down;
+} moe_layer;
+
+/* Bytes of device workspace moe_verify_block needs for blocks of up to k_max tokens
+ * (0 if the layer description is invalid). Host only. */
+size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max);
+
+/* One MoE layer over a verify block.
+ *   x        fp32 [k][H]  block hidden states (input; not modified)
+ *   k        1 <= k <= 16 block tokens (a block carries 1 known token and up to 15 drafted
+ *            ones: "Speculating on a Strix Halo", section "Speculative decoding")
+ *   flags    MOE_PRE_RMSNORM | MOE_RESIDUAL
+ *   y        fp32 [k][H]  output; must not overlap x or the workspace
+ *   topk_ids int32 [k][K] or NULL: each token's experts, descending router logit, equal logits
+ *            to the lower expert index
+ *   topk_w   fp32  [k][K] or NULL: the matching weights, softmax over the K selected logits
+ *   n_woken  int32 [1]    or NULL: size of the union of the block's routed experts (shared
+ *            expert not counted)
+ *   workspace, ws_bytes: device scratch of at least moe_verify_workspace_size(layer, k) bytes;
+ *            its contents need no initialisation and are overwritten.
+ * Returns MOE_OK or an MOE_ERR_* code (nothing is enqueued on error). */
+int moe_verify_block(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
+                     int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
+                     size_t ws_bytes, void* hip_stream);
+
+/* Bytes of device workspace accept_prefix needs (0 if the sizes are invalid). Host only. */
+size_t accept_prefix_workspace_size(int32_t n_target, int32_t vocab);
+
+/* Greedy acceptance of a draft block ("Speculating on a Strix Halo", section "Speculative
+ * decoding": the target keeps the draft prefix it would itself produce, then adds its own next
+ * token; the n-th draft counts only if the ones before it did: "Speculating on a Strix Halo
+ * (part 2)", section "Why drafter performance doesn't really matter").
+ *   logits     fp32 [n_target][vocab]: the target's logits at each block position
+ *   draft_ids  int32 [n_draft] (may be NULL when n_draft == 0); draft i is compared with the
+ *              target's choice at position i; ids outside [0, vocab) never match
+ *   target_ids int32 [n_target] out: per-row argmax, equal values to the lowest index
+ *   accepted   int32 [1] out: a = the longest prefix with draft_ids[i] == target_ids[i]; the
+ *              committed tokens are draft_ids[0..a) followed by target_ids[a] when a < n_target
+ * Limits: 1 <= n_target <= 64, 0 <= n_draft <= n_target, 1 <= vocab <= 2^24.
+ * NaN logits give an unspecified argmax. Returns MOE_OK or an MOE_ERR_* code. */
+int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const int32_t* draft_ids,
+                  int32_t n_draft, int32_t* target_ids, int32_t* accepted, void* workspace,
+                  size_t ws_bytes, void* hip_stream);
+
+/* Static description of a status code. Host only. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_VERIFY_H */

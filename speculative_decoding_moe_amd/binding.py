@@ -1,0 +1,133 @@
+"""Thin Python binding of libmoeverify.so (include/moe_verify.h): argument marshalling only.
+
+Every step of the MoE verify pass runs in the library's HIP kernels. Tensors are torch tensors
+on a ROCm device; the call is enqueued on torch's current stream. If the library cannot be
+loaded, import fails loudly: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoeverify.so")
+
+MOE_OK = 0
+MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN = -1, -2, -3, -4
+MOE_ERR_WORKSPACE, MOE_ERR_ALIAS, MOE_ERR_HIP, MOE_ERR_ARG = -5, -6, -7, -8
+MOE_W_BF16, MOE_W_MXFP4 = 0, 1
+MOE_PRE_RMSNORM, MOE_RESIDUAL = 1, 2
+
+EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "accept_prefix_workspace_size",
+           "accept_prefix", "moe_status_string")
+
+
+class MoeLayerStruct(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("wdtype", ctypes.c_int32),
+        ("rms_eps", ctypes.c_float),
+        ("router_w", ctypes.c_void_p),
+        ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+        ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+        ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
+    ]
+
+
+class MoeVerifyError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m speculative_decoding_moe_amd._build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    lib.moe_verify_workspace_size.argtypes = [ctypes.POINTER(MoeLayerStruct), i32]
+    lib.moe_verify_workspace_size.restype = sz
+    lib.moe_verify_block.argtypes = [ctypes.POINTER(MoeLayerStruct), vp, i32, u32, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_verify_block.restype = ctypes.c_int
+    lib.accept_prefix_workspace_size.argtypes = [i32, i32]
+    lib.accept_prefix_workspace_size.restype = sz
+    lib.accept_prefix.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, sz, vp]
+    lib.accept_prefix.restype = ctypes.c_int
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.moe_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoeVerifyError(status, status_string(status))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle():
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+class MoeLayer:
+    """Holds the device tensors of one MoE layer and the C descriptor that points at them.
+
+    bf16 weights are passed as int16/uint16/bfloat16 tensors of the documented shapes; mxfp4
+    weights as uint8 code tensors plus uint8 scale tensors."""
+
+    def __init__(self, *, hidden, n_experts, top_k, inter, shared_inter, router_w, w_gate, w_up,
+                 w_down, s_gate=None, s_up=None, s_down=None, sh_gate=None, sh_up=None,
+                 sh_down=None, rms_eps=1e-6):
+        self.tensors = dict(router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down,
+                            s_gate=s_gate, s_up=s_up, s_down=s_down, sh_gate=sh_gate,
+                            sh_up=sh_up, sh_down=sh_down)
+        self.hidden, self.n_experts, self.top_k = hidden, n_experts, top_k
+        self.inter, self.shared_inter = inter, shared_inter
+        self.wdtype = MOE_W_MXFP4 if s_gate is not None else MOE_W_BF16
+        self.struct = MoeLayerStruct(
+            hidden, n_experts, top_k, inter, shared_inter, self.wdtype, rms_eps,
+            *(_ptr(self.tensors[n]) for n in ("router_w", "w_gate", "w_up", "w_down", "s_gate",
+                                              "s_up", "s_down", "sh_gate", "sh_up", "sh_down")))
+
+    def workspace_size(self, k_max: int) -> int:
+        return int(lib.moe_verify_workspace_size(ctypes.byref(self.struct), int(k_max)))
+
+
+def moe_verify_workspace_size(layer: MoeLayer, k_max: int) -> int:
+    return layer.workspace_size(k_max)
+
+
+def moe_verify_block(layer: MoeLayer, x, flags: int, y, topk_ids=None, topk_w=None, n_woken=None,
+                     workspace=None, stream=None) -> None:
+    """y = [x +] MoE([RMSNorm](x)) over a block of k = x.shape[0] tokens (library call)."""
+    k = int(x.shape[0])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.moe_verify_block(ctypes.byref(layer.struct), _ptr(x), k, int(flags), _ptr(y),
+                              _ptr(topk_ids), _ptr(topk_w), _ptr(n_woken), _ptr(workspace),
+                              ws_bytes, _stream_handle() if stream is None else stream)
+    _check(st)
+
+
+def accept_prefix_workspace_size(n_target: int, vocab: int) -> int:
+    return int(lib.accept_prefix_workspace_size(int(n_target), int(vocab)))
+
+
+def accept_prefix(logits, draft_ids, target_ids, accepted, workspace, n_draft=None, stream=None) -> None:
+    """Per-row argmax of logits [n_target][V] and the greedy accepted length (library call)."""
+    n_target, vocab = int(logits.shape[0]), int(logits.shape[1])
+    nd = int(draft_ids.shape[0]) if (n_draft is None and draft_ids is not None) else int(n_draft or 0)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.accept_prefix(_ptr(logits), n_target, vocab, _ptr(draft_ids), nd, _ptr(target_ids),
+                           _ptr(accepted), _ptr(workspace), ws_bytes,
+                           _stream_handle() if stream is None else stream)
+    _check(st)

@@ -1,0 +1,100 @@
+"""Seeded workloads as device tensors (input preparation; no arithmetic of the method).
+
+Bulk expert weights are filled on the GPU by libworkload_fill.so, the device twin of
+``gen.weight_bf16`` / ``gen.weight_mxfp4`` (identical bits); small inputs are drawn on the host by
+``gen`` and copied over.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+from . import gen
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libworkload_fill.so")
+_lib = None
+_tables = {}
+
+
+def _fill_lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: build with `python -m speculative_decoding_moe_amd._build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, u64, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32
+        lib.workload_fill_bf16.argtypes = [vp, u64, u32, u64, u64, vp, vp]
+        lib.workload_fill_bf16.restype = ctypes.c_int
+        lib.workload_fill_mxfp4.argtypes = [vp, vp, u64, u32, u64, u64, vp, vp]
+        lib.workload_fill_mxfp4.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _table(kind: str, device) -> torch.Tensor:
+    key = (kind, str(device))
+    if key not in _tables:
+        if kind == "bf16":
+            arr = gen.bf16_table().view(np.int16)
+        else:
+            arr = gen.normal_quantile_table()
+        _tables[key] = torch.from_numpy(arr.copy()).to(device)
+    return _tables[key]
+
+
+def fill_bf16(out: torch.Tensor, seed: int, layer: int, kind: int, expert0: int, n_tensors: int):
+    """out: contiguous int16 tensor of n_tensors x (rows*cols) elements."""
+    n = out.numel() // n_tensors
+    st = _fill_lib().workload_fill_bf16(out.data_ptr(), n, n_tensors, seed, gen.tensor_id(layer, kind, expert0),
+                                        _table("bf16", out.device).data_ptr(), torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"workload_fill_bf16 failed ({st})")
+
+
+def fill_mxfp4(codes: torch.Tensor, scales: torch.Tensor, seed: int, layer: int, kind: int, expert0: int,
+               n_tensors: int):
+    n = codes.numel() * 2 // n_tensors
+    st = _fill_lib().workload_fill_mxfp4(codes.data_ptr(), scales.data_ptr(), n, n_tensors, seed,
+                                         gen.tensor_id(layer, kind, expert0), _table("f32", codes.device).data_ptr(),
+                                         torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"workload_fill_mxfp4 failed ({st})")
+
+
+def layer_tensors(wl: gen.Workload, layer: int = 0, device="cuda") -> dict:
+    """All tensors of one MoE layer on the device, in the library's layouts."""
+    s = wl.shape
+    E, H, I, Is = s.n_experts, s.hidden, s.inter, s.shared_inter
+    t = {"router_w": torch.from_numpy(gen.router_weight(wl, layer)).to(device)}
+    if s.wdtype == "bf16":
+        for name, kind, shape in (("w_gate", gen.KIND_GATE, (E, I, H)), ("w_up", gen.KIND_UP, (E, I, H)),
+                                  ("w_down", gen.KIND_DOWN, (E, H, I))):
+            w = torch.empty(shape, dtype=torch.int16, device=device)
+            fill_bf16(w, wl.seed, layer, kind, 0, E)
+            t[name] = w
+    else:
+        for name, kind, rows, cols in (("gate", gen.KIND_GATE, I, H), ("up", gen.KIND_UP, I, H),
+                                       ("down", gen.KIND_DOWN, H, I)):
+            c = torch.empty((E, rows, cols // 2), dtype=torch.uint8, device=device)
+            sc = torch.empty((E, rows, cols // 32), dtype=torch.uint8, device=device)
+            fill_mxfp4(c, sc, wl.seed, layer, kind, 0, E)
+            t["w_" + name], t["s_" + name] = c, sc
+    if Is:
+        for name, kind, shape in (("sh_gate", gen.KIND_GATE, (Is, H)), ("sh_up", gen.KIND_UP, (Is, H)),
+                                  ("sh_down", gen.KIND_DOWN, (H, Is))):
+            w = torch.empty(shape, dtype=torch.int16, device=device)
+            fill_bf16(w, wl.seed, layer, kind, gen.SHARED_EXPERT_ID, 1)
+            t[name] = w
+    return t
+
+
+def make_layer(wl: gen.Workload, layer: int = 0, device="cuda", tensors: dict | None = None):
+    """A binding.MoeLayer for one generated layer (tensors kept alive by the object)."""
+    from .. import binding
+    s = wl.shape
+    t = layer_tensors(wl, layer, device) if tensors is None else tensors
+    return binding.MoeLayer(hidden=s.hidden, n_experts=s.n_experts, top_k=s.top_k, inter=s.inter,
+                            shared_inter=s.shared_inter, rms_eps=wl.rms_eps, **t)

@@ -1,0 +1,123 @@
+// Device twin of the seeded weight generator (input preparation, not part of the MoE path).
+//
+// Element n of tensor (seed, tensor_id) is 16-bit word n of the Philox4x64-10 stream keyed by
+// [seed, tensor_id] (Salmon, Moraes, Dror, Shaw: "Parallel random numbers: as easy as 1, 2, 3",
+// SC 2011), block b of four 64-bit outputs computed on counter (b + 1, 0, 0, 0), words taken
+// little-endian. The word indexes a caller-supplied 65536-entry table (bf16 bits for bf16
+// weights, float32 values for the mxfp4 quantiser). The host generator produces identical bits.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+struct U64x4 { uint64_t v[4]; };
+
+__device__ __forceinline__ U64x4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                               uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) { k0 += W0; k1 += W1; }
+    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+  }
+  U64x4 o;
+  o.v[0] = c0; o.v[1] = c1; o.v[2] = c2; o.v[3] = c3;
+  return o;
+}
+
+// 16 consecutive words (one Philox block) per thread.
+__device__ __forceinline__ void block_words(uint64_t seed, uint64_t tid, uint64_t b, uint32_t (&w)[16]) {
+  const U64x4 r = philox4x64_10(b + 1, 0, 0, 0, seed, tid);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) w[4 * i + h] = (uint32_t)((r.v[i] >> (16 * h)) & 0xFFFFu);
+}
+
+// grid.y = expert offset; tensor id of expert e = tid0 + e (consecutive experts).
+__global__ void k_fill_bf16(uint16_t* out, uint64_t n_per_tensor, uint64_t seed, uint64_t tid0,
+                            const uint16_t* table) {
+  const uint64_t e = blockIdx.y;
+  const uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b * 16 >= n_per_tensor) return;
+  uint32_t w[16];
+  block_words(seed, tid0 + e, b, w);
+  uint16_t* dst = out + e * n_per_tensor + b * 16;
+  uint4 o0, o1;
+  o0.x = table[w[0]] | ((uint32_t)table[w[1]] << 16);   o0.y = table[w[2]] | ((uint32_t)table[w[3]] << 16);
+  o0.z = table[w[4]] | ((uint32_t)table[w[5]] << 16);   o0.w = table[w[6]] | ((uint32_t)table[w[7]] << 16);
+  o1.x = table[w[8]] | ((uint32_t)table[w[9]] << 16);   o1.y = table[w[10]] | ((uint32_t)table[w[11]] << 16);
+  o1.z = table[w[12]] | ((uint32_t)table[w[13]] << 16); o1.w = table[w[14]] | ((uint32_t)table[w[15]] << 16);
+  reinterpret_cast<uint4*>(dst)[0] = o0;
+  reinterpret_cast<uint4*>(dst)[1] = o1;
+}
+
+// One 32-value block per thread: shared exponent s = floor(log2 max|w|) - 2, scale byte s + 127,
+// codes = |w| / 2^s rounded to the nearest E2M1 magnitude (ties to the even code, saturating at
+// 6) with the sign in bit 3; element 2j in the low nibble of byte j.
+__global__ void k_fill_mxfp4(uint8_t* codes, uint8_t* scales, uint64_t n_per_tensor, uint64_t seed,
+                             uint64_t tid0, const float* table) {
+  const uint64_t e = blockIdx.y;
+  const uint64_t blk = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk * 32 >= n_per_tensor) return;
+  uint32_t w0[16], w1[16];
+  block_words(seed, tid0 + e, 2 * blk, w0);
+  block_words(seed, tid0 + e, 2 * blk + 1, w1);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { v[i] = table[w0[i]]; v[16 + i] = table[w1[i]]; }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int s = (int)((__float_as_uint(amax) >> 23) & 0xFFu) - 127 - 2;
+  if (amax == 0.f) s = -127;
+  const float mid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float q = fabsf(ldexpf(v[i], -s));
+    uint32_t mag = 0;
+#pragma unroll
+    for (int m = 0; m < 7; ++m) mag += (q > mid[m]) || (q == mid[m] && (m & 1));
+    const uint32_t code = mag | (v[i] < 0.f ? 8u : 0u);
+    packed[i / 8] |= code << (4 * (i % 8));
+  }
+  uint4 o;
+  o.x = packed[0]; o.y = packed[1]; o.z = packed[2]; o.w = packed[3];
+  reinterpret_cast<uint4*>(codes + e * (n_per_tensor / 2))[blk] = o;
+  scales[e * (n_per_tensor / 32) + blk] = (uint8_t)(s + 127);
+}
+
+}  // namespace
+
+extern "C" {
+
+// out: bf16 [n_tensors][n_per_tensor] (n_per_tensor a multiple of 16, out 16-byte aligned);
+// tensor i uses tensor id tid0 + i. Returns 0 or a hipError_t code.
+int workload_fill_bf16(void* out, uint64_t n_per_tensor, uint32_t n_tensors, uint64_t seed, uint64_t tid0,
+                       const void* table_bf16, void* stream) {
+  if (!out || !table_bf16 || n_per_tensor % 16 || n_tensors == 0 || n_tensors > 65535) return -1;
+  const uint64_t nb = n_per_tensor / 16;
+  dim3 grid((unsigned)((nb + 255) / 256), n_tensors);
+  k_fill_bf16<<<grid, 256, 0, (hipStream_t)stream>>>((uint16_t*)out, n_per_tensor, seed, tid0,
+                                                     (const uint16_t*)table_bf16);
+  return (int)hipGetLastError();
+}
+
+// codes: [n_tensors][n_per_tensor/2], scales: [n_tensors][n_per_tensor/32] (n_per_tensor a multiple
+// of 32, blocks run along the contiguous dimension).
+int workload_fill_mxfp4(void* codes, void* scales, uint64_t n_per_tensor, uint32_t n_tensors, uint64_t seed,
+                        uint64_t tid0, const void* table_f32, void* stream) {
+  if (!codes || !scales || !table_f32 || n_per_tensor % 32 || n_tensors == 0 || n_tensors > 65535) return -1;
+  const uint64_t nb = n_per_tensor / 32;
+  dim3 grid((unsigned)((nb + 255) / 256), n_tensors);
+  k_fill_mxfp4<<<grid, 256, 0, (hipStream_t)stream>>>((uint8_t*)codes, (uint8_t*)scales, n_per_tensor, seed,
+                                                      tid0, (const float*)table_f32);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments on the host
+before any HIP call (no GPU needed: nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_verify.h")
+LIB = os.path.join(ROOT, "speculative_decoding_moe_amd", "libmoeverify.so")
+
+
+@pytest.fixture(scope="module")
+def b():
+    if not os.path.exists(LIB):
+        from speculative_decoding_moe_amd import _build
+        _build.build()
+    from speculative_decoding_moe_amd import binding
+    return binding
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points(b):
+    assert _declared_functions() == sorted(b.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(b):
+    lib = ctypes.CDLL(LIB)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(b):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, -8):
+        s = b.status_string(st)
+        assert s and s != "unknown status"
+    assert b.status_string(12345) == "unknown status"
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned stand-in address; never dereferenced by host validation
+
+
+def _layer(b, **over):
+    d = dict(hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512, wdtype=0, rms_eps=1e-6,
+             router_w=FAKE, w_gate=FAKE + 0x1000, w_up=FAKE + 0x2000, w_down=FAKE + 0x3000, s_gate=None,
+             s_up=None, s_down=None, sh_gate=FAKE + 0x4000, sh_up=FAKE + 0x5000, sh_down=FAKE + 0x6000)
+    d.update(over)
+    return b.MoeLayerStruct(*(d[f] for f, _ in b.MoeLayerStruct._fields_))
+
+
+def _call(b, L, k=16, flags=0, x=FAKE + 0x10000000, y=FAKE + 0x20000000, ids=None, w=None, n=None,
+          ws=FAKE + 0x40000000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = b.lib.moe_verify_workspace_size(ctypes.byref(L), k) if 1 <= k <= 16 else 1 << 30
+    return b.lib.moe_verify_block(ctypes.byref(L), x, k, flags, y, ids, w, n, ws, ws_bytes, None)
+
+
+def test_workspace_size(b):
+    L = _layer(b)
+    n1 = b.lib.moe_verify_workspace_size(ctypes.byref(L), 1)
+    n16 = b.lib.moe_verify_workspace_size(ctypes.byref(L), 16)
+    assert 0 < n1 < n16
+    assert n16 % 256 == 0
+    assert b.lib.moe_verify_workspace_size(ctypes.byref(L), 0) == 0
+    assert b.lib.moe_verify_workspace_size(ctypes.byref(L), 17) == 0
+    assert b.lib.moe_verify_workspace_size(None, 4) == 0
+    assert b.lib.moe_verify_workspace_size(ctypes.byref(_layer(b, hidden=100)), 4) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(hidden=100), -2), (dict(hidden=64), -2), (dict(hidden=4096), -2), (dict(hidden=1152), -2),
+    (dict(n_experts=0), -2), (dict(n_experts=513), -2), (dict(top_k=0), -2), (dict(top_k=17), -2),
+    (dict(n_experts=4, top_k=5), -2), (dict(inter=384), -2), (dict(inter=2048), -2),
+    (dict(shared_inter=256), -2), (dict(wdtype=2), -3), (dict(wdtype=1), -3),
+    (dict(router_w=None), -1), (dict(w_down=None), -1), (dict(sh_up=None), -1),
+    (dict(w_gate=FAKE + 8), -4), (dict(rms_eps=-1.0), -8), (dict(rms_eps=float("nan")), -8),
+])
+def test_bad_layer_rejected(b, over, status):
+    assert _call(b, _layer(b, **over), ws_bytes=1 << 30) == status
+
+
+def test_bad_call_arguments_rejected(b):
+    L = _layer(b)
+    assert b.lib.moe_verify_block(None, FAKE, 4, 0, FAKE, None, None, None, FAKE, 1 << 30, None) == -1
+    assert _call(b, L, x=None) == -1
+    assert _call(b, L, y=None) == -1
+    assert _call(b, L, ws=None) == -1
+    assert _call(b, L, k=0) == -2
+    assert _call(b, L, k=17) == -2
+    assert _call(b, L, flags=4) == -8
+    assert _call(b, L, x=FAKE + 0x10000004) == -4
+    assert _call(b, L, ids=FAKE + 0x30000002) == -4
+    need = b.lib.moe_verify_workspace_size(ctypes.byref(L), 16)
+    assert _call(b, L, ws_bytes=need - 1) == -5
+    # y overlapping x, or the workspace
+    assert _call(b, L, y=FAKE + 0x10000000) == -6
+    assert _call(b, L, y=FAKE + 0x40000000 + 256) == -6
+    assert _call(b, L, x=FAKE + 0x40000000 + 4096) == -6
+    assert _call(b, L, ids=FAKE + 0x40000000 + 512) == -6
+
+
+def test_mxfp4_layer_needs_h_multiple_of_256(b):
+    L = _layer(b, hidden=384, wdtype=1, s_gate=FAKE + 0x7000, s_up=FAKE + 0x8000, s_down=FAKE + 0x9000)
+    assert _call(b, L, ws_bytes=1 << 30) == -2
+
+
+def test_mxfp4_layer_needs_scales(b):
+    L = _layer(b, wdtype=1, s_gate=FAKE + 0x7000, s_up=FAKE + 0x8000, s_down=None)
+    assert _call(b, L, ws_bytes=1 << 30) == -3
+
+
+def test_accept_prefix_validation(b):
+    f = b.lib.accept_prefix
+    ws = FAKE + 0x50000000
+    need = b.lib.accept_prefix_workspace_size(17, 151936)
+    assert need > 0
+    assert b.lib.accept_prefix_workspace_size(0, 10) == 0
+    assert b.lib.accept_prefix_workspace_size(65, 10) == 0
+    assert b.lib.accept_prefix_workspace_size(4, 0) == 0
+    lg, dr, tg, ac = FAKE, FAKE + 0x10000000, FAKE + 0x20000000, FAKE + 0x30000000
+    assert f(None, 17, 151936, dr, 16, tg, ac, ws, need, None) == -1
+    assert f(lg, 17, 151936, None, 16, tg, ac, ws, need, None) == -1
+    assert f(lg, 0, 151936, dr, 0, tg, ac, ws, need, None) == -2
+    assert f(lg, 17, 151936, dr, 18, tg, ac, ws, need, None) == -2
+    assert f(lg, 17, 151936, dr, -1, tg, ac, ws, need, None) == -2
+    assert f(lg, 17, 0, dr, 16, tg, ac, ws, need, None) == -2
+    assert f(lg, 17, 151936, dr, 16, tg + 4, ac, ws, need, None) == -4
+    assert f(lg, 17, 151936, dr, 16, tg, ac, ws, need - 1, None) == -5
+    assert f(lg, 17, 151936, dr, 16, lg + 64, ac, ws, need, None) == -6
+    assert f(lg, 17, 151936, dr, 16, tg, tg, ws, need, None) == -6

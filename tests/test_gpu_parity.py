@@ -1,0 +1,360 @@
+"""GPU parity of the HIP path, called through the C ABI, against the CPU oracle on the same seeded
+inputs. Run on an MI355X: ``pytest -m gpu``.
+
+Bars: expert ids bit-exact except where the oracle's logits are within 1e-4 of a different
+valid selection (then the oracle is re-run with the GPU's ids forced); routing weights within
+1e-6; woken counts, argmax ids and accepted lengths bit-exact; outputs within 1e-2 x RMS (bf16
+experts) or 3e-2 x RMS (mxfp4 experts) in max-abs error.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import GenLayer
+from speculative_decoding_moe_amd.workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 1e-2
+MX_TOL = 3e-2
+TIE = 1e-4
+PRE, RES = 1, 2
+
+
+@pytest.fixture(scope="session")
+def B():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    torch.cuda.set_device(0)
+    from speculative_decoding_moe_amd import binding
+    return binding
+
+
+_LAYERS = {}
+
+
+def dev_layer(wl, layer=0):
+    from speculative_decoding_moe_amd.workloads import device
+    key = (wl, layer)
+    if key not in _LAYERS:
+        if len(_LAYERS) > 6:
+            _LAYERS.clear()
+        _LAYERS[key] = device.make_layer(wl, layer, "cuda")
+    return _LAYERS[key]
+
+
+def run_block(B, layer, x, flags=0, ws_fill=None, ws=None):
+    k = x.shape[0]
+    xd = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+    y = torch.empty_like(xd)
+    ids = torch.empty((k, layer.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((k, layer.top_k), dtype=torch.float32, device="cuda")
+    nw = torch.empty(4, dtype=torch.int32, device="cuda")
+    if ws is None:
+        ws = torch.empty(layer.workspace_size(k), dtype=torch.uint8, device="cuda")
+    if ws_fill is not None:
+        ws.fill_(ws_fill)
+    B.moe_verify_block(layer, xd, flags, y, ids, w, nw, ws)
+    torch.cuda.synchronize()
+    return {"y": y.cpu().numpy(), "ids": ids.cpu().numpy().astype(np.int64), "w": w.cpu().numpy(),
+            "n_woken": int(nw[0].item())}
+
+
+def _valid_topk_within(logits_row, ids, tie):
+    """ids is a correct descending top-K of logits perturbed by at most `tie`."""
+    sel = set(int(e) for e in ids)
+    l = logits_row
+    rest = [e for e in range(l.size) if e not in sel]
+    worst_sel = min(l[list(sel)])
+    if rest and max(l[rest]) > worst_sel + tie:
+        return False
+    return all(l[ids[j]] >= l[ids[j + 1]] - tie for j in range(len(ids) - 1))
+
+
+def check_parity(g, x, wl, layer_idx=0, flags=0, tol=BF16_TOL, compare_delta=False, tokens=None):
+    """Compare one GPU block result with the oracle; returns max-abs error / RMS."""
+    K = wl.shape.top_k
+    L = GenLayer(wl, layer_idx)
+    kw = dict(pre_norm=bool(flags & PRE), residual=bool(flags & RES), rms_eps=wl.rms_eps)
+    rows = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
+    xs = x[rows]
+    ref = oracle.moe_block(xs, L, K, **kw)
+    gids = g["ids"][rows]
+    if not np.array_equal(gids, ref["ids"]):
+        for i in range(len(rows)):
+            if not np.array_equal(gids[i], ref["ids"][i]):
+                assert _valid_topk_within(ref["logits"][i], gids[i], TIE), (
+                    f"token {rows[i]}: ids {gids[i]} vs oracle {ref['ids'][i]} beyond the {TIE} near-tie margin")
+        ref = oracle.moe_block(xs, L, K, forced_ids=gids, **kw)
+    if tokens is None:
+        assert g["n_woken"] == len(set(g["ids"].ravel().tolist()))
+        assert g["n_woken"] == ref["n_woken"]
+    np.testing.assert_allclose(g["w"][rows], ref["w"], rtol=0, atol=1e-6)
+    assert np.all(np.abs(g["w"][rows].astype(np.float64).sum(axis=1) - 1.0) <= 1e-6)
+    gy = g["y"][rows].astype(np.float64)
+    ry = ref["y"]
+    if compare_delta:  # residual stream: compare the MoE delta against its own RMS
+        gy, ry = gy - xs, ry - xs
+    rms = float(np.sqrt(np.mean(ry ** 2)))
+    err = float(np.abs(gy - ry).max())
+    assert err <= tol * rms, f"max|dy| {err:.3e} > {tol} x RMS {rms:.3e}"
+    return err / rms
+
+
+# ---------------------------------------------------------------------------------------------
+def test_device_fill_matches_host_generator(B):
+    from speculative_decoding_moe_amd.workloads import device
+    for name in ("tiny", "verify", "stack40_mxfp4"):
+        wl = gen.WORKLOADS[name]
+        t = device.layer_tensors(wl, 3 if name == "stack40_mxfp4" else 0, "cuda")
+        layer = 3 if name == "stack40_mxfp4" else 0
+        for e in (0, 5, wl.shape.n_experts - 1):
+            host = gen.expert_tensors(wl, layer, e)
+            for nm in ("gate", "up", "down"):
+                d = t["w_" + nm][e].cpu().numpy()
+                assert np.array_equal(d.view(host[nm].dtype), host[nm]), (name, e, nm)
+                if wl.shape.wdtype == "mxfp4":
+                    assert np.array_equal(t["s_" + nm][e].cpu().numpy(), host[nm + "_scale"]), (name, e, nm)
+        sh = gen.shared_tensors(wl, layer)
+        if sh is not None:
+            for nm in ("gate", "up", "down"):
+                assert np.array_equal(t["sh_" + nm].cpu().numpy().view(np.uint16), sh[nm])
+        del t
+    torch.cuda.empty_cache()
+
+
+def test_tiny_layer_parity(B):
+    wl = gen.WORKLOADS["tiny"]
+    g = run_block(B, dev_layer(wl), gen.hidden_states(wl))
+    r = check_parity(g, gen.hidden_states(wl), wl)
+    print(f"tiny: U={g['n_woken']} err/rms={r:.2e}")
+
+
+def test_decode_parity(B):
+    wl = gen.WORKLOADS["decode"]
+    x = gen.hidden_states(wl)
+    g = run_block(B, dev_layer(wl), x)
+    assert g["n_woken"] == 8
+    r = check_parity(g, x, wl)
+    print(f"decode: err/rms={r:.2e}")
+
+
+def test_verify_block_parity(B):
+    wl = gen.WORKLOADS["verify"]
+    x = gen.hidden_states(wl)
+    g = run_block(B, dev_layer(wl), x)
+    r = check_parity(g, x, wl)
+    print(f"verify k=16: U={g['n_woken']} err/rms={r:.2e}")
+    assert 50 <= g["n_woken"] <= 128
+
+
+@pytest.mark.parametrize("k", [2, 3, 7, 9, 15])
+def test_k_sweep_parity(B, k):
+    wl = gen.WORKLOADS["verify"]
+    x = gen.hidden_states(wl, rep=100 + k, k=k)
+    g = run_block(B, dev_layer(wl), x)
+    r = check_parity(g, x, wl)
+    print(f"verify k={k}: U={g['n_woken']} err/rms={r:.2e}")
+
+
+@pytest.mark.parametrize("sigma", [0.0, 0.05, 0.1, 0.3, 1.0])
+def test_correlated_block_parity(B, sigma):
+    wl = gen.WORKLOADS["correlated"]
+    x = gen.hidden_states(wl, sigma=sigma)
+    g = run_block(B, dev_layer(wl), x)
+    if sigma == 0.0:
+        assert g["n_woken"] == wl.shape.top_k
+    r = check_parity(g, x, wl)
+    print(f"correlated sigma={sigma}: U={g['n_woken']} err/rms={r:.2e}")
+
+
+def test_mxfp4_layer_parity(B):
+    wl = gen.WORKLOADS["stack40_mxfp4"]
+    x = gen.hidden_states(wl)
+    g = run_block(B, dev_layer(wl, 0), x, flags=PRE | RES)
+    r = check_parity(g, x, wl, 0, flags=PRE | RES, tol=MX_TOL, compare_delta=True)
+    print(f"mxfp4 layer: U={g['n_woken']} delta err/rms={r:.2e}")
+
+
+def test_flags_without_shared_and_prenorm_only(B):
+    wl = gen.WORKLOADS["tiny"]
+    x = gen.hidden_states(wl) * 5.0
+    g = run_block(B, dev_layer(wl), x, flags=PRE)
+    check_parity(g, x, wl, flags=PRE)
+    g = run_block(B, dev_layer(wl), x, flags=RES)
+    check_parity(g, x, wl, flags=RES, compare_delta=True)
+
+
+@pytest.mark.parametrize("shape", [
+    gen.LayerShape(hidden=128, n_experts=4, top_k=4, inter=128, shared_inter=128),     # K = E, smallest H
+    gen.LayerShape(hidden=256, n_experts=512, top_k=16, inter=256, shared_inter=256),  # largest E and K
+    gen.LayerShape(hidden=1024, n_experts=64, top_k=6, inter=1024, shared_inter=0),    # I = 1024
+    gen.LayerShape(hidden=512, n_experts=32, top_k=4, inter=256, shared_inter=256, wdtype="mxfp4"),
+])
+def test_edge_shapes_parity(B, shape):
+    wl = gen.Workload("edge", shape, k=16, seed=4321)
+    from speculative_decoding_moe_amd.workloads import device
+    layer = device.make_layer(wl, 0, "cuda")
+    for k in (1, 16):
+        x = gen.hidden_states(wl, rep=k, k=k)
+        g = run_block(B, layer, x)
+        check_parity(g, x, wl, tol=MX_TOL if shape.wdtype == "mxfp4" else BF16_TOL)
+
+
+def test_determinism_and_stale_workspace(B):
+    """Bit-identical results across reruns and whatever the workspace held before (stale
+    contents never reach the MFMA tiles)."""
+    wl = gen.WORKLOADS["verify"]
+    x = gen.hidden_states(wl, rep=7)
+    layer = dev_layer(wl)
+    base = run_block(B, layer, x, ws_fill=0)
+    for fill in (0xFF, 0x80, 0x7F, 0):
+        g = run_block(B, layer, x, ws_fill=fill)
+        for key in ("y", "ids", "w"):
+            assert np.array_equal(g[key], base[key]), (fill, key)
+        assert g["n_woken"] == base["n_woken"]
+
+
+def test_block_rows_equal_single_token_runs_and_permutation(B):
+    """Batch invariance: each block row is bit-identical to that token run alone (k = 1), and
+    permuting the block permutes the rows (the greedy output cannot depend on the block)."""
+    wl = gen.WORKLOADS["verify"]
+    x = gen.hidden_states(wl, rep=8)
+    layer = dev_layer(wl)
+    blk = run_block(B, layer, x)
+    for t in (0, 6, 15):
+        one = run_block(B, layer, x[t:t + 1])
+        assert np.array_equal(one["y"][0], blk["y"][t])
+        assert np.array_equal(one["ids"][0], blk["ids"][t])
+        assert np.array_equal(one["w"][0], blk["w"][t])
+    p = np.random.default_rng(3).permutation(16)
+    pb = run_block(B, layer, x[p])
+    assert np.array_equal(pb["y"], blk["y"][p])
+    assert np.array_equal(pb["ids"], blk["ids"][p])
+    assert pb["n_woken"] == blk["n_woken"]
+
+
+def test_stack_teacher_forced_sampled_layers(B):
+    """40 stacked mxfp4 layers at full size: each sampled layer is checked on the GPU's own input
+    stream (teacher forcing), on sampled tokens, against the MoE delta."""
+    wl = gen.WORKLOADS["stack40_mxfp4"]
+    from speculative_decoding_moe_amd.workloads import device
+    x = gen.hidden_states(wl)
+    xs = [x]
+    cur = torch.from_numpy(x).cuda()
+    ws = None
+    sampled = {0, 13, 26, 39}
+    checks = {}
+    for li in range(wl.n_layers):
+        layer = device.make_layer(wl, li, "cuda")
+        if ws is None:
+            ws = torch.empty(layer.workspace_size(16), dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(cur)
+        ids = torch.empty((16, 8), dtype=torch.int32, device="cuda")
+        w = torch.empty((16, 8), dtype=torch.float32, device="cuda")
+        nw = torch.empty(4, dtype=torch.int32, device="cuda")
+        B.moe_verify_block(layer, cur, PRE | RES, y, ids, w, nw, ws)
+        torch.cuda.synchronize()
+        if li in sampled:
+            checks[li] = {"x": cur.cpu().numpy(), "y": y.cpu().numpy(), "ids": ids.cpu().numpy().astype(np.int64),
+                          "w": w.cpu().numpy(), "n_woken": int(nw[0].item())}
+        cur = y
+        del layer
+    for li, g in checks.items():
+        r = check_parity(g, g["x"], wl, li, flags=PRE | RES, tol=MX_TOL, compare_delta=True, tokens=[0, 7, 15])
+        print(f"stack layer {li}: U={g['n_woken']} delta err/rms={r:.2e}")
+
+
+def test_stack_full_stream_shallow(B):
+    """The final residual stream of a 3-layer mxfp4 stack (k = 4) against the oracle's stack."""
+    base = gen.WORKLOADS["stack40_mxfp4"]
+    wl = gen.Workload("stack3", base.shape, k=4, seed=base.seed, n_layers=3, pre_norm=True, residual=True)
+    from speculative_decoding_moe_amd.workloads import device
+    x = gen.hidden_states(wl)
+    cur = torch.from_numpy(x).cuda()
+    for li in range(3):
+        layer = device.make_layer(wl, li, "cuda")
+        ws = torch.empty(layer.workspace_size(4), dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(cur)
+        B.moe_verify_block(layer, cur, PRE | RES, y, None, None, None, ws)
+        cur = y
+    torch.cuda.synchronize()
+    ref = oracle.moe_stack(x, [GenLayer(wl, li) for li in range(3)], 8)
+    gy = cur.cpu().numpy().astype(np.float64)
+    delta_ref = ref[-1]["y"] - x
+    rms = float(np.sqrt(np.mean(delta_ref ** 2)))
+    err = float(np.abs((gy - x) - delta_ref).max())
+    assert err <= MX_TOL * rms, f"{err:.3e} vs {rms:.3e}"
+
+
+# ---------------------------------------------------------------------------------------------
+def run_accept(B, logits, draft, n_draft=None):
+    n_target, vocab = logits.shape
+    ld = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).cuda()
+    dd = torch.from_numpy(np.ascontiguousarray(draft, dtype=np.int32)).cuda() if len(draft) else \
+        torch.zeros(4, dtype=torch.int32, device="cuda")
+    tg = torch.empty(n_target, dtype=torch.int32, device="cuda")
+    acc = torch.empty(4, dtype=torch.int32, device="cuda")
+    ws = torch.empty(B.accept_prefix_workspace_size(n_target, vocab), dtype=torch.uint8, device="cuda")
+    B.accept_prefix(ld, dd, tg, acc, ws, n_draft=len(draft) if n_draft is None else n_draft)
+    torch.cuda.synchronize()
+    return tg.cpu().numpy().astype(np.int64), int(acc[0].item())
+
+
+def test_accept_prefix_geometric_drafts(B):
+    wl = gen.WORKLOADS["verify"]
+    for rep in range(6):
+        logits, planted = gen.target_logits(wl, rep=rep)
+        draft, L = gen.draft_ids(wl, planted, rep=rep)
+        tg, a = run_accept(B, logits, draft)
+        t_ref = oracle.argmax_first(logits)
+        assert np.array_equal(tg, t_ref)
+        assert a == oracle.accept_length(draft, t_ref) == L
+
+
+def test_accept_prefix_uniform_tiny(B):
+    wl = gen.WORKLOADS["tiny"]
+    logits, _ = gen.target_logits(wl)
+    draft, _ = gen.draft_ids(wl, None)
+    tg, a = run_accept(B, logits, draft)
+    assert np.array_equal(tg, oracle.argmax_first(logits))
+    assert a == oracle.accept_length(draft, tg)
+
+
+@pytest.mark.parametrize("vocab", [1, 3, 1001, 8192, 2 * 8192 + 3, 151936])
+def test_accept_prefix_edges(B, vocab):
+    rng = np.random.default_rng(vocab)
+    n_target = 17 if vocab > 1 else 2
+    logits = rng.standard_normal((n_target, vocab), dtype=np.float32)
+    # exact ties: the maximum appears twice (and at the chunk boundary when the row is long)
+    for i in range(n_target):
+        if vocab >= 3:
+            m = float(logits[i].max()) + 1.0
+            a, b = sorted(rng.choice(vocab, size=2, replace=False))
+            if vocab > 8193 and i == 0:
+                a, b = 8191, 8192
+            logits[i, a] = logits[i, b] = m
+    t_ref = oracle.argmax_first(logits)
+    full = t_ref[:n_target - 1]
+    tg, a = run_accept(B, logits, full)
+    assert np.array_equal(tg, t_ref)
+    assert a == n_target - 1
+    tg, a = run_accept(B, logits, np.array([], dtype=np.int32), n_draft=0)
+    assert np.array_equal(tg, t_ref) and a == 0
+    if n_target > 3:
+        d = full.copy()
+        d[2] = (d[2] + 1) % max(vocab, 2)
+        _, a = run_accept(B, logits, d)
+        assert a == oracle.accept_length(d, t_ref)
+    # n_draft == n_target (no bonus token) and ids outside [0, V) never match
+    d = np.concatenate([t_ref[:-1], [vocab + 5]]).astype(np.int32)
+    _, a = run_accept(B, logits, d)
+    assert a == n_target - 1
+
+
+def test_accept_prefix_max_rows(B):
+    rng = np.random.default_rng(64)
+    logits = rng.standard_normal((64, 5000), dtype=np.float32)
+    t_ref = oracle.argmax_first(logits)
+    tg, a = run_accept(B, logits, t_ref[:63])
+    assert np.array_equal(tg, t_ref) and a == 63
