@@ -119,6 +119,15 @@ int moe_verify_block(const moe_layer* layer, const float* x, int32_t k, uint32_t
                      int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
                      size_t ws_bytes, void* hip_stream);
 
+/* moe_verify_block with per-kernel timing, for profiling: the same computation and launches;
+ * additionally records events[i] (hipEvent_t created and owned by the caller; any entry may be
+ * NULL) on hip_stream at the kernel boundaries: [0] before the router kernel, [1] after it,
+ * [2] after the gate/up kernel, [3] after the down kernel, [4] after the combine. A failing
+ * event record returns MOE_ERR_HIP. */
+int moe_verify_block_timed(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
+                           int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
+                           size_t ws_bytes, void* hip_stream, void* const* events /* [5] */);
+
 /* Bytes of device workspace accept_prefix needs (0 if the sizes are invalid). Host only. */
 size_t accept_prefix_workspace_size(int32_t n_target, int32_t vocab);
 

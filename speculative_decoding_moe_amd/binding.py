@@ -18,8 +18,8 @@ MOE_ERR_WORKSPACE, MOE_ERR_ALIAS, MOE_ERR_HIP, MOE_ERR_ARG = -5, -6, -7, -8
 MOE_W_BF16, MOE_W_MXFP4 = 0, 1
 MOE_PRE_RMSNORM, MOE_RESIDUAL = 1, 2
 
-EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "accept_prefix_workspace_size",
-           "accept_prefix", "moe_status_string")
+EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "moe_verify_block_timed",
+           "accept_prefix_workspace_size", "accept_prefix", "moe_status_string")
 
 
 class MoeLayerStruct(ctypes.Structure):
@@ -49,6 +49,9 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_workspace_size.restype = sz
     lib.moe_verify_block.argtypes = [ctypes.POINTER(MoeLayerStruct), vp, i32, u32, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_verify_block.restype = ctypes.c_int
+    lib.moe_verify_block_timed.argtypes = [ctypes.POINTER(MoeLayerStruct), vp, i32, u32, vp, vp, vp, vp, vp, sz,
+                                           vp, ctypes.POINTER(vp)]
+    lib.moe_verify_block_timed.restype = ctypes.c_int
     lib.accept_prefix_workspace_size.argtypes = [i32, i32]
     lib.accept_prefix_workspace_size.restype = sz
     lib.accept_prefix.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, sz, vp]
@@ -115,6 +118,18 @@ def moe_verify_block(layer: MoeLayer, x, flags: int, y, topk_ids=None, topk_w=No
     st = lib.moe_verify_block(ctypes.byref(layer.struct), _ptr(x), k, int(flags), _ptr(y),
                               _ptr(topk_ids), _ptr(topk_w), _ptr(n_woken), _ptr(workspace),
                               ws_bytes, _stream_handle() if stream is None else stream)
+    _check(st)
+
+
+def moe_verify_block_timed(layer: MoeLayer, x, flags: int, y, events, topk_ids=None, topk_w=None,
+                           n_woken=None, workspace=None, stream=None) -> None:
+    """moe_verify_block that also records 5 caller-owned hipEvent_t handles at kernel boundaries."""
+    k = int(x.shape[0])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ev = (ctypes.c_void_p * 5)(*[e for e in events])
+    st = lib.moe_verify_block_timed(ctypes.byref(layer.struct), _ptr(x), k, int(flags), _ptr(y),
+                                    _ptr(topk_ids), _ptr(topk_w), _ptr(n_woken), _ptr(workspace),
+                                    ws_bytes, _stream_handle() if stream is None else stream, ev)
     _check(st)
 
 

@@ -837,9 +837,9 @@ size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max) {
   return make_layout(layer, k_max).total;
 }
 
-int moe_verify_block(const moe_layer* L, const float* x, int32_t k, uint32_t flags, float* y,
-                     int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
-                     size_t ws_bytes, void* hip_stream) {
+static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint32_t flags, float* y,
+                             int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
+                             size_t ws_bytes, void* hip_stream, void* const* events) {
   int st = check_layer(L);
   if (st != MOE_OK) return st;
   if (!x || !y || !workspace) return MOE_ERR_NULL;
@@ -867,11 +867,16 @@ int moe_verify_block(const moe_layer* L, const float* x, int32_t k, uint32_t fla
   const bool mx = L->wdtype == MOE_W_MXFP4;
 
   (void)hipGetLastError();  // clear a stale error so the check below reports these launches
+  auto mark = [&](int i) -> bool {
+    return !events || !events[i] || hipEventRecord((hipEvent_t)events[i], s) == hipSuccess;
+  };
+  if (!mark(0)) return MOE_ERR_HIP;
 
   RouterArgs ra;
   ra.x = x; ra.wr = L->router_w; ra.logits = (float*)(ws + lay.logits); ra.xfrag = (u32x4*)(ws + lay.xfrag);
   ra.H = H; ra.E = E; ra.k = k; ra.pre_norm = (flags & MOE_PRE_RMSNORM) ? 1 : 0; ra.eps = L->rms_eps;
   k_router<<<(E + RT_EPB - 1) / RT_EPB, RT_THREADS, 0, s>>>(ra);
+  if (!mark(1)) return MOE_ERR_HIP;
 
   GUArgs g;
   g.logits = ra.logits; g.xfrag = ra.xfrag;
@@ -885,6 +890,7 @@ int moe_verify_block(const moe_layer* L, const float* x, int32_t k, uint32_t fla
   const int cus = num_cus();
   if (H > 1024) { if (mx) launch_gateup<2, true>(g, s, cus); else launch_gateup<2, false>(g, s, cus); }
   else          { if (mx) launch_gateup<1, true>(g, s, cus); else launch_gateup<1, false>(g, s, cus); }
+  if (!mark(2)) return MOE_ERR_HIP;
 
   DNArgs d;
   d.afrag = g.afrag; d.afrag_sh = g.afrag_sh;
@@ -895,11 +901,27 @@ int moe_verify_block(const moe_layer* L, const float* x, int32_t k, uint32_t fla
   const int wpwd = L->inter == 1024 ? 2 : 1;
   if (wpwd == 1) { if (mx) launch_down<1, true>(d, s, 2 * cus); else launch_down<1, false>(d, s, 2 * cus); }
   else           { if (mx) launch_down<2, true>(d, s, 2 * cus); else launch_down<2, false>(d, s, 2 * cus); }
+  if (!mark(3)) return MOE_ERR_HIP;
 
   const int n4 = k * (H / 4);
   k_combine<<<(n4 + 255) / 256, 256, 0, s>>>(d.part, x, y, H, L->top_k, k, L->shared_inter > 0,
                                             (flags & MOE_RESIDUAL) ? 1 : 0);
+  if (!mark(4)) return MOE_ERR_HIP;
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_verify_block(const moe_layer* L, const float* x, int32_t k, uint32_t flags, float* y,
+                     int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
+                     size_t ws_bytes, void* hip_stream) {
+  return verify_block_impl(L, x, k, flags, y, topk_ids, topk_w, n_woken, workspace, ws_bytes, hip_stream,
+                           nullptr);
+}
+
+int moe_verify_block_timed(const moe_layer* L, const float* x, int32_t k, uint32_t flags, float* y,
+                           int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
+                           size_t ws_bytes, void* hip_stream, void* const* events) {
+  return verify_block_impl(L, x, k, flags, y, topk_ids, topk_w, n_woken, workspace, ws_bytes, hip_stream,
+                           events);
 }
 
 size_t accept_prefix_workspace_size(int32_t n_target, int32_t vocab) {
