@@ -1,31 +1,38 @@
 // MoE verify-block library for gfx950 (CDNA4). C ABI in include/moe_verify.h.
 //
 // One MoE layer over a speculative block of k <= 16 tokens ("Speculating on a Strix Halo",
-// sections "Speculative decoding", "What the pieces cost", "The verify's own cost"), in four
-// launches on the caller's stream:
+// sections "Speculative decoding", "What the pieces cost", "The verify's own cost") runs as four
+// stream-ordered launches; the kernel boundaries publish each phase's results to every CU:
 //
-//   k_router   fp32 router GEMV for all block tokens (W_r read once), optional RMSNorm, and the
-//              normalised block packed as bf16 hi/lo MFMA B-operand fragments.
-//   k_gateup   per workgroup: top-K + softmax per token and the woken-expert union (LDS, wave
-//              ballot + prefix count), then a grid-stride loop over (woken expert, row tile)
-//              items: each woken expert's gate/up rows are streamed from HBM exactly once
-//              (128-bit nontemporal loads) and applied to the whole block with MFMA; the SwiGLU
-//              epilogue scales by the routing weight and writes the down projection's B operand.
-//   k_down     grid-stride loop over (woken expert, row group) items: W_down streamed once, MFMA
-//              against that expert's activations, per-(token, slot) partial rows.
-//   k_combine  y[t] = sum_j P[t, j] + P[t, shared] (+ x[t]) in fixed order.
+//   k_router    (expert tile, H slice) items: fp32 MFMA partial logits and sums of squares; the
+//               block is also packed as bf16 hi/lo MFMA B-operand fragments.
+//   k_gateup    every workgroup first computes the routing in LDS: RMSNorm factor, logits, top-K
+//               per token (ties to the lower expert), softmax over the K, the woken-expert union
+//               (wave ballot + prefix count) and the weight table. Then (woken expert, row tile)
+//               items, assigned statically and balanced: the expert's gate and up rows are
+//               streamed from HBM once (128-bit nontemporal loads, the next item prefetched) and
+//               applied to all 16 token columns with MFMA; SwiGLU, the routing weight and the
+//               hi/lo split are fused into the epilogue, which writes the down B operand.
+//   k_down      (woken expert, row group) items: W_down streamed once, partial rows per (token,
+//               slot).
+//   k_combine   y[t] = sum_j P[t, j] + P[t, shared] (+ x[t]), fixed slot order.
+//
+// Kernel boundaries are the cheapest way to publish data across the XCDs' separate L2 caches on
+// this part (a grid barrier needs agent-scope fences, measured several times dearer), so no kernel
+// waits on another workgroup.
 //
 // Tokens are the MFMA N dimension (16 columns; unused columns are explicit zeros written every
 // call), expert rows the M dimension, the hidden / intermediate size the K dimension. MFMA work
-// is free next to the HBM stream, so every expert is applied to all 16 columns and columns of
-// tokens not routed to it carry weight 0. Activations enter MFMA as a bf16 hi + lo pair, which
-// keeps the products at ~2^-17 relative precision at the cost of a second MFMA per tile.
+// is free next to the HBM stream, so every expert is applied to all 16 columns; columns of tokens
+// not routed to it carry weight 0. Activations enter MFMA as bf16 hi + lo pairs (~2^-17 relative).
 //
-// K-index mapping used by every MFMA tile: the reduction dimension is cut into windows of 128;
-// in window w, k-step j (0..3), lane l = c + 16 q (c = row or token column, q = 0..3) holds the
-// 8 values at offsets 128 w + 32 q + 8 j + (0..7). A lane's four k-steps of one window are 64
-// contiguous bf16 bytes, or one 32-value mxfp4 block with a single scale byte.
+// K-index mapping of every MFMA tile: the reduction dimension is cut into windows of 128; in
+// window w, k-step j (0..3), lane l = c + 16 q (c = row or token column, q = 0..3) holds the 8
+// values at 128 w + 32 j + 8 q + (0..7) for bf16 layers (a lane quad reads 64 contiguous bytes
+// per row and instruction) and at 128 w + 32 q + 8 j + (0..7) for mxfp4 layers (a lane holds one
+// whole 32-value block and its single scale byte).
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <stdint.h>
 #include <string.h>
 
@@ -33,22 +40,21 @@
 
 namespace {
 
-constexpr int KMAX = 16;       // block tokens = MFMA N
-constexpr int WIN = 128;       // reduction window
-constexpr int GU_WAVES = 8;    // gate/up workgroup = 512 threads, WPW 128-windows of H per wave
-constexpr int DN_WAVES = 4;    // down workgroup = 256 threads
-constexpr int RT_EPB = 4;      // router: experts per workgroup
+constexpr int KMAX = 16;          // block tokens = MFMA N
+constexpr int WIN = 128;          // reduction window
+constexpr int NW = 8;             // waves per workgroup
+constexpr int NTH = NW * 64;      // threads per workgroup
 constexpr int MAX_E = 512;
 constexpr int MAX_K = 16;
-constexpr int GU_MX_RT = 2;    // gate/up row tiles per mxfp4 item (bf16 items: 1)
-constexpr int DN_RT_BF = 8;    // down row tiles per bf16 item (divided by windows per wave)
-constexpr int DN_RT_MX = 16;   // down row tiles per mxfp4 item (divided by windows per wave)
-constexpr int AM_CHUNK = 8192; // argmax values per workgroup
+constexpr int MAX_U = KMAX * MAX_K;  // woken experts at most
+constexpr int GU_MX_RT = 2;       // gate/up row tiles per mxfp4 item (bf16: 1)
+constexpr int CG = 64;            // combine row group
+constexpr int AM_CHUNK = 8192;    // argmax values per workgroup
+
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -72,6 +78,10 @@ __device__ __forceinline__ void split_bf16(float f, uint32_t& hi, uint32_t& lo) 
   lo = bf16_rne(f - __uint_as_float(hi << 16));
 }
 
+__device__ __forceinline__ void pack8(const uint32_t (&v)[8], u32x4& o) {
+  o.x = v[0] | (v[1] << 16); o.y = v[2] | (v[3] << 16); o.z = v[4] | (v[5] << 16); o.w = v[6] | (v[7] << 16);
+}
+
 // Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) -> eight bf16 scaled by
 // `scale` (a power of two built from the e8m0 byte).
 __device__ __forceinline__ u32x4 dec_fp4x8(uint32_t c, float scale) {
@@ -86,6 +96,10 @@ __device__ __forceinline__ float e8m0_scale(uint32_t byte) { return __uint_as_fl
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Offset (in values) of lane quad q, k-step j inside a 128-wide window.
+template <bool NAT>
+__device__ __forceinline__ int kofs(int j, int q) { return NAT ? 32 * j + 8 * q : 32 * q + 8 * j; }
+
 // (value, index) maximum with equal values going to the lower index.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
   if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
@@ -98,362 +112,148 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
     argmax_merge(v, i, ov, oi);
   }
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
 
-// ------------------------------------------------------------------------------------------
-// workspace layout (host and device agree through the offsets passed in the kernel args)
-// ------------------------------------------------------------------------------------------
-struct Layout {
-  size_t xfrag, logits, tab_n, tab_woken, tab_slot, afrag, afrag_sh, part, total;
-  int umax;
-};
-
-inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
-
-Layout make_layout(const moe_layer* L, int k) {
-  Layout o;
-  const size_t H = L->hidden, E = L->n_experts, K = L->top_k, I = L->inter, Is = L->shared_inter;
-  o.umax = (int)((E < (size_t)KMAX * K) ? E : (size_t)KMAX * K);
-  size_t off = 0;
-  o.xfrag = off;     off = align256(off + H * 64);               // (H/32) k-steps x hi/lo x 64 lanes x 16 B
-  o.logits = off;    off = align256(off + (size_t)KMAX * E * 4);
-  o.tab_n = off;     off = align256(off + 16);
-  o.tab_woken = off; off = align256(off + (size_t)o.umax * 4);
-  o.tab_slot = off;  off = align256(off + (size_t)o.umax * KMAX);
-  o.afrag = off;     off = align256(off + (size_t)o.umax * I * 64);
-  o.afrag_sh = off;  off = align256(off + Is * 64);
-  o.part = off;      off = align256(off + (size_t)k * (K + 1) * H * 4);
-  o.total = off;
-  return o;
-}
-
-// ------------------------------------------------------------------------------------------
-// k_router: logits[t][e] = rinv_t * sum_h x[t][h] W_r[e][h]  (fp32), rinv_t = 1 or the RMSNorm
-// factor; also packs x_hat = rinv_t * x[t] into the gate/up B-operand fragments.
-// ------------------------------------------------------------------------------------------
-struct RouterArgs {
+struct Args {
   const float* x;
-  const float* wr;
-  float* logits;
-  u32x4* xfrag;
-  int H, E, k;
-  int pre_norm;
-  float eps;
-};
-
-constexpr int RT_THREADS = 256;
-constexpr int RT_MAXC = 2048 / 4 / RT_THREADS;  // float4 chunks per thread per row (H <= 2048)
-
-__global__ void __launch_bounds__(RT_THREADS) k_router(RouterArgs a) {
-  __shared__ float s_part[RT_THREADS / 64][KMAX * (RT_EPB + 1)];
-  __shared__ float s_rinv[KMAX];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  const int H4 = a.H / 4, k = a.k;
-  const int e0 = blockIdx.x * RT_EPB;
-
-  float4 w[RT_EPB][RT_MAXC];
-#pragma unroll
-  for (int e = 0; e < RT_EPB; ++e)
-#pragma unroll
-    for (int c = 0; c < RT_MAXC; ++c) {
-      int col = tid + c * RT_THREADS;
-      w[e][c] = (e0 + e < a.E && col < H4)
-                    ? reinterpret_cast<const float4*>(a.wr + (size_t)(e0 + e) * a.H)[col]
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-  float acc[KMAX][RT_EPB + 1];  // [.][RT_EPB] holds the sum of squares
-#pragma unroll
-  for (int t = 0; t < KMAX; ++t) {
-#pragma unroll
-    for (int e = 0; e <= RT_EPB; ++e) acc[t][e] = 0.f;
-    if (t < k) {
-#pragma unroll
-      for (int c = 0; c < RT_MAXC; ++c) {
-        int col = tid + c * RT_THREADS;
-        if (col < H4) {
-          float4 xv = reinterpret_cast<const float4*>(a.x + (size_t)t * a.H)[col];
-#pragma unroll
-          for (int e = 0; e < RT_EPB; ++e)
-            acc[t][e] += w[e][c].x * xv.x + w[e][c].y * xv.y + w[e][c].z * xv.z + w[e][c].w * xv.w;
-          acc[t][RT_EPB] += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < KMAX; ++t)
-#pragma unroll
-    for (int e = 0; e <= RT_EPB; ++e) {
-      float v = wave_sum(acc[t][e]);
-      if (lane == 0) s_part[wave][t * (RT_EPB + 1) + e] = v;
-    }
-  __syncthreads();
-  if (tid < KMAX * (RT_EPB + 1)) {
-    float v = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < RT_THREADS / 64; ++wv) v += s_part[wv][tid];
-    s_part[0][tid] = v;
-  }
-  __syncthreads();
-  if (tid < KMAX) {
-    float ss = s_part[0][tid * (RT_EPB + 1) + RT_EPB];
-    s_rinv[tid] = a.pre_norm ? 1.0f / sqrtf(ss / (float)a.H + a.eps) : 1.0f;
-  }
-  __syncthreads();
-  if (tid < k * RT_EPB) {
-    int t = tid / RT_EPB, e = tid % RT_EPB;
-    if (e0 + e < a.E) a.logits[(size_t)t * a.E + e0 + e] = s_rinv[t] * s_part[0][t * (RT_EPB + 1) + e];
-  }
-  // B-operand fragments of x_hat: k-steps s = blockIdx.x, blockIdx.x + gridDim.x, ...
-  const int nsteps = a.H / 32;
-  for (int s = blockIdx.x; s < nsteps; s += gridDim.x) {
-    if (tid < 64) {
-      const int t = tid & 15, q = tid >> 4, w = s >> 2, j = s & 3;
-      uint32_t hi[8], lo[8];
-      if (t < k) {
-        const float* src = a.x + (size_t)t * a.H + w * WIN + 32 * q + 8 * j;
-        float4 v0 = *reinterpret_cast<const float4*>(src);
-        float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-        float r = s_rinv[t];
-        float f[8] = {v0.x * r, v0.y * r, v0.z * r, v0.w * r, v1.x * r, v1.y * r, v1.z * r, v1.w * r};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) split_bf16(f[i], hi[i], lo[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hi[i] = lo[i] = 0u;
-      }
-      u32x4 h, l;
-      h.x = hi[0] | (hi[1] << 16); h.y = hi[2] | (hi[3] << 16); h.z = hi[4] | (hi[5] << 16); h.w = hi[6] | (hi[7] << 16);
-      l.x = lo[0] | (lo[1] << 16); l.y = lo[2] | (lo[3] << 16); l.z = lo[4] | (lo[5] << 16); l.w = lo[6] | (lo[7] << 16);
-      a.xfrag[((size_t)s * 2 + 0) * 64 + tid] = h;
-      a.xfrag[((size_t)s * 2 + 1) * 64 + tid] = l;
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// k_gateup: routing prologue, then (woken expert, row tile) items. Wave w owns H-window w.
-// ------------------------------------------------------------------------------------------
-struct GUArgs {
-  const float* logits;
-  const u32x4* xfrag;
-  const uint8_t* wg;   // routed gate (bf16 or fp4 codes)
-  const uint8_t* wu;
-  const uint8_t* sg;   // routed scales (mxfp4)
-  const uint8_t* su;
-  const uint8_t* shg;  // shared gate/up (bf16)
-  const uint8_t* shu;
-  u32x4* afrag;
-  u32x4* afrag_sh;
-  int32_t* tab_n;
-  int32_t* tab_woken;
-  int8_t* tab_slot;
+  float* y;
   int32_t* out_ids;
   float* out_w;
   int32_t* out_n;
-  int H, E, K, I, Is, k;
-};
-
-// One item's weights for one wave (its WPW windows of H).
-//   bf16 item:  v[(wi * 2 + mat) * 4 + j] = 8 values of k-step j     (64 B per lane, window, matrix)
-//   mxfp4 item: v[(tile * WPW + wi) * 2 + mat] = 32 codes, sc[...] = their e8m0 scale byte
-template <int WPW>
-struct GUItem {
-  u32x4 v[WPW * 8];
-  uint32_t sc[GU_MX_RT * WPW * 2];
-};
-
-struct GUDesc {
-  int routed, u, row0, mx, ntile;
-  const uint8_t* g;
-  const uint8_t* up;
+  const float* wr;
+  const uint8_t* wg;
+  const uint8_t* wu;
+  const uint8_t* wd;
   const uint8_t* sg;
   const uint8_t* su;
+  const uint8_t* sd;
+  const uint8_t* shg;
+  const uint8_t* shu;
+  const uint8_t* shd;
+  int32_t* tab_n;     // U
+  int32_t* tab_woken; // [umax] woken expert ids, ascending
+  int8_t* tab_slot;   // [umax][16] slot of token t for woken expert u, or -1
+  u32x4* xfrag;   // (H/32) k-steps x {hi, lo} x 64 lanes
+  float* plog;    // [hs][16][E] partial raw logits
+  float* psq;     // [hs][16] partial sums of squares
+  u32x4* afrag;   // [umax][(I/32) x {hi, lo} x 64 lanes]
+  u32x4* afrag_sh;
+  float* part;    // [k][K+1][H]
+  int H, E, K, I, Is, k, hs, ntile_e, umax, pre_norm, residual;
+  float eps;
 };
 
-__device__ __forceinline__ GUDesc gu_desc(const GUArgs& a, int item, int n_routed, int ipe, int U,
-                                          const int* woken, bool MX) {
-  GUDesc d;
-  d.routed = item < n_routed;
-  d.u = d.routed ? item / ipe : U;
-  d.mx = MX && d.routed;
-  d.ntile = d.mx ? GU_MX_RT : 1;
-  d.row0 = (d.routed ? item % ipe : item - n_routed) * 16 * d.ntile;
-  const size_t H = a.H, I = a.I;
-  if (d.routed) {
-    const size_t e = (size_t)__builtin_amdgcn_readfirstlane(woken[d.u]);
-    if (d.mx) {
-      d.g = a.wg + e * I * (H / 2); d.up = a.wu + e * I * (H / 2);
-      d.sg = a.sg + e * I * (H / 32); d.su = a.su + e * I * (H / 32);
-    } else {
-      d.g = a.wg + e * I * H * 2; d.up = a.wu + e * I * H * 2;
-      d.sg = d.su = nullptr;
-    }
-  } else {
-    d.g = a.shg; d.up = a.shu; d.sg = d.su = nullptr;
-  }
-  return d;
-}
-
-template <int WPW>
-__device__ __forceinline__ void gu_load(GUItem<WPW>& T, const GUDesc& d, int H, int win0, int lane) {
-  const int q = lane >> 4, r = lane & 15;
-  if (d.mx) {
-    const size_t base = ((size_t)d.row0 + r) * (H / 2) + (size_t)win0 * 64 + 16 * q;
-    const size_t sbase = ((size_t)d.row0 + r) * (H / 32) + (size_t)win0 * 4 + q;
-#pragma unroll
-    for (int tl = 0; tl < GU_MX_RT; ++tl)
-#pragma unroll
-      for (int wi = 0; wi < WPW; ++wi) {
-        const size_t off = base + (size_t)tl * 16 * (H / 2) + wi * 64;
-        const size_t soff = sbase + (size_t)tl * 16 * (H / 32) + wi * 4;
-        T.v[(tl * WPW + wi) * 2 + 0] = ld_stream(d.g + off);
-        T.v[(tl * WPW + wi) * 2 + 1] = ld_stream(d.up + off);
-        T.sc[(tl * WPW + wi) * 2 + 0] = d.sg[soff];
-        T.sc[(tl * WPW + wi) * 2 + 1] = d.su[soff];
-      }
-  } else {
-    const size_t off = (((size_t)d.row0 + r) * H + (size_t)win0 * WIN + 32 * q) * 2;
-#pragma unroll
-    for (int wi = 0; wi < WPW; ++wi)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        T.v[(wi * 2 + 0) * 4 + j] = ld_stream(d.g + off + wi * WIN * 2 + 16 * j);
-        T.v[(wi * 2 + 1) * 4 + j] = ld_stream(d.up + off + wi * WIN * 2 + 16 * j);
-      }
-  }
-}
-
-struct alignas(16) GUShared {
-  float red[GU_WAVES][GU_MX_RT][2][256];  // per-wave partial tiles
-  float act[GU_MX_RT][256];               // reduced, activated tiles
+struct alignas(16) Smem {
+  float red[16384];           // per-wave partial tiles (gate/up, down)
+  float act[GU_MX_RT][256];   // reduced, activated gate/up tiles
   int ids[KMAX][MAX_K];
   float val[KMAX][MAX_K];
   float w[KMAX][MAX_K];
   uint8_t flag[MAX_E];
   int pos[MAX_E];
-  int woken[KMAX * MAX_K];
-  float wcol[KMAX * MAX_K + 1][KMAX];
-  int8_t slot[KMAX * MAX_K][KMAX];
+  int woken[MAX_U];
+  float wcol[MAX_U + 1][KMAX];
+  int8_t slot[MAX_U][KMAX];
+  float rinv[KMAX];
   int nw;
 };
 
-// MFMA of one item, cross-wave reduction, SwiGLU, weight, hi/lo split, store as down-projection
-// B fragments. Contains two workgroup barriers.
-template <int WPW>
-__device__ __forceinline__ void gu_process(const GUArgs& a, GUShared& S, const GUItem<WPW>& T,
-                                           const GUDesc& d, const u32x4 (&xb)[WPW][4][2], bool active,
-                                           int wave, int lane, int tid) {
-  f32x4 acc[GU_MX_RT][2];
+// ------------------------------------------------------------------------------------------
+// router item (expert tile, H slice) with fp32 MFMA 16x16x4
+// ------------------------------------------------------------------------------------------
+struct RouterSmem {
+  float red[NW * 256];
+  float rsq[NW][64];
+};
+
+template <bool NAT>
+__device__ void router_item(const Args& a, RouterSmem& S, int r, int wave, int lane, int tid) {
+  const int H = a.H, E = a.E, k = a.k;
+  const int tile = r % a.ntile_e, hsi = r / a.ntile_e;
+  const int cpw = H / (a.hs * NW);  // columns per wave, a multiple of 16
+  const int c0 = hsi * (H / a.hs) + wave * cpw;
+  const int row = lane & 15, q = lane >> 4;
+  const int e = tile * 16 + row;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  const float* wrow = a.wr + (size_t)(e < E ? e : 0) * H;
+  const float* xrow = a.x + (size_t)(row < k ? row : 0) * H;
+  for (int m = 0; m < cpw / 16; ++m) {
+    const int h = c0 + 16 * m + 4 * q;
+    float4 wv = *reinterpret_cast<const float4*>(wrow + h);
+    float4 xv = *reinterpret_cast<const float4*>(xrow + h);
+    if (e >= E) wv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row >= k) xv = make_float4(0.f, 0.f, 0.f, 0.f);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.x, xv.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.y, xv.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.z, xv.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.w, xv.w, acc, 0, 0, 0);
+    ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+  }
+  *reinterpret_cast<f32x4*>(&S.red[wave * 256 + lane * 4]) = acc;
+  S.rsq[wave][lane] = ss;
+  __syncthreads();
+  if (tid < 256) {
+    // D[i][j]: lane j + 16 (i / 4), element i % 4; i = expert within the tile, j = token
+    float d = 0.f;
 #pragma unroll
-  for (int tl = 0; tl < GU_MX_RT; ++tl) acc[tl][0] = acc[tl][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (active) {
-    if (d.mx) {
+    for (int w = 0; w < NW; ++w) d += S.red[w * 256 + tid];
+    const int l = tid >> 2, v = tid & 3;
+    const int t = l & 15, ei = tile * 16 + 4 * (l >> 4) + v;
+    if (t < k && ei < E) a.plog[((size_t)hsi * KMAX + t) * E + ei] = d;
+  }
+  if (tile == 0 && tid < KMAX) {
+    float s = 0.f;
+    for (int w = 0; w < NW; ++w)
+      for (int qq = 0; qq < 4; ++qq) s += S.rsq[w][tid + 16 * qq];
+    a.psq[hsi * KMAX + tid] = s;
+  }
+  // B-operand fragments of the raw block: k-steps s = r + nr * (tid / 64) + 8 nr * i
+  const int nr = a.ntile_e * a.hs;
+  for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) {
+    const int t = lane & 15, qq = lane >> 4, w = s >> 2, j = s & 3;
+    uint32_t hi[8], lo[8];
+    if (t < k) {
+      const float* src = a.x + (size_t)t * H + w * WIN + kofs<NAT>(j, qq);
+      const float4 v0 = *reinterpret_cast<const float4*>(src);
+      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int tl = 0; tl < GU_MX_RT; ++tl)
-#pragma unroll
-        for (int wi = 0; wi < WPW; ++wi)
-#pragma unroll
-          for (int mat = 0; mat < 2; ++mat) {
-            const u32x4 c = T.v[(tl * WPW + wi) * 2 + mat];
-            const float sc = e8m0_scale(T.sc[(tl * WPW + wi) * 2 + mat]);
-            const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const u32x4 av = dec_fp4x8(cw[j], sc);
-              acc[tl][mat] = mfma16(av, xb[wi][j][0], acc[tl][mat]);
-              acc[tl][mat] = mfma16(av, xb[wi][j][1], acc[tl][mat]);
-            }
-          }
+      for (int i = 0; i < 8; ++i) split_bf16(f[i], hi[i], lo[i]);
     } else {
 #pragma unroll
-      for (int wi = 0; wi < WPW; ++wi)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int mat = 0; mat < 2; ++mat) {
-            acc[0][mat] = mfma16(T.v[(wi * 2 + mat) * 4 + j], xb[wi][j][0], acc[0][mat]);
-            acc[0][mat] = mfma16(T.v[(wi * 2 + mat) * 4 + j], xb[wi][j][1], acc[0][mat]);
-          }
+      for (int i = 0; i < 8; ++i) hi[i] = lo[i] = 0u;
     }
-  }
-  // D[r][c] of a tile: lane c + 16 (r / 4), element r % 4  ->  red[...][lane * 4 + element]
-#pragma unroll
-  for (int tl = 0; tl < GU_MX_RT; ++tl)
-    if (tl < d.ntile) {
-      *reinterpret_cast<f32x4*>(&S.red[wave][tl][0][lane * 4]) = acc[tl][0];
-      *reinterpret_cast<f32x4*>(&S.red[wave][tl][1][lane * 4]) = acc[tl][1];
-    }
-  __syncthreads();
-  for (int i = tid; i < d.ntile * 256; i += GU_WAVES * 64) {
-    const int tl = i >> 8, p = i & 255;
-    float g = 0.f, up = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < GU_WAVES; ++wv) {
-      g += S.red[wv][tl][0][p];
-      up += S.red[wv][tl][1][p];
-    }
-    const int c = (p >> 2) & 15;
-    S.act[tl][p] = silu(g) * up * S.wcol[d.u][c];
-  }
-  __syncthreads();
-  // thread (tile, half, column c) -> rows R .. R+7 of the expert's intermediate dimension
-  if (tid < d.ntile * 2 * KMAX) {
-    const int tl = tid / (2 * KMAX), half = (tid / KMAX) & 1, c = tid % KMAX;
-    uint32_t hi[8], lo[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = half * 8 + i;
-      split_bf16(S.act[tl][(c + 16 * (r >> 2)) * 4 + (r & 3)], hi[i], lo[i]);
-    }
-    const int R = d.row0 + 16 * tl + 8 * half;
-    const int w = R / WIN, q = (R % WIN) / 32, j = (R % 32) / 8;
-    const int s = w * 4 + j;
-    u32x4* dst = d.routed ? a.afrag + (size_t)d.u * (a.I / 32) * 128 : a.afrag_sh;
     u32x4 h, l;
-    h.x = hi[0] | (hi[1] << 16); h.y = hi[2] | (hi[3] << 16); h.z = hi[4] | (hi[5] << 16); h.w = hi[6] | (hi[7] << 16);
-    l.x = lo[0] | (lo[1] << 16); l.y = lo[2] | (lo[3] << 16); l.z = lo[4] | (lo[5] << 16); l.w = lo[6] | (lo[7] << 16);
-    dst[((size_t)s * 2 + 0) * 64 + c + 16 * q] = h;
-    dst[((size_t)s * 2 + 1) * 64 + c + 16 * q] = l;
+    pack8(hi, h);
+    pack8(lo, l);
+    a.xfrag[((size_t)s * 2 + 0) * 64 + lane] = h;
+    a.xfrag[((size_t)s * 2 + 1) * 64 + lane] = l;
   }
 }
 
-template <int WPW, bool MX>
-__global__ void __launch_bounds__(GU_WAVES * 64) k_gateup(GUArgs a) {
-  __shared__ GUShared S;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  const int E = a.E, K = a.K, k = a.k, H = a.H;
-  // H is a multiple of 128 * WPW, so a wave's windows all exist or none does
-  const int win0 = wave * WPW;
-  const bool active = win0 < H / WIN;
-
-  // B fragments of this wave's windows, used by every item.
-  u32x4 xb[WPW][4][2];
-#pragma unroll
-  for (int wi = 0; wi < WPW; ++wi)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int hl = 0; hl < 2; ++hl)
-        xb[wi][j][hl] = active ? ld16(a.xfrag + ((size_t)((win0 + wi) * 4 + j) * 2 + hl) * 64 + lane)
-                               : u32x4{0u, 0u, 0u, 0u};
-
-  // ---- routing: top-K per token (one wave per token), softmax over the K, union ----
-  for (int i = tid; i < MAX_E; i += GU_WAVES * 64) S.flag[i] = 0;
-  for (int t = wave; t < k; t += GU_WAVES) {
+// ------------------------------------------------------------------------------------------
+// routing (every gate/up workgroup, into LDS)
+// ------------------------------------------------------------------------------------------
+__device__ void route(const Args& a, Smem& S, int wave, int lane, int tid) {
+  const int E = a.E, K = a.K, k = a.k, hs = a.hs;
+  if (tid < KMAX) {
+    float ssq = 0.f;
+    for (int i = 0; i < hs; ++i) ssq += a.psq[i * KMAX + tid];
+    S.rinv[tid] = a.pre_norm ? 1.0f / sqrtf(ssq / (float)a.H + a.eps) : 1.0f;
+  }
+  for (int i = tid; i < MAX_E; i += NTH) S.flag[i] = 0;
+  __syncthreads();
+  for (int t = wave; t < k; t += NW) {
     float v[MAX_E / 64];
     uint32_t taken = 0;
+    const float rv = S.rinv[t];
 #pragma unroll
     for (int m = 0; m < MAX_E / 64; ++m) {
       const int e = lane + 64 * m;
-      v[m] = (e < E) ? a.logits[(size_t)t * E + e] : 0.f;
+      float s = 0.f;
+      if (e < E)
+        for (int i = 0; i < hs; ++i) s += a.plog[((size_t)i * KMAX + t) * E + e];
+      v[m] = rv * s;
       if (e >= E) taken |= 1u << m;
     }
     for (int j = 0; j < K; ++j) {
@@ -490,8 +290,8 @@ __global__ void __launch_bounds__(GU_WAVES * 64) k_gateup(GUArgs a) {
     if (lane == 0) S.nw = base;
   }
   __syncthreads();
-  const int U = __builtin_amdgcn_readfirstlane(S.nw);
-  for (int i = tid; i < (U + 1) * KMAX; i += GU_WAVES * 64) {
+  const int U = S.nw;
+  for (int i = tid; i < (U + 1) * KMAX; i += NTH) {
     S.wcol[i / KMAX][i % KMAX] = 0.f;
     if (i < U * KMAX) S.slot[i / KMAX][i % KMAX] = -1;
   }
@@ -504,211 +304,520 @@ __global__ void __launch_bounds__(GU_WAVES * 64) k_gateup(GUArgs a) {
   }
   if (tid < KMAX) S.wcol[U][tid] = (tid < k) ? 1.0f : 0.f;  // shared expert column weights
   __syncthreads();
-  if (blockIdx.x == 0) {
+  if (blockIdx.x == 0) {  // outputs, and the tables the down kernel reads
     if (tid < k * K) {
       const int t = tid / K, j = tid % K;
       if (a.out_ids) a.out_ids[t * K + j] = S.ids[t][j];
       if (a.out_w) a.out_w[t * K + j] = S.w[t][j];
     }
     if (tid == 0) {
-      a.tab_n[0] = U;
       if (a.out_n) a.out_n[0] = U;
+      a.tab_n[0] = U;
     }
-    for (int i = tid; i < U; i += GU_WAVES * 64) a.tab_woken[i] = S.woken[i];
-    for (int i = tid; i < U * KMAX; i += GU_WAVES * 64) a.tab_slot[i] = S.slot[i / KMAX][i % KMAX];
-  }
-
-  // ---- expert items, next item's weights prefetched while the current one is reduced ----
-  const int ipe = a.I / (16 * (MX ? GU_MX_RT : 1));  // items per routed expert
-  const int n_routed = U * ipe;
-  const int n_items = n_routed + a.Is / 16;
-  int item = blockIdx.x;
-  GUItem<WPW> T0, T1;
-  GUDesc d0, d1;
-  if (item < n_items) {
-    d0 = gu_desc(a, item, n_routed, ipe, U, S.woken, MX);
-    if (active) gu_load<WPW>(T0, d0, H, win0, lane);
-  }
-  while (item < n_items) {
-    int nxt = item + gridDim.x;
-    if (nxt < n_items) {
-      d1 = gu_desc(a, nxt, n_routed, ipe, U, S.woken, MX);
-      if (active) gu_load<WPW>(T1, d1, H, win0, lane);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // the next item's loads stay ahead of this item's math
-    gu_process<WPW>(a, S, T0, d0, xb, active, wave, lane, tid);
-    item = nxt;
-    if (item >= n_items) break;
-    nxt = item + gridDim.x;
-    if (nxt < n_items) {
-      d0 = gu_desc(a, nxt, n_routed, ipe, U, S.woken, MX);
-      if (active) gu_load<WPW>(T0, d0, H, win0, lane);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    gu_process<WPW>(a, S, T1, d1, xb, active, wave, lane, tid);
-    item = nxt;
+    for (int i = tid; i < U; i += NTH) a.tab_woken[i] = S.woken[i];
+    for (int i = tid; i < U * KMAX; i += NTH) a.tab_slot[i] = S.slot[i / KMAX][i % KMAX];
   }
 }
 
 // ------------------------------------------------------------------------------------------
-// k_down: P[t][slot][h] = sum_i W_down[e][h][i] * A'[e][t][i] for tokens routed to e.
-// Wave w owns I-windows w*WPWD .. w*WPWD+WPWD-1; an item is (woken expert, group of row tiles).
+// gate/up items. Wave w owns H-windows w*WPW .. w*WPW+WPW-1.
 // ------------------------------------------------------------------------------------------
-struct DNArgs {
-  const u32x4* afrag;
-  const u32x4* afrag_sh;
-  const uint8_t* wd;
-  const uint8_t* sd;
-  const uint8_t* shd;
-  const int32_t* tab_n;
-  const int32_t* tab_woken;
-  const int8_t* tab_slot;
-  float* part;
-  int H, E, K, I, Is, k;
+template <int WPW>
+struct GUItem {
+  u32x4 v[WPW * 8];                // bf16: [(wi*2 + mat)*4 + j]; mxfp4: [(tile*WPW + wi)*2 + mat]
+  uint32_t sc[GU_MX_RT * WPW * 2];
 };
 
-template <int WPWD, bool MX>
-__global__ void __launch_bounds__(DN_WAVES * 64) k_down(DNArgs a) {
-  constexpr int RT_BF = DN_RT_BF / WPWD;  // row tiles per bf16 item
-  constexpr int RT_MX = DN_RT_MX / WPWD;  // row tiles per mxfp4 item
-  constexpr int RT_ACC = MX ? RT_MX : RT_BF;
-  __shared__ __attribute__((aligned(16))) float red[DN_WAVES][RT_ACC][256];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  const int H = a.H, I = a.I, K = a.K, k = a.k;
-  const int U = a.tab_n[0];
-  const int ipe = H / (16 * (MX ? RT_MX : RT_BF));
-  const int n_routed = U * ipe;
-  const int n_items = n_routed + (a.Is > 0 ? H / (16 * RT_BF) : 0);
-  const int q = lane >> 4, r16 = lane & 15;
-  // I (== Is when there is a shared expert) is 128 * 2^n, so a wave's WPWD windows all exist or
-  // none does.
-  const bool active = wave * WPWD < I / WIN;
-  const int win0 = wave * WPWD;
+struct GUDesc {
+  int u, row0, ntile;
+  const uint8_t* g;
+  const uint8_t* up;
+  const uint8_t* sg;
+  const uint8_t* su;
+};
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const bool routed = item < n_routed;
-    const int u = routed ? item / ipe : U;
-    const bool mx_item = MX && routed;
-    const int ntile = mx_item ? RT_MX : RT_BF;
-    const int row0 = (routed ? item % ipe : item - n_routed) * 16 * ntile;
-    const u32x4* af = routed ? a.afrag + (size_t)u * (I / 32) * 128 : a.afrag_sh;
-
-    f32x4 acc[RT_ACC];
+// bf16 item (16 rows from g / up): lane (r, q) reads 16 B per k-step of each of its windows
+template <int WPW, bool NAT>
+__device__ __forceinline__ void gu_load_bf16(GUItem<WPW>& T, const uint8_t* g, const uint8_t* up, int H,
+                                             int win0, int lane) {
+  const int q = lane >> 4, r = lane & 15;
+  const uint32_t lo = (uint32_t)(r * H + win0 * WIN) * 2u;
 #pragma unroll
-    for (int tl = 0; tl < RT_ACC; ++tl) acc[tl] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    if (active) {
-      u32x4 bf[WPWD][4][2];
+  for (int wi = 0; wi < WPW; ++wi)
 #pragma unroll
-      for (int wi = 0; wi < WPWD; ++wi)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int hl = 0; hl < 2; ++hl)
-            bf[wi][j][hl] = ld16(af + ((size_t)((win0 + wi) * 4 + j) * 2 + hl) * 64 + lane);
-      if (mx_item) {
-        u32x4 v[RT_MX * WPWD];
-        uint32_t sc[RT_MX * WPWD];
-        const size_t e = (size_t)a.tab_woken[u];
-        const uint8_t* w = a.wd + e * H * (I / 2) + (size_t)(row0 + r16) * (I / 2) + (size_t)win0 * 64 + 16 * q;
-        const uint8_t* sw = a.sd + e * H * (I / 32) + (size_t)(row0 + r16) * (I / 32) + (size_t)win0 * 4 + q;
-#pragma unroll
-        for (int tl = 0; tl < RT_MX; ++tl)
-#pragma unroll
-          for (int wi = 0; wi < WPWD; ++wi) {
-            v[tl * WPWD + wi] = ld_stream(w + (size_t)tl * 16 * (I / 2) + wi * 64);
-            sc[tl * WPWD + wi] = sw[(size_t)tl * 16 * (I / 32) + wi * 4];
-          }
-        __builtin_amdgcn_sched_barrier(0);  // keep every load of the item ahead of the math
-#pragma unroll
-        for (int tl = 0; tl < RT_MX; ++tl)
-#pragma unroll
-          for (int wi = 0; wi < WPWD; ++wi) {
-            const u32x4 c = v[tl * WPWD + wi];
-            const float s = e8m0_scale(sc[tl * WPWD + wi]);
-            const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const u32x4 av = dec_fp4x8(cw[j], s);
-              acc[tl] = mfma16(av, bf[wi][j][0], acc[tl]);
-              acc[tl] = mfma16(av, bf[wi][j][1], acc[tl]);
-            }
-          }
-      } else {
-        u32x4 v[RT_BF * WPWD * 4];
-        const uint8_t* w = (routed ? a.wd + (size_t)a.tab_woken[u] * H * I * 2 : a.shd) +
-                           ((size_t)(row0 + r16) * I + (size_t)win0 * WIN + 32 * q) * 2;
-#pragma unroll
-        for (int tl = 0; tl < RT_BF; ++tl)
-#pragma unroll
-          for (int wi = 0; wi < WPWD; ++wi)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              v[(tl * WPWD + wi) * 4 + j] = ld_stream(w + ((size_t)tl * 16 * I + wi * WIN) * 2 + 16 * j);
-        __builtin_amdgcn_sched_barrier(0);  // keep every load of the item ahead of the math
-#pragma unroll
-        for (int tl = 0; tl < RT_BF; ++tl)
-#pragma unroll
-          for (int wi = 0; wi < WPWD; ++wi)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              acc[tl] = mfma16(v[(tl * WPWD + wi) * 4 + j], bf[wi][j][0], acc[tl]);
-              acc[tl] = mfma16(v[(tl * WPWD + wi) * 4 + j], bf[wi][j][1], acc[tl]);
-            }
-      }
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t off = lo + (uint32_t)(wi * WIN + kofs<NAT>(j, q)) * 2u;
+      T.v[(wi * 2 + 0) * 4 + j] = ld_stream(g + off);
+      T.v[(wi * 2 + 1) * 4 + j] = ld_stream(up + off);
     }
+}
+
+// mxfp4 item (GU_MX_RT tiles of 16 rows): lane (r, q) reads one 32-value block per window
+template <int WPW>
+__device__ __forceinline__ void gu_load_mx(GUItem<WPW>& T, const GUDesc& d, int H, int win0, int lane) {
+  const int q = lane >> 4, r = lane & 15;
 #pragma unroll
-    for (int tl = 0; tl < RT_ACC; ++tl)
-      if (tl < ntile) *reinterpret_cast<f32x4*>(&red[wave][tl][lane * 4]) = acc[tl];
-    __syncthreads();
-    {
-      const int r = tid & 15, c = tid >> 4;  // row within a tile, token column
-      int slot = -1;
-      if (c < k) slot = routed ? (int)a.tab_slot[u * KMAX + c] : K;
-      if (slot >= 0) {
-        float* dst = a.part + ((size_t)c * (K + 1) + slot) * H + row0 + r;
-        const int idx = (c + 16 * (r >> 2)) * 4 + (r & 3);
-        for (int tl = 0; tl < ntile; ++tl) {
-          float v = 0.f;
+  for (int tl = 0; tl < GU_MX_RT; ++tl)
 #pragma unroll
-          for (int wv = 0; wv < DN_WAVES; ++wv) v += red[wv][tl][idx];
-          dst[tl * 16] = v;
-        }
-      }
+    for (int wi = 0; wi < WPW; ++wi) {
+      const uint32_t off = (uint32_t)((16 * tl + r) * (H / 2) + (win0 + wi) * 64 + 16 * q);
+      const uint32_t soff = (uint32_t)((16 * tl + r) * (H / 32) + (win0 + wi) * 4 + q);
+      T.v[(tl * WPW + wi) * 2 + 0] = ld_stream(d.g + off);
+      T.v[(tl * WPW + wi) * 2 + 1] = ld_stream(d.up + off);
+      T.sc[(tl * WPW + wi) * 2 + 0] = d.sg[soff];
+      T.sc[(tl * WPW + wi) * 2 + 1] = d.su[soff];
     }
-    __syncthreads();
+}
+
+// Cross-wave reduction, SwiGLU with the RMSNorm factor and the routing weight, hi/lo split, and
+// the store as down-projection B fragments (rows row0 .. row0 + 16 ntile of expert slot `u`).
+template <bool NAT>
+__device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 (&acc)[GU_MX_RT][2],
+                                            int ntile, int u, int row0, bool routed, int wave,
+                                            int lane, int tid) {
+#pragma unroll
+  for (int tl = 0; tl < GU_MX_RT; ++tl)
+    if (tl < ntile) {
+      *reinterpret_cast<f32x4*>(&S.red[((wave * GU_MX_RT + tl) * 2 + 0) * 256 + lane * 4]) = acc[tl][0];
+      *reinterpret_cast<f32x4*>(&S.red[((wave * GU_MX_RT + tl) * 2 + 1) * 256 + lane * 4]) = acc[tl][1];
+    }
+  __syncthreads();
+  if (tid < ntile * 256) {
+    const int tl = tid >> 8, p = tid & 255;
+    float g = 0.f, up = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NW; ++wv) {
+      g += S.red[((wv * GU_MX_RT + tl) * 2 + 0) * 256 + p];
+      up += S.red[((wv * GU_MX_RT + tl) * 2 + 1) * 256 + p];
+    }
+    const int c = (p >> 2) & 15;
+    const float rv = S.rinv[c];
+    S.act[tl][p] = silu(g * rv) * (up * rv) * S.wcol[u][c];
+  }
+  __syncthreads();
+  // thread (tile, half, column c) -> rows R .. R+7 of the expert's intermediate dimension
+  if (tid < ntile * 2 * KMAX) {
+    const int tl = tid / (2 * KMAX), half = (tid / KMAX) & 1, c = tid % KMAX;
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = half * 8 + i;
+      split_bf16(S.act[tl][(c + 16 * (r >> 2)) * 4 + (r & 3)], hi[i], lo[i]);
+    }
+    const int R = row0 + 16 * tl + 8 * half;
+    const int w = R / WIN, o = R % WIN;
+    const int j = NAT ? o / 32 : (o % 32) / 8, q = NAT ? (o % 32) / 8 : o / 32;
+    const int s = w * 4 + j;
+    const int I = routed ? a.I : a.Is;
+    u32x4* dst = routed ? a.afrag + (size_t)u * (I / 32) * 128 : a.afrag_sh;
+    u32x4 h, l;
+    pack8(hi, h);
+    pack8(lo, l);
+    dst[((size_t)s * 2 + 0) * 64 + c + 16 * q] = h;
+    dst[((size_t)s * 2 + 1) * 64 + c + 16 * q] = l;
   }
 }
 
+template <int WPW>
+__device__ __forceinline__ void gu_math_bf16(f32x4 (&acc)[GU_MX_RT][2], const GUItem<WPW>& T,
+                                             const u32x4 (&xb)[WPW][4][2]) {
+#pragma unroll
+  for (int tl = 0; tl < GU_MX_RT; ++tl) acc[tl][0] = acc[tl][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int wi = 0; wi < WPW; ++wi)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat) {
+        acc[0][mat] = mfma16(T.v[(wi * 2 + mat) * 4 + j], xb[wi][j][0], acc[0][mat]);
+        acc[0][mat] = mfma16(T.v[(wi * 2 + mat) * 4 + j], xb[wi][j][1], acc[0][mat]);
+      }
+}
+
+template <int WPW>
+__device__ __forceinline__ void gu_math_mx(f32x4 (&acc)[GU_MX_RT][2], const GUItem<WPW>& T,
+                                           const u32x4 (&xb)[WPW][4][2]) {
+#pragma unroll
+  for (int tl = 0; tl < GU_MX_RT; ++tl) acc[tl][0] = acc[tl][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tl = 0; tl < GU_MX_RT; ++tl)
+#pragma unroll
+    for (int wi = 0; wi < WPW; ++wi)
+#pragma unroll
+      for (int mat = 0; mat < 2; ++mat) {
+        const u32x4 c = T.v[(tl * WPW + wi) * 2 + mat];
+        const float sc = e8m0_scale(T.sc[(tl * WPW + wi) * 2 + mat]);
+        const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 av = dec_fp4x8(cw[j], sc);
+          acc[tl][mat] = mfma16(av, xb[wi][j][0], acc[tl][mat]);
+          acc[tl][mat] = mfma16(av, xb[wi][j][1], acc[tl][mat]);
+        }
+      }
+}
+
+// Routed item `idx` (or a valid stand-in when idx is out of range, so that every path issues
+// the same loads).
+template <bool MX>
+__device__ __forceinline__ GUDesc gu_desc(const Args& a, const Smem& S, int idx, int n_items, int ipe) {
+  const int it = idx < n_items ? idx : 0;
+  GUDesc d;
+  d.u = it / ipe;
+  d.ntile = MX ? GU_MX_RT : 1;
+  d.row0 = (it % ipe) * 16 * d.ntile;
+  const size_t H = a.H, I = a.I;
+  const size_t e = (size_t)__builtin_amdgcn_readfirstlane(S.woken[d.u]);
+  if (MX) {
+    d.g = a.wg + e * I * (H / 2) + (size_t)d.row0 * (H / 2);
+    d.up = a.wu + e * I * (H / 2) + (size_t)d.row0 * (H / 2);
+    d.sg = a.sg + e * I * (H / 32) + (size_t)d.row0 * (H / 32);
+    d.su = a.su + e * I * (H / 32) + (size_t)d.row0 * (H / 32);
+  } else {
+    d.g = a.wg + (e * I + d.row0) * H * 2;
+    d.up = a.wu + (e * I + d.row0) * H * 2;
+    d.sg = d.su = nullptr;
+  }
+  return d;
+}
+
+template <int WPW, bool MX>
+__device__ __forceinline__ void gu_load(GUItem<WPW>& T, const GUDesc& d, int H, int win0, int lane) {
+  if (MX) gu_load_mx<WPW>(T, d, H, win0, lane);
+  else gu_load_bf16<WPW, true>(T, d.g, d.up, H, win0, lane);
+}
+
+template <int WPW, bool MX>
+__device__ __forceinline__ void gu_math(f32x4 (&acc)[GU_MX_RT][2], const GUItem<WPW>& T,
+                                        const u32x4 (&xb)[WPW][4][2]) {
+  if (MX) gu_math_mx<WPW>(acc, T, xb);
+  else gu_math_bf16<WPW>(acc, T, xb);
+}
+
 // ------------------------------------------------------------------------------------------
-// k_combine: y[t] = (sum_j P[t][j]) + P[t][K] (+ x[t]), fixed order
+// down items. NWIN = I / 128 windows; wave w owns window w % NWIN and tile group
+// w / NWIN, with TPW row tiles (bf16) or 2 TPW (mxfp4).
 // ------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) k_combine(const float* part, const float* x, float* y, int H,
-                                                 int K, int k, int has_shared, int residual) {
-  const int H4 = H / 4;
+template <int NWIN>
+struct DnShape {
+  static constexpr int WPWIN = NW / NWIN;                   // waves per window
+  static constexpr int TPI_BF = NWIN == 8 ? 4 : 8;           // row tiles per bf16 item
+  static constexpr int TPW_BF = TPI_BF / WPWIN;              // row tiles per wave, bf16
+  static constexpr int TPI_MX = 2 * TPI_BF;
+  static constexpr int TPW_MX = 2 * TPW_BF;
+};
+
+template <int NWIN>
+struct DNItem {
+  u32x4 v[DnShape<NWIN>::TPW_BF * 4];  // bf16: [tile*4 + j]; mxfp4: [tile] (first TPW_MX entries)
+  uint32_t sc[DnShape<NWIN>::TPW_MX];
+};
+
+struct DNDesc {
+  int u, row0, ntile;
+  const uint8_t* w;
+  const uint8_t* s;
+};
+
+template <int NWIN, bool MX>
+__device__ __forceinline__ DNDesc dn_desc(const Args& a, const Smem& S, int idx, int n_items, int ipe) {
+  using SH = DnShape<NWIN>;
+  const int it = idx < n_items ? idx : 0;
+  DNDesc d;
+  d.u = it / ipe;
+  d.ntile = MX ? SH::TPI_MX : SH::TPI_BF;
+  d.row0 = (it % ipe) * 16 * d.ntile;
+  const size_t H = a.H, I = a.I;
+  const size_t e = (size_t)__builtin_amdgcn_readfirstlane(S.woken[d.u]);
+  if (MX) {
+    d.w = a.wd + e * H * (I / 2) + (size_t)d.row0 * (I / 2);
+    d.s = a.sd + e * H * (I / 32) + (size_t)d.row0 * (I / 32);
+  } else {
+    d.w = a.wd + (e * H + d.row0) * I * 2;
+    d.s = nullptr;
+  }
+  return d;
+}
+
+template <int NWIN, bool NAT>
+__device__ __forceinline__ void dn_load_bf16(DNItem<NWIN>& T, const uint8_t* w, int I, int wave, int lane) {
+  using SH = DnShape<NWIN>;
+  const int q = lane >> 4, r = lane & 15;
+  const int win = wave % NWIN, tg = wave / NWIN;
+#pragma unroll
+  for (int tl = 0; tl < SH::TPW_BF; ++tl) {
+    const uint32_t base = (uint32_t)(((tg * SH::TPW_BF + tl) * 16 + r) * I + win * WIN) * 2u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) T.v[tl * 4 + j] = ld_stream(w + base + (uint32_t)kofs<NAT>(j, q) * 2u);
+  }
+}
+
+template <int NWIN>
+__device__ __forceinline__ void dn_load_mx(DNItem<NWIN>& T, const DNDesc& d, int I, int wave, int lane) {
+  using SH = DnShape<NWIN>;
+  const int q = lane >> 4, r = lane & 15;
+  const int win = wave % NWIN, tg = wave / NWIN;
+#pragma unroll
+  for (int tl = 0; tl < SH::TPW_MX; ++tl) {
+    const int row = (tg * SH::TPW_MX + tl) * 16 + r;
+    T.v[tl] = ld_stream(d.w + (uint32_t)(row * (I / 2) + win * 64 + 16 * q));
+    T.sc[tl] = d.s[(uint32_t)(row * (I / 32) + win * 4 + q)];
+  }
+}
+
+template <int NWIN, bool MX>
+__device__ __forceinline__ void dn_load(DNItem<NWIN>& T, const DNDesc& d, int I, int wave, int lane) {
+  if (MX) dn_load_mx<NWIN>(T, d, I, wave, lane);
+  else dn_load_bf16<NWIN, true>(T, d.w, I, wave, lane);
+}
+
+// B fragments (down activations) of this wave's window for one expert slot
+template <int NWIN>
+__device__ __forceinline__ void dn_load_b(u32x4 (&bf)[4][2], const u32x4* af, int wave, int lane) {
+  const int win = wave % NWIN;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl) bf[j][hl] = ld16(af + ((size_t)(win * 4 + j) * 2 + hl) * 64 + lane);
+}
+
+template <int NWIN, bool MX>
+__device__ __forceinline__ void dn_math(f32x4 (&acc)[DnShape<NWIN>::TPW_MX], const DNItem<NWIN>& T,
+                                        const u32x4 (&bf)[4][2]) {
+  using SH = DnShape<NWIN>;
+#pragma unroll
+  for (int tl = 0; tl < SH::TPW_MX; ++tl) acc[tl] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (MX) {
+#pragma unroll
+    for (int tl = 0; tl < SH::TPW_MX; ++tl) {
+      const u32x4 c = T.v[tl];
+      const float s = e8m0_scale(T.sc[tl]);
+      const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 av = dec_fp4x8(cw[j], s);
+        acc[tl] = mfma16(av, bf[j][0], acc[tl]);
+        acc[tl] = mfma16(av, bf[j][1], acc[tl]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int tl = 0; tl < SH::TPW_BF; ++tl)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[tl] = mfma16(T.v[tl * 4 + j], bf[j][0], acc[tl]);
+        acc[tl] = mfma16(T.v[tl * 4 + j], bf[j][1], acc[tl]);
+      }
+  }
+}
+
+template <int NWIN>
+__device__ __forceinline__ void dn_store_partial(Smem& S, const f32x4* acc, int tpw, int wave, int lane) {
+  const int win = wave % NWIN, tg = wave / NWIN;
+  for (int tl = 0; tl < tpw; ++tl)
+    *reinterpret_cast<f32x4*>(&S.red[((win + NWIN * tg) * tpw + tl) * 256 + lane * 4]) = acc[tl];
+}
+
+// Reduce the item's partial tiles over windows and write the P rows of the tokens routed to it.
+template <int NWIN>
+__device__ void dn_epilogue(const Args& a, Smem& S, int ntile, int tpw, int u, bool routed, int row0,
+                            int tid) {
+  const int H = a.H, K = a.K, k = a.k;
+  __syncthreads();
+  {
+    const int r = tid & 15, c = (tid >> 4) & 15, par = tid >> 8;  // par: tile parity
+    int slot = -1;
+    if (c < k) slot = routed ? (int)S.slot[u][c] : K;
+    if (slot >= 0) {
+      float* dst = a.part + ((size_t)c * (K + 1) + slot) * H + row0 + r;
+      const int idx = (c + 16 * (r >> 2)) * 4 + (r & 3);
+      for (int tl = par; tl < ntile; tl += 2) {
+        const int tg = tl / tpw, lt = tl % tpw;  // tile tl: tile group tg, local tile lt
+        float v = 0.f;
+#pragma unroll
+        for (int win = 0; win < NWIN; ++win) v += S.red[((win + NWIN * tg) * tpw + lt) * 256 + idx];
+        dst[tl * 16] = v;
+      }
+    }
+  }
+  __syncthreads();  // the next item's partial tiles reuse S.red
+}
+
+// y[t][h] = sum_j P[t][j][h] + P[t][K][h] (+ x[t][h]); one thread per four outputs
+__global__ void __launch_bounds__(256) k_combine(Args a) {
+  const int H = a.H, K = a.K, H4 = H / 4;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= k * H4) return;
+  if (idx >= a.k * H4) return;
   const int t = idx / H4, c = idx % H4;
-  const float4* p = reinterpret_cast<const float4*>(part + (size_t)t * (K + 1) * H) + c;
+  const float4* p = reinterpret_cast<const float4*>(a.part + (size_t)t * (K + 1) * H) + c;
   float4 acc = p[0];
   for (int j = 1; j < K; ++j) {
     const float4 v = p[(size_t)j * H4];
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
-  if (has_shared) {
+  if (a.Is > 0) {
     const float4 v = p[(size_t)K * H4];
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
-  if (residual) {
-    const float4 v = reinterpret_cast<const float4*>(x + (size_t)t * H)[c];
+  if (a.residual) {
+    const float4 v = reinterpret_cast<const float4*>(a.x + (size_t)t * H)[c];
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
-  reinterpret_cast<float4*>(y + (size_t)t * H)[c] = acc;
+  reinterpret_cast<float4*>(a.y + (size_t)t * H)[c] = acc;
 }
 
 // ------------------------------------------------------------------------------------------
-// accept_prefix kernels
+// kernels
+// ------------------------------------------------------------------------------------------
+template <bool NAT>
+__global__ void __launch_bounds__(NTH) k_router(Args a) {
+  __shared__ RouterSmem S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  router_item<NAT>(a, S, blockIdx.x, wave, lane, tid);
+}
+
+template <int WPW, bool MX>
+__global__ void __launch_bounds__(NTH) k_gateup(Args a) {
+  constexpr bool NAT = !MX;  // K mapping of this layer's fragments
+  __shared__ Smem S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int H = a.H, I = a.I, Is = a.Is;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int win0 = wave * WPW;
+  const bool active = win0 < H / WIN;  // H is a multiple of 128 * WPW
+  const int wsafe = active ? win0 : 0; // inactive waves load window 0 and multiply it by zero
+
+  // Item sequence: the shared expert's row tiles (known before routing, so their weights are
+  // requested first), then the routed items.
+  const int n_sh = Is / 16;
+  GUItem<WPW> Ts;
+  if (b < n_sh)
+    gu_load_bf16<WPW, NAT>(Ts, a.shg + (size_t)b * 16 * H * 2, a.shu + (size_t)b * 16 * H * 2, H, wsafe, lane);
+
+  route(a, S, wave, lane, tid);
+  const int U = __builtin_amdgcn_readfirstlane(S.nw);
+
+  // B fragments of this wave's H windows (the raw block), used by every item
+  u32x4 xb[WPW][4][2];
+#pragma unroll
+  for (int wi = 0; wi < WPW; ++wi)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl)
+        xb[wi][j][hl] = active ? ld16(a.xfrag + ((size_t)((win0 + wi) * 4 + j) * 2 + hl) * 64 + lane)
+                               : u32x4{0u, 0u, 0u, 0u};
+
+  const int ipe = I / (16 * (MX ? GU_MX_RT : 1));
+  const int n_gu = U * ipe;
+  int p = b;
+  if (p < n_sh) {
+    f32x4 acc[GU_MX_RT][2];
+    gu_math_bf16<WPW>(acc, Ts, xb);
+    gu_epilogue<NAT>(a, S, acc, 1, U, p * 16, false, wave, lane, tid);
+    p += G;
+  }
+  // routed items of this workgroup: r0, r0 + G, ...
+  const int r0 = p - n_sh;
+  const int nmine = r0 < n_gu ? (n_gu - r0 + G - 1) / G : 0;
+  if (nmine > 0) {
+    GUItem<WPW> T0, T1;
+    GUDesc d0 = gu_desc<MX>(a, S, r0, n_gu, ipe), d1;
+    gu_load<WPW, MX>(T0, d0, H, wsafe, lane);
+    for (int j = 0;;) {
+      d1 = gu_desc<MX>(a, S, r0 + (j + 1) * G, n_gu, ipe);  // a valid stand-in past the end
+      gu_load<WPW, MX>(T1, d1, H, wsafe, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f32x4 acc[GU_MX_RT][2];
+        gu_math<WPW, MX>(acc, T0, xb);
+        gu_epilogue<NAT>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid);
+      }
+      if (++j >= nmine) break;
+      d0 = gu_desc<MX>(a, S, r0 + (j + 1) * G, n_gu, ipe);
+      gu_load<WPW, MX>(T0, d0, H, wsafe, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f32x4 acc[GU_MX_RT][2];
+        gu_math<WPW, MX>(acc, T1, xb);
+        gu_epilogue<NAT>(a, S, acc, d1.ntile, d1.u, d1.row0, true, wave, lane, tid);
+      }
+      if (++j >= nmine) break;
+    }
+  }
+}
+
+template <int NWIN, bool MX>
+__global__ void __launch_bounds__(NTH) k_down(Args a) {
+  using SH = DnShape<NWIN>;
+  constexpr bool NAT = !MX;
+  constexpr int TPW = MX ? SH::TPW_MX : SH::TPW_BF;
+  __shared__ Smem S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int H = a.H, I = a.I, Is = a.Is;
+  const int G = gridDim.x, b = blockIdx.x;
+
+  // Item sequence: the shared expert's row groups (requested first), then the routed items.
+  const int n_sh = Is > 0 ? H / (16 * SH::TPI_BF) : 0;
+  DNItem<NWIN> Ts;
+  if (b < n_sh) dn_load_bf16<NWIN, NAT>(Ts, a.shd + (size_t)b * 16 * SH::TPI_BF * Is * 2, Is, wave, lane);
+
+  const int U = __builtin_amdgcn_readfirstlane(a.tab_n[0]);
+  for (int i = tid; i < U; i += NTH) S.woken[i] = a.tab_woken[i];
+  for (int i = tid; i < U * KMAX; i += NTH) S.slot[i / KMAX][i % KMAX] = a.tab_slot[i];
+  __syncthreads();
+
+  const int ipe = H / (16 * (MX ? SH::TPI_MX : SH::TPI_BF));
+  const int n_dn = U * ipe;
+  int p = b;
+  if (p < n_sh) {
+    u32x4 bf[4][2];
+    dn_load_b<NWIN>(bf, a.afrag_sh, wave, lane);
+    f32x4 acc[SH::TPW_MX];
+    dn_math<NWIN, false>(acc, Ts, bf);
+    dn_store_partial<NWIN>(S, acc, SH::TPW_BF, wave, lane);
+    dn_epilogue<NWIN>(a, S, SH::TPI_BF, SH::TPW_BF, U, false, p * 16 * SH::TPI_BF, tid);
+    p += G;
+  }
+  const int q0 = p - n_sh;
+  const int nmine = q0 < n_dn ? (n_dn - q0 + G - 1) / G : 0;
+  if (nmine > 0) {
+    DNItem<NWIN> T0, T1;
+    DNDesc e0 = dn_desc<NWIN, MX>(a, S, q0, n_dn, ipe), e1;
+    dn_load<NWIN, MX>(T0, e0, I, wave, lane);
+    for (int j = 0;;) {
+      u32x4 bf[4][2];
+      dn_load_b<NWIN>(bf, a.afrag + (size_t)e0.u * (I / 32) * 128, wave, lane);
+      e1 = dn_desc<NWIN, MX>(a, S, q0 + (j + 1) * G, n_dn, ipe);  // a valid stand-in past the end
+      dn_load<NWIN, MX>(T1, e1, I, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f32x4 acc[SH::TPW_MX];
+        dn_math<NWIN, MX>(acc, T0, bf);
+        dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
+        dn_epilogue<NWIN>(a, S, e0.ntile, TPW, e0.u, true, e0.row0, tid);
+      }
+      if (++j >= nmine) break;
+      dn_load_b<NWIN>(bf, a.afrag + (size_t)e1.u * (I / 32) * 128, wave, lane);
+      e0 = dn_desc<NWIN, MX>(a, S, q0 + (j + 1) * G, n_dn, ipe);
+      dn_load<NWIN, MX>(T0, e0, I, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f32x4 acc[SH::TPW_MX];
+        dn_math<NWIN, MX>(acc, T1, bf);
+        dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
+        dn_epilogue<NWIN>(a, S, e1.ntile, TPW, e1.u, true, e1.row0, tid);
+      }
+      if (++j >= nmine) break;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// accept_prefix: chunked argmax, then one workgroup reduces the rows and scans the prefix
 // ------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_argmax_partial(const float* logits, int V, int nchunks,
                                                         float* pv, int* pi) {
@@ -764,6 +873,34 @@ __global__ void __launch_bounds__(64) k_accept_final(const float* pv, const int*
 // ------------------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------------------
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t tab_n, tab_woken, tab_slot, xfrag, plog, psq, afrag, afrag_sh, part, total;
+  int umax, hs;
+};
+
+int router_splits(int H) { return H >= 2048 ? 4 : (H >= 1024 ? 2 : 1); }
+
+Layout make_layout(const moe_layer* L, int k) {
+  Layout o;
+  const size_t H = L->hidden, E = L->n_experts, K = L->top_k, I = L->inter, Is = L->shared_inter;
+  o.umax = (int)((E < (size_t)KMAX * K) ? E : (size_t)KMAX * K);
+  o.hs = router_splits(L->hidden);
+  size_t off = 0;
+  o.tab_n = off;     off = align256(off + 16);
+  o.tab_woken = off; off = align256(off + (size_t)o.umax * 4);
+  o.tab_slot = off;  off = align256(off + (size_t)o.umax * KMAX);
+  o.xfrag = off;    off = align256(off + H * 64);
+  o.plog = off;     off = align256(off + (size_t)o.hs * KMAX * E * 4);
+  o.psq = off;      off = align256(off + (size_t)o.hs * KMAX * 4);
+  o.afrag = off;    off = align256(off + (size_t)o.umax * I * 64);
+  o.afrag_sh = off; off = align256(off + Is * 64);
+  o.part = off;     off = align256(off + (size_t)k * (K + 1) * H * 4);
+  o.total = off;
+  return o;
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -804,13 +941,34 @@ int num_cus() {
   return cached[dev];
 }
 
-template <int WPW, bool MX>
-void launch_gateup(const GUArgs& g, hipStream_t s, int grid) {
-  k_gateup<WPW, MX><<<grid, GU_WAVES * 64, 0, s>>>(g);
+// Records events[i] (any may be NULL) on the stream; false if a record fails.
+bool mark(void* const* events, int i, hipStream_t s) {
+  return !events || !events[i] || hipEventRecord((hipEvent_t)events[i], s) == hipSuccess;
 }
-template <int WPWD, bool MX>
-void launch_down(const DNArgs& d, hipStream_t s, int grid) {
-  k_down<WPWD, MX><<<grid, DN_WAVES * 64, 0, s>>>(d);
+
+template <int WPW, int NWIN, bool MX>
+bool launch_layer(const Args& a, hipStream_t s, void* const* ev) {
+  // one workgroup per CU; never fewer workgroups than shared-expert items (one each)
+  const int cus = std::max(num_cus(), std::max(a.Is / 16, a.H / 64));
+  if (!mark(ev, 0, s)) return false;
+  k_router<!MX><<<a.ntile_e * a.hs, NTH, 0, s>>>(a);
+  if (!mark(ev, 1, s)) return false;
+  k_gateup<WPW, MX><<<cus, NTH, 0, s>>>(a);
+  if (!mark(ev, 2, s)) return false;
+  k_down<NWIN, MX><<<cus, NTH, 0, s>>>(a);
+  if (!mark(ev, 3, s)) return false;
+  k_combine<<<(a.k * a.H / 4 + 255) / 256, 256, 0, s>>>(a);
+  return mark(ev, 4, s);
+}
+
+template <int WPW, bool MX>
+bool launch_nwin(const Args& a, hipStream_t s, void* const* ev) {
+  switch (a.I / WIN) {
+    case 1: return launch_layer<WPW, 1, MX>(a, s, ev);
+    case 2: return launch_layer<WPW, 2, MX>(a, s, ev);
+    case 4: return launch_layer<WPW, 4, MX>(a, s, ev);
+    default: return launch_layer<WPW, 8, MX>(a, s, ev);
+  }
 }
 
 }  // namespace
@@ -861,53 +1019,29 @@ static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint
   if (n_woken && (overlaps(n_woken, 4, workspace, lay.total) || overlaps(n_woken, 4, y, xy_bytes)))
     return MOE_ERR_ALIAS;
 
-  hipStream_t s = (hipStream_t)hip_stream;
   uint8_t* ws = (uint8_t*)workspace;
-  const int H = L->hidden, E = L->n_experts;
+  Args a;
+  a.x = x; a.y = y; a.out_ids = topk_ids; a.out_w = topk_w; a.out_n = n_woken;
+  a.wr = L->router_w;
+  a.wg = (const uint8_t*)L->w_gate; a.wu = (const uint8_t*)L->w_up; a.wd = (const uint8_t*)L->w_down;
+  a.sg = L->s_gate; a.su = L->s_up; a.sd = L->s_down;
+  a.shg = (const uint8_t*)L->sh_gate; a.shu = (const uint8_t*)L->sh_up; a.shd = (const uint8_t*)L->sh_down;
+  a.tab_n = (int32_t*)(ws + lay.tab_n); a.tab_woken = (int32_t*)(ws + lay.tab_woken);
+  a.tab_slot = (int8_t*)(ws + lay.tab_slot);
+  a.xfrag = (u32x4*)(ws + lay.xfrag); a.plog = (float*)(ws + lay.plog); a.psq = (float*)(ws + lay.psq);
+  a.afrag = (u32x4*)(ws + lay.afrag); a.afrag_sh = (u32x4*)(ws + lay.afrag_sh); a.part = (float*)(ws + lay.part);
+  a.H = L->hidden; a.E = L->n_experts; a.K = L->top_k; a.I = L->inter; a.Is = L->shared_inter; a.k = k;
+  a.hs = lay.hs; a.ntile_e = (L->n_experts + 15) / 16; a.umax = lay.umax;
+  a.pre_norm = (flags & MOE_PRE_RMSNORM) ? 1 : 0; a.residual = (flags & MOE_RESIDUAL) ? 1 : 0;
+  a.eps = L->rms_eps;
+
+  hipStream_t s = (hipStream_t)hip_stream;
+  (void)hipGetLastError();  // clear a stale error so the check below reports this launch
   const bool mx = L->wdtype == MOE_W_MXFP4;
-
-  (void)hipGetLastError();  // clear a stale error so the check below reports these launches
-  auto mark = [&](int i) -> bool {
-    return !events || !events[i] || hipEventRecord((hipEvent_t)events[i], s) == hipSuccess;
-  };
-  if (!mark(0)) return MOE_ERR_HIP;
-
-  RouterArgs ra;
-  ra.x = x; ra.wr = L->router_w; ra.logits = (float*)(ws + lay.logits); ra.xfrag = (u32x4*)(ws + lay.xfrag);
-  ra.H = H; ra.E = E; ra.k = k; ra.pre_norm = (flags & MOE_PRE_RMSNORM) ? 1 : 0; ra.eps = L->rms_eps;
-  k_router<<<(E + RT_EPB - 1) / RT_EPB, RT_THREADS, 0, s>>>(ra);
-  if (!mark(1)) return MOE_ERR_HIP;
-
-  GUArgs g;
-  g.logits = ra.logits; g.xfrag = ra.xfrag;
-  g.wg = (const uint8_t*)L->w_gate; g.wu = (const uint8_t*)L->w_up; g.sg = L->s_gate; g.su = L->s_up;
-  g.shg = (const uint8_t*)L->sh_gate; g.shu = (const uint8_t*)L->sh_up;
-  g.afrag = (u32x4*)(ws + lay.afrag); g.afrag_sh = (u32x4*)(ws + lay.afrag_sh);
-  g.tab_n = (int32_t*)(ws + lay.tab_n); g.tab_woken = (int32_t*)(ws + lay.tab_woken);
-  g.tab_slot = (int8_t*)(ws + lay.tab_slot);
-  g.out_ids = topk_ids; g.out_w = topk_w; g.out_n = n_woken;
-  g.H = H; g.E = E; g.K = L->top_k; g.I = L->inter; g.Is = L->shared_inter; g.k = k;
-  const int cus = num_cus();
-  if (H > 1024) { if (mx) launch_gateup<2, true>(g, s, cus); else launch_gateup<2, false>(g, s, cus); }
-  else          { if (mx) launch_gateup<1, true>(g, s, cus); else launch_gateup<1, false>(g, s, cus); }
-  if (!mark(2)) return MOE_ERR_HIP;
-
-  DNArgs d;
-  d.afrag = g.afrag; d.afrag_sh = g.afrag_sh;
-  d.wd = (const uint8_t*)L->w_down; d.sd = L->s_down; d.shd = (const uint8_t*)L->sh_down;
-  d.tab_n = g.tab_n; d.tab_woken = g.tab_woken; d.tab_slot = g.tab_slot;
-  d.part = (float*)(ws + lay.part);
-  d.H = H; d.E = E; d.K = L->top_k; d.I = L->inter; d.Is = L->shared_inter; d.k = k;
-  const int wpwd = L->inter == 1024 ? 2 : 1;
-  if (wpwd == 1) { if (mx) launch_down<1, true>(d, s, 2 * cus); else launch_down<1, false>(d, s, 2 * cus); }
-  else           { if (mx) launch_down<2, true>(d, s, 2 * cus); else launch_down<2, false>(d, s, 2 * cus); }
-  if (!mark(3)) return MOE_ERR_HIP;
-
-  const int n4 = k * (H / 4);
-  k_combine<<<(n4 + 255) / 256, 256, 0, s>>>(d.part, x, y, H, L->top_k, k, L->shared_inter > 0,
-                                            (flags & MOE_RESIDUAL) ? 1 : 0);
-  if (!mark(4)) return MOE_ERR_HIP;
-  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  bool ok;
+  if (L->hidden > 1024) ok = mx ? launch_nwin<2, true>(a, s, events) : launch_nwin<2, false>(a, s, events);
+  else                  ok = mx ? launch_nwin<1, true>(a, s, events) : launch_nwin<1, false>(a, s, events);
+  return (ok && hipGetLastError() == hipSuccess) ? MOE_OK : MOE_ERR_HIP;
 }
 
 int moe_verify_block(const moe_layer* L, const float* x, int32_t k, uint32_t flags, float* y,

@@ -208,8 +208,9 @@ def test_determinism_and_stale_workspace(B):
     x = gen.hidden_states(wl, rep=7)
     layer = dev_layer(wl)
     base = run_block(B, layer, x, ws_fill=0)
-    for fill in (0xFF, 0x80, 0x7F, 0):
-        g = run_block(B, layer, x, ws_fill=fill)
+    ws = torch.empty(layer.workspace_size(16), dtype=torch.uint8, device="cuda")
+    for fill in (0xFF, 0x80, 0x7F, 0, None, None):  # None: reuse the workspace as the last call left it
+        g = run_block(B, layer, x, ws_fill=fill, ws=ws)
         for key in ("y", "ids", "w"):
             assert np.array_equal(g[key], base[key]), (fill, key)
         assert g["n_woken"] == base["n_woken"]
@@ -296,6 +297,7 @@ def run_accept(B, logits, draft, n_draft=None):
     tg = torch.empty(n_target, dtype=torch.int32, device="cuda")
     acc = torch.empty(4, dtype=torch.int32, device="cuda")
     ws = torch.empty(B.accept_prefix_workspace_size(n_target, vocab), dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)  # stale workspace contents must not matter
     B.accept_prefix(ld, dd, tg, acc, ws, n_draft=len(draft) if n_draft is None else n_draft)
     torch.cuda.synchronize()
     return tg.cpu().numpy().astype(np.int64), int(acc[0].item())
