@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE verify-block latency (ms) and achieved HBM GB/s vs k=1..16, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 GATEUP_SRC = os.path.join(ROOT, "speculative_decoding_moe_amd", "csrc", "moe_verify.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_gateup_verify_k16_traffic.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_gateup_verify_k16_bf16_traffic.txt")
 
 
 class HipEvents:
@@ -164,6 +164,9 @@ def main():
     ap.add_argument("--cpu-samples", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="counter-collection run: warmup + steps without events, then a plain copy of "
+                         "known size for calibrating HBM traffic counters; prints one JSON line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -225,6 +228,25 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+
+    if args.profile_run:
+        for i in range(nsteps):
+            step(i)
+        torch.cuda.synchronize()
+        Un = nw_all[:nsteps, 0].cpu().numpy().astype(np.int64)
+        Uw = nw_all[:args.warmup, 0].cpu().numpy().astype(np.int64)
+        Uall = np.concatenate([Uw, Un])
+        copy_mib = 512
+        src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            device.copy_bytes(dst, src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": True, "launches": int(len(Uall)),
+                          "gateup_bytes_mean": float(np.mean([gateup_bytes(s, u) for u in Uall])),
+                          "layer_bytes_mean": float(np.mean([layer_bytes(s, u, k) for u in Uall])),
+                          "copy_bytes": copy_mib << 20, "copy_launches": 3}), flush=True)
+        return
 
     # ---- headline: K whole steps bracketed by synchronisations ----
     t_start, t_stop = ev.create(2)

@@ -30,6 +30,8 @@ def _fill_lib():
         lib.workload_fill_bf16.restype = ctypes.c_int
         lib.workload_fill_mxfp4.argtypes = [vp, vp, u64, u32, u64, u64, vp, vp]
         lib.workload_fill_mxfp4.restype = ctypes.c_int
+        lib.workload_copy.argtypes = [vp, vp, u64, vp]
+        lib.workload_copy.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -62,6 +64,15 @@ def fill_mxfp4(codes: torch.Tensor, scales: torch.Tensor, seed: int, layer: int,
                                          torch.cuda.current_stream().cuda_stream)
     if st != 0:
         raise RuntimeError(f"workload_fill_mxfp4 failed ({st})")
+
+
+def copy_bytes(dst: torch.Tensor, src: torch.Tensor):
+    """A plain device copy of known size (the calibration point for HBM traffic counters)."""
+    nb = src.numel() * src.element_size()
+    assert dst.numel() * dst.element_size() >= nb and src.is_contiguous() and dst.is_contiguous()
+    st = _fill_lib().workload_copy(src.data_ptr(), dst.data_ptr(), nb, torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"workload_copy failed ({st})")
 
 
 def layer_tensors(wl: gen.Workload, layer: int = 0, device="cuda") -> dict:

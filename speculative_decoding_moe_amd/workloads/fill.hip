@@ -92,6 +92,13 @@ __global__ void k_fill_mxfp4(uint8_t* codes, uint8_t* scales, uint64_t n_per_ten
   scales[e * (n_per_tensor / 32) + blk] = (uint8_t)(s + 127);
 }
 
+// Plain copy, 16 bytes per lane, grid-stride: a transfer of known size against which the HBM
+// traffic counters of the MoE kernels are calibrated.
+__global__ void __launch_bounds__(256) k_copy16(const uint4* src, uint4* dst, uint64_t n16) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
 }  // namespace
 
 extern "C" {
@@ -117,6 +124,15 @@ int workload_fill_mxfp4(void* codes, void* scales, uint64_t n_per_tensor, uint32
   dim3 grid((unsigned)((nb + 255) / 256), n_tensors);
   k_fill_mxfp4<<<grid, 256, 0, (hipStream_t)stream>>>((uint8_t*)codes, (uint8_t*)scales, n_per_tensor, seed,
                                                       tid0, (const float*)table_f32);
+  return (int)hipGetLastError();
+}
+
+// dst[0:bytes] = src[0:bytes] (bytes a multiple of 16, both 16-byte aligned, no overlap).
+int workload_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
+  if (!src || !dst || bytes % 16 || ((uintptr_t)src | (uintptr_t)dst) % 16) return -1;
+  if ((uintptr_t)src < (uintptr_t)dst + bytes && (uintptr_t)dst < (uintptr_t)src + bytes) return -1;
+  if (bytes == 0) return 0;
+  k_copy16<<<2048, 256, 0, (hipStream_t)stream>>>((const uint4*)src, (uint4*)dst, bytes / 16);
   return (int)hipGetLastError();
 }
 
