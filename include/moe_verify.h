@@ -9,12 +9,14 @@
  * section "The verify's own cost"). The verify cost tracks the expert bytes streamed
  * ("Speculating on a Strix Halo (part 2)", section "The verification cog").
  *
- * Two calls cover that pass:
+ * Two calls cover that pass, and a third prepares the weights they read:
  *   moe_verify_block -- one MoE layer over a block of k <= 16 tokens: fp32 router logits,
  *                       top-K with softmax renormalised over the K, woken-expert union, grouped
  *                       SwiGLU experts (bf16 or mxfp4 weights), weighted combine with the shared
  *                       expert, optional RMSNorm pre-norm and residual add;
- *   accept_prefix    -- per-position target argmax and greedy longest-prefix acceptance.
+ *   accept_prefix    -- per-position target argmax and greedy longest-prefix acceptance;
+ *   moe_pack_weights -- rearranges row-major expert matrices into the tiled layout the verify
+ *                       block streams (done once, when the weights are loaded).
  *
  * Conventions (all calls):
  *   - Pointers are DEVICE memory owned by the caller unless stated otherwise; the library never
@@ -41,7 +43,7 @@ enum {
   MOE_OK = 0,
   MOE_ERR_NULL = -1,      /* a required pointer is NULL                                     */
   MOE_ERR_SHAPE = -2,     /* a size is outside the supported range (see each call)           */
-  MOE_ERR_DTYPE = -3,     /* unknown weight format, or mxfp4 without its scale arrays        */
+  MOE_ERR_DTYPE = -3,     /* unknown weight format or layout, or mxfp4 without its scales   */
   MOE_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned                         */
   MOE_ERR_WORKSPACE = -5, /* workspace smaller than the matching *_workspace_size()          */
   MOE_ERR_ALIAS = -6,     /* output overlaps an input it must not overlap                    */
@@ -60,6 +62,23 @@ enum {
                       block whose codes are all zero; 255 (NaN) is not supported. */
 };
 
+/* Weight layouts (moe_layer.layout). The verify block streams every woken expert's bytes once
+ * per block ("Speculating on a Strix Halo (part 2)", section "The verification cog"), so the
+ * expert matrices are stored in the order the kernels consume them: MFMA operand tiles, each
+ * 16 rows x 32 reduction columns, 1 KiB contiguous, one 16-byte lane slice after another.
+ *
+ * MOE_LAYOUT_TILED, for a row-major matrix W[R][C] (R % 16 == 0, C % 128 == 0):
+ *   bf16:  16-byte chunk ((rt * (C/32) + s) * 64 + l) holds W[16 rt + l%16][32 s + 8 (l/16) + i],
+ *          i = 0..7 (rt < R/16, s < C/32, l < 64).
+ *   mxfp4: 16-byte code chunk ((rt * (C/128) + w) * 64 + l) holds the 16 code bytes of 32-value
+ *          block 4 w + l/16 of row 16 rt + l%16; scale byte of the same index holds that block's
+ *          scale (w < C/128).
+ * Each matrix of a stacked [n][R][C] array is tiled on its own (same byte size as row-major).
+ * moe_pack_weights produces this layout from row-major arrays. */
+enum {
+  MOE_LAYOUT_TILED = 1
+};
+
 /* moe_verify_block flags: y = [x +] MoE([RMSNorm](x)). */
 enum {
   MOE_PRE_RMSNORM = 1u, /* x_hat = x / sqrt(mean(x^2) + rms_eps) (unit gain) before the router
@@ -68,7 +87,8 @@ enum {
 };
 
 /* One MoE layer (a host struct, read only during the call; the arrays are device memory).
- * Shapes (row-major):
+ * Shapes (router_w row-major; expert and shared-expert matrices in MOE_LAYOUT_TILED, each
+ * [R][C] below tiled as a matrix of R rows and C reduction columns):
  *   router_w  fp32 [E][H]
  *   w_gate, w_up   bf16 [E][I][H]    | mxfp4 codes [E][I][H/2],  s_gate, s_up  [E][I][H/32]
  *   w_down         bf16 [E][H][I]    | mxfp4 codes [E][H][I/2],  s_down        [E][H][I/32]
@@ -84,6 +104,7 @@ typedef struct moe_layer {
   int32_t inter;        /* I, routed expert intermediate size */
   int32_t shared_inter; /* Is, shared expert intermediate size; 0 = no shared expert */
   int32_t wdtype;       /* MOE_W_BF16 | MOE_W_MXFP4 */
+  int32_t layout;       /* MOE_LAYOUT_TILED (anything else: MOE_ERR_DTYPE) */
   float rms_eps;        /* used with MOE_PRE_RMSNORM; must be finite and >= 0 */
   const float* router_w;
   const void* w_gate;
@@ -127,6 +148,18 @@ int moe_verify_block(const moe_layer* layer, const float* x, int32_t k, uint32_t
 int moe_verify_block_timed(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
                            int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
                            size_t ws_bytes, void* hip_stream, void* const* events /* [5] */);
+
+/* Rearranges n_mats row-major matrices of rows x cols into MOE_LAYOUT_TILED (a permutation of
+ * 16-byte chunks and, for mxfp4, of scale bytes; output sizes equal input sizes).
+ *   wdtype      MOE_W_BF16: src, dst bf16 [n_mats][rows][cols]
+ *               MOE_W_MXFP4: src, dst codes [n_mats][rows][cols/2]; src_scales, dst_scales
+ *               [n_mats][rows][cols/32] (NULL for bf16)
+ *   rows, cols  multiples of 16 and 128 (cols is the reduction dimension: H for gate/up, I for
+ *               down), each <= 2^20
+ * Outputs must not overlap inputs. Enqueued on hip_stream. Returns MOE_OK, MOE_ERR_NULL,
+ * MOE_ERR_DTYPE, MOE_ERR_SHAPE, MOE_ERR_ALIGN (src, dst), MOE_ERR_ALIAS or MOE_ERR_HIP. */
+int moe_pack_weights(int32_t wdtype, int32_t n_mats, int32_t rows, int32_t cols, const void* src,
+                     const uint8_t* src_scales, void* dst, uint8_t* dst_scales, void* hip_stream);
 
 /* Bytes of device workspace accept_prefix needs (0 if the sizes are invalid). Host only. */
 size_t accept_prefix_workspace_size(int32_t n_target, int32_t vocab);

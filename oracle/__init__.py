@@ -4,3 +4,4 @@ from .moe_oracle import (accept_length, argmax_first, committed_tokens, decode_b
                          decode_mxfp4, decode_tensor, expert_ffn, moe_block, moe_stack,
                          rms_norm, router_logits, routing_weights, select_topk, silu, topk_gap,
                          woken_experts)
+from .layout import tile_bf16, tile_mxfp4, tiled_position_bf16  # noqa: F401,E402

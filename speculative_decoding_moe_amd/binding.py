@@ -16,17 +16,18 @@ MOE_OK = 0
 MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN = -1, -2, -3, -4
 MOE_ERR_WORKSPACE, MOE_ERR_ALIAS, MOE_ERR_HIP, MOE_ERR_ARG = -5, -6, -7, -8
 MOE_W_BF16, MOE_W_MXFP4 = 0, 1
+MOE_LAYOUT_TILED = 1
 MOE_PRE_RMSNORM, MOE_RESIDUAL = 1, 2
 
 EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "moe_verify_block_timed",
-           "accept_prefix_workspace_size", "accept_prefix", "moe_status_string")
+           "moe_pack_weights", "accept_prefix_workspace_size", "accept_prefix", "moe_status_string")
 
 
 class MoeLayerStruct(ctypes.Structure):
     _fields_ = [
         ("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
         ("inter", ctypes.c_int32), ("shared_inter", ctypes.c_int32), ("wdtype", ctypes.c_int32),
-        ("rms_eps", ctypes.c_float),
+        ("layout", ctypes.c_int32), ("rms_eps", ctypes.c_float),
         ("router_w", ctypes.c_void_p),
         ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
         ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
@@ -52,6 +53,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_block_timed.argtypes = [ctypes.POINTER(MoeLayerStruct), vp, i32, u32, vp, vp, vp, vp, vp, sz,
                                            vp, ctypes.POINTER(vp)]
     lib.moe_verify_block_timed.restype = ctypes.c_int
+    lib.moe_pack_weights.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
+    lib.moe_pack_weights.restype = ctypes.c_int
     lib.accept_prefix_workspace_size.argtypes = [i32, i32]
     lib.accept_prefix_workspace_size.restype = sz
     lib.accept_prefix.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, sz, vp]
@@ -82,15 +85,51 @@ def _stream_handle():
     return torch.cuda.current_stream().cuda_stream
 
 
+def pack_weights(src, src_scales=None, stream=None):
+    """Tiled copy (MOE_LAYOUT_TILED) of stacked row-major matrices: bf16 src [n][rows][cols] (any
+    16-bit dtype), or mxfp4 codes [n][rows][cols/2] uint8 with scales [n][rows][cols/32]. A 2-D
+    input is one matrix. Returns (dst, dst_scales); library call."""
+    import torch
+    mx = src_scales is not None
+    shp = tuple(src.shape) if src.dim() == 3 else (1,) + tuple(src.shape)
+    n, rows = shp[0], shp[1]
+    cols = shp[2] * 2 if mx else shp[2]
+    src = src.contiguous()
+    dst = torch.empty_like(src)
+    dst_s = None
+    if mx:
+        src_scales = src_scales.contiguous()
+        dst_s = torch.empty_like(src_scales)
+    st = lib.moe_pack_weights(MOE_W_MXFP4 if mx else MOE_W_BF16, n, rows, cols, _ptr(src), _ptr(src_scales),
+                              _ptr(dst), _ptr(dst_s), _stream_handle() if stream is None else stream)
+    _check(st)
+    return dst, dst_s
+
+
 class MoeLayer:
     """Holds the device tensors of one MoE layer and the C descriptor that points at them.
 
-    bf16 weights are passed as int16/uint16/bfloat16 tensors of the documented shapes; mxfp4
-    weights as uint8 code tensors plus uint8 scale tensors."""
+    Expert matrices are in MOE_LAYOUT_TILED (see pack_weights / from_rowmajor): bf16 as 16-bit
+    tensors, mxfp4 as uint8 code tensors plus uint8 scale tensors, with the documented shapes."""
+
+    @classmethod
+    def from_rowmajor(cls, **kw):
+        """Packs row-major expert weights (pack_weights) and builds the layer from the copies."""
+        t = dict(kw)
+        mx = t.get("s_gate") is not None
+        for n in ("gate", "up", "down"):
+            if mx:
+                t["w_" + n], t["s_" + n] = pack_weights(t["w_" + n], t["s_" + n])
+            else:
+                t["w_" + n], _ = pack_weights(t["w_" + n])
+        for n in ("sh_gate", "sh_up", "sh_down"):
+            if t.get(n) is not None:
+                t[n], _ = pack_weights(t[n])
+        return cls(**t)
 
     def __init__(self, *, hidden, n_experts, top_k, inter, shared_inter, router_w, w_gate, w_up,
                  w_down, s_gate=None, s_up=None, s_down=None, sh_gate=None, sh_up=None,
-                 sh_down=None, rms_eps=1e-6):
+                 sh_down=None, rms_eps=1e-6, layout=MOE_LAYOUT_TILED):
         self.tensors = dict(router_w=router_w, w_gate=w_gate, w_up=w_up, w_down=w_down,
                             s_gate=s_gate, s_up=s_up, s_down=s_down, sh_gate=sh_gate,
                             sh_up=sh_up, sh_down=sh_down)
@@ -98,7 +137,7 @@ class MoeLayer:
         self.inter, self.shared_inter = inter, shared_inter
         self.wdtype = MOE_W_MXFP4 if s_gate is not None else MOE_W_BF16
         self.struct = MoeLayerStruct(
-            hidden, n_experts, top_k, inter, shared_inter, self.wdtype, rms_eps,
+            hidden, n_experts, top_k, inter, shared_inter, self.wdtype, layout, rms_eps,
             *(_ptr(self.tensors[n]) for n in ("router_w", "w_gate", "w_up", "w_down", "s_gate",
                                               "s_up", "s_down", "sh_gate", "sh_up", "sh_down")))
 

@@ -47,6 +47,8 @@ constexpr int NTH = NW * 64;      // threads per workgroup
 constexpr int MAX_E = 512;
 constexpr int MAX_K = 16;
 constexpr int MAX_U = KMAX * MAX_K;  // woken experts at most
+constexpr int HS_MAX = 4;            // H slices of the router at most
+static_assert(MAX_E <= NTH, "routing assigns one expert per thread");
 constexpr int GU_MX_RT = 2;       // gate/up row tiles per mxfp4 item (bf16: 1)
 constexpr int CG = 64;            // combine row group
 constexpr int AM_CHUNK = 8192;    // argmax values per workgroup
@@ -104,6 +106,54 @@ __device__ __forceinline__ int kofs(int j, int q) { return NAT ? 32 * j + 8 * q 
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
   if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
 }
+// Top-K sort key of logit v for expert e: larger logit first, then lower e; -0 counts as +0;
+// NaN ranks below every number (but above the 0 used for empty slots).
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  if (v != v) hi = 0u;
+  return ((uint64_t)hi << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ float topk_key_value(uint64_t key) {
+  const uint32_t hi = (uint32_t)(key >> 32);
+  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void cx_desc(uint64_t& a, uint64_t& b) {
+  const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
+  a = hi;
+  b = lo;
+}
+// Sorts 8 keys into descending order (19-comparator network).
+__device__ __forceinline__ void sort8_desc(uint64_t (&k)[8]) {
+  cx_desc(k[0], k[2]); cx_desc(k[1], k[3]); cx_desc(k[4], k[6]); cx_desc(k[5], k[7]);
+  cx_desc(k[0], k[4]); cx_desc(k[1], k[5]); cx_desc(k[2], k[6]); cx_desc(k[3], k[7]);
+  cx_desc(k[0], k[1]); cx_desc(k[2], k[3]); cx_desc(k[4], k[5]); cx_desc(k[6], k[7]);
+  cx_desc(k[2], k[4]); cx_desc(k[3], k[5]);
+  cx_desc(k[1], k[4]); cx_desc(k[3], k[6]);
+  cx_desc(k[1], k[2]); cx_desc(k[3], k[4]); cx_desc(k[5], k[6]);
+}
+// Maximum over the wave's 64 lanes, returned wave-uniform: DPP permutations inside each 16-lane
+// row (swap neighbours, swap pairs, mirror halves, mirror rows), then the four row results.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+  x = umax64(x, dpp_u64<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = umax64(x, dpp_u64<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = umax64(x, dpp_u64<0x141>(x));  // row_half_mirror
+  x = umax64(x, dpp_u64<0x140>(x));  // row_mirror
+  return umax64(umax64(readlane_u64(x, 0), readlane_u64(x, 16)), umax64(readlane_u64(x, 32), readlane_u64(x, 48)));
+}
+
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -132,7 +182,8 @@ struct Args {
   int32_t* tab_n;     // U
   int32_t* tab_woken; // [umax] woken expert ids, ascending
   int8_t* tab_slot;   // [umax][16] slot of token t for woken expert u, or -1
-  u32x4* xfrag;   // (H/32) k-steps x {hi, lo} x 64 lanes
+  u32x4* xfrag;   // (H/32) k-steps x {hi, lo} x 64 lanes, the layer's K order
+  u32x4* xfrag_nat;  // the same in the bf16 K order (mxfp4 layers with a shared expert)
   float* plog;    // [hs][16][E] partial raw logits
   float* psq;     // [hs][16] partial sums of squares
   u32x4* afrag;   // [umax][(I/32) x {hi, lo} x 64 lanes]
@@ -146,7 +197,6 @@ struct alignas(16) Smem {
   float red[16384];           // per-wave partial tiles (gate/up, down)
   float act[GU_MX_RT][256];   // reduced, activated gate/up tiles
   int ids[KMAX][MAX_K];
-  float val[KMAX][MAX_K];
   float w[KMAX][MAX_K];
   uint8_t flag[MAX_E];
   int pos[MAX_E];
@@ -160,6 +210,29 @@ struct alignas(16) Smem {
 // ------------------------------------------------------------------------------------------
 // router item (expert tile, H slice) with fp32 MFMA 16x16x4
 // ------------------------------------------------------------------------------------------
+// k-step s of the block as bf16 hi/lo MFMA B fragments in the K order of NAT
+template <bool NAT>
+__device__ __forceinline__ void write_xfrag(const float* x, u32x4* dst, int H, int k, int s, int lane) {
+  const int t = lane & 15, qq = lane >> 4, w = s >> 2, j = s & 3;
+  uint32_t hi[8], lo[8];
+  if (t < k) {
+    const float* src = x + (size_t)t * H + w * WIN + kofs<NAT>(j, qq);
+    const float4 v0 = *reinterpret_cast<const float4*>(src);
+    const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+    const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split_bf16(f[i], hi[i], lo[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hi[i] = lo[i] = 0u;
+  }
+  u32x4 h, l;
+  pack8(hi, h);
+  pack8(lo, l);
+  dst[((size_t)s * 2 + 0) * 64 + lane] = h;
+  dst[((size_t)s * 2 + 1) * 64 + lane] = l;
+}
+
 struct RouterSmem {
   float red[NW * 256];
   float rsq[NW][64];
@@ -207,27 +280,30 @@ __device__ void router_item(const Args& a, RouterSmem& S, int r, int wave, int l
       for (int qq = 0; qq < 4; ++qq) s += S.rsq[w][tid + 16 * qq];
     a.psq[hsi * KMAX + tid] = s;
   }
-  // B-operand fragments of the raw block: k-steps s = r + nr * (tid / 64) + 8 nr * i
+  // B-operand fragments of the raw block: k-steps s = r + nr * (tid / 64) + 8 nr * i. mxfp4
+  // layers with a shared expert also get the bf16 fragment order for the shared expert's tiles.
   const int nr = a.ntile_e * a.hs;
   for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) {
-    const int t = lane & 15, qq = lane >> 4, w = s >> 2, j = s & 3;
-    uint32_t hi[8], lo[8];
-    if (t < k) {
-      const float* src = a.x + (size_t)t * H + w * WIN + kofs<NAT>(j, qq);
-      const float4 v0 = *reinterpret_cast<const float4*>(src);
-      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    write_xfrag<NAT>(a.x, a.xfrag, H, k, s, lane);
+    if (!NAT && a.Is > 0) write_xfrag<true>(a.x, a.xfrag_nat, H, k, s, lane);
+  }
+}
+
+// K rounds over NC tokens' sorted candidate lists: the wave-wide maximum of the lane heads is
+// the next pick; the lane that held it pops its head; lane j records pick j.
+template <int NC>
+__device__ __forceinline__ void topk_rounds(uint64_t (&key)[2][8], int K, int lane, int (&my_id)[2],
+                                            float (&my_val)[2]) {
+  for (int j = 0; j < K; ++j) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) split_bf16(f[i], hi[i], lo[i]);
-    } else {
+    for (int c = 0; c < NC; ++c) {
+      const uint64_t win = wave_max_u64(key[c][0]);  // wave-uniform
+      const bool own = key[c][0] == win;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) hi[i] = lo[i] = 0u;
+      for (int m = 0; m < 7; ++m) key[c][m] = own ? key[c][m + 1] : key[c][m];
+      key[c][7] = own ? 0ull : key[c][7];
+      if (lane == j) { my_id[c] = (int)~(uint32_t)win; my_val[c] = topk_key_value(win); }
     }
-    u32x4 h, l;
-    pack8(hi, h);
-    pack8(lo, l);
-    a.xfrag[((size_t)s * 2 + 0) * 64 + lane] = h;
-    a.xfrag[((size_t)s * 2 + 1) * 64 + lane] = l;
   }
 }
 
@@ -236,46 +312,77 @@ __device__ void router_item(const Args& a, RouterSmem& S, int r, int wave, int l
 // ------------------------------------------------------------------------------------------
 __device__ void route(const Args& a, Smem& S, int wave, int lane, int tid) {
   const int E = a.E, K = a.K, k = a.k, hs = a.hs;
+  // Sum the router's H-slice partials into S.red[t * E + e]. Thread e loads all of expert e's
+  // partials unconditionally (clamped addresses, results selected) before the first is used, so
+  // the slab costs one memory round trip.
+  float* lg = S.red;
+  {
+    const int e = tid < E ? tid : 0;
+    float p[KMAX][HS_MAX];
+#pragma unroll
+    for (int t = 0; t < KMAX; ++t)
+#pragma unroll
+      for (int h = 0; h < HS_MAX; ++h)
+        p[t][h] = a.plog[((size_t)(h < hs ? h : 0) * KMAX + (t < k ? t : 0)) * E + e];
+#pragma unroll
+    for (int t = 0; t < KMAX; ++t) {
+      float sum = 0.f;
+#pragma unroll
+      for (int h = 0; h < HS_MAX; ++h) sum = h < hs ? sum + p[t][h] : sum;
+      if (t < k && tid < E) lg[t * E + tid] = sum;
+    }
+  }
   if (tid < KMAX) {
+    float p[HS_MAX];
+#pragma unroll
+    for (int h = 0; h < HS_MAX; ++h) p[h] = a.psq[(h < hs ? h : 0) * KMAX + tid];
     float ssq = 0.f;
-    for (int i = 0; i < hs; ++i) ssq += a.psq[i * KMAX + tid];
+#pragma unroll
+    for (int h = 0; h < HS_MAX; ++h) ssq = h < hs ? ssq + p[h] : ssq;
     S.rinv[tid] = a.pre_norm ? 1.0f / sqrtf(ssq / (float)a.H + a.eps) : 1.0f;
   }
   for (int i = tid; i < MAX_E; i += NTH) S.flag[i] = 0;
   __syncthreads();
-  for (int t = wave; t < k; t += NW) {
-    float v[MAX_E / 64];
-    uint32_t taken = 0;
-    const float rv = S.rinv[t];
+  // Top-K per token with 64-bit keys (order-preserving logit bits, then the inverted expert id,
+  // so ties go to the lower id). Each lane sorts its 8 candidates once; each of the K rounds
+  // takes the wave-wide maximum of the lane heads and the winning lane pops its head. Wave w
+  // serves tokens w and w + 8 together (independent chains interleave). Lane j keeps the j-th
+  // pick; softmax over the K picks in the same wave.
+  static_assert(MAX_E / 64 == 8 && KMAX == 2 * NW, "top-K layout");
+  for (int t0 = wave; t0 < k; t0 += 2 * NW) {
+    const int t1 = t0 + NW;
+    const bool two = t1 < k;  // wave-uniform
+    uint64_t key[2][8];
 #pragma unroll
-    for (int m = 0; m < MAX_E / 64; ++m) {
-      const int e = lane + 64 * m;
-      float s = 0.f;
-      if (e < E)
-        for (int i = 0; i < hs; ++i) s += a.plog[((size_t)i * KMAX + t) * E + e];
-      v[m] = rv * s;
-      if (e >= E) taken |= 1u << m;
+    for (int c = 0; c < 2; ++c) {
+      const int t = c ? (two ? t1 : t0) : t0;
+      const float rv = S.rinv[t];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int e = lane + 64 * m;
+        key[c][m] = e < E ? topk_key(rv * lg[t * E + e], e) : 0ull;
+      }
+      sort8_desc(key[c]);
     }
-    for (int j = 0; j < K; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+    int my_id[2] = {0, 0};
+    float my_val[2] = {0.f, 0.f};
+    if (two) topk_rounds<2>(key, K, lane, my_id, my_val);
+    else     topk_rounds<1>(key, K, lane, my_id, my_val);
 #pragma unroll
-      for (int m = 0; m < MAX_E / 64; ++m)
-        if (!((taken >> m) & 1u)) argmax_merge(bv, bi, v[m], lane + 64 * m);
-      wave_argmax(bv, bi);
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == 0) { S.ids[t][j] = bi; S.val[t][j] = bv; }
+    for (int c = 0; c < 2; ++c) {
+      if (c == 1 && !two) break;
+      const int t = c ? t1 : t0;
+      const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val[c]), 0));
+      const float ex = expf(my_val[c] - m0);
+      float sum = 0.f;
+      for (int j = 0; j < K; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+      if (lane < K) {
+        S.ids[t][lane] = my_id[c];
+        S.w[t][lane] = ex / sum;
+        S.flag[my_id[c]] = 1;
+      }
     }
   }
-  __syncthreads();
-  if (tid < k) {
-    const int t = tid;
-    const float m = S.val[t][0];
-    float sum = 0.f;
-    for (int j = 0; j < K; ++j) sum += expf(S.val[t][j] - m);
-    for (int j = 0; j < K; ++j) S.w[t][j] = expf(S.val[t][j] - m) / sum;
-  }
-  if (tid < k * K) S.flag[S.ids[tid / K][tid % K]] = 1;
   __syncthreads();
   if (wave == 0) {
     int base = 0;
@@ -336,32 +443,31 @@ struct GUDesc {
   const uint8_t* su;
 };
 
-// bf16 item (16 rows from g / up): lane (r, q) reads 16 B per k-step of each of its windows
-template <int WPW, bool NAT>
-__device__ __forceinline__ void gu_load_bf16(GUItem<WPW>& T, const uint8_t* g, const uint8_t* up, int H,
-                                             int win0, int lane) {
-  const int q = lane >> 4, r = lane & 15;
-  const uint32_t lo = (uint32_t)(r * H + win0 * WIN) * 2u;
+// bf16 item (one 16-row tile of g / up, tiled layout): lane reads its 16 B of each 1 KiB
+// fragment tile; the four k-steps of a window are 4 KiB contiguous.
+template <int WPW>
+__device__ __forceinline__ void gu_load_bf16(GUItem<WPW>& T, const uint8_t* g, const uint8_t* up, int win0,
+                                             int lane) {
 #pragma unroll
   for (int wi = 0; wi < WPW; ++wi)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t off = lo + (uint32_t)(wi * WIN + kofs<NAT>(j, q)) * 2u;
+      const uint32_t off = (uint32_t)((4 * (win0 + wi) + j) * 64 + lane) * 16u;
       T.v[(wi * 2 + 0) * 4 + j] = ld_stream(g + off);
       T.v[(wi * 2 + 1) * 4 + j] = ld_stream(up + off);
     }
 }
 
-// mxfp4 item (GU_MX_RT tiles of 16 rows): lane (r, q) reads one 32-value block per window
+// mxfp4 item (GU_MX_RT tiles of 16 rows, tiled layout): per (tile, window) the codes are 1 KiB
+// contiguous (lane = one 32-value block) and the scales 64 B contiguous.
 template <int WPW>
 __device__ __forceinline__ void gu_load_mx(GUItem<WPW>& T, const GUDesc& d, int H, int win0, int lane) {
-  const int q = lane >> 4, r = lane & 15;
 #pragma unroll
   for (int tl = 0; tl < GU_MX_RT; ++tl)
 #pragma unroll
     for (int wi = 0; wi < WPW; ++wi) {
-      const uint32_t off = (uint32_t)((16 * tl + r) * (H / 2) + (win0 + wi) * 64 + 16 * q);
-      const uint32_t soff = (uint32_t)((16 * tl + r) * (H / 32) + (win0 + wi) * 4 + q);
+      const uint32_t off = (uint32_t)(16 * tl * (H / 2) + ((win0 + wi) * 64 + lane) * 16);
+      const uint32_t soff = (uint32_t)(16 * tl * (H / 32) + (win0 + wi) * 64 + lane);
       T.v[(tl * WPW + wi) * 2 + 0] = ld_stream(d.g + off);
       T.v[(tl * WPW + wi) * 2 + 1] = ld_stream(d.up + off);
       T.sc[(tl * WPW + wi) * 2 + 0] = d.sg[soff];
@@ -457,6 +563,19 @@ __device__ __forceinline__ void gu_math_mx(f32x4 (&acc)[GU_MX_RT][2], const GUIt
       }
 }
 
+template <int WPW>
+__device__ __forceinline__ void gu_load_xb(u32x4 (&xb)[WPW][4][2], const u32x4* xf, int win0, bool active,
+                                           int lane) {
+#pragma unroll
+  for (int wi = 0; wi < WPW; ++wi)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int hl = 0; hl < 2; ++hl)
+        xb[wi][j][hl] = active ? ld16(xf + ((size_t)((win0 + wi) * 4 + j) * 2 + hl) * 64 + lane)
+                               : u32x4{0u, 0u, 0u, 0u};
+}
+
 // Routed item `idx` (or a valid stand-in when idx is out of range, so that every path issues
 // the same loads).
 template <bool MX>
@@ -484,7 +603,7 @@ __device__ __forceinline__ GUDesc gu_desc(const Args& a, const Smem& S, int idx,
 template <int WPW, bool MX>
 __device__ __forceinline__ void gu_load(GUItem<WPW>& T, const GUDesc& d, int H, int win0, int lane) {
   if (MX) gu_load_mx<WPW>(T, d, H, win0, lane);
-  else gu_load_bf16<WPW, true>(T, d.g, d.up, H, win0, lane);
+  else gu_load_bf16<WPW>(T, d.g, d.up, win0, lane);
 }
 
 template <int WPW, bool MX>
@@ -539,36 +658,37 @@ __device__ __forceinline__ DNDesc dn_desc(const Args& a, const Smem& S, int idx,
   return d;
 }
 
-template <int NWIN, bool NAT>
+// bf16 item (tiled layout): wave (window win, tile group tg) reads, for each of its tiles, the
+// window's four 1 KiB fragment tiles (4 KiB contiguous).
+template <int NWIN>
 __device__ __forceinline__ void dn_load_bf16(DNItem<NWIN>& T, const uint8_t* w, int I, int wave, int lane) {
   using SH = DnShape<NWIN>;
-  const int q = lane >> 4, r = lane & 15;
   const int win = wave % NWIN, tg = wave / NWIN;
 #pragma unroll
   for (int tl = 0; tl < SH::TPW_BF; ++tl) {
-    const uint32_t base = (uint32_t)(((tg * SH::TPW_BF + tl) * 16 + r) * I + win * WIN) * 2u;
+    const uint32_t base = (uint32_t)((tg * SH::TPW_BF + tl) * 16 * I) * 2u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) T.v[tl * 4 + j] = ld_stream(w + base + (uint32_t)kofs<NAT>(j, q) * 2u);
+    for (int j = 0; j < 4; ++j) T.v[tl * 4 + j] = ld_stream(w + base + (uint32_t)((4 * win + j) * 64 + lane) * 16u);
   }
 }
 
+// mxfp4 item (tiled layout): per (tile, window) 1 KiB of codes and 64 B of scales
 template <int NWIN>
 __device__ __forceinline__ void dn_load_mx(DNItem<NWIN>& T, const DNDesc& d, int I, int wave, int lane) {
   using SH = DnShape<NWIN>;
-  const int q = lane >> 4, r = lane & 15;
   const int win = wave % NWIN, tg = wave / NWIN;
 #pragma unroll
   for (int tl = 0; tl < SH::TPW_MX; ++tl) {
-    const int row = (tg * SH::TPW_MX + tl) * 16 + r;
-    T.v[tl] = ld_stream(d.w + (uint32_t)(row * (I / 2) + win * 64 + 16 * q));
-    T.sc[tl] = d.s[(uint32_t)(row * (I / 32) + win * 4 + q)];
+    const int tile = tg * SH::TPW_MX + tl;
+    T.v[tl] = ld_stream(d.w + (uint32_t)(tile * 16 * (I / 2) + (win * 64 + lane) * 16));
+    T.sc[tl] = d.s[(uint32_t)(tile * 16 * (I / 32) + win * 64 + lane)];
   }
 }
 
 template <int NWIN, bool MX>
 __device__ __forceinline__ void dn_load(DNItem<NWIN>& T, const DNDesc& d, int I, int wave, int lane) {
   if (MX) dn_load_mx<NWIN>(T, d, I, wave, lane);
-  else dn_load_bf16<NWIN, true>(T, d.w, I, wave, lane);
+  else dn_load_bf16<NWIN>(T, d.w, I, wave, lane);
 }
 
 // B fragments (down activations) of this wave's window for one expert slot
@@ -693,22 +813,15 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
   // requested first), then the routed items.
   const int n_sh = Is / 16;
   GUItem<WPW> Ts;
-  if (b < n_sh)
-    gu_load_bf16<WPW, NAT>(Ts, a.shg + (size_t)b * 16 * H * 2, a.shu + (size_t)b * 16 * H * 2, H, wsafe, lane);
+  if (b < n_sh) gu_load_bf16<WPW>(Ts, a.shg + (size_t)b * 16 * H * 2, a.shu + (size_t)b * 16 * H * 2, wsafe, lane);
 
   route(a, S, wave, lane, tid);
   const int U = __builtin_amdgcn_readfirstlane(S.nw);
 
-  // B fragments of this wave's H windows (the raw block), used by every item
+  // B fragments of this wave's H windows (the raw block), used by every item; the shared
+  // expert's tiles are bf16 and take the bf16 K order
   u32x4 xb[WPW][4][2];
-#pragma unroll
-  for (int wi = 0; wi < WPW; ++wi)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int hl = 0; hl < 2; ++hl)
-        xb[wi][j][hl] = active ? ld16(a.xfrag + ((size_t)((win0 + wi) * 4 + j) * 2 + hl) * 64 + lane)
-                               : u32x4{0u, 0u, 0u, 0u};
+  gu_load_xb<WPW>(xb, (MX && b < n_sh) ? a.xfrag_nat : a.xfrag, win0, active, lane);
 
   const int ipe = I / (16 * (MX ? GU_MX_RT : 1));
   const int n_gu = U * ipe;
@@ -716,8 +829,9 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
   if (p < n_sh) {
     f32x4 acc[GU_MX_RT][2];
     gu_math_bf16<WPW>(acc, Ts, xb);
-    gu_epilogue<NAT>(a, S, acc, 1, U, p * 16, false, wave, lane, tid);
+    gu_epilogue<true>(a, S, acc, 1, U, p * 16, false, wave, lane, tid);
     p += G;
+    if (MX) gu_load_xb<WPW>(xb, a.xfrag, win0, active, lane);
   }
   // routed items of this workgroup: r0, r0 + G, ...
   const int r0 = p - n_sh;
@@ -763,7 +877,7 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   // Item sequence: the shared expert's row groups (requested first), then the routed items.
   const int n_sh = Is > 0 ? H / (16 * SH::TPI_BF) : 0;
   DNItem<NWIN> Ts;
-  if (b < n_sh) dn_load_bf16<NWIN, NAT>(Ts, a.shd + (size_t)b * 16 * SH::TPI_BF * Is * 2, Is, wave, lane);
+  if (b < n_sh) dn_load_bf16<NWIN>(Ts, a.shd + (size_t)b * 16 * SH::TPI_BF * Is * 2, Is, wave, lane);
 
   const int U = __builtin_amdgcn_readfirstlane(a.tab_n[0]);
   for (int i = tid; i < U; i += NTH) S.woken[i] = a.tab_woken[i];
@@ -785,34 +899,70 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   const int q0 = p - n_sh;
   const int nmine = q0 < n_dn ? (n_dn - q0 + G - 1) / G : 0;
   if (nmine > 0) {
+    // weights and activation fragments of the next item are requested before this item's math
     DNItem<NWIN> T0, T1;
+    u32x4 b0[4][2], b1[4][2];
     DNDesc e0 = dn_desc<NWIN, MX>(a, S, q0, n_dn, ipe), e1;
     dn_load<NWIN, MX>(T0, e0, I, wave, lane);
+    dn_load_b<NWIN>(b0, a.afrag + (size_t)e0.u * (I / 32) * 128, wave, lane);
     for (int j = 0;;) {
-      u32x4 bf[4][2];
-      dn_load_b<NWIN>(bf, a.afrag + (size_t)e0.u * (I / 32) * 128, wave, lane);
       e1 = dn_desc<NWIN, MX>(a, S, q0 + (j + 1) * G, n_dn, ipe);  // a valid stand-in past the end
       dn_load<NWIN, MX>(T1, e1, I, wave, lane);
+      dn_load_b<NWIN>(b1, a.afrag + (size_t)e1.u * (I / 32) * 128, wave, lane);
       __builtin_amdgcn_sched_barrier(0);
       {
         f32x4 acc[SH::TPW_MX];
-        dn_math<NWIN, MX>(acc, T0, bf);
+        dn_math<NWIN, MX>(acc, T0, b0);
         dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
         dn_epilogue<NWIN>(a, S, e0.ntile, TPW, e0.u, true, e0.row0, tid);
       }
       if (++j >= nmine) break;
-      dn_load_b<NWIN>(bf, a.afrag + (size_t)e1.u * (I / 32) * 128, wave, lane);
       e0 = dn_desc<NWIN, MX>(a, S, q0 + (j + 1) * G, n_dn, ipe);
       dn_load<NWIN, MX>(T0, e0, I, wave, lane);
+      dn_load_b<NWIN>(b0, a.afrag + (size_t)e0.u * (I / 32) * 128, wave, lane);
       __builtin_amdgcn_sched_barrier(0);
       {
         f32x4 acc[SH::TPW_MX];
-        dn_math<NWIN, MX>(acc, T1, bf);
+        dn_math<NWIN, MX>(acc, T1, b1);
         dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
         dn_epilogue<NWIN>(a, S, e1.ntile, TPW, e1.u, true, e1.row0, tid);
       }
       if (++j >= nmine) break;
     }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// weight packing: row-major expert matrices -> fragment tiles (a pure permutation)
+// ------------------------------------------------------------------------------------------
+// bf16: 16-byte chunk c of the tiled array is (matrix m, row tile rt, k-step s, lane l) and holds
+// row 16 rt + l % 16, columns 32 s + 8 (l / 16) .. +7.
+__global__ void __launch_bounds__(256) k_pack_bf16(const uint8_t* src, uint8_t* dst, int rows, int cols,
+                                                   uint64_t n_chunks) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  const uint64_t per_mat = (uint64_t)rows * cols / 8;
+  const int ks = cols / 32;
+  for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n_chunks; c += stride) {
+    const uint64_t m = c / per_mat, rem = c % per_mat;
+    const int l = (int)(rem % 64), s = (int)((rem / 64) % ks), rt = (int)(rem / 64 / ks);
+    const uint64_t from = m * per_mat * 16 + ((uint64_t)(16 * rt + (l & 15)) * cols + 32 * s + 8 * (l >> 4)) * 2;
+    *reinterpret_cast<u32x4*>(dst + c * 16) = *reinterpret_cast<const u32x4*>(src + from);
+  }
+}
+
+// mxfp4: codes chunk c is (matrix m, row tile rt, window w, lane l) = the 16 code bytes of block
+// 4 w + l / 16 of row 16 rt + l % 16; scale byte c is that block's scale.
+__global__ void __launch_bounds__(256) k_pack_mx(const uint8_t* src, const uint8_t* src_s, uint8_t* dst,
+                                                 uint8_t* dst_s, int rows, int cols, uint64_t n_blocks) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  const uint64_t per_mat = (uint64_t)rows * cols / 32;
+  const int nw = cols / 128;
+  for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n_blocks; c += stride) {
+    const uint64_t m = c / per_mat, rem = c % per_mat;
+    const int l = (int)(rem % 64), w = (int)((rem / 64) % nw), rt = (int)(rem / 64 / nw);
+    const uint64_t blk = m * per_mat + (uint64_t)(16 * rt + (l & 15)) * (cols / 32) + 4 * w + (l >> 4);
+    *reinterpret_cast<u32x4*>(dst + c * 16) = *reinterpret_cast<const u32x4*>(src + blk * 16);
+    dst_s[c] = src_s[blk];
   }
 }
 
@@ -876,11 +1026,11 @@ __global__ void __launch_bounds__(64) k_accept_final(const float* pv, const int*
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t tab_n, tab_woken, tab_slot, xfrag, plog, psq, afrag, afrag_sh, part, total;
+  size_t tab_n, tab_woken, tab_slot, xfrag, xfrag_nat, plog, psq, afrag, afrag_sh, part, total;
   int umax, hs;
 };
 
-int router_splits(int H) { return H >= 2048 ? 4 : (H >= 1024 ? 2 : 1); }
+int router_splits(int H) { return H >= 2048 ? HS_MAX : (H >= 1024 ? 2 : 1); }
 
 Layout make_layout(const moe_layer* L, int k) {
   Layout o;
@@ -892,6 +1042,7 @@ Layout make_layout(const moe_layer* L, int k) {
   o.tab_woken = off; off = align256(off + (size_t)o.umax * 4);
   o.tab_slot = off;  off = align256(off + (size_t)o.umax * KMAX);
   o.xfrag = off;    off = align256(off + H * 64);
+  o.xfrag_nat = off; off = align256(off + H * 64);
   o.plog = off;     off = align256(off + (size_t)o.hs * KMAX * E * 4);
   o.psq = off;      off = align256(off + (size_t)o.hs * KMAX * 4);
   o.afrag = off;    off = align256(off + (size_t)o.umax * I * 64);
@@ -917,6 +1068,7 @@ int check_layer(const moe_layer* L) {
   if (I != 128 && I != 256 && I != 512 && I != 1024) return MOE_ERR_SHAPE;
   if (Is != 0 && Is != I) return MOE_ERR_SHAPE;
   if (L->wdtype != MOE_W_BF16 && L->wdtype != MOE_W_MXFP4) return MOE_ERR_DTYPE;
+  if (L->layout != MOE_LAYOUT_TILED) return MOE_ERR_DTYPE;
   if (L->wdtype == MOE_W_MXFP4 && H % 256) return MOE_ERR_SHAPE;  // mxfp4 down items are 256 rows
   if (!L->router_w || !L->w_gate || !L->w_up || !L->w_down) return MOE_ERR_NULL;
   if (L->wdtype == MOE_W_MXFP4 && (!L->s_gate || !L->s_up || !L->s_down)) return MOE_ERR_DTYPE;
@@ -980,7 +1132,7 @@ const char* moe_status_string(int status) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "a required pointer is NULL";
     case MOE_ERR_SHAPE: return "a size is outside the supported range";
-    case MOE_ERR_DTYPE: return "unknown weight format or missing mxfp4 scales";
+    case MOE_ERR_DTYPE: return "unknown weight format or layout, or missing mxfp4 scales";
     case MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_ALIAS: return "an output overlaps an input";
@@ -1028,7 +1180,7 @@ static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint
   a.shg = (const uint8_t*)L->sh_gate; a.shu = (const uint8_t*)L->sh_up; a.shd = (const uint8_t*)L->sh_down;
   a.tab_n = (int32_t*)(ws + lay.tab_n); a.tab_woken = (int32_t*)(ws + lay.tab_woken);
   a.tab_slot = (int8_t*)(ws + lay.tab_slot);
-  a.xfrag = (u32x4*)(ws + lay.xfrag); a.plog = (float*)(ws + lay.plog); a.psq = (float*)(ws + lay.psq);
+  a.xfrag = (u32x4*)(ws + lay.xfrag); a.xfrag_nat = (u32x4*)(ws + lay.xfrag_nat); a.plog = (float*)(ws + lay.plog); a.psq = (float*)(ws + lay.psq);
   a.afrag = (u32x4*)(ws + lay.afrag); a.afrag_sh = (u32x4*)(ws + lay.afrag_sh); a.part = (float*)(ws + lay.part);
   a.H = L->hidden; a.E = L->n_experts; a.K = L->top_k; a.I = L->inter; a.Is = L->shared_inter; a.k = k;
   a.hs = lay.hs; a.ntile_e = (L->n_experts + 15) / 16; a.umax = lay.umax;
@@ -1056,6 +1208,34 @@ int moe_verify_block_timed(const moe_layer* L, const float* x, int32_t k, uint32
                            size_t ws_bytes, void* hip_stream, void* const* events) {
   return verify_block_impl(L, x, k, flags, y, topk_ids, topk_w, n_woken, workspace, ws_bytes, hip_stream,
                            events);
+}
+
+int moe_pack_weights(int32_t wdtype, int32_t n_mats, int32_t rows, int32_t cols, const void* src,
+                     const uint8_t* src_scales, void* dst, uint8_t* dst_scales, void* hip_stream) {
+  if (!src || !dst) return MOE_ERR_NULL;
+  if (wdtype != MOE_W_BF16 && wdtype != MOE_W_MXFP4) return MOE_ERR_DTYPE;
+  if (wdtype == MOE_W_MXFP4 && (!src_scales || !dst_scales)) return MOE_ERR_NULL;
+  if (n_mats < 1 || rows < 16 || rows % 16 || cols < 128 || cols % 128 || rows > (1 << 20) ||
+      cols > (1 << 20) || n_mats > (1 << 20))
+    return MOE_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
+  const uint64_t elems = (uint64_t)n_mats * rows * cols;
+  const size_t bytes = wdtype == MOE_W_BF16 ? elems * 2 : elems / 2;
+  if (overlaps(src, bytes, dst, bytes)) return MOE_ERR_ALIAS;
+  if (wdtype == MOE_W_MXFP4 && (overlaps(src_scales, elems / 32, dst_scales, elems / 32) ||
+                                overlaps(dst_scales, elems / 32, src, bytes) ||
+                                overlaps(dst_scales, elems / 32, dst, bytes) ||
+                                overlaps(dst, bytes, src_scales, elems / 32)))
+    return MOE_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  const int grid = 2048;
+  if (wdtype == MOE_W_BF16)
+    k_pack_bf16<<<grid, 256, 0, s>>>((const uint8_t*)src, (uint8_t*)dst, rows, cols, elems / 8);
+  else
+    k_pack_mx<<<grid, 256, 0, s>>>((const uint8_t*)src, src_scales, (uint8_t*)dst, dst_scales, rows, cols,
+                                   elems / 32);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 size_t accept_prefix_workspace_size(int32_t n_target, int32_t vocab) {

@@ -76,7 +76,7 @@ def copy_bytes(dst: torch.Tensor, src: torch.Tensor):
 
 
 def layer_tensors(wl: gen.Workload, layer: int = 0, device="cuda") -> dict:
-    """All tensors of one MoE layer on the device, in the library's layouts."""
+    """All tensors of one MoE layer on the device, row-major (the oracle's layout)."""
     s = wl.shape
     E, H, I, Is = s.n_experts, s.hidden, s.inter, s.shared_inter
     t = {"router_w": torch.from_numpy(gen.router_weight(wl, layer)).to(device)}
@@ -103,9 +103,10 @@ def layer_tensors(wl: gen.Workload, layer: int = 0, device="cuda") -> dict:
 
 
 def make_layer(wl: gen.Workload, layer: int = 0, device="cuda", tensors: dict | None = None):
-    """A binding.MoeLayer for one generated layer (tensors kept alive by the object)."""
+    """A binding.MoeLayer for one generated layer: the row-major tensors are packed into the
+    library's tiled layout (the packed copies are kept alive by the object)."""
     from .. import binding
     s = wl.shape
     t = layer_tensors(wl, layer, device) if tensors is None else tensors
-    return binding.MoeLayer(hidden=s.hidden, n_experts=s.n_experts, top_k=s.top_k, inter=s.inter,
-                            shared_inter=s.shared_inter, rms_eps=wl.rms_eps, **t)
+    return binding.MoeLayer.from_rowmajor(hidden=s.hidden, n_experts=s.n_experts, top_k=s.top_k, inter=s.inter,
+                                          shared_inter=s.shared_inter, rms_eps=wl.rms_eps, **t)

@@ -47,7 +47,7 @@ FAKE = 0x7F0000000000  # 16-byte aligned stand-in address; never dereferenced by
 
 
 def _layer(b, **over):
-    d = dict(hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512, wdtype=0, rms_eps=1e-6,
+    d = dict(hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512, wdtype=0, layout=1, rms_eps=1e-6,
              router_w=FAKE, w_gate=FAKE + 0x1000, w_up=FAKE + 0x2000, w_down=FAKE + 0x3000, s_gate=None,
              s_up=None, s_down=None, sh_gate=FAKE + 0x4000, sh_up=FAKE + 0x5000, sh_down=FAKE + 0x6000)
     d.update(over)
@@ -77,7 +77,7 @@ def test_workspace_size(b):
     (dict(hidden=100), -2), (dict(hidden=64), -2), (dict(hidden=4096), -2), (dict(hidden=1152), -2),
     (dict(n_experts=0), -2), (dict(n_experts=513), -2), (dict(top_k=0), -2), (dict(top_k=17), -2),
     (dict(n_experts=4, top_k=5), -2), (dict(inter=384), -2), (dict(inter=2048), -2),
-    (dict(shared_inter=256), -2), (dict(wdtype=2), -3), (dict(wdtype=1), -3),
+    (dict(shared_inter=256), -2), (dict(wdtype=2), -3), (dict(wdtype=1), -3), (dict(layout=0), -3),
     (dict(router_w=None), -1), (dict(w_down=None), -1), (dict(sh_up=None), -1),
     (dict(w_gate=FAKE + 8), -4), (dict(rms_eps=-1.0), -8), (dict(rms_eps=float("nan")), -8),
 ])
@@ -134,3 +134,20 @@ def test_accept_prefix_validation(b):
     assert f(lg, 17, 151936, dr, 16, tg, ac, ws, need - 1, None) == -5
     assert f(lg, 17, 151936, dr, 16, lg + 64, ac, ws, need, None) == -6
     assert f(lg, 17, 151936, dr, 16, tg, tg, ws, need, None) == -6
+
+
+def test_pack_weights_validation(b):
+    f = b.lib.moe_pack_weights
+    src, dst, ss, ds = FAKE, FAKE + 0x10000000, FAKE + 0x20000000, FAKE + 0x30000000
+    assert f(0, 4, 512, 2048, None, None, dst, None, None) == -1
+    assert f(0, 4, 512, 2048, src, None, None, None, None) == -1
+    assert f(1, 4, 512, 2048, src, None, dst, ds, None) == -1   # mxfp4 without source scales
+    assert f(1, 4, 512, 2048, src, ss, dst, None, None) == -1
+    assert f(2, 4, 512, 2048, src, None, dst, None, None) == -3
+    assert f(0, 0, 512, 2048, src, None, dst, None, None) == -2
+    assert f(0, 4, 520, 2048, src, None, dst, None, None) == -2  # rows not a multiple of 16
+    assert f(0, 4, 512, 2000, src, None, dst, None, None) == -2  # cols not a multiple of 128
+    assert f(0, 4, 512, 64, src, None, dst, None, None) == -2
+    assert f(0, 4, 512, 2048, src + 8, None, dst, None, None) == -4
+    assert f(0, 4, 512, 2048, src, None, src + 4096, None, None) == -6   # dst overlaps src
+    assert f(1, 1, 512, 2048, src, ss, dst, ss + 16, None) == -6          # scales overlap

@@ -360,3 +360,25 @@ def test_accept_prefix_max_rows(B):
     t_ref = oracle.argmax_first(logits)
     tg, a = run_accept(B, logits, t_ref[:63])
     assert np.array_equal(tg, t_ref) and a == 63
+
+
+# ---- weight packing (bit-exact permutation) ---------------------------------------------------
+@pytest.mark.parametrize("n,rows,cols", [(1, 16, 128), (3, 48, 384), (2, 512, 2048), (4, 2048, 512)])
+def test_pack_weights_bf16_matches_oracle(B, n, rows, cols):
+    rng = np.random.default_rng(rows * 7 + cols)
+    w = rng.integers(0, 1 << 16, size=(n, rows, cols), dtype=np.uint16)
+    dst, _ = B.pack_weights(torch.from_numpy(w.view(np.int16)).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy().view(np.uint16), oracle.tile_bf16(w))
+
+
+@pytest.mark.parametrize("n,rows,cols", [(1, 16, 128), (3, 48, 384), (2, 512, 2048), (4, 2048, 512)])
+def test_pack_weights_mxfp4_matches_oracle(B, n, rows, cols):
+    rng = np.random.default_rng(rows * 11 + cols)
+    codes = rng.integers(0, 256, size=(n, rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(n, rows, cols // 32), dtype=np.uint8)
+    dc, ds = B.pack_weights(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda())
+    torch.cuda.synchronize()
+    rc, rs = oracle.tile_mxfp4(codes, scales)
+    assert np.array_equal(dc.cpu().numpy(), rc)
+    assert np.array_equal(ds.cpu().numpy(), rs)

@@ -414,3 +414,52 @@ def test_signed_zero_worked_example():
         for i, j, v, bits in rows:
             assert D[int(i), int(j)] == float(v)
             assert struct.unpack("<I", struct.pack("<f", D[int(i), int(j)]))[0] == int(bits, 16)
+
+
+# ---- tiled storage layout -------------------------------------------------------------------
+def test_tile_bf16_hand_positions():
+    """Positions read off the layout's definition by hand, for a 32 x 256 matrix whose entry is
+    its own row-major index: slice l of tile (band, step) starts at chunk (band*8 + step)*64 + l."""
+    from oracle import tile_bf16
+    R, C = 32, 256
+    w = np.arange(R * C, dtype=np.int64).reshape(R, C)
+    t = tile_bf16(w).reshape(-1)
+    assert t[0] == 0                     # band 0, step 0, slice 0: W[0][0]
+    assert t[8] == 1 * C                 # slice 1 -> row 1, column 0
+    assert t[15 * 8] == 15 * C           # slice 15 -> row 15
+    assert t[16 * 8] == 8                # slice 16 -> row 0, columns 8..15
+    assert t[16 * 8 + 7] == 15
+    assert t[63 * 8] == 15 * C + 24      # slice 63 -> row 15, columns 24..31
+    assert t[64 * 8] == 32               # next step: row 0, column 32
+    assert t[8 * 64 * 8] == 16 * C       # band 1 starts after C/32 = 8 steps: row 16
+    assert t[-1] == R * C - 1            # last element stays last
+
+
+def test_tile_bf16_is_a_permutation_and_matches_position_formula():
+    from oracle import tile_bf16, tiled_position_bf16
+    rng = np.random.default_rng(5)
+    w = rng.integers(0, 1 << 16, size=(3, 48, 384), dtype=np.uint16)
+    t = tile_bf16(w)
+    assert np.array_equal(np.sort(t.reshape(-1)), np.sort(w.reshape(-1)))
+    for m, row, col in [(0, 0, 0), (1, 47, 383), (2, 17, 130), (0, 31, 95), (1, 5, 200)]:
+        assert t[m].reshape(-1)[tiled_position_bf16(48, 384, row, col)] == w[m, row, col]
+
+
+def test_tile_mxfp4_hand_positions():
+    """Block b of row r occupies code bytes 16 b .. 16 b + 15; in the tiled order slice l of
+    window w (band 0) is block 4 w + l // 16 of row l % 16."""
+    from oracle import tile_mxfp4
+    R, C = 16, 256                                    # 2 windows of 4 blocks per row
+    blk = np.arange(R * C // 32, dtype=np.int64).reshape(R, C // 32)   # block id = row * 8 + block
+    codes = np.repeat(blk[:, :, None], 16, axis=2).reshape(R, C // 2) % 256
+    scales = (blk % 256).astype(np.int64)
+    tc, ts = tile_mxfp4(codes, scales)
+    tcb = tc.reshape(-1, 16)
+    assert np.all(tcb == tcb[:, :1])                  # 16-byte slices stay whole
+    ids = tcb[:, 0]
+    assert ids[0] == 0                                # window 0, slice 0: row 0 block 0
+    assert ids[1] == 8                                # slice 1: row 1 block 0
+    assert ids[16] == 1                               # slice 16: row 0 block 1
+    assert ids[63] == 15 * 8 + 3                      # slice 63: row 15 block 3
+    assert ids[64] == 4                               # window 1, slice 0: row 0 block 4
+    assert np.array_equal(ts.reshape(-1), ids)        # each scale travels with its block
