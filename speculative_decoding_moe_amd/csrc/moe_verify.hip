@@ -50,7 +50,6 @@ constexpr int MAX_U = KMAX * MAX_K;  // woken experts at most
 constexpr int HS_MAX = 4;            // H slices of the router at most
 static_assert(MAX_E <= NTH, "routing assigns one expert per thread");
 constexpr int GU_MX_RT = 2;       // gate/up row tiles per mxfp4 item (bf16: 1)
-constexpr int CG = 64;            // combine row group
 constexpr int AM_CHUNK = 8192;    // argmax values per workgroup
 
 
@@ -63,9 +62,23 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Weights are read once per call: nontemporal 128-bit loads.
-__device__ __forceinline__ u32x4 ld_stream(const void* p) {
-  return __builtin_nontemporal_load((const u32x4*)p);
+// Buffer loads for the weight streams: an SGPR resource per tensor, a per-lane constant VGPR
+// offset, the tile step as an immediate and the item offset in an SGPR, so the streaming loops do
+// no per-load address arithmetic in VGPRs. Loads are nontemporal; offsets past `bytes` read 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int BUF_NT = 2;
+__device__ __forceinline__ rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, BUF_NT);
+}
+// cached (the down kernel's activation fragments are re-read by every row group of an expert)
+__device__ __forceinline__ u32x4 bld16_cached(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bld1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, BUF_NT);
 }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 
@@ -437,41 +450,43 @@ struct GUItem {
 
 struct GUDesc {
   int u, row0, ntile;
-  const uint8_t* g;
-  const uint8_t* up;
-  const uint8_t* sg;
-  const uint8_t* su;
+  uint32_t off;   // byte offset of the item in the gate / up tensors (codes for mxfp4)
+  uint32_t soff;  // byte offset of the item's scales (mxfp4)
+};
+
+// buffer resources of the gate/up kernel's weight streams
+struct GURes {
+  rsrc_t g, u, sg, su;
 };
 
 // bf16 item (one 16-row tile of g / up, tiled layout): lane reads its 16 B of each 1 KiB
 // fragment tile; the four k-steps of a window are 4 KiB contiguous.
 template <int WPW>
-__device__ __forceinline__ void gu_load_bf16(GUItem<WPW>& T, const uint8_t* g, const uint8_t* up, int win0,
-                                             int lane) {
+__device__ __forceinline__ void gu_load_bf16(GUItem<WPW>& T, rsrc_t rg, rsrc_t ru, uint32_t soff, uint32_t vb) {
 #pragma unroll
   for (int wi = 0; wi < WPW; ++wi)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t off = (uint32_t)((4 * (win0 + wi) + j) * 64 + lane) * 16u;
-      T.v[(wi * 2 + 0) * 4 + j] = ld_stream(g + off);
-      T.v[(wi * 2 + 1) * 4 + j] = ld_stream(up + off);
+      const uint32_t o = vb + (uint32_t)((4 * wi + j) * 1024);
+      T.v[(wi * 2 + 0) * 4 + j] = bld16(rg, o, soff);
+      T.v[(wi * 2 + 1) * 4 + j] = bld16(ru, o, soff);
     }
 }
 
 // mxfp4 item (GU_MX_RT tiles of 16 rows, tiled layout): per (tile, window) the codes are 1 KiB
 // contiguous (lane = one 32-value block) and the scales 64 B contiguous.
 template <int WPW>
-__device__ __forceinline__ void gu_load_mx(GUItem<WPW>& T, const GUDesc& d, int H, int win0, int lane) {
+__device__ __forceinline__ void gu_load_mx(GUItem<WPW>& T, const GURes& R, const GUDesc& d, int H, uint32_t vbc,
+                                           uint32_t vbs) {
 #pragma unroll
   for (int tl = 0; tl < GU_MX_RT; ++tl)
 #pragma unroll
     for (int wi = 0; wi < WPW; ++wi) {
-      const uint32_t off = (uint32_t)(16 * tl * (H / 2) + ((win0 + wi) * 64 + lane) * 16);
-      const uint32_t soff = (uint32_t)(16 * tl * (H / 32) + (win0 + wi) * 64 + lane);
-      T.v[(tl * WPW + wi) * 2 + 0] = ld_stream(d.g + off);
-      T.v[(tl * WPW + wi) * 2 + 1] = ld_stream(d.up + off);
-      T.sc[(tl * WPW + wi) * 2 + 0] = d.sg[soff];
-      T.sc[(tl * WPW + wi) * 2 + 1] = d.su[soff];
+      const uint32_t sc = d.off + (uint32_t)(16 * tl * (H / 2)), ss = d.soff + (uint32_t)(16 * tl * (H / 32));
+      T.v[(tl * WPW + wi) * 2 + 0] = bld16(R.g, vbc + wi * 1024, sc);
+      T.v[(tl * WPW + wi) * 2 + 1] = bld16(R.u, vbc + wi * 1024, sc);
+      T.sc[(tl * WPW + wi) * 2 + 0] = bld1(R.sg, vbs + wi * 64, ss);
+      T.sc[(tl * WPW + wi) * 2 + 1] = bld1(R.su, vbs + wi * 64, ss);
     }
 }
 
@@ -576,34 +591,54 @@ __device__ __forceinline__ void gu_load_xb(u32x4 (&xb)[WPW][4][2], const u32x4* 
                                : u32x4{0u, 0u, 0u, 0u};
 }
 
+// The woken-expert list held across the lanes of every wave: lane l keeps entries l, l + 64, ...
+// A lookup is v_readlane with a uniform lane index, so an item descriptor is computed without
+// writing any VGPR: the streaming loops then never overwrite, between an epilogue's stores and
+// the next loads, a register that the waitcnt logic would have to drain first.
+struct Woken {
+  int v[MAX_U / 64];
+};
+__device__ __forceinline__ Woken load_woken(const Smem& S, int lane) {
+  Woken w;
+#pragma unroll
+  for (int m = 0; m < MAX_U / 64; ++m) w.v[m] = S.woken[lane + 64 * m];
+  return w;
+}
+__device__ __forceinline__ uint32_t woken_at(const Woken& w, int u) {  // u wave-uniform
+  const int l = u & 63, m = u >> 6;
+  int e = __builtin_amdgcn_readlane(w.v[0], l);
+#pragma unroll
+  for (int i = 1; i < MAX_U / 64; ++i)
+    if (m == i) e = __builtin_amdgcn_readlane(w.v[i], l);
+  return (uint32_t)e;
+}
+
 // Routed item `idx` (or a valid stand-in when idx is out of range, so that every path issues
 // the same loads).
 template <bool MX>
-__device__ __forceinline__ GUDesc gu_desc(const Args& a, const Smem& S, int idx, int n_items, int ipe) {
+__device__ __forceinline__ GUDesc gu_desc(const Args& a, const Woken& wk, int idx, int n_items, int ipe) {
   const int it = idx < n_items ? idx : 0;
   GUDesc d;
   d.u = it / ipe;
   d.ntile = MX ? GU_MX_RT : 1;
   d.row0 = (it % ipe) * 16 * d.ntile;
-  const size_t H = a.H, I = a.I;
-  const size_t e = (size_t)__builtin_amdgcn_readfirstlane(S.woken[d.u]);
+  const uint32_t e = woken_at(wk, d.u);
+  const uint32_t row = e * (uint32_t)a.I + (uint32_t)d.row0;  // tensor row of the item's first tile
   if (MX) {
-    d.g = a.wg + e * I * (H / 2) + (size_t)d.row0 * (H / 2);
-    d.up = a.wu + e * I * (H / 2) + (size_t)d.row0 * (H / 2);
-    d.sg = a.sg + e * I * (H / 32) + (size_t)d.row0 * (H / 32);
-    d.su = a.su + e * I * (H / 32) + (size_t)d.row0 * (H / 32);
+    d.off = row * (uint32_t)(a.H / 2);
+    d.soff = row * (uint32_t)(a.H / 32);
   } else {
-    d.g = a.wg + (e * I + d.row0) * H * 2;
-    d.up = a.wu + (e * I + d.row0) * H * 2;
-    d.sg = d.su = nullptr;
+    d.off = row * (uint32_t)(a.H * 2);
+    d.soff = 0;
   }
   return d;
 }
 
 template <int WPW, bool MX>
-__device__ __forceinline__ void gu_load(GUItem<WPW>& T, const GUDesc& d, int H, int win0, int lane) {
-  if (MX) gu_load_mx<WPW>(T, d, H, win0, lane);
-  else gu_load_bf16<WPW>(T, d.g, d.up, win0, lane);
+__device__ __forceinline__ void gu_load(GUItem<WPW>& T, const GURes& R, const GUDesc& d, int H, uint32_t vbc,
+                                        uint32_t vbs) {
+  if (MX) gu_load_mx<WPW>(T, R, d, H, vbc, vbs);
+  else gu_load_bf16<WPW>(T, R.g, R.u, d.off, vbc);
 }
 
 template <int WPW, bool MX>
@@ -634,26 +669,26 @@ struct DNItem {
 
 struct DNDesc {
   int u, row0, ntile;
-  const uint8_t* w;
-  const uint8_t* s;
+  uint32_t off;   // byte offset of the item in the down tensor (codes for mxfp4)
+  uint32_t soff;  // byte offset of the item's scales (mxfp4)
 };
 
 template <int NWIN, bool MX>
-__device__ __forceinline__ DNDesc dn_desc(const Args& a, const Smem& S, int idx, int n_items, int ipe) {
+__device__ __forceinline__ DNDesc dn_desc(const Args& a, const Woken& wk, int idx, int n_items, int ipe) {
   using SH = DnShape<NWIN>;
   const int it = idx < n_items ? idx : 0;
   DNDesc d;
   d.u = it / ipe;
   d.ntile = MX ? SH::TPI_MX : SH::TPI_BF;
   d.row0 = (it % ipe) * 16 * d.ntile;
-  const size_t H = a.H, I = a.I;
-  const size_t e = (size_t)__builtin_amdgcn_readfirstlane(S.woken[d.u]);
+  const uint32_t e = woken_at(wk, d.u);
+  const uint32_t row = e * (uint32_t)a.H + (uint32_t)d.row0;  // tensor row of the item's first tile
   if (MX) {
-    d.w = a.wd + e * H * (I / 2) + (size_t)d.row0 * (I / 2);
-    d.s = a.sd + e * H * (I / 32) + (size_t)d.row0 * (I / 32);
+    d.off = row * (uint32_t)(a.I / 2);
+    d.soff = row * (uint32_t)(a.I / 32);
   } else {
-    d.w = a.wd + (e * H + d.row0) * I * 2;
-    d.s = nullptr;
+    d.off = row * (uint32_t)(a.I * 2);
+    d.soff = 0;
   }
   return d;
 }
@@ -661,44 +696,48 @@ __device__ __forceinline__ DNDesc dn_desc(const Args& a, const Smem& S, int idx,
 // bf16 item (tiled layout): wave (window win, tile group tg) reads, for each of its tiles, the
 // window's four 1 KiB fragment tiles (4 KiB contiguous).
 template <int NWIN>
-__device__ __forceinline__ void dn_load_bf16(DNItem<NWIN>& T, const uint8_t* w, int I, int wave, int lane) {
+__device__ __forceinline__ void dn_load_bf16(DNItem<NWIN>& T, rsrc_t rw, uint32_t soff, int I, int wave, int lane) {
   using SH = DnShape<NWIN>;
   const int win = wave % NWIN, tg = wave / NWIN;
+  const uint32_t vb = (uint32_t)(256 * win + lane) * 16u;
 #pragma unroll
   for (int tl = 0; tl < SH::TPW_BF; ++tl) {
-    const uint32_t base = (uint32_t)((tg * SH::TPW_BF + tl) * 16 * I) * 2u;
+    const uint32_t st = soff + (uint32_t)((tg * SH::TPW_BF + tl) * 16 * I * 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) T.v[tl * 4 + j] = ld_stream(w + base + (uint32_t)((4 * win + j) * 64 + lane) * 16u);
+    for (int j = 0; j < 4; ++j) T.v[tl * 4 + j] = bld16(rw, vb + j * 1024, st);
   }
 }
 
 // mxfp4 item (tiled layout): per (tile, window) 1 KiB of codes and 64 B of scales
 template <int NWIN>
-__device__ __forceinline__ void dn_load_mx(DNItem<NWIN>& T, const DNDesc& d, int I, int wave, int lane) {
+__device__ __forceinline__ void dn_load_mx(DNItem<NWIN>& T, rsrc_t rw, rsrc_t rs, const DNDesc& d, int I, int wave,
+                                           int lane) {
   using SH = DnShape<NWIN>;
   const int win = wave % NWIN, tg = wave / NWIN;
 #pragma unroll
   for (int tl = 0; tl < SH::TPW_MX; ++tl) {
     const int tile = tg * SH::TPW_MX + tl;
-    T.v[tl] = ld_stream(d.w + (uint32_t)(tile * 16 * (I / 2) + (win * 64 + lane) * 16));
-    T.sc[tl] = d.s[(uint32_t)(tile * 16 * (I / 32) + win * 64 + lane)];
+    T.v[tl] = bld16(rw, (uint32_t)(win * 64 + lane) * 16u, d.off + (uint32_t)(tile * 16 * (I / 2)));
+    T.sc[tl] = bld1(rs, (uint32_t)(win * 64 + lane), d.soff + (uint32_t)(tile * 16 * (I / 32)));
   }
 }
 
 template <int NWIN, bool MX>
-__device__ __forceinline__ void dn_load(DNItem<NWIN>& T, const DNDesc& d, int I, int wave, int lane) {
-  if (MX) dn_load_mx<NWIN>(T, d, I, wave, lane);
-  else dn_load_bf16<NWIN>(T, d.w, I, wave, lane);
+__device__ __forceinline__ void dn_load(DNItem<NWIN>& T, rsrc_t rw, rsrc_t rs, const DNDesc& d, int I, int wave,
+                                        int lane) {
+  if (MX) dn_load_mx<NWIN>(T, rw, rs, d, I, wave, lane);
+  else dn_load_bf16<NWIN>(T, rw, d.off, I, wave, lane);
 }
 
 // B fragments (down activations) of this wave's window for one expert slot
 template <int NWIN>
-__device__ __forceinline__ void dn_load_b(u32x4 (&bf)[4][2], const u32x4* af, int wave, int lane) {
+__device__ __forceinline__ void dn_load_b(u32x4 (&bf)[4][2], rsrc_t raf, uint32_t soff, int wave, int lane) {
   const int win = wave % NWIN;
+  const uint32_t vb = (uint32_t)(512 * win + lane) * 16u;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int hl = 0; hl < 2; ++hl) bf[j][hl] = ld16(af + ((size_t)(win * 4 + j) * 2 + hl) * 64 + lane);
+    for (int hl = 0; hl < 2; ++hl) bf[j][hl] = bld16_cached(raf, vb + (uint32_t)((j * 2 + hl) * 1024), soff);
 }
 
 template <int NWIN, bool MX>
@@ -810,11 +849,21 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
   const int wsafe = active ? win0 : 0; // inactive waves load window 0 and multiply it by zero
 
   // Item sequence: the shared expert's row tiles (known before routing, so their weights are
-  // requested first), then the routed items.
+  // requested first), then the routed items, dealt round-robin over the workgroups.
   const int n_sh = Is / 16;
   GUItem<WPW> Ts;
-  if (b < n_sh) gu_load_bf16<WPW>(Ts, a.shg + (size_t)b * 16 * H * 2, a.shu + (size_t)b * 16 * H * 2, wsafe, lane);
-
+  const uint32_t E = a.E;
+  GURes R;
+  const uint32_t wbytes = MX ? E * I * (H / 2) : E * I * H * 2;
+  R.g = buf_rsrc(a.wg, wbytes);
+  R.u = buf_rsrc(a.wu, wbytes);
+  R.sg = buf_rsrc(a.sg, MX ? E * I * (H / 32) : 0);
+  R.su = buf_rsrc(a.su, MX ? E * I * (H / 32) : 0);
+  const uint32_t vbb = (uint32_t)(256 * wsafe + lane) * 16u;            // bf16 tiles
+  const uint32_t vbc = MX ? (uint32_t)(64 * wsafe + lane) * 16u : vbb;  // this layer's tiles
+  const uint32_t vbs = (uint32_t)(64 * wsafe + lane);                   // mxfp4 scales
+  if (b < n_sh)
+    gu_load_bf16<WPW>(Ts, buf_rsrc(a.shg, Is * H * 2), buf_rsrc(a.shu, Is * H * 2), (uint32_t)(b * 16 * H * 2), vbb);
   route(a, S, wave, lane, tid);
   const int U = __builtin_amdgcn_readfirstlane(S.nw);
 
@@ -829,44 +878,44 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
   if (p < n_sh) {
     f32x4 acc[GU_MX_RT][2];
     gu_math_bf16<WPW>(acc, Ts, xb);
-    gu_epilogue<true>(a, S, acc, 1, U, p * 16, false, wave, lane, tid);
+    gu_epilogue<true>(a, S, acc, 1, U, b * 16, false, wave, lane, tid);
     p += G;
     if (MX) gu_load_xb<WPW>(xb, a.xfrag, win0, active, lane);
   }
-  // routed items of this workgroup: r0, r0 + G, ...
+  // routed items of this workgroup: r0, r0 + G, ... (the next item's loads are in flight while
+  // this item is multiplied)
   const int r0 = p - n_sh;
   const int nmine = r0 < n_gu ? (n_gu - r0 + G - 1) / G : 0;
-  if (nmine > 0) {
-    GUItem<WPW> T0, T1;
-    GUDesc d0 = gu_desc<MX>(a, S, r0, n_gu, ipe), d1;
-    gu_load<WPW, MX>(T0, d0, H, wsafe, lane);
-    for (int j = 0;;) {
-      d1 = gu_desc<MX>(a, S, r0 + (j + 1) * G, n_gu, ipe);  // a valid stand-in past the end
-      gu_load<WPW, MX>(T1, d1, H, wsafe, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        f32x4 acc[GU_MX_RT][2];
-        gu_math<WPW, MX>(acc, T0, xb);
-        gu_epilogue<NAT>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid);
-      }
-      if (++j >= nmine) break;
-      d0 = gu_desc<MX>(a, S, r0 + (j + 1) * G, n_gu, ipe);
-      gu_load<WPW, MX>(T0, d0, H, wsafe, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        f32x4 acc[GU_MX_RT][2];
-        gu_math<WPW, MX>(acc, T1, xb);
-        gu_epilogue<NAT>(a, S, acc, d1.ntile, d1.u, d1.row0, true, wave, lane, tid);
-      }
-      if (++j >= nmine) break;
+  if (nmine == 0) return;
+  const Woken wk = load_woken(S, lane);
+  GUItem<WPW> T0, T1;
+  GUDesc d0 = gu_desc<MX>(a, wk, r0, n_gu, ipe), d1;
+  gu_load<WPW, MX>(T0, R, d0, H, vbc, vbs);
+  for (int j = 0;;) {
+    d1 = gu_desc<MX>(a, wk, r0 + (j + 1) * G, n_gu, ipe);  // a valid stand-in past the end
+    gu_load<WPW, MX>(T1, R, d1, H, vbc, vbs);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      f32x4 acc[GU_MX_RT][2];
+      gu_math<WPW, MX>(acc, T0, xb);
+      gu_epilogue<NAT>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid);
     }
+    if (++j >= nmine) break;
+    d0 = gu_desc<MX>(a, wk, r0 + (j + 1) * G, n_gu, ipe);
+    gu_load<WPW, MX>(T0, R, d0, H, vbc, vbs);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      f32x4 acc[GU_MX_RT][2];
+      gu_math<WPW, MX>(acc, T1, xb);
+      gu_epilogue<NAT>(a, S, acc, d1.ntile, d1.u, d1.row0, true, wave, lane, tid);
+    }
+    if (++j >= nmine) break;
   }
 }
 
 template <int NWIN, bool MX>
 __global__ void __launch_bounds__(NTH) k_down(Args a) {
   using SH = DnShape<NWIN>;
-  constexpr bool NAT = !MX;
   constexpr int TPW = MX ? SH::TPW_MX : SH::TPW_BF;
   __shared__ Smem S;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -874,11 +923,15 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   const int H = a.H, I = a.I, Is = a.Is;
   const int G = gridDim.x, b = blockIdx.x;
 
-  // Item sequence: the shared expert's row groups (requested first), then the routed items.
+  // Item sequence: the shared expert's row groups (requested first), then the routed items,
+  // dealt round-robin over the workgroups.
   const int n_sh = Is > 0 ? H / (16 * SH::TPI_BF) : 0;
   DNItem<NWIN> Ts;
-  if (b < n_sh) dn_load_bf16<NWIN>(Ts, a.shd + (size_t)b * 16 * SH::TPI_BF * Is * 2, Is, wave, lane);
-
+  const uint32_t E = a.E;
+  const rsrc_t rw = buf_rsrc(a.wd, MX ? E * H * (I / 2) : E * H * I * 2);
+  const rsrc_t rs = buf_rsrc(a.sd, MX ? E * H * (I / 32) : 0);
+  const rsrc_t raf = buf_rsrc(a.afrag, (uint32_t)a.umax * (I / 32) * 2048);
+  if (b < n_sh) dn_load_bf16<NWIN>(Ts, buf_rsrc(a.shd, H * Is * 2), (uint32_t)(b * 16 * SH::TPI_BF * Is * 2), Is, wave, lane);
   const int U = __builtin_amdgcn_readfirstlane(a.tab_n[0]);
   for (int i = tid; i < U; i += NTH) S.woken[i] = a.tab_woken[i];
   for (int i = tid; i < U * KMAX; i += NTH) S.slot[i / KMAX][i % KMAX] = a.tab_slot[i];
@@ -889,46 +942,46 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   int p = b;
   if (p < n_sh) {
     u32x4 bf[4][2];
-    dn_load_b<NWIN>(bf, a.afrag_sh, wave, lane);
+    dn_load_b<NWIN>(bf, buf_rsrc(a.afrag_sh, (Is / 32) * 2048), 0u, wave, lane);
     f32x4 acc[SH::TPW_MX];
     dn_math<NWIN, false>(acc, Ts, bf);
     dn_store_partial<NWIN>(S, acc, SH::TPW_BF, wave, lane);
-    dn_epilogue<NWIN>(a, S, SH::TPI_BF, SH::TPW_BF, U, false, p * 16 * SH::TPI_BF, tid);
+    dn_epilogue<NWIN>(a, S, SH::TPI_BF, SH::TPW_BF, U, false, b * 16 * SH::TPI_BF, tid);
     p += G;
   }
   const int q0 = p - n_sh;
   const int nmine = q0 < n_dn ? (n_dn - q0 + G - 1) / G : 0;
-  if (nmine > 0) {
-    // weights and activation fragments of the next item are requested before this item's math
-    DNItem<NWIN> T0, T1;
-    u32x4 b0[4][2], b1[4][2];
-    DNDesc e0 = dn_desc<NWIN, MX>(a, S, q0, n_dn, ipe), e1;
-    dn_load<NWIN, MX>(T0, e0, I, wave, lane);
-    dn_load_b<NWIN>(b0, a.afrag + (size_t)e0.u * (I / 32) * 128, wave, lane);
-    for (int j = 0;;) {
-      e1 = dn_desc<NWIN, MX>(a, S, q0 + (j + 1) * G, n_dn, ipe);  // a valid stand-in past the end
-      dn_load<NWIN, MX>(T1, e1, I, wave, lane);
-      dn_load_b<NWIN>(b1, a.afrag + (size_t)e1.u * (I / 32) * 128, wave, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        f32x4 acc[SH::TPW_MX];
-        dn_math<NWIN, MX>(acc, T0, b0);
-        dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
-        dn_epilogue<NWIN>(a, S, e0.ntile, TPW, e0.u, true, e0.row0, tid);
-      }
-      if (++j >= nmine) break;
-      e0 = dn_desc<NWIN, MX>(a, S, q0 + (j + 1) * G, n_dn, ipe);
-      dn_load<NWIN, MX>(T0, e0, I, wave, lane);
-      dn_load_b<NWIN>(b0, a.afrag + (size_t)e0.u * (I / 32) * 128, wave, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        f32x4 acc[SH::TPW_MX];
-        dn_math<NWIN, MX>(acc, T1, b1);
-        dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
-        dn_epilogue<NWIN>(a, S, e1.ntile, TPW, e1.u, true, e1.row0, tid);
-      }
-      if (++j >= nmine) break;
+  if (nmine == 0) return;
+  const Woken wk = load_woken(S, lane);
+  // weights and activation fragments of the next item are requested before this item's math
+  DNItem<NWIN> T0, T1;
+  u32x4 b0[4][2], b1[4][2];
+  DNDesc e0 = dn_desc<NWIN, MX>(a, wk, q0, n_dn, ipe), e1;
+  dn_load<NWIN, MX>(T0, rw, rs, e0, I, wave, lane);
+  dn_load_b<NWIN>(b0, raf, (uint32_t)(e0.u * (I / 32) * 2048), wave, lane);
+  for (int j = 0;;) {
+    e1 = dn_desc<NWIN, MX>(a, wk, q0 + (j + 1) * G, n_dn, ipe);  // a valid stand-in past the end
+    dn_load<NWIN, MX>(T1, rw, rs, e1, I, wave, lane);
+    dn_load_b<NWIN>(b1, raf, (uint32_t)(e1.u * (I / 32) * 2048), wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      f32x4 acc[SH::TPW_MX];
+      dn_math<NWIN, MX>(acc, T0, b0);
+      dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
+      dn_epilogue<NWIN>(a, S, e0.ntile, TPW, e0.u, true, e0.row0, tid);
     }
+    if (++j >= nmine) break;
+    e0 = dn_desc<NWIN, MX>(a, wk, q0 + (j + 1) * G, n_dn, ipe);
+    dn_load<NWIN, MX>(T0, rw, rs, e0, I, wave, lane);
+    dn_load_b<NWIN>(b0, raf, (uint32_t)(e0.u * (I / 32) * 2048), wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      f32x4 acc[SH::TPW_MX];
+      dn_math<NWIN, MX>(acc, T1, b1);
+      dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
+      dn_epilogue<NWIN>(a, S, e1.ntile, TPW, e1.u, true, e1.row0, tid);
+    }
+    if (++j >= nmine) break;
   }
 }
 
