@@ -591,6 +591,17 @@ __device__ __forceinline__ void gu_load_xb(u32x4 (&xb)[WPW][4][2], const u32x4* 
                                : u32x4{0u, 0u, 0u, 0u};
 }
 
+// Static item schedule: at step s workgroup b takes item s G + (b + s) mod G of the combined
+// sequence (shared-expert items first, then routed items). Rotating by the step spreads every
+// workgroup (and every XCD, which owns workgroups b mod 8) over all tile positions, so that no
+// workgroup keeps hitting the same slice of the address space.
+__device__ __forceinline__ int sched_item(int step, int b, int G) { return step * G + (b + step) % G; }
+// steps whose item is below n for workgroup b
+__device__ __forceinline__ int sched_count(int n, int b, int G) {
+  const int full = n / G;
+  return full + ((b + full) % G < n % G ? 1 : 0);
+}
+
 // The woken-expert list held across the lanes of every wave: lane l keeps entries l, l + 64, ...
 // A lookup is v_readlane with a uniform lane index, so an item descriptor is computed without
 // writing any VGPR: the streaming loops then never overwrite, between an epilogue's stores and
@@ -617,7 +628,7 @@ __device__ __forceinline__ uint32_t woken_at(const Woken& w, int u) {  // u wave
 // the same loads).
 template <bool MX>
 __device__ __forceinline__ GUDesc gu_desc(const Args& a, const Woken& wk, int idx, int n_items, int ipe) {
-  const int it = idx < n_items ? idx : 0;
+  const int it = (idx >= 0 && idx < n_items) ? idx : 0;
   GUDesc d;
   d.u = it / ipe;
   d.ntile = MX ? GU_MX_RT : 1;
@@ -676,7 +687,7 @@ struct DNDesc {
 template <int NWIN, bool MX>
 __device__ __forceinline__ DNDesc dn_desc(const Args& a, const Woken& wk, int idx, int n_items, int ipe) {
   using SH = DnShape<NWIN>;
-  const int it = idx < n_items ? idx : 0;
+  const int it = (idx >= 0 && idx < n_items) ? idx : 0;
   DNDesc d;
   d.u = it / ipe;
   d.ntile = MX ? SH::TPI_MX : SH::TPI_BF;
@@ -874,25 +885,24 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
 
   const int ipe = I / (16 * (MX ? GU_MX_RT : 1));
   const int n_gu = U * ipe;
-  int p = b;
-  if (p < n_sh) {
+  int s0 = 0;  // first step of this workgroup that is a routed item
+  if (b < n_sh) {
     f32x4 acc[GU_MX_RT][2];
     gu_math_bf16<WPW>(acc, Ts, xb);
     gu_epilogue<true>(a, S, acc, 1, U, b * 16, false, wave, lane, tid);
-    p += G;
+    s0 = 1;
     if (MX) gu_load_xb<WPW>(xb, a.xfrag, win0, active, lane);
   }
-  // routed items of this workgroup: r0, r0 + G, ... (the next item's loads are in flight while
-  // this item is multiplied)
-  const int r0 = p - n_sh;
-  const int nmine = r0 < n_gu ? (n_gu - r0 + G - 1) / G : 0;
-  if (nmine == 0) return;
+  // routed items of this workgroup, steps s0, s0 + 1, ... (the next item's loads are in flight
+  // while this item is multiplied)
+  const int nmine = sched_count(n_sh + n_gu, b, G) - s0;
+  if (nmine <= 0) return;
   const Woken wk = load_woken(S, lane);
   GUItem<WPW> T0, T1;
-  GUDesc d0 = gu_desc<MX>(a, wk, r0, n_gu, ipe), d1;
+  GUDesc d0 = gu_desc<MX>(a, wk, sched_item(s0, b, G) - n_sh, n_gu, ipe), d1;
   gu_load<WPW, MX>(T0, R, d0, H, vbc, vbs);
   for (int j = 0;;) {
-    d1 = gu_desc<MX>(a, wk, r0 + (j + 1) * G, n_gu, ipe);  // a valid stand-in past the end
+    d1 = gu_desc<MX>(a, wk, sched_item(s0 + j + 1, b, G) - n_sh, n_gu, ipe);  // a valid stand-in past the end
     gu_load<WPW, MX>(T1, R, d1, H, vbc, vbs);
     __builtin_amdgcn_sched_barrier(0);
     {
@@ -901,7 +911,7 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
       gu_epilogue<NAT>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid);
     }
     if (++j >= nmine) break;
-    d0 = gu_desc<MX>(a, wk, r0 + (j + 1) * G, n_gu, ipe);
+    d0 = gu_desc<MX>(a, wk, sched_item(s0 + j + 1, b, G) - n_sh, n_gu, ipe);
     gu_load<WPW, MX>(T0, R, d0, H, vbc, vbs);
     __builtin_amdgcn_sched_barrier(0);
     {
@@ -939,28 +949,27 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
 
   const int ipe = H / (16 * (MX ? SH::TPI_MX : SH::TPI_BF));
   const int n_dn = U * ipe;
-  int p = b;
-  if (p < n_sh) {
+  int s0 = 0;  // first step of this workgroup that is a routed item
+  if (b < n_sh) {
     u32x4 bf[4][2];
     dn_load_b<NWIN>(bf, buf_rsrc(a.afrag_sh, (Is / 32) * 2048), 0u, wave, lane);
     f32x4 acc[SH::TPW_MX];
     dn_math<NWIN, false>(acc, Ts, bf);
     dn_store_partial<NWIN>(S, acc, SH::TPW_BF, wave, lane);
     dn_epilogue<NWIN>(a, S, SH::TPI_BF, SH::TPW_BF, U, false, b * 16 * SH::TPI_BF, tid);
-    p += G;
+    s0 = 1;
   }
-  const int q0 = p - n_sh;
-  const int nmine = q0 < n_dn ? (n_dn - q0 + G - 1) / G : 0;
-  if (nmine == 0) return;
+  const int nmine = sched_count(n_sh + n_dn, b, G) - s0;
+  if (nmine <= 0) return;
   const Woken wk = load_woken(S, lane);
   // weights and activation fragments of the next item are requested before this item's math
   DNItem<NWIN> T0, T1;
   u32x4 b0[4][2], b1[4][2];
-  DNDesc e0 = dn_desc<NWIN, MX>(a, wk, q0, n_dn, ipe), e1;
+  DNDesc e0 = dn_desc<NWIN, MX>(a, wk, sched_item(s0, b, G) - n_sh, n_dn, ipe), e1;
   dn_load<NWIN, MX>(T0, rw, rs, e0, I, wave, lane);
   dn_load_b<NWIN>(b0, raf, (uint32_t)(e0.u * (I / 32) * 2048), wave, lane);
   for (int j = 0;;) {
-    e1 = dn_desc<NWIN, MX>(a, wk, q0 + (j + 1) * G, n_dn, ipe);  // a valid stand-in past the end
+    e1 = dn_desc<NWIN, MX>(a, wk, sched_item(s0 + j + 1, b, G) - n_sh, n_dn, ipe);  // a valid stand-in past the end
     dn_load<NWIN, MX>(T1, rw, rs, e1, I, wave, lane);
     dn_load_b<NWIN>(b1, raf, (uint32_t)(e1.u * (I / 32) * 2048), wave, lane);
     __builtin_amdgcn_sched_barrier(0);
@@ -971,7 +980,7 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
       dn_epilogue<NWIN>(a, S, e0.ntile, TPW, e0.u, true, e0.row0, tid);
     }
     if (++j >= nmine) break;
-    e0 = dn_desc<NWIN, MX>(a, wk, q0 + (j + 1) * G, n_dn, ipe);
+    e0 = dn_desc<NWIN, MX>(a, wk, sched_item(s0 + j + 1, b, G) - n_sh, n_dn, ipe);
     dn_load<NWIN, MX>(T0, rw, rs, e0, I, wave, lane);
     dn_load_b<NWIN>(b0, raf, (uint32_t)(e0.u * (I / 32) * 2048), wave, lane);
     __builtin_amdgcn_sched_barrier(0);
@@ -1022,6 +1031,8 @@ __global__ void __launch_bounds__(256) k_pack_mx(const uint8_t* src, const uint8
 // ------------------------------------------------------------------------------------------
 // accept_prefix: chunked argmax, then one workgroup reduces the rows and scans the prefix
 // ------------------------------------------------------------------------------------------
+// Each workgroup takes AM_CHUNK consecutive logits of one row: every thread issues all of its
+// loads before merging any (one memory round trip), then the workgroup reduces.
 __global__ void __launch_bounds__(256) k_argmax_partial(const float* logits, int V, int nchunks,
                                                         float* pv, int* pi) {
   __shared__ float sv[4];
@@ -1033,12 +1044,22 @@ __global__ void __launch_bounds__(256) k_argmax_partial(const float* logits, int
   float bv = -INFINITY;
   int bi = 0x7fffffff;
   if ((V & 3) == 0) {
-    for (int i = base + 4 * tid; i < end; i += 4 * 256) {
-      const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + i));
-      argmax_merge(bv, bi, v.x, i);
-      argmax_merge(bv, bi, v.y, i + 1);
-      argmax_merge(bv, bi, v.z, i + 2);
-      argmax_merge(bv, bi, v.w, i + 3);
+    constexpr int PER = AM_CHUNK / (4 * 256);  // float4 loads per thread
+    f32x4 v[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int i = base + 4 * (tid + 256 * m);
+      v[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + (i < end ? i : base)));
+    }
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int i = base + 4 * (tid + 256 * m);
+      if (i < end) {
+        argmax_merge(bv, bi, v[m].x, i);
+        argmax_merge(bv, bi, v[m].y, i + 1);
+        argmax_merge(bv, bi, v[m].z, i + 2);
+        argmax_merge(bv, bi, v[m].w, i + 3);
+      }
     }
   } else {
     for (int i = base + tid; i < end; i += 256) argmax_merge(bv, bi, r[i], i);
@@ -1053,17 +1074,23 @@ __global__ void __launch_bounds__(256) k_argmax_partial(const float* logits, int
   }
 }
 
-__global__ void __launch_bounds__(64) k_accept_final(const float* pv, const int* pi, int nchunks,
-                                                     int n_target, const int32_t* draft, int n_draft,
-                                                     int32_t* target_ids, int32_t* accepted) {
+// One workgroup of 16 waves: wave w reduces rows w, w + 16, ... (lane l takes chunks l, l + 64,
+// ...), then thread 0 scans the longest accepted prefix.
+__global__ void __launch_bounds__(1024) k_accept_final(const float* pv, const int* pi, int nchunks,
+                                                       int n_target, const int32_t* draft, int n_draft,
+                                                       int32_t* target_ids, int32_t* accepted) {
   __shared__ int tgt[64];
-  const int tid = threadIdx.x;
-  if (tid < n_target) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int row = wave; row < n_target; row += 16) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int c = 0; c < nchunks; ++c) argmax_merge(bv, bi, pv[(size_t)tid * nchunks + c], pi[(size_t)tid * nchunks + c]);
-    tgt[tid] = bi;
-    target_ids[tid] = bi;
+    for (int c = lane; c < nchunks; c += 64)
+      argmax_merge(bv, bi, pv[(size_t)row * nchunks + c], pi[(size_t)row * nchunks + c]);
+    wave_argmax(bv, bi);
+    if (lane == 0) {
+      tgt[row] = bi;
+      target_ids[row] = bi;
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -1319,7 +1346,7 @@ int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const in
   hipStream_t s = (hipStream_t)hip_stream;
   (void)hipGetLastError();
   k_argmax_partial<<<dim3(nchunks, n_target), 256, 0, s>>>(logits, vocab, nchunks, pv, pi);
-  k_accept_final<<<1, 64, 0, s>>>(pv, pi, nchunks, n_target, draft_ids, n_draft, target_ids, accepted);
+  k_accept_final<<<1, 1024, 0, s>>>(pv, pi, nchunks, n_target, draft_ids, n_draft, target_ids, accepted);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
