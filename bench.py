@@ -103,9 +103,10 @@ def traffic_from_profile():
         return None
 
 
-def cpu_baseline(wl, n_samples):
-    """The oracle as it stands, timed on the host for a bounded sample of the same steps."""
-    import numpy as np
+def cpu_baseline(wl, n_samples, one_core_samples=1):
+    """The oracle as it stands, timed on the host for a bounded sample of the same steps, with the
+    BLAS thread pool as configured and with one thread."""
+    import numpy as np  # noqa: F401
 
     import oracle
     from speculative_decoding_moe_amd.workloads import gen
@@ -130,28 +131,60 @@ def cpu_baseline(wl, n_samples):
             return self.cache["s"]
 
     layer = CachedLayer()
-    total_t, total_bytes = 0.0, 0.0
-    for p in range(n_samples):
-        x = gen.hidden_states(wl, rep=p)
-        logits, planted = gen.target_logits(wl, rep=p)
-        draft, _ = gen.draft_ids(wl, planted, rep=p)
-        oracle.moe_block(x, layer, wl.shape.top_k)  # untimed pass: generates the woken experts
-        t0 = time.perf_counter()
-        r = oracle.moe_block(x, layer, wl.shape.top_k)
-        tg = oracle.argmax_first(logits)
-        oracle.accept_length(draft, tg)
-        total_t += time.perf_counter() - t0
-        total_bytes += layer_bytes(wl.shape, r["n_woken"], wl.k) + logits.nbytes
+
+    def run(n):
+        total_t, total_bytes = 0.0, 0.0
+        for p in range(n):
+            x = gen.hidden_states(wl, rep=p)
+            logits, planted = gen.target_logits(wl, rep=p)
+            draft, _ = gen.draft_ids(wl, planted, rep=p)
+            oracle.moe_block(x, layer, wl.shape.top_k)  # untimed pass: generates the woken experts
+            t0 = time.perf_counter()
+            r = oracle.moe_block(x, layer, wl.shape.top_k)
+            tg = oracle.argmax_first(logits)
+            oracle.accept_length(draft, tg)
+            total_t += time.perf_counter() - t0
+            total_bytes += layer_bytes(wl.shape, r["n_woken"], wl.k) + logits.nbytes
+        return total_t, total_bytes
+
+    total_t, total_bytes = run(n_samples)
     threads = 1
+    one = None
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        with threadpool_limits(limits=1):
+            t1, b1 = run(one_core_samples)
+        one = round(b1 / t1 / 1e9, 4)
     except Exception:
+        pass
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
         pass
     return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{n_samples} verify steps (k=16 MoE layer + acceptance over 17x151936 logits), "
-                      f"{total_t / n_samples:.2f} s per step on the host, host has {os.cpu_count()} CPUs"}
+                      f"{total_t / n_samples:.2f} s per step on the host, host has {os.cpu_count()} CPUs "
+                      f"({cpu_model})",
+            "value_1core": one, "sample_1core": f"{one_core_samples} step(s) with one BLAS thread"}
+
+
+def fit_line(points):
+    """Least squares t = t0 + B / BW over (bytes, seconds) points: t0 in us, BW in GB/s, and the
+    residuals in us."""
+    import numpy as np
+    B = np.array([p[0] for p in points], dtype=np.float64)
+    t = np.array([p[1] for p in points], dtype=np.float64)
+    A = np.stack([np.ones_like(B), B], axis=1)
+    (t0, inv_bw), *_ = np.linalg.lstsq(A, t, rcond=None)
+    res = t - (t0 + inv_bw * B)
+    return {"t0_us": round(t0 * 1e6, 2), "bw_GBps": round(1.0 / inv_bw / 1e9, 1) if inv_bw > 0 else None,
+            "residual_us": [round(r * 1e6, 2) for r in res]}
 
 
 def main():
@@ -164,6 +197,7 @@ def main():
     ap.add_argument("--cpu-samples", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer mxfp4 stack measurement")
     ap.add_argument("--profile-run", action="store_true",
                     help="counter-collection run: warmup + steps without events, then a plain copy of "
                          "known size for calibrating HBM traffic counters; prints one JSON line")
@@ -193,6 +227,7 @@ def main():
     base = device.layer_tensors(wl, 0, dev)
     copies = [base] + [{n: (t.clone() if t is not None else None) for n, t in base.items()} for _ in range(R - 1)]
     layers = [device.make_layer(wl, 0, dev, tensors=c) for c in copies]
+    del copies, base
 
     print(f"[bench] preparing {P} blocks and logits", file=sys.stderr, flush=True)
     xs, lgs, drs = [], [], []
@@ -233,9 +268,7 @@ def main():
         for i in range(nsteps):
             step(i)
         torch.cuda.synchronize()
-        Un = nw_all[:nsteps, 0].cpu().numpy().astype(np.int64)
-        Uw = nw_all[:args.warmup, 0].cpu().numpy().astype(np.int64)
-        Uall = np.concatenate([Uw, Un])
+        Uall = nw_all[:max(nsteps, args.warmup), 0].cpu().numpy().astype(np.int64)
         copy_mib = 512
         src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -259,10 +292,25 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = ev.ms(t_start, t_stop)
+    ev.destroy([t_start, t_stop])
     U = nw_all[:nsteps, 0].cpu().numpy().astype(np.int64)
-    step_bytes = np.array([layer_bytes(s, u, k) + NT * V * 4 for u in U])
+    step_bytes = np.array([layer_bytes(s, u, k) + NT * V * 4 for u in U], dtype=np.float64)
     ms_per_step = total_ms / nsteps
     value = float(step_bytes.sum() / (total_ms * 1e-3) / 1e9)
+
+    # ---- step-time distribution: one event between consecutive steps ----
+    marks = ev.create(nsteps + 1)
+    torch.cuda.synchronize()
+    for i in range(nsteps):
+        ev.record(marks[i], stream)
+        step(i)
+    ev.record(marks[nsteps], stream)
+    torch.cuda.synchronize()
+    per_step_us = np.array([ev.ms(marks[i], marks[i + 1]) * 1e3 for i in range(nsteps)])
+    ev.destroy(marks)
+    dist = {"p10_us": round(float(np.percentile(per_step_us, 10)), 2),
+            "p50_us": round(float(np.median(per_step_us)), 2),
+            "p90_us": round(float(np.percentile(per_step_us, 90)), 2)}
 
     # ---- per-kernel pass: the library records events at its kernel boundaries ----
     evs = [ev.create(6) for _ in range(nsteps)]
@@ -280,14 +328,38 @@ def main():
     gu_ms = float(np.mean(dur["gateup"]))
     gu_bytes = float(np.mean([gateup_bytes(s, u) for u in U2]))
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    kernels_us = {n: round(float(np.mean(v)) * 1e3, 2) for n, v in dur.items()}
+    expert_ms = float(np.mean(np.array(dur["gateup"]) + np.array(dur["down"])))
+    expert_bytes = float(np.mean([layer_bytes(s, u, k) - s.n_experts * s.hidden * 4 - 2 * k * s.hidden * 4
+                                  for u in U2]))
+
+    # ---- achievable streaming read (reference kernel, 2 GiB so the LLC cannot hold it) ----
+    rd = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        device.stream_read(rd, sink)
+    a_, b_ = ev.create(2)
+    rd_times = []
+    for _ in range(5):
+        ev.record(a_, stream)
+        device.stream_read(rd, sink)
+        ev.record(b_, stream)
+        torch.cuda.synchronize()
+        rd_times.append(ev.ms(a_, b_))
+    ev.destroy([a_, b_])
+    read_ceiling = float(rd.numel() / (np.median(rd_times) * 1e-3) / 1e9)
+    del rd
+
     roofline = {"bound": "hbm", "kernel": "k_gateup", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic_from_profile(),
-                "bytes_per_launch": round(gu_bytes), "avg_launch_us": round(gu_ms * 1e3, 2)}
-    kernels_us = {n: round(float(np.mean(v)) * 1e3, 2) for n, v in dur.items()}
+                "bytes_per_launch": round(gu_bytes), "avg_launch_us": round(gu_ms * 1e3, 2),
+                "achievable_read_GBps": round(read_ceiling, 1),
+                "frac_of_achievable": round(achieved / read_ceiling, 4),
+                "expert_kernels_GBps": round(expert_bytes / (expert_ms * 1e-3) / 1e9, 1)}
 
     # ---- sweeps (same layer; k = 1..16 and correlated blocks at k = 16) ----
-    sweep_k, sweep_sigma = [], []
+    sweep_k, sweep_sigma, fit = [], [], None
     if not args.no_sweep:
         reps = 20
 
@@ -311,18 +383,68 @@ def main():
             byt = float(np.mean([layer_bytes(s, u, blocks[0].shape[0]) for u in Us]))
             return t, float(Us.mean()), byt
 
+        points = []
         for kk in range(1, 17):
             blocks = [torch.from_numpy(gen.hidden_states(wl, rep=200 + p, k=kk)).to(dev) for p in range(4)]
             t, Um, byt = time_blocks(blocks)
+            points.append((byt, t * 1e-3))
             sweep_k.append({"k": kk, "U_mean": round(Um, 2), "ms": round(t, 4),
                             "GBps": round(byt / (t * 1e-3) / 1e9, 1)})
         cw = gen.WORKLOADS["correlated"]
         for sg in cw.sigmas:
             blocks = [torch.from_numpy(gen.hidden_states(cw, rep=300 + p, sigma=sg)).to(dev) for p in range(4)]
             t, Um, byt = time_blocks(blocks)
+            points.append((byt, t * 1e-3))
             sweep_sigma.append({"sigma": sg, "U_mean": round(Um, 2), "ms": round(t, 4),
                                 "GBps": round(byt / (t * 1e-3) / 1e9, 1)})
-        print(f"[bench] sweeps done", file=sys.stderr, flush=True)
+        fit = fit_line(points)
+        fit["points"] = "16 k-sweep points then 5 sigma points (k = 16), layer calls only"
+        fit["same_U_check_ms"] = {"k1_U8": sweep_k[0]["ms"], "k16_sigma0_U8": sweep_sigma[0]["ms"]}
+        print("[bench] sweeps done", file=sys.stderr, flush=True)
+
+    # ---- 40-layer mxfp4 stack: one verify pass (pre-norm, residual) + acceptance ----
+    stack = None
+    if not args.no_stack:
+        del layers
+        torch.cuda.empty_cache()
+        sw = gen.WORKLOADS["stack40_mxfp4"]
+        print(f"[bench] filling the {sw.n_layers}-layer mxfp4 stack", file=sys.stderr, flush=True)
+        slayers = [device.make_layer(sw, li, dev) for li in range(sw.n_layers)]
+        sws = torch.empty(slayers[0].workspace_size(sw.k), dtype=torch.uint8, device=dev)
+        bufs = [torch.empty((sw.k, sw.shape.hidden), dtype=torch.float32, device=dev) for _ in range(2)]
+        snw = torch.zeros((sw.n_layers * 8, 4), dtype=torch.int32, device=dev)
+        sxs = [torch.from_numpy(gen.hidden_states(sw, rep=p)).to(dev) for p in range(4)]
+        flags = binding.MOE_PRE_RMSNORM | binding.MOE_RESIDUAL
+
+        def stack_pass(rep, record=None):
+            cur = sxs[rep % len(sxs)]
+            for li, L in enumerate(slayers):
+                out = bufs[li % 2]
+                binding.moe_verify_block(L, cur, flags, out, None, None,
+                                         snw[(rep % 8) * sw.n_layers + li], sws)
+                cur = out
+            binding.accept_prefix(lgs[rep % P], drs[rep % P], tgt, acc, aws)
+
+        for r in range(2):
+            stack_pass(r)
+        a_, b_ = ev.create(2)
+        torch.cuda.synchronize()
+        sreps = 8
+        ev.record(a_, stream)
+        for r in range(sreps):
+            stack_pass(r)
+        ev.record(b_, stream)
+        torch.cuda.synchronize()
+        st_ms = ev.ms(a_, b_) / sreps
+        ev.destroy([a_, b_])
+        SU = snw[:sreps * sw.n_layers, 0].cpu().numpy().astype(np.int64)
+        sbytes = float(np.sum([layer_bytes(sw.shape, u, sw.k) for u in SU]) / sreps) + NT * V * 4
+        stack = {"workload": f"{sw.n_layers} x MoE layer (H {sw.shape.hidden}, 256 experts, top-8, I 512, "
+                             "mxfp4 routed experts, bf16 shared, pre-norm + residual), k = 16, then acceptance",
+                 "ms": round(st_ms, 4), "GBps": round(sbytes / (st_ms * 1e-3) / 1e9, 1),
+                 "U_mean": round(float(SU.mean()), 2), "bytes_per_pass": round(sbytes),
+                 "ms_per_layer": round(st_ms / sw.n_layers, 5)}
+        print("[bench] stack done", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -340,9 +462,12 @@ def main():
                    "block_pool": P, "U_mean": round(float(U.mean()), 2),
                    "bytes_per_step_mean": round(float(step_bytes.mean())), "wall_s": round(wall, 4)},
         "roofline": roofline,
+        "step_time": dist,
         "kernels_us": kernels_us,
         "sweep_k": sweep_k,
         "sweep_sigma": sweep_sigma,
+        "sweep_fit": fit,
+        "stack40_mxfp4": stack,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -32,6 +32,8 @@ def _fill_lib():
         lib.workload_fill_mxfp4.restype = ctypes.c_int
         lib.workload_copy.argtypes = [vp, vp, u64, vp]
         lib.workload_copy.restype = ctypes.c_int
+        lib.workload_stream_read.argtypes = [vp, u64, vp, vp]
+        lib.workload_stream_read.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -73,6 +75,15 @@ def copy_bytes(dst: torch.Tensor, src: torch.Tensor):
     st = _fill_lib().workload_copy(src.data_ptr(), dst.data_ptr(), nb, torch.cuda.current_stream().cuda_stream)
     if st != 0:
         raise RuntimeError(f"workload_copy failed ({st})")
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor):
+    """A plain streaming read of src (the achievable-bandwidth reference)."""
+    nb = src.numel() * src.element_size()
+    st = _fill_lib().workload_stream_read(src.data_ptr(), nb - nb % 131072, sink.data_ptr(),
+                                          torch.cuda.current_stream().cuda_stream)
+    if st != 0:
+        raise RuntimeError(f"workload_stream_read failed ({st})")
 
 
 def layer_tensors(wl: gen.Workload, layer: int = 0, device="cuda") -> dict:

@@ -99,6 +99,26 @@ __global__ void __launch_bounds__(256) k_copy16(const uint4* src, uint4* dst, ui
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// Plain streaming read (the achievable-bandwidth reference for the MoE kernels): each workgroup
+// reads 128 KiB chunks, every thread keeping 8 nontemporal 16-byte loads in flight.
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+__global__ void __launch_bounds__(256) k_stream_read(const u32x4v* src, uint64_t n_chunks, unsigned* sink) {
+  constexpr int PER_CHUNK = 131072 / 16;  // 16-byte words per chunk
+  unsigned acc = 0;
+  for (uint64_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    const u32x4v* p = src + c * PER_CHUNK + threadIdx.x;
+#pragma unroll 1
+    for (int i = 0; i < PER_CHUNK / 256; i += 8) {
+      u32x4v v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(p + (i + j) * 256);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; practically never taken
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,6 +153,15 @@ int workload_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
   if ((uintptr_t)src < (uintptr_t)dst + bytes && (uintptr_t)dst < (uintptr_t)src + bytes) return -1;
   if (bytes == 0) return 0;
   k_copy16<<<2048, 256, 0, (hipStream_t)stream>>>((const uint4*)src, (uint4*)dst, bytes / 16);
+  return (int)hipGetLastError();
+}
+
+// Reads src[0:bytes] once (bytes a multiple of 128 KiB, src 16-byte aligned); sink: one device
+// uint32 the kernel may write.
+int workload_stream_read(const void* src, uint64_t bytes, void* sink, void* stream) {
+  if (!src || !sink || bytes % 131072 || (uintptr_t)src % 16) return -1;
+  if (bytes == 0) return 0;
+  k_stream_read<<<512, 256, 0, (hipStream_t)stream>>>((const u32x4v*)src, bytes / 131072, (unsigned*)sink);
   return (int)hipGetLastError();
 }
 

@@ -382,3 +382,21 @@ def test_pack_weights_mxfp4_matches_oracle(B, n, rows, cols):
     rc, rs = oracle.tile_mxfp4(codes, scales)
     assert np.array_equal(dc.cpu().numpy(), rc)
     assert np.array_equal(ds.cpu().numpy(), rs)
+
+
+def test_accept_prefix_reuses_one_workspace(B):
+    """Consecutive calls on one workspace, the second on a smaller problem, match the oracle."""
+    ws = torch.empty(B.accept_prefix_workspace_size(17, 151936), dtype=torch.uint8, device="cuda")
+    for n_target, vocab, seed in ((17, 151936, 11), (5, 3001, 12), (17, 151936, 13)):
+        rng = np.random.default_rng(seed)
+        logits = rng.standard_normal((n_target, vocab), dtype=np.float32)
+        ref = oracle.argmax_first(logits)
+        draft = ref[:n_target - 1].copy()
+        draft[n_target // 2] = (draft[n_target // 2] + 1) % vocab
+        tg = torch.empty(n_target, dtype=torch.int32, device="cuda")
+        acc = torch.empty(4, dtype=torch.int32, device="cuda")
+        B.accept_prefix(torch.from_numpy(logits).cuda(), torch.from_numpy(draft.astype(np.int32)).cuda(),
+                        tg, acc, ws, n_draft=len(draft))
+        torch.cuda.synchronize()
+        assert np.array_equal(tg.cpu().numpy().astype(np.int64), ref)
+        assert int(acc[0]) == oracle.accept_length(draft, ref)
