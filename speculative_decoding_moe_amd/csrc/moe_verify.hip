@@ -119,54 +119,6 @@ __device__ __forceinline__ int kofs(int j, int q) { return NAT ? 32 * j + 8 * q 
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
   if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
 }
-// Top-K sort key of logit v for expert e: larger logit first, then lower e; -0 counts as +0;
-// NaN ranks below every number (but above the 0 used for empty slots).
-__device__ __forceinline__ uint64_t topk_key(float v, int e) {
-  const uint32_t u = __float_as_uint(v + 0.0f);
-  uint32_t hi = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  if (v != v) hi = 0u;
-  return ((uint64_t)hi << 32) | (uint32_t)~(uint32_t)e;
-}
-__device__ __forceinline__ float topk_key_value(uint64_t key) {
-  const uint32_t hi = (uint32_t)(key >> 32);
-  return __uint_as_float((hi & 0x80000000u) ? (hi & 0x7fffffffu) : ~hi);
-}
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xf, 0xf, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xf, 0xf, false);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ void cx_desc(uint64_t& a, uint64_t& b) {
-  const uint64_t hi = a > b ? a : b, lo = a > b ? b : a;
-  a = hi;
-  b = lo;
-}
-// Sorts 8 keys into descending order (19-comparator network).
-__device__ __forceinline__ void sort8_desc(uint64_t (&k)[8]) {
-  cx_desc(k[0], k[2]); cx_desc(k[1], k[3]); cx_desc(k[4], k[6]); cx_desc(k[5], k[7]);
-  cx_desc(k[0], k[4]); cx_desc(k[1], k[5]); cx_desc(k[2], k[6]); cx_desc(k[3], k[7]);
-  cx_desc(k[0], k[1]); cx_desc(k[2], k[3]); cx_desc(k[4], k[5]); cx_desc(k[6], k[7]);
-  cx_desc(k[2], k[4]); cx_desc(k[3], k[5]);
-  cx_desc(k[1], k[4]); cx_desc(k[3], k[6]);
-  cx_desc(k[1], k[2]); cx_desc(k[3], k[4]); cx_desc(k[5], k[6]);
-}
-// Maximum over the wave's 64 lanes, returned wave-uniform: DPP permutations inside each 16-lane
-// row (swap neighbours, swap pairs, mirror halves, mirror rows), then the four row results.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-  x = umax64(x, dpp_u64<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = umax64(x, dpp_u64<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = umax64(x, dpp_u64<0x141>(x));  // row_half_mirror
-  x = umax64(x, dpp_u64<0x140>(x));  // row_mirror
-  return umax64(umax64(readlane_u64(x, 0), readlane_u64(x, 16)), umax64(readlane_u64(x, 32), readlane_u64(x, 48)));
-}
-
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -193,6 +145,8 @@ struct Args {
   const uint8_t* shu;
   const uint8_t* shd;
   int32_t* tab_n;     // U
+  uint32_t* ctr;      // [2][NGRP] pool counters of the gate/up and down kernels, CTR_STRIDE words
+                      // apart (zeroed by the router)
   int32_t* tab_woken; // [umax] woken expert ids, ascending
   int8_t* tab_slot;   // [umax][16] slot of token t for woken expert u, or -1
   u32x4* xfrag;   // (H/32) k-steps x {hi, lo} x 64 lanes, the layer's K order
@@ -218,6 +172,7 @@ struct alignas(16) Smem {
   int8_t slot[MAX_U][KMAX];
   float rinv[KMAX];
   int nw;
+  int claim[4];  // ring of claimed item indices: item n sits in claim[n % 4]
 };
 
 // ------------------------------------------------------------------------------------------
@@ -302,20 +257,53 @@ __device__ void router_item(const Args& a, RouterSmem& S, int r, int wave, int l
   }
 }
 
-// K rounds over NC tokens' sorted candidate lists: the wave-wide maximum of the lane heads is
-// the next pick; the lane that held it pops its head; lane j records pick j.
+// Order-preserving 32-bit key of a logit: a larger logit has a larger key; -0 counts as +0; NaN
+// maps to 1, below every number; 0 marks an empty or already-picked slot.
+__device__ __forceinline__ uint32_t okey32(float v) {
+  const uint32_t u = __float_as_uint(v + 0.0f);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return v != v ? 1u : k;
+}
+__device__ __forceinline__ float okey32_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+// Maximum over the wave's 64 lanes, wave-uniform: DPP permutations inside each 16-lane row (swap
+// neighbours, swap pairs, mirror halves, mirror rows), then the four row results.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = max(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = max(x, dpp_u32<0x141>(x));  // row_half_mirror
+  x = max(x, dpp_u32<0x140>(x));  // row_mirror
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+  return max(a, b);
+}
+
+// K rounds over NC tokens' candidate keys (lane l holds experts l + 64 m, m < 8): each round takes
+// the wave maximum of the lane maxima, finds the lowest expert id holding it (first slot m with a
+// match, then the lowest lane) and clears that slot. Lane j records pick j of each token.
 template <int NC>
-__device__ __forceinline__ void topk_rounds(uint64_t (&key)[2][8], int K, int lane, int (&my_id)[2],
+__device__ __forceinline__ void topk_rounds(uint32_t (&key)[2][8], int K, int lane, int (&my_id)[2],
                                             float (&my_val)[2]) {
   for (int j = 0; j < K; ++j) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const uint64_t win = wave_max_u64(key[c][0]);  // wave-uniform
-      const bool own = key[c][0] == win;
+      uint32_t lm = max(max(max(key[c][0], key[c][1]), max(key[c][2], key[c][3])),
+                        max(max(key[c][4], key[c][5]), max(key[c][6], key[c][7])));
+      const uint32_t w = wave_max_u32(lm);
+      int sm = 7, sl = 0;
 #pragma unroll
-      for (int m = 0; m < 7; ++m) key[c][m] = own ? key[c][m + 1] : key[c][m];
-      key[c][7] = own ? 0ull : key[c][7];
-      if (lane == j) { my_id[c] = (int)~(uint32_t)win; my_val[c] = topk_key_value(win); }
+      for (int m = 7; m >= 0; --m) {  // ends on the lowest slot holding w
+        const uint64_t b = __ballot(key[c][m] == w);
+        if (b) { sm = m; sl = __builtin_ctzll(b); }
+      }
+#pragma unroll
+      for (int m = 0; m < 8; ++m) key[c][m] = (m == sm && lane == sl) ? 0u : key[c][m];
+      if (lane == j) { my_id[c] = sl + 64 * sm; my_val[c] = okey32_value(w); }
     }
   }
 }
@@ -356,16 +344,14 @@ __device__ void route(const Args& a, Smem& S, int wave, int lane, int tid) {
   }
   for (int i = tid; i < MAX_E; i += NTH) S.flag[i] = 0;
   __syncthreads();
-  // Top-K per token with 64-bit keys (order-preserving logit bits, then the inverted expert id,
-  // so ties go to the lower id). Each lane sorts its 8 candidates once; each of the K rounds
-  // takes the wave-wide maximum of the lane heads and the winning lane pops its head. Wave w
-  // serves tokens w and w + 8 together (independent chains interleave). Lane j keeps the j-th
-  // pick; softmax over the K picks in the same wave.
+  // Top-K per token: wave w serves tokens w and w + 8 together (the two round chains interleave);
+  // 32-bit keys (order-preserving logit bits), equal logits to the lower expert id; softmax over
+  // the K in the same wave. Lane j keeps pick j.
   static_assert(MAX_E / 64 == 8 && KMAX == 2 * NW, "top-K layout");
   for (int t0 = wave; t0 < k; t0 += 2 * NW) {
     const int t1 = t0 + NW;
     const bool two = t1 < k;  // wave-uniform
-    uint64_t key[2][8];
+    uint32_t key[2][8];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int t = c ? (two ? t1 : t0) : t0;
@@ -373,9 +359,8 @@ __device__ void route(const Args& a, Smem& S, int wave, int lane, int tid) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int e = lane + 64 * m;
-        key[c][m] = e < E ? topk_key(rv * lg[t * E + e], e) : 0ull;
+        key[c][m] = e < E ? okey32(rv * lg[t * E + e]) : 0u;
       }
-      sort8_desc(key[c]);
     }
     int my_id[2] = {0, 0};
     float my_val[2] = {0.f, 0.f};
@@ -495,7 +480,7 @@ __device__ __forceinline__ void gu_load_mx(GUItem<WPW>& T, const GURes& R, const
 template <bool NAT>
 __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 (&acc)[GU_MX_RT][2],
                                             int ntile, int u, int row0, bool routed, int wave,
-                                            int lane, int tid) {
+                                            int lane, int tid, int ring = -1, int* next = nullptr) {
 #pragma unroll
   for (int tl = 0; tl < GU_MX_RT; ++tl)
     if (tl < ntile) {
@@ -516,6 +501,10 @@ __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 
     S.act[tl][p] = silu(g * rv) * (up * rv) * S.wcol[u][c];
   }
   __syncthreads();
+  if (ring >= 0) {  // the next item index, read before this epilogue's stores are issued
+    *next = __builtin_amdgcn_readfirstlane(S.claim[ring]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   // thread (tile, half, column c) -> rows R .. R+7 of the expert's intermediate dimension
   if (tid < ntile * 2 * KMAX) {
     const int tl = tid / (2 * KMAX), half = (tid / KMAX) & 1, c = tid % KMAX;
@@ -591,15 +580,45 @@ __device__ __forceinline__ void gu_load_xb(u32x4 (&xb)[WPW][4][2], const u32x4* 
                                : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Static item schedule: at step s workgroup b takes item s G + (b + s) mod G of the combined
-// sequence (shared-expert items first, then routed items). Rotating by the step spreads every
-// workgroup (and every XCD, which owns workgroups b mod 8) over all tile positions, so that no
-// workgroup keeps hitting the same slice of the address space.
-__device__ __forceinline__ int sched_item(int step, int b, int G) { return step * G + (b + step) % G; }
-// steps whose item is below n for workgroup b
-__device__ __forceinline__ int sched_count(int n, int b, int G) {
-  const int full = n / G;
-  return full + ((b + full) % G < n % G ? 1 : 0);
+// Item schedule of the gate/up and down kernels (routed items; the shared expert's items go to
+// workgroups b < n_sh first).
+//  * Static part: rounds 0 .. S-1; in round s workgroup b takes item s G + f with
+//    f = (b - n_sh) mod G, i.e. the workgroups that took a shared item start the routed deal last.
+//    With at least 6 rounds of items S = n / G - 2 and the rest is claimed; with fewer, every
+//    round is static.
+//  * Claimed part: items S G .. n-1, split into NGRP interleaved pools (item S G + p + NGRP c for
+//    pool p and counter value c). Workgroup b draws from pool (b / 8) mod NGRP, so every pool is
+//    served by workgroups on all XCDs: the XCDs of this part stream at noticeably different rates,
+//    which a fully static deal turns into a tail, and claiming lets the faster ones take more.
+//    Device-scope atomics on one address serialise (about 30 ns each), hence several pools, and
+//    only the last rounds are claimed.
+//  * Vector memory results complete in issue order, so a claim is issued right after an item's
+//    loads and its result is stored (into the LDS ring that the epilogues publish) two items
+//    later; it never holds up a load that is needed sooner.
+constexpr int NGRP = 8;          // claim pools
+constexpr int CTR_STRIDE = 64;   // uint32 words between pool counters (256 B)
+struct Sched {
+  int G, S, f, pool;  // workgroups, static rounds, first item, pool
+  bool claims;        // whether the last rounds are claimed
+  uint32_t* ctr;      // this workgroup's pool counter
+};
+__device__ __forceinline__ Sched make_sched(int n, int G, int b, int n_sh, uint32_t* ctr_base) {
+  Sched q;
+  q.G = G;
+  q.claims = n >= 6 * G;
+  q.S = q.claims ? n / G - 2 : (n + G - 1) / G;
+  q.f = (b - n_sh + G) % G;
+  q.pool = (b >> 3) % NGRP;
+  q.ctr = ctr_base + q.pool * CTR_STRIDE;
+  return q;
+}
+__device__ __forceinline__ bool is_static(const Sched& q, int h) { return !q.claims || h < q.S; }
+// item of step h if it is static (h < S)
+__device__ __forceinline__ int static_item(const Sched& q, int h) { return h * q.G + q.f; }
+// item for counter value c of this workgroup's pool
+__device__ __forceinline__ int pool_item(const Sched& q, uint32_t c) { return q.S * q.G + q.pool + NGRP * (int)c; }
+__device__ __forceinline__ uint32_t claim_raw(uint32_t* ctr) {
+  return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The woken-expert list held across the lanes of every wave: lane l keeps entries l, l + 64, ...
@@ -791,9 +810,13 @@ __device__ __forceinline__ void dn_store_partial(Smem& S, const f32x4* acc, int 
 // Reduce the item's partial tiles over windows and write the P rows of the tokens routed to it.
 template <int NWIN>
 __device__ void dn_epilogue(const Args& a, Smem& S, int ntile, int tpw, int u, bool routed, int row0,
-                            int tid) {
+                            int tid, int ring = -1, int* next = nullptr) {
   const int H = a.H, K = a.K, k = a.k;
   __syncthreads();
+  if (ring >= 0) {  // the next item index, read before this epilogue's stores are issued
+    *next = __builtin_amdgcn_readfirstlane(S.claim[ring]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   {
     const int r = tid & 15, c = (tid >> 4) & 15, par = tid >> 8;  // par: tile parity
     int slot = -1;
@@ -844,6 +867,7 @@ __global__ void __launch_bounds__(NTH) k_router(Args a) {
   __shared__ RouterSmem S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  if (blockIdx.x == 0 && tid < 2 * NGRP) a.ctr[tid * CTR_STRIDE] = 0u;  // this layer's pools start at 0
   router_item<NAT>(a, S, blockIdx.x, wave, lane, tid);
 }
 
@@ -860,7 +884,7 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
   const int wsafe = active ? win0 : 0; // inactive waves load window 0 and multiply it by zero
 
   // Item sequence: the shared expert's row tiles (known before routing, so their weights are
-  // requested first), then the routed items, dealt round-robin over the workgroups.
+  // requested first), then the routed items (see make_sched).
   const int n_sh = Is / 16;
   GUItem<WPW> Ts;
   const uint32_t E = a.E;
@@ -885,41 +909,52 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
 
   const int ipe = I / (16 * (MX ? GU_MX_RT : 1));
   const int n_gu = U * ipe;
-  int s0 = 0;  // first step of this workgroup that is a routed item
   if (b < n_sh) {
     f32x4 acc[GU_MX_RT][2];
     gu_math_bf16<WPW>(acc, Ts, xb);
     gu_epilogue<true>(a, S, acc, 1, U, b * 16, false, wave, lane, tid);
-    s0 = 1;
     if (MX) gu_load_xb<WPW>(xb, a.xfrag, win0, active, lane);
   }
-  // routed items of this workgroup, steps s0, s0 + 1, ... (the next item's loads are in flight
-  // while this item is multiplied)
-  const int nmine = sched_count(n_sh + n_gu, b, G) - s0;
-  if (nmine <= 0) return;
+  // Routed items (see make_sched). Step h: item h is in T[h % 2] with its loads in flight; the
+  // loads of item h + 1 are issued; thread 0 stores item h + 2 into the ring (static, or claimed
+  // two steps earlier) and claims item h + 4 when that one is claimed; the epilogue reads item
+  // h + 2 back for the next step.
+  const Sched q = make_sched(n_gu, G, b, n_sh, a.ctr);
+  const int r0 = static_item(q, 0);
+  if (r0 >= n_gu) return;  // every later item is past the end too
   const Woken wk = load_woken(S, lane);
   GUItem<WPW> T0, T1;
-  GUDesc d0 = gu_desc<MX>(a, wk, sched_item(s0, b, G) - n_sh, n_gu, ipe), d1;
+  GUDesc d0 = gu_desc<MX>(a, wk, r0, n_gu, ipe), d1;
   gu_load<WPW, MX>(T0, R, d0, H, vbc, vbs);
-  for (int j = 0;;) {
-    d1 = gu_desc<MX>(a, wk, sched_item(s0 + j + 1, b, G) - n_sh, n_gu, ipe);  // a valid stand-in past the end
+  int n1 = static_item(q, 1), n2;  // items h + 1 and h + 2
+  uint32_t ca = 0, cb = 0;         // claims in flight (thread 0): items h + 2 / h + 3
+  for (int h = 0;; h += 2) {
+    d1 = gu_desc<MX>(a, wk, n1, n_gu, ipe);  // a valid stand-in past the end
     gu_load<WPW, MX>(T1, R, d1, H, vbc, vbs);
+    if (tid == 0) {
+      S.claim[(h + 2) & 3] = is_static(q, h + 2) ? static_item(q, h + 2) : pool_item(q, ca);
+      if (!is_static(q, h + 4)) ca = claim_raw(q.ctr);
+    }
     __builtin_amdgcn_sched_barrier(0);
     {
       f32x4 acc[GU_MX_RT][2];
       gu_math<WPW, MX>(acc, T0, xb);
-      gu_epilogue<NAT>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid);
+      gu_epilogue<NAT>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid, (h + 2) & 3, &n2);
     }
-    if (++j >= nmine) break;
-    d0 = gu_desc<MX>(a, wk, sched_item(s0 + j + 1, b, G) - n_sh, n_gu, ipe);
+    if (n1 >= n_gu) break;
+    d0 = gu_desc<MX>(a, wk, n2, n_gu, ipe);
     gu_load<WPW, MX>(T0, R, d0, H, vbc, vbs);
+    if (tid == 0) {
+      S.claim[(h + 3) & 3] = is_static(q, h + 3) ? static_item(q, h + 3) : pool_item(q, cb);
+      if (!is_static(q, h + 5)) cb = claim_raw(q.ctr);
+    }
     __builtin_amdgcn_sched_barrier(0);
     {
       f32x4 acc[GU_MX_RT][2];
       gu_math<WPW, MX>(acc, T1, xb);
-      gu_epilogue<NAT>(a, S, acc, d1.ntile, d1.u, d1.row0, true, wave, lane, tid);
+      gu_epilogue<NAT>(a, S, acc, d1.ntile, d1.u, d1.row0, true, wave, lane, tid, (h + 3) & 3, &n1);
     }
-    if (++j >= nmine) break;
+    if (n2 >= n_gu) break;
   }
 }
 
@@ -933,8 +968,8 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   const int H = a.H, I = a.I, Is = a.Is;
   const int G = gridDim.x, b = blockIdx.x;
 
-  // Item sequence: the shared expert's row groups (requested first), then the routed items,
-  // dealt round-robin over the workgroups.
+  // Item sequence: the shared expert's row groups (requested first), then the routed items
+  // (see make_sched).
   const int n_sh = Is > 0 ? H / (16 * SH::TPI_BF) : 0;
   DNItem<NWIN> Ts;
   const uint32_t E = a.E;
@@ -942,6 +977,7 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   const rsrc_t rs = buf_rsrc(a.sd, MX ? E * H * (I / 32) : 0);
   const rsrc_t raf = buf_rsrc(a.afrag, (uint32_t)a.umax * (I / 32) * 2048);
   if (b < n_sh) dn_load_bf16<NWIN>(Ts, buf_rsrc(a.shd, H * Is * 2), (uint32_t)(b * 16 * SH::TPI_BF * Is * 2), Is, wave, lane);
+
   const int U = __builtin_amdgcn_readfirstlane(a.tab_n[0]);
   for (int i = tid; i < U; i += NTH) S.woken[i] = a.tab_woken[i];
   for (int i = tid; i < U * KMAX; i += NTH) S.slot[i / KMAX][i % KMAX] = a.tab_slot[i];
@@ -949,7 +985,6 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
 
   const int ipe = H / (16 * (MX ? SH::TPI_MX : SH::TPI_BF));
   const int n_dn = U * ipe;
-  int s0 = 0;  // first step of this workgroup that is a routed item
   if (b < n_sh) {
     u32x4 bf[4][2];
     dn_load_b<NWIN>(bf, buf_rsrc(a.afrag_sh, (Is / 32) * 2048), 0u, wave, lane);
@@ -957,40 +992,51 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
     dn_math<NWIN, false>(acc, Ts, bf);
     dn_store_partial<NWIN>(S, acc, SH::TPW_BF, wave, lane);
     dn_epilogue<NWIN>(a, S, SH::TPI_BF, SH::TPW_BF, U, false, b * 16 * SH::TPI_BF, tid);
-    s0 = 1;
   }
-  const int nmine = sched_count(n_sh + n_dn, b, G) - s0;
-  if (nmine <= 0) return;
+  // routed items, scheduled as in the gate/up kernel; the weights and activation fragments of
+  // the next item are requested before this item's math
+  const Sched q = make_sched(n_dn, G, b, n_sh, a.ctr + NGRP * CTR_STRIDE);
+  const int q0 = static_item(q, 0);
+  if (q0 >= n_dn) return;  // every later item is past the end too
   const Woken wk = load_woken(S, lane);
-  // weights and activation fragments of the next item are requested before this item's math
   DNItem<NWIN> T0, T1;
   u32x4 b0[4][2], b1[4][2];
-  DNDesc e0 = dn_desc<NWIN, MX>(a, wk, sched_item(s0, b, G) - n_sh, n_dn, ipe), e1;
+  DNDesc e0 = dn_desc<NWIN, MX>(a, wk, q0, n_dn, ipe), e1;
   dn_load<NWIN, MX>(T0, rw, rs, e0, I, wave, lane);
   dn_load_b<NWIN>(b0, raf, (uint32_t)(e0.u * (I / 32) * 2048), wave, lane);
-  for (int j = 0;;) {
-    e1 = dn_desc<NWIN, MX>(a, wk, sched_item(s0 + j + 1, b, G) - n_sh, n_dn, ipe);  // a valid stand-in past the end
+  int n1 = static_item(q, 1), n2;  // items h + 1 and h + 2
+  uint32_t ca = 0, cb = 0;         // claims in flight (thread 0): items h + 2 / h + 3
+  for (int h = 0;; h += 2) {
+    e1 = dn_desc<NWIN, MX>(a, wk, n1, n_dn, ipe);  // a valid stand-in past the end
     dn_load<NWIN, MX>(T1, rw, rs, e1, I, wave, lane);
     dn_load_b<NWIN>(b1, raf, (uint32_t)(e1.u * (I / 32) * 2048), wave, lane);
+    if (tid == 0) {
+      S.claim[(h + 2) & 3] = is_static(q, h + 2) ? static_item(q, h + 2) : pool_item(q, ca);
+      if (!is_static(q, h + 4)) ca = claim_raw(q.ctr);
+    }
     __builtin_amdgcn_sched_barrier(0);
     {
       f32x4 acc[SH::TPW_MX];
       dn_math<NWIN, MX>(acc, T0, b0);
       dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
-      dn_epilogue<NWIN>(a, S, e0.ntile, TPW, e0.u, true, e0.row0, tid);
+      dn_epilogue<NWIN>(a, S, e0.ntile, TPW, e0.u, true, e0.row0, tid, (h + 2) & 3, &n2);
     }
-    if (++j >= nmine) break;
-    e0 = dn_desc<NWIN, MX>(a, wk, sched_item(s0 + j + 1, b, G) - n_sh, n_dn, ipe);
+    if (n1 >= n_dn) break;
+    e0 = dn_desc<NWIN, MX>(a, wk, n2, n_dn, ipe);
     dn_load<NWIN, MX>(T0, rw, rs, e0, I, wave, lane);
     dn_load_b<NWIN>(b0, raf, (uint32_t)(e0.u * (I / 32) * 2048), wave, lane);
+    if (tid == 0) {
+      S.claim[(h + 3) & 3] = is_static(q, h + 3) ? static_item(q, h + 3) : pool_item(q, cb);
+      if (!is_static(q, h + 5)) cb = claim_raw(q.ctr);
+    }
     __builtin_amdgcn_sched_barrier(0);
     {
       f32x4 acc[SH::TPW_MX];
       dn_math<NWIN, MX>(acc, T1, b1);
       dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
-      dn_epilogue<NWIN>(a, S, e1.ntile, TPW, e1.u, true, e1.row0, tid);
+      dn_epilogue<NWIN>(a, S, e1.ntile, TPW, e1.u, true, e1.row0, tid, (h + 3) & 3, &n1);
     }
-    if (++j >= nmine) break;
+    if (n2 >= n_dn) break;
   }
 }
 
@@ -1106,7 +1152,7 @@ __global__ void __launch_bounds__(1024) k_accept_final(const float* pv, const in
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t tab_n, tab_woken, tab_slot, xfrag, xfrag_nat, plog, psq, afrag, afrag_sh, part, total;
+  size_t ctr, tab_n, tab_woken, tab_slot, xfrag, xfrag_nat, plog, psq, afrag, afrag_sh, part, total;
   int umax, hs;
 };
 
@@ -1118,6 +1164,7 @@ Layout make_layout(const moe_layer* L, int k) {
   o.umax = (int)((E < (size_t)KMAX * K) ? E : (size_t)KMAX * K);
   o.hs = router_splits(L->hidden);
   size_t off = 0;
+  o.ctr = off;       off = align256(off + (size_t)2 * NGRP * CTR_STRIDE * 4);
   o.tab_n = off;     off = align256(off + 16);
   o.tab_woken = off; off = align256(off + (size_t)o.umax * 4);
   o.tab_slot = off;  off = align256(off + (size_t)o.umax * KMAX);
@@ -1258,7 +1305,7 @@ static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint
   a.wg = (const uint8_t*)L->w_gate; a.wu = (const uint8_t*)L->w_up; a.wd = (const uint8_t*)L->w_down;
   a.sg = L->s_gate; a.su = L->s_up; a.sd = L->s_down;
   a.shg = (const uint8_t*)L->sh_gate; a.shu = (const uint8_t*)L->sh_up; a.shd = (const uint8_t*)L->sh_down;
-  a.tab_n = (int32_t*)(ws + lay.tab_n); a.tab_woken = (int32_t*)(ws + lay.tab_woken);
+  a.tab_n = (int32_t*)(ws + lay.tab_n); a.ctr = (uint32_t*)(ws + lay.ctr); a.tab_woken = (int32_t*)(ws + lay.tab_woken);
   a.tab_slot = (int8_t*)(ws + lay.tab_slot);
   a.xfrag = (u32x4*)(ws + lay.xfrag); a.xfrag_nat = (u32x4*)(ws + lay.xfrag_nat); a.plog = (float*)(ws + lay.plog); a.psq = (float*)(ws + lay.psq);
   a.afrag = (u32x4*)(ws + lay.afrag); a.afrag_sh = (u32x4*)(ws + lay.afrag_sh); a.part = (float*)(ws + lay.part);
