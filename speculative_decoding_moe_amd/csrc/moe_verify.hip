@@ -169,7 +169,7 @@ struct alignas(16) Smem {
   int pos[MAX_E];
   int woken[MAX_U];
   float wcol[MAX_U + 1][KMAX];
-  int8_t slot[MAX_U][KMAX];
+  alignas(8) int8_t slot[MAX_U][KMAX];
   float rinv[KMAX];
   int nw;
   int claim[4];  // ring of claimed item indices: item n sits in claim[n % 4]
@@ -978,9 +978,12 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   const rsrc_t raf = buf_rsrc(a.afrag, (uint32_t)a.umax * (I / 32) * 2048);
   if (b < n_sh) dn_load_bf16<NWIN>(Ts, buf_rsrc(a.shd, H * Is * 2), (uint32_t)(b * 16 * SH::TPI_BF * Is * 2), Is, wave, lane);
 
+  // the routing tables, up to umax entries regardless of U, in one memory round trip
+  static_assert(MAX_U <= NTH && MAX_U * KMAX / 8 <= NTH, "one table load per thread");
   const int U = __builtin_amdgcn_readfirstlane(a.tab_n[0]);
-  for (int i = tid; i < U; i += NTH) S.woken[i] = a.tab_woken[i];
-  for (int i = tid; i < U * KMAX; i += NTH) S.slot[i / KMAX][i % KMAX] = a.tab_slot[i];
+  if (tid < a.umax) S.woken[tid] = a.tab_woken[tid];
+  if (tid < a.umax * KMAX / 8)
+    reinterpret_cast<uint2*>(&S.slot[0][0])[tid] = reinterpret_cast<const uint2*>(a.tab_slot)[tid];
   __syncthreads();
 
   const int ipe = H / (16 * (MX ? SH::TPI_MX : SH::TPI_BF));
