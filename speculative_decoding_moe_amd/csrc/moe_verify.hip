@@ -308,6 +308,37 @@ __device__ __forceinline__ void topk_rounds(uint32_t (&key)[2][8], int K, int la
   }
 }
 
+// Two tokens in one chain when E <= 256: lanes 0-31 hold token A's experts, lanes 32-63 token B's
+// (lane l, slot m: expert (l mod 32) + 32 m). The DPP steps stay inside 16-lane rows, so rows 0-1
+// reduce token A and rows 2-3 token B; each round picks both tokens' next expert. Lane j (j < 32)
+// records pick j of token A, lane 32 + j pick j of token B.
+__device__ __forceinline__ void topk_rounds_pair(uint32_t (&key)[8], int K, int lane, int& my_id, float& my_val) {
+  const bool hi = lane >= 32;
+  const int hl = lane & 31;
+  for (int j = 0; j < K; ++j) {
+    uint32_t x = max(max(max(key[0], key[1]), max(key[2], key[3])), max(max(key[4], key[5]), max(key[6], key[7])));
+    x = max(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = max(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = max(x, dpp_u32<0x141>(x));  // row_half_mirror
+    x = max(x, dpp_u32<0x140>(x));  // row_mirror
+    const uint32_t wa = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
+    const uint32_t wb = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
+    const uint32_t w = hi ? wb : wa;
+    int sma = 7, sla = 0, smb = 7, slb = 0;
+#pragma unroll
+    for (int m = 7; m >= 0; --m) {  // ends on the lowest slot holding each token's maximum
+      const uint64_t bm = __ballot(key[m] == w);
+      const uint32_t ba = (uint32_t)bm, bb = (uint32_t)(bm >> 32);
+      if (ba) { sma = m; sla = __builtin_ctz(ba); }
+      if (bb) { smb = m; slb = __builtin_ctz(bb); }
+    }
+    const int sm = hi ? smb : sma, sl = hi ? slb : sla;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) key[m] = (m == sm && hl == sl) ? 0u : key[m];
+    if (hl == j) { my_id = sl + 32 * sm; my_val = okey32_value(w); }
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // routing (every gate/up workgroup, into LDS)
 // ------------------------------------------------------------------------------------------
@@ -344,40 +375,72 @@ __device__ void route(const Args& a, Smem& S, int wave, int lane, int tid) {
   }
   for (int i = tid; i < MAX_E; i += NTH) S.flag[i] = 0;
   __syncthreads();
-  // Top-K per token: wave w serves tokens w and w + 8 together (the two round chains interleave);
-  // 32-bit keys (order-preserving logit bits), equal logits to the lower expert id; softmax over
-  // the K in the same wave. Lane j keeps pick j.
+  // Top-K per token: wave w serves tokens w and w + 8; 32-bit keys (order-preserving logit bits),
+  // equal logits to the lower expert id; softmax over the K in the same wave.
   static_assert(MAX_E / 64 == 8 && KMAX == 2 * NW, "top-K layout");
-  for (int t0 = wave; t0 < k; t0 += 2 * NW) {
-    const int t1 = t0 + NW;
-    const bool two = t1 < k;  // wave-uniform
-    uint32_t key[2][8];
+  if (E <= 256 && k > NW) {
+    // both tokens in one chain, half a wave each (topk_rounds_pair); lane 32 h + j keeps pick j
+    const int t = wave + (lane >= 32 ? NW : 0);
+    const bool live = t < k;
+    uint32_t key[8];
+    const float rv = S.rinv[live ? t : wave];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int t = c ? (two ? t1 : t0) : t0;
-      const float rv = S.rinv[t];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int e = lane + 64 * m;
-        key[c][m] = e < E ? okey32(rv * lg[t * E + e]) : 0u;
+    for (int m = 0; m < 8; ++m) {
+      const int e = (lane & 31) + 32 * m;
+      key[m] = (live && e < E) ? okey32(rv * lg[t * E + e]) : 0u;
+    }
+    if (wave < k) {  // wave-uniform: token `wave` exists
+      int my_id = 0;
+      float my_val = 0.f;
+      topk_rounds_pair(key, K, lane, my_id, my_val);
+      const int base = lane & 32;  // first lane of this half
+      const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
+      const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 32));
+      const float ex = expf(my_val - (base ? m1 : m0));
+      float sa = 0.f, sb = 0.f;
+      for (int j = 0; j < K; ++j) {
+        sa += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+        sb += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), 32 + j));
+      }
+      const int j = lane & 31;
+      if (live && j < K) {
+        S.ids[t][j] = my_id;
+        S.w[t][j] = ex / (base ? sb : sa);
+        S.flag[my_id] = 1;
       }
     }
-    int my_id[2] = {0, 0};
-    float my_val[2] = {0.f, 0.f};
-    if (two) topk_rounds<2>(key, K, lane, my_id, my_val);
-    else     topk_rounds<1>(key, K, lane, my_id, my_val);
+  } else {
+    for (int t0 = wave; t0 < k; t0 += 2 * NW) {
+      const int t1 = t0 + NW;
+      const bool two = t1 < k;  // wave-uniform
+      uint32_t key[2][8];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (c == 1 && !two) break;
-      const int t = c ? t1 : t0;
-      const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val[c]), 0));
-      const float ex = expf(my_val[c] - m0);
-      float sum = 0.f;
-      for (int j = 0; j < K; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
-      if (lane < K) {
-        S.ids[t][lane] = my_id[c];
-        S.w[t][lane] = ex / sum;
-        S.flag[my_id[c]] = 1;
+      for (int c = 0; c < 2; ++c) {
+        const int t = c ? (two ? t1 : t0) : t0;
+        const float rv = S.rinv[t];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const int e = lane + 64 * m;
+          key[c][m] = e < E ? okey32(rv * lg[t * E + e]) : 0u;
+        }
+      }
+      int my_id[2] = {0, 0};
+      float my_val[2] = {0.f, 0.f};
+      if (two) topk_rounds<2>(key, K, lane, my_id, my_val);
+      else     topk_rounds<1>(key, K, lane, my_id, my_val);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        if (c == 1 && !two) break;
+        const int t = c ? t1 : t0;
+        const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val[c]), 0));
+        const float ex = expf(my_val[c] - m0);
+        float sum = 0.f;
+        for (int j = 0; j < K; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+        if (lane < K) {
+          S.ids[t][lane] = my_id[c];
+          S.w[t][lane] = ex / sum;
+          S.flag[my_id[c]] = 1;
+        }
       }
     }
   }
