@@ -271,71 +271,77 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
 }
-// Maximum over the wave's 64 lanes, wave-uniform: DPP permutations inside each 16-lane row (swap
-// neighbours, swap pairs, mirror halves, mirror rows), then the four row results.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-  x = max(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = max(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = max(x, dpp_u32<0x141>(x));  // row_half_mirror
-  x = max(x, dpp_u32<0x140>(x));  // row_mirror
-  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
-  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
-  return max(a, b);
+// Top-K candidates are (key, expert) composites: the order-preserving logit key in the upper word
+// and the inverted expert id in the lower, so the larger composite is the larger logit and, on
+// equal logits, the lower expert id. Experts are laid out lane-major (lane l holds experts
+// NS l .. NS l + NS - 1), so among lanes whose heads tie, the lowest lane holds the lowest id.
+__device__ __forceinline__ uint64_t topk_comp(uint32_t key, int e) {
+  return ((uint64_t)key << 32) | (uint64_t)(~(uint32_t)e);
 }
-
-// K rounds over NC tokens' candidate keys (lane l holds experts l + 64 m, m < 8): each round takes
-// the wave maximum of the lane maxima, finds the lowest expert id holding it (first slot m with a
-// match, then the lowest lane) and clears that slot. Lane j records pick j of each token.
-template <int NC>
-__device__ __forceinline__ void topk_rounds(uint32_t (&key)[2][8], int K, int lane, int (&my_id)[2],
-                                            float (&my_val)[2]) {
-  for (int j = 0; j < K; ++j) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      uint32_t lm = max(max(max(key[c][0], key[c][1]), max(key[c][2], key[c][3])),
-                        max(max(key[c][4], key[c][5]), max(key[c][6], key[c][7])));
-      const uint32_t w = wave_max_u32(lm);
-      int sm = 7, sl = 0;
-#pragma unroll
-      for (int m = 7; m >= 0; --m) {  // ends on the lowest slot holding w
-        const uint64_t b = __ballot(key[c][m] == w);
-        if (b) { sm = m; sl = __builtin_ctzll(b); }
-      }
-#pragma unroll
-      for (int m = 0; m < 8; ++m) key[c][m] = (m == sm && lane == sl) ? 0u : key[c][m];
-      if (lane == j) { my_id[c] = sl + 64 * sm; my_val[c] = okey32_value(w); }
-    }
+__device__ __forceinline__ void cmpx(uint64_t& a, uint64_t& b) {  // a takes the larger
+  const bool s = b > a;
+  const uint64_t t = s ? b : a;
+  b = s ? a : b;
+  a = t;
+}
+// descending sort of a lane's candidates: the 5- and 19-comparator networks for 4 and 8 inputs
+template <int NS>
+__device__ __forceinline__ void sort_desc(uint64_t (&c)[NS]) {
+  static_assert(NS == 4 || NS == 8, "4 or 8 candidates per lane");
+  if constexpr (NS == 4) {
+    cmpx(c[0], c[1]); cmpx(c[2], c[3]); cmpx(c[0], c[2]); cmpx(c[1], c[3]); cmpx(c[1], c[2]);
+  } else {
+    cmpx(c[0], c[1]); cmpx(c[2], c[3]); cmpx(c[4], c[5]); cmpx(c[6], c[7]);
+    cmpx(c[0], c[2]); cmpx(c[1], c[3]); cmpx(c[4], c[6]); cmpx(c[5], c[7]);
+    cmpx(c[1], c[2]); cmpx(c[5], c[6]);
+    cmpx(c[0], c[4]); cmpx(c[1], c[5]); cmpx(c[2], c[6]); cmpx(c[3], c[7]);
+    cmpx(c[2], c[4]); cmpx(c[3], c[5]);
+    cmpx(c[1], c[2]); cmpx(c[3], c[4]); cmpx(c[5], c[6]);
   }
 }
 
-// Two tokens in one chain when E <= 256: lanes 0-31 hold token A's experts, lanes 32-63 token B's
-// (lane l, slot m: expert (l mod 32) + 32 m). The DPP steps stay inside 16-lane rows, so rows 0-1
-// reduce token A and rows 2-3 token B; each round picks both tokens' next expert. Lane j (j < 32)
-// records pick j of token A, lane 32 + j pick j of token B.
-__device__ __forceinline__ void topk_rounds_pair(uint32_t (&key)[8], int K, int lane, int& my_id, float& my_val) {
-  const bool hi = lane >= 32;
-  const int hl = lane & 31;
+// K rounds over the lanes' sorted candidate lists: each round takes the maximum of the list
+// heads (DPP steps inside 16-lane rows, then the row results), the lowest lane whose head equals
+// it (one ballot) and pops that lane's head. HALF: the wave serves two tokens, lanes 0-31 and
+// 32-63; the DPP steps never cross a half, so each half picks its own token's next expert. Lane
+// j of a half records pick j (expert and key).
+template <int NS, bool HALF>
+__device__ __forceinline__ void topk_sorted(uint64_t (&c)[NS], int K, int lane, int& my_e, uint32_t& my_key) {
+  const bool hi = HALF && lane >= 32;
+  const int jl = HALF ? (lane & 31) : lane;
   for (int j = 0; j < K; ++j) {
-    uint32_t x = max(max(max(key[0], key[1]), max(key[2], key[3])), max(max(key[4], key[5]), max(key[6], key[7])));
+    const uint32_t h = (uint32_t)(c[0] >> 32);
+    uint32_t x = h;
     x = max(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
     x = max(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
     x = max(x, dpp_u32<0x141>(x));  // row_half_mirror
     x = max(x, dpp_u32<0x140>(x));  // row_mirror
-    const uint32_t wa = max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16));
-    const uint32_t wb = max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48));
-    const uint32_t w = hi ? wb : wa;
-    int sma = 7, sla = 0, smb = 7, slb = 0;
-#pragma unroll
-    for (int m = 7; m >= 0; --m) {  // ends on the lowest slot holding each token's maximum
-      const uint64_t bm = __ballot(key[m] == w);
-      const uint32_t ba = (uint32_t)bm, bb = (uint32_t)(bm >> 32);
-      if (ba) { sma = m; sla = __builtin_ctz(ba); }
-      if (bb) { smb = m; slb = __builtin_ctz(bb); }
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    const uint32_t lo = (uint32_t)c[0];
+    uint32_t w, e;
+    int sl;
+    if constexpr (HALF) {
+      const uint32_t wa = max(r0, r1), wb = max(r2, r3);
+      w = hi ? wb : wa;
+      const uint64_t bm = __ballot(h == w);  // each half holds its own maximum
+      const int sla = __builtin_ctz((uint32_t)bm), slb = 32 + __builtin_ctz((uint32_t)(bm >> 32));
+      const uint32_t ea = (uint32_t)__builtin_amdgcn_readlane((int)lo, sla);
+      const uint32_t eb = (uint32_t)__builtin_amdgcn_readlane((int)lo, slb);
+      sl = hi ? slb : sla;
+      e = hi ? eb : ea;
+    } else {
+      w = max(max(r0, r1), max(r2, r3));
+      sl = __builtin_ctzll(__ballot(h == w));
+      e = (uint32_t)__builtin_amdgcn_readlane((int)lo, sl);
     }
-    const int sm = hi ? smb : sma, sl = hi ? slb : sla;
+    if (jl == j) { my_e = (int)~e; my_key = w; }
+    const bool pop = lane == sl;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) key[m] = (m == sm && hl == sl) ? 0u : key[m];
-    if (hl == j) { my_id = sl + 32 * sm; my_val = okey32_value(w); }
+    for (int m = 0; m + 1 < NS; ++m) c[m] = pop ? c[m + 1] : c[m];
+    c[NS - 1] = pop ? 0ull : c[NS - 1];
   }
 }
 
@@ -375,72 +381,77 @@ __device__ void route(const Args& a, Smem& S, int wave, int lane, int tid) {
   }
   for (int i = tid; i < MAX_E; i += NTH) S.flag[i] = 0;
   __syncthreads();
-  // Top-K per token: wave w serves tokens w and w + 8; 32-bit keys (order-preserving logit bits),
-  // equal logits to the lower expert id; softmax over the K in the same wave.
-  static_assert(MAX_E / 64 == 8 && KMAX == 2 * NW, "top-K layout");
+  // Top-K per token (wave w serves tokens w and w + 8), then the softmax over the K in the same
+  // wave. Ties go to the lower expert id.
+  static_assert(MAX_E == 8 * 64 && KMAX == 2 * NW, "top-K layout");
   if (E <= 256 && k > NW) {
-    // both tokens in one chain, half a wave each (topk_rounds_pair); lane 32 h + j keeps pick j
+    // both tokens at once, half a wave each, 8 candidates per lane (expert 8 (lane mod 32) + m)
     const int t = wave + (lane >= 32 ? NW : 0);
     const bool live = t < k;
-    uint32_t key[8];
     const float rv = S.rinv[live ? t : wave];
+    const int e0 = 8 * (lane & 31);
+    uint64_t c[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const int e = (lane & 31) + 32 * m;
-      key[m] = (live && e < E) ? okey32(rv * lg[t * E + e]) : 0u;
+      const int e = e0 + m;
+      const float v = lg[t * E + (e < E ? e : E - 1)];  // rows past k are in bounds, unused
+      c[m] = topk_comp((live && e < E) ? okey32(rv * v) : 0u, e);
     }
-    if (wave < k) {  // wave-uniform: token `wave` exists
-      int my_id = 0;
-      float my_val = 0.f;
-      topk_rounds_pair(key, K, lane, my_id, my_val);
-      const int base = lane & 32;  // first lane of this half
-      const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
-      const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 32));
-      const float ex = expf(my_val - (base ? m1 : m0));
-      float sa = 0.f, sb = 0.f;
-      for (int j = 0; j < K; ++j) {
-        sa += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
-        sb += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), 32 + j));
-      }
-      const int j = lane & 31;
-      if (live && j < K) {
-        S.ids[t][j] = my_id;
-        S.w[t][j] = ex / (base ? sb : sa);
-        S.flag[my_id] = 1;
-      }
+    sort_desc<8>(c);
+    int my_e = 0;
+    uint32_t my_key = 0;
+    topk_sorted<8, true>(c, K, lane, my_e, my_key);
+    const float my_val = okey32_value(my_key);
+    const int base = lane & 32;  // first lane of this half
+    const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
+    const float m1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 32));
+    const float ex = expf(my_val - (base ? m1 : m0));
+    float sa = 0.f, sb = 0.f;
+    for (int j = 0; j < K; ++j) {
+      sa += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+      sb += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), 32 + j));
+    }
+    const int j = lane & 31;
+    if (live && j < K) {
+      S.ids[t][j] = my_e;
+      S.w[t][j] = ex / (base ? sb : sa);
+      S.flag[my_e] = 1;
     }
   } else {
-    for (int t0 = wave; t0 < k; t0 += 2 * NW) {
-      const int t1 = t0 + NW;
-      const bool two = t1 < k;  // wave-uniform
-      uint32_t key[2][8];
+    for (int t = wave; t < k; t += NW) {
+      const float rv = S.rinv[t];
+      int my_e = 0;
+      uint32_t my_key = 0;
+      if (E <= 256) {  // 4 candidates per lane: experts 4 lane + m
+        uint64_t c[4];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int t = c ? (two ? t1 : t0) : t0;
-        const float rv = S.rinv[t];
+        for (int m = 0; m < 4; ++m) {
+          const int e = 4 * lane + m;
+          const float v = lg[t * E + (e < E ? e : E - 1)];
+          c[m] = topk_comp(e < E ? okey32(rv * v) : 0u, e);
+        }
+        sort_desc<4>(c);
+        topk_sorted<4, false>(c, K, lane, my_e, my_key);
+      } else {  // 8 candidates per lane: experts 8 lane + m
+        uint64_t c[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
-          const int e = lane + 64 * m;
-          key[c][m] = e < E ? okey32(rv * lg[t * E + e]) : 0u;
+          const int e = 8 * lane + m;
+          const float v = lg[t * E + (e < E ? e : E - 1)];
+          c[m] = topk_comp(e < E ? okey32(rv * v) : 0u, e);
         }
+        sort_desc<8>(c);
+        topk_sorted<8, false>(c, K, lane, my_e, my_key);
       }
-      int my_id[2] = {0, 0};
-      float my_val[2] = {0.f, 0.f};
-      if (two) topk_rounds<2>(key, K, lane, my_id, my_val);
-      else     topk_rounds<1>(key, K, lane, my_id, my_val);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        if (c == 1 && !two) break;
-        const int t = c ? t1 : t0;
-        const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val[c]), 0));
-        const float ex = expf(my_val[c] - m0);
-        float sum = 0.f;
-        for (int j = 0; j < K; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
-        if (lane < K) {
-          S.ids[t][lane] = my_id[c];
-          S.w[t][lane] = ex / sum;
-          S.flag[my_id[c]] = 1;
-        }
+      const float my_val = okey32_value(my_key);
+      const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
+      const float ex = expf(my_val - m0);
+      float sum = 0.f;
+      for (int j = 0; j < K; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+      if (lane < K) {
+        S.ids[t][lane] = my_e;
+        S.w[t][lane] = ex / sum;
+        S.flag[my_e] = 1;
       }
     }
   }

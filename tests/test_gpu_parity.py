@@ -201,6 +201,43 @@ def test_edge_shapes_parity(B, shape):
         check_parity(g, x, wl, tol=MX_TOL if shape.wdtype == "mxfp4" else BF16_TOL)
 
 
+class _PeriodicRouterLayer(GenLayer):
+    """A generated layer whose router rows repeat with period P, so logits tie exactly."""
+
+    def __init__(self, wl, period):
+        super().__init__(wl, 0)
+        self.period = period
+
+    def router(self):
+        r = gen.router_weight(self.wl, 0)
+        return np.ascontiguousarray(r[np.arange(r.shape[0]) % self.period])
+
+
+@pytest.mark.parametrize("shape,period", [
+    (gen.LayerShape(hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512), 5),
+    (gen.LayerShape(hidden=256, n_experts=512, top_k=16, inter=256, shared_inter=256), 7),
+    (gen.LayerShape(hidden=256, n_experts=200, top_k=6, inter=256, shared_inter=0), 3),
+])
+def test_exact_router_ties_pick_lower_expert_ids(B, shape, period):
+    """Identical router rows give bit-identical logits, so most picks are exact ties: the GPU
+    must take equal logits in ascending expert order, exactly as the oracle does."""
+    from speculative_decoding_moe_amd.workloads import device
+    wl = gen.Workload("ties", shape, k=16, seed=99)
+    L = _PeriodicRouterLayer(wl, period)
+    t = device.layer_tensors(wl, 0, "cuda")
+    t["router_w"] = torch.from_numpy(L.router()).cuda()
+    layer = device.make_layer(wl, 0, "cuda", tensors=t)
+    for k in (1, 9, 16):
+        x = gen.hidden_states(wl, rep=50 + k, k=k)
+        g = run_block(B, layer, x)
+        ref = oracle.moe_block(x, L, shape.top_k)
+        assert np.array_equal(g["ids"], ref["ids"]), (k, g["ids"][:2], ref["ids"][:2])
+        assert g["n_woken"] == ref["n_woken"]
+        np.testing.assert_allclose(g["w"], ref["w"], rtol=0, atol=1e-6)
+        rms = float(np.sqrt(np.mean(ref["y"] ** 2)))
+        assert float(np.abs(g["y"] - ref["y"]).max()) <= BF16_TOL * rms
+
+
 def test_determinism_and_stale_workspace(B):
     """Bit-identical results across reruns and whatever the workspace held before (stale
     contents never reach the MFMA tiles)."""
