@@ -380,6 +380,12 @@ __device__ void route(const Args& a, Smem& S, int wave, int lane, int tid) {
     S.rinv[tid] = a.pre_norm ? 1.0f / sqrtf(ssq / (float)a.H + a.eps) : 1.0f;
   }
   for (int i = tid; i < MAX_E; i += NTH) S.flag[i] = 0;
+  {  // the weight table (umax routed rows and the shared row) and the slot table start empty
+    float* wc = &S.wcol[0][0];
+    for (int i = tid; i < (a.umax + 1) * KMAX; i += NTH) wc[i] = 0.f;
+    uint32_t* sl = reinterpret_cast<uint32_t*>(&S.slot[0][0]);
+    for (int i = tid; i < a.umax * KMAX / 4; i += NTH) sl[i] = 0xFFFFFFFFu;  // every byte -1
+  }
   __syncthreads();
   // Top-K per token (wave w serves tokens w and w + 8), then the softmax over the K in the same
   // wave. Ties go to the lower expert id.
@@ -456,25 +462,23 @@ __device__ void route(const Args& a, Smem& S, int wave, int lane, int tid) {
     }
   }
   __syncthreads();
-  if (wave == 0) {
+  if (wave == 0) {  // the union in ascending expert order: all flags read at once, then ballots
+    bool f[MAX_E / 64];
+#pragma unroll
+    for (int c = 0; c < MAX_E / 64; ++c) f[c] = S.flag[c * 64 + lane] != 0;  // zero past E
     int base = 0;
-    for (int c = 0; c < (E + 63) / 64; ++c) {
+#pragma unroll
+    for (int c = 0; c < MAX_E / 64; ++c) {
       const int e = c * 64 + lane;
-      const bool f = e < E && S.flag[e];
-      const unsigned long long m = __ballot(f);
+      const unsigned long long m = __ballot(f[c]);
       const int p = base + __popcll(m & ((1ull << lane) - 1ull));
-      if (f) { S.woken[p] = e; S.pos[e] = p; }
+      if (f[c]) { S.woken[p] = e; S.pos[e] = p; }
       base += __popcll(m);
     }
     if (lane == 0) S.nw = base;
   }
   __syncthreads();
   const int U = S.nw;
-  for (int i = tid; i < (U + 1) * KMAX; i += NTH) {
-    S.wcol[i / KMAX][i % KMAX] = 0.f;
-    if (i < U * KMAX) S.slot[i / KMAX][i % KMAX] = -1;
-  }
-  __syncthreads();
   if (tid < k * K) {
     const int t = tid / K, j = tid % K;
     const int u = S.pos[S.ids[t][j]];
@@ -1198,12 +1202,14 @@ __global__ void __launch_bounds__(256) k_argmax_partial(const float* logits, int
 }
 
 // One workgroup of 16 waves: wave w reduces rows w, w + 16, ... (lane l takes chunks l, l + 64,
-// ...), then thread 0 scans the longest accepted prefix.
+// ...); then wave 0 compares the drafts with the targets, one position per lane, and the first
+// mismatch (a ballot) is the accepted length. The draft ids are requested before the partials.
 __global__ void __launch_bounds__(1024) k_accept_final(const float* pv, const int* pi, int nchunks,
                                                        int n_target, const int32_t* draft, int n_draft,
                                                        int32_t* target_ids, int32_t* accepted) {
   __shared__ int tgt[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t d = (tid < n_draft) ? draft[tid] : 0;  // n_draft <= n_target <= 64
   for (int row = wave; row < n_target; row += 16) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
@@ -1216,10 +1222,10 @@ __global__ void __launch_bounds__(1024) k_accept_final(const float* pv, const in
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    int a = 0;
-    while (a < n_draft && draft[a] == tgt[a]) ++a;
-    accepted[0] = a;
+  if (wave == 0) {
+    const bool miss = lane < n_draft && d != tgt[lane];
+    const unsigned long long m = __ballot(miss);
+    if (lane == 0) accepted[0] = m ? __builtin_ctzll(m) : n_draft;
   }
 }
 
