@@ -211,6 +211,21 @@ def moe_stack(x0: np.ndarray, layers, top_k: int, *, rms_eps: float = 1e-6) -> l
 # ----------------------------------------------------------------------------------------------
 # acceptance
 # ----------------------------------------------------------------------------------------------
+def head_logits(h: np.ndarray, w_head_bits: np.ndarray) -> np.ndarray:
+    """Target logits of the block positions, l[i, v] = sum_c h[i, c] * W[v, c], with the output
+    head W [V][H] in bf16 and the positions' final hidden states h [n][H] taken as given (no
+    final normalisation). The head is one matrix read once for the whole block ([SH1] 'What the
+    pieces cost'); it is the [hidden x V] matrix whose streaming cost grows with V ([SH1] 'Should
+    we shrink the vocab?')."""
+    return np.asarray(h, dtype=np.float64) @ decode_bf16(w_head_bits).T
+
+
+def head_accept(h: np.ndarray, w_head_bits: np.ndarray, draft: np.ndarray):
+    """The output head followed by greedy acceptance: (target ids, accepted length)."""
+    t = argmax_first(head_logits(h, w_head_bits))
+    return t, accept_length(np.asarray(draft), t)
+
+
 def argmax_first(logits: np.ndarray) -> np.ndarray:
     """Greedy target token per block position: the lowest index attaining the row maximum."""
     return np.argmax(np.asarray(logits), axis=1).astype(np.int64)

@@ -360,6 +360,63 @@ def test_accept_length_brute_force_and_edges():
         assert oracle.accept_length(d, tg) == brute
 
 
+# ---------------------------------------------------------------- output head
+def _bf16_bits(x):
+    return gen.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def test_head_logits_brute_force_tiny():
+    rng = np.random.default_rng(31)
+    n, V, H = 3, 7, 5
+    h = rng.standard_normal((n, H))
+    w = _bf16_bits(rng.standard_normal((V, H)))
+    got = oracle.head_logits(h, w)
+    assert got.shape == (n, V)
+    for i in range(n):
+        for v in range(V):
+            ref = sum(float(h[i, c]) * _bf16_closed_form(int(w[v, c])) for c in range(H))
+            assert abs(got[i, v] - ref) <= 1e-12 * (1 + abs(ref))
+
+
+def test_head_logits_one_hot_and_ones_rows():
+    """A one-hot hidden state picks one weight column; an all-ones one sums every row (a
+    transposed operand or a dropped term fails one of the two)."""
+    rng = np.random.default_rng(32)
+    V, H = 40, 24
+    w = _bf16_bits(rng.standard_normal((V, H)) * 0.02)
+    wf = np.array([[_bf16_closed_form(int(b)) for b in row] for row in w])
+    h = np.zeros((3, H))
+    h[0, 5] = 1.0
+    h[1, 23] = -2.0
+    h[2, :] = 1.0
+    got = oracle.head_logits(h, w)
+    assert np.array_equal(got[0], wf[:, 5])
+    assert np.array_equal(got[1], -2.0 * wf[:, 23])
+    np.testing.assert_allclose(got[2], wf.sum(axis=1), rtol=0, atol=1e-15)
+
+
+def test_head_accept_planted_winners_ties_and_prefix():
+    """Position i's hidden state points along coordinate c_i and row v_i is the unit vector of
+    c_i, so v_i wins with logit ~10 against random rows of ~0.2; an identical later row loses the
+    tie; the accepted length follows the drafts."""
+    rng = np.random.default_rng(33)
+    V, H = 300, 64
+    planted, coords = [17, 250, 3, 17], [5, 40, 63, 5]
+    w = _bf16_bits(rng.standard_normal((V, H)) * 0.02)
+    h = 0.01 * np.abs(rng.standard_normal((4, H)))
+    for i, (v, c) in enumerate(zip(planted, coords)):
+        h[i, c] += 10.0
+        w[v] = _bf16_bits(np.eye(H)[c])
+    w[260] = w[250]                                        # exact tie: the lower index wins
+    logits = oracle.head_logits(h, w)
+    assert logits[1, 250] == logits[1, 260]
+    t, a = oracle.head_accept(h, w, np.array([17, 250, 9, 17]))
+    assert list(t) == planted
+    assert a == 2
+    assert oracle.head_accept(h, w, np.array(planted))[1] == 4
+    assert oracle.head_accept(h, w, np.array([], dtype=np.int64))[1] == 0
+
+
 def _read_golden(name):
     rows = []
     with open(os.path.join(GOLDEN, name)) as f:
