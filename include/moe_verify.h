@@ -180,6 +180,30 @@ int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const in
                   int32_t n_draft, int32_t* target_ids, int32_t* accepted, void* workspace,
                   size_t ws_bytes, void* hip_stream);
 
+/* Bytes of device workspace lm_head_accept needs (0 if the sizes are invalid). Host only. */
+size_t lm_head_accept_workspace_size(int32_t n_target, int32_t hidden, int32_t vocab);
+
+/* The target's output head with a fused argmax, then greedy acceptance. The head is a single
+ * [V x H] matrix read once for the whole block ("Speculating on a Strix Halo", section "What the
+ * pieces cost"); it is the hidden-by-vocabulary matrix whose streaming cost grows with V (same
+ * page, section "Should we shrink the vocab?"). The logits are never written to memory.
+ *   h          fp32 [n_target][hidden]: final hidden states of the block positions (taken as
+ *              given, no final normalisation)
+ *   w_head     bf16 head weights [V][hidden] in MOE_LAYOUT_TILED, produced by moe_pack_weights
+ *              (wdtype MOE_W_BF16, n_mats 1, rows = V rounded up to a multiple of 16, cols =
+ *              hidden); rows past V are never selected, whatever they hold
+ *   layout     must be MOE_LAYOUT_TILED
+ *   draft_ids, n_draft, target_ids, accepted: as in accept_prefix; target_ids[i] is the lowest
+ *              row attaining the maximum of h[i] . W[v] over v < vocab
+ * Limits: 1 <= n_target <= 16, 0 <= n_draft <= n_target, hidden a multiple of 128 in
+ * [128, 2048], 1 <= vocab with round_up(vocab, 16) * hidden * 2 < 2^32. h, w_head, target_ids,
+ * accepted, draft_ids and workspace 16-byte aligned; the outputs may not overlap the inputs or
+ * the workspace. Non-finite inputs give unspecified ids. Returns MOE_OK or an MOE_ERR_* code;
+ * the work is enqueued on hip_stream (NULL: the default stream). */
+int lm_head_accept(const float* h, int32_t n_target, int32_t hidden, const void* w_head, int32_t vocab,
+                   int32_t layout, const int32_t* draft_ids, int32_t n_draft, int32_t* target_ids,
+                   int32_t* accepted, void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Static description of a status code. Host only. */
 const char* moe_status_string(int status);
 

@@ -20,7 +20,8 @@ MOE_LAYOUT_TILED = 1
 MOE_PRE_RMSNORM, MOE_RESIDUAL = 1, 2
 
 EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "moe_verify_block_timed",
-           "moe_pack_weights", "accept_prefix_workspace_size", "accept_prefix", "moe_status_string")
+           "moe_pack_weights", "accept_prefix_workspace_size", "accept_prefix",
+           "lm_head_accept_workspace_size", "lm_head_accept", "moe_status_string")
 
 
 class MoeLayerStruct(ctypes.Structure):
@@ -59,6 +60,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.accept_prefix_workspace_size.restype = sz
     lib.accept_prefix.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     lib.accept_prefix.restype = ctypes.c_int
+    lib.lm_head_accept_workspace_size.argtypes = [i32, i32, i32]
+    lib.lm_head_accept_workspace_size.restype = sz
+    lib.lm_head_accept.argtypes = [vp, i32, i32, vp, i32, i32, vp, i32, vp, vp, vp, sz, vp]
+    lib.lm_head_accept.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     return lib
@@ -184,4 +189,34 @@ def accept_prefix(logits, draft_ids, target_ids, accepted, workspace, n_draft=No
     st = lib.accept_prefix(_ptr(logits), n_target, vocab, _ptr(draft_ids), nd, _ptr(target_ids),
                            _ptr(accepted), _ptr(workspace), ws_bytes,
                            _stream_handle() if stream is None else stream)
+    _check(st)
+
+
+def pack_head(w_rowmajor, stream=None):
+    """Tiled copy of a bf16 output head [V][H] (any 16-bit dtype) for lm_head_accept: the rows
+    are zero-padded to a multiple of 16, then packed (library call). Returns the packed tensor."""
+    import torch
+    V, H = int(w_rowmajor.shape[0]), int(w_rowmajor.shape[1])
+    v16 = (V + 15) // 16 * 16
+    src = w_rowmajor.contiguous()
+    if v16 != V:
+        src = torch.cat([src, torch.zeros((v16 - V, H), dtype=src.dtype, device=src.device)])
+    dst, _ = pack_weights(src, stream=stream)
+    return dst
+
+
+def lm_head_accept_workspace_size(n_target: int, hidden: int, vocab: int) -> int:
+    return int(lib.lm_head_accept_workspace_size(int(n_target), int(hidden), int(vocab)))
+
+
+def lm_head_accept(h, w_head_tiled, vocab, draft_ids, target_ids, accepted, workspace, n_draft=None,
+                   stream=None) -> None:
+    """Output head h [n][H] . W[v] over v < vocab with the argmax fused, then the greedy accepted
+    length (library call); w_head_tiled comes from pack_head."""
+    n_target, hidden = int(h.shape[0]), int(h.shape[1])
+    nd = int(draft_ids.shape[0]) if (n_draft is None and draft_ids is not None) else int(n_draft or 0)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.lm_head_accept(_ptr(h), n_target, hidden, _ptr(w_head_tiled), int(vocab), MOE_LAYOUT_TILED,
+                            _ptr(draft_ids), nd, _ptr(target_ids), _ptr(accepted), _ptr(workspace), ws_bytes,
+                            _stream_handle() if stream is None else stream)
     _check(st)

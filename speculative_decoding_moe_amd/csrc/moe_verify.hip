@@ -1230,6 +1230,144 @@ __global__ void __launch_bounds__(1024) k_accept_final(const float* pv, const in
 }
 
 // ------------------------------------------------------------------------------------------
+// lm_head_accept: the target's output head streamed once per block, argmax fused
+// ------------------------------------------------------------------------------------------
+// The head is one [V x H] matrix read once for the whole block ("Speculating on a Strix Halo",
+// "What the pieces cost"; "Should we shrink the vocab?"). An item is 32 head rows (two 16-row
+// tiles of the tiled bf16 layout, 64 H bytes); workgroup b takes items b, b + G, ... with the
+// next item's loads in flight while the current one is multiplied (wave w owns H windows
+// w WPW .. w WPW + WPW - 1, the block's hidden states enter MFMA as bf16 hi + lo fragments that
+// every workgroup builds once). The logits never leave the chip: after the cross-wave sum each
+// thread owns one fixed (tile, row, position) slot and keeps the best (logit, row) seen in it;
+// the workgroup reduces its slots once at the end into one partial per position, and
+// k_accept_final reduces the partials and scans the accepted prefix.
+struct HeadSmem {
+  float red[2][NW * 2 * 256];  // per-wave partial tiles, double-buffered across items
+  float bv[NW][KMAX];
+  int bi[NW][KMAX];
+};
+
+// B fragments of this wave's H windows from the fp32 hidden states (bf16 K order). Every lane
+// loads unconditionally (clamped to position 0 / window 0) so that all loads are in flight at
+// once, then positions past n and inactive waves take zeros.
+template <int WPW>
+__device__ __forceinline__ void head_xb(u32x4 (&xb)[WPW][4][2], const float* h, int H, int n, int win0,
+                                        bool active, int lane) {
+  const int c = lane & 15, q = lane >> 4;
+  const bool live = active && c < n;
+  const float* row = h + (size_t)(c < n ? c : 0) * H + (active ? win0 : 0) * WIN;
+  float4 v[WPW][4][2];
+#pragma unroll
+  for (int wi = 0; wi < WPW; ++wi)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* src = row + wi * WIN + kofs<true>(j, q);
+      v[wi][j][0] = *reinterpret_cast<const float4*>(src);
+      v[wi][j][1] = *reinterpret_cast<const float4*>(src + 4);
+    }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first conversion
+#pragma unroll
+  for (int wi = 0; wi < WPW; ++wi)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float f[8] = {v[wi][j][0].x, v[wi][j][0].y, v[wi][j][0].z, v[wi][j][0].w,
+                          v[wi][j][1].x, v[wi][j][1].y, v[wi][j][1].z, v[wi][j][1].w};
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        split_bf16(f[i], hi[i], lo[i]);
+        hi[i] = live ? hi[i] : 0u;
+        lo[i] = live ? lo[i] : 0u;
+      }
+      pack8(hi, xb[wi][j][0]);
+      pack8(lo, xb[wi][j][1]);
+    }
+}
+
+// Cross-wave sum of one item's two tiles, then each thread's running best for its slot:
+// tile tl = tid / 256, row r = 4 (p / 64) + p % 4 and position c = (p / 4) % 16 of p = tid % 256.
+__device__ __forceinline__ void head_epilogue(float* red, const f32x4 (&acc)[GU_MX_RT][2], int item, int V,
+                                              int n, int wave, int lane, int tid, float& bv, int& bi) {
+  *reinterpret_cast<f32x4*>(&red[(wave * 2 + 0) * 256 + lane * 4]) = acc[0][0];
+  *reinterpret_cast<f32x4*>(&red[(wave * 2 + 1) * 256 + lane * 4]) = acc[0][1];
+  __syncthreads();  // one barrier per item: the other buffer takes the next item's tiles
+  const int tl = tid >> 8, p = tid & 255;
+  float v = 0.f;
+#pragma unroll
+  for (int wv = 0; wv < NW; ++wv) v += red[(wv * 2 + tl) * 256 + p];
+  const int c = (p >> 2) & 15, r = 4 * (p >> 6) + (p & 3);
+  const int row = item * 32 + 16 * tl + r;
+  if (c < n && row < V) argmax_merge(bv, bi, v, row);
+}
+
+template <int WPW>
+__global__ void __launch_bounds__(NTH) k_head(const float* h, const uint8_t* w, int H, int V, int n,
+                                              int n_items, float* pv, int* pi) {
+  __shared__ HeadSmem S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = gridDim.x, b = blockIdx.x;
+  const int win0 = wave * WPW;
+  const bool active = win0 < H / WIN;
+  const int wsafe = active ? win0 : 0;  // inactive waves load window 0 and multiply it by zero
+  const uint32_t tile = (uint32_t)H * 32u;       // bytes of one 16-row tile
+  const uint32_t ntile = (uint32_t)(V + 15) / 16u;
+  // second-tile loads of an odd last item fall past the second resource's range and read zeros
+  const rsrc_t r0 = buf_rsrc(w, ntile * tile), r1 = buf_rsrc(w + tile, (ntile - 1u) * tile);
+  const uint32_t vb = (uint32_t)(256 * wsafe + lane) * 16u;
+  u32x4 xb[WPW][4][2];
+  head_xb<WPW>(xb, h, H, n, win0, active, lane);
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  int i0 = b;
+  if (i0 < n_items) {
+    GUItem<WPW> T0, T1;
+    gu_load_bf16<WPW>(T0, r0, r1, (uint32_t)i0 * 2u * tile, vb);
+    for (;;) {
+      const int i1 = i0 + G;  // item 0 stands in past the end (the same bytes for every workgroup)
+      gu_load_bf16<WPW>(T1, r0, r1, (uint32_t)(i1 < n_items ? i1 : 0) * 2u * tile, vb);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f32x4 acc[GU_MX_RT][2];
+        gu_math_bf16<WPW>(acc, T0, xb);
+        head_epilogue(S.red[0], acc, i0, V, n, wave, lane, tid, bv, bi);
+      }
+      if (i1 >= n_items) break;
+      const int i2 = i1 + G;
+      gu_load_bf16<WPW>(T0, r0, r1, (uint32_t)(i2 < n_items ? i2 : 0) * 2u * tile, vb);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f32x4 acc[GU_MX_RT][2];
+        gu_math_bf16<WPW>(acc, T1, xb);
+        head_epilogue(S.red[1], acc, i1, V, n, wave, lane, tid, bv, bi);
+      }
+      if (i2 >= n_items) break;
+      i0 = i2;
+    }
+  }
+  // the four row slots of a position sit in lanes 4c .. 4c + 3 of each wave
+#pragma unroll
+  for (int off = 1; off <= 2; off <<= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    argmax_merge(bv, bi, ov, oi);
+  }
+  if ((lane & 3) == 0) {
+    S.bv[wave][lane >> 2] = bv;
+    S.bi[wave][lane >> 2] = bi;
+  }
+  __syncthreads();
+  if (tid < n) {
+    float v = S.bv[0][tid];
+    int i = S.bi[0][tid];
+#pragma unroll
+    for (int wv = 1; wv < NW; ++wv) argmax_merge(v, i, S.bv[wv][tid], S.bi[wv][tid]);
+    pv[(size_t)tid * G + b] = v;
+    pi[(size_t)tid * G + b] = i;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------------------
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -1477,6 +1615,49 @@ int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const in
   (void)hipGetLastError();
   k_argmax_partial<<<dim3(nchunks, n_target), 256, 0, s>>>(logits, vocab, nchunks, pv, pi);
   k_accept_final<<<1, 1024, 0, s>>>(pv, pi, nchunks, n_target, draft_ids, n_draft, target_ids, accepted);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+constexpr int HEAD_GMAX = 1024;  // largest grid the head workspace provides for
+
+size_t lm_head_accept_workspace_size(int32_t n_target, int32_t hidden, int32_t vocab) {
+  if (n_target < 1 || n_target > KMAX || hidden < 1 || vocab < 1) return 0;
+  return 2 * align256((size_t)n_target * HEAD_GMAX * 4);
+}
+
+int lm_head_accept(const float* h, int32_t n_target, int32_t hidden, const void* w_head, int32_t vocab,
+                   int32_t layout, const int32_t* draft_ids, int32_t n_draft, int32_t* target_ids,
+                   int32_t* accepted, void* workspace, size_t ws_bytes, void* hip_stream) {
+  if (!h || !w_head || !target_ids || !accepted || !workspace || (n_draft > 0 && !draft_ids)) return MOE_ERR_NULL;
+  if (n_target < 1 || n_target > KMAX || n_draft < 0 || n_draft > n_target || hidden < WIN ||
+      hidden > 2 * NW * WIN || hidden % WIN != 0 || vocab < 1)
+    return MOE_ERR_SHAPE;
+  const uint64_t v16 = ((uint64_t)vocab + 15) / 16 * 16;
+  if (v16 * (uint64_t)hidden * 2 > 0xFFFFFFFFull) return MOE_ERR_SHAPE;  // 32-bit buffer offsets
+  if (layout != MOE_LAYOUT_TILED) return MOE_ERR_DTYPE;
+  if (!aligned16(h) || !aligned16(w_head) || !aligned16(target_ids) || !aligned16(accepted) ||
+      !aligned16(workspace) || (draft_ids && !aligned16(draft_ids)))
+    return MOE_ERR_ALIGN;
+  const size_t need = lm_head_accept_workspace_size(n_target, hidden, vocab);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const size_t hbytes = (size_t)n_target * hidden * 4, wbytes = (size_t)v16 * hidden * 2;
+  const size_t tbytes = (size_t)n_target * 4;
+  if (overlaps(target_ids, tbytes, h, hbytes) || overlaps(target_ids, tbytes, w_head, wbytes) ||
+      overlaps(target_ids, tbytes, workspace, need) || overlaps(accepted, 4, h, hbytes) ||
+      overlaps(accepted, 4, w_head, wbytes) || overlaps(accepted, 4, workspace, need) ||
+      overlaps(accepted, 4, target_ids, tbytes) || overlaps(workspace, need, h, hbytes) ||
+      overlaps(workspace, need, w_head, wbytes))
+    return MOE_ERR_ALIAS;
+  const int G = std::min(num_cus(), HEAD_GMAX);
+  const int n_items = (int)((v16 / 16 + 1) / 2);
+  float* pv = (float*)workspace;
+  int* pi = (int*)((uint8_t*)workspace + need / 2);
+  hipStream_t s = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  const uint8_t* w = (const uint8_t*)w_head;
+  if (hidden <= NW * WIN) k_head<1><<<G, NTH, 0, s>>>(h, w, hidden, vocab, n_target, n_items, pv, pi);
+  else                    k_head<2><<<G, NTH, 0, s>>>(h, w, hidden, vocab, n_target, n_items, pv, pi);
+  k_accept_final<<<1, 1024, 0, s>>>(pv, pi, G, n_target, draft_ids, n_draft, target_ids, accepted);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -113,6 +113,14 @@ def layer_tensors(wl: gen.Workload, layer: int = 0, device="cuda") -> dict:
     return t
 
 
+def head_tensor(wl: gen.Workload, device="cuda") -> torch.Tensor:
+    """The output head [V][H] (bf16 bits as int16), row-major, filled on the device with the
+    generator's stream (gen.head_weight draws the same bits on the host)."""
+    w = torch.empty((1, wl.vocab, wl.shape.hidden), dtype=torch.int16, device=device)
+    fill_bf16(w, wl.seed, 0, gen.KIND_HEAD, 0, 1)
+    return w.view(wl.vocab, wl.shape.hidden)
+
+
 def make_layer(wl: gen.Workload, layer: int = 0, device="cuda", tensors: dict | None = None):
     """A binding.MoeLayer for one generated layer: the row-major tensors are packed into the
     library's tiled layout (the packed copies are kept alive by the object)."""

@@ -7,7 +7,7 @@ GPU library consume exactly the arrays made here.
 The pages measure real prompts (MATH-500, HumanEval, ...) on a real Qwen3.6-35B-A3B target;
 neither is available, so seeded synthetic inputs with the workload shapes stand in for them:
 
-* expert weights: bf16 ~N(0, 0.02^2), or mxfp4 (E2M1 codes, one e8m0 scale per 32 values along
+* expert and output-head weights: bf16 ~N(0, 0.02^2), or (experts) mxfp4 (E2M1 codes, one e8m0 scale per 32 values along
   the reduction dimension) quantised from the same fp32 draws;
 * router weights: fp32 ~N(0, 0.02^2); block hidden states: fp32 ~N(0, 1);
 * target logits: fp32 ~N(0, 1); draft ids: uniform, or agreeing with a planted target id for a
@@ -31,6 +31,7 @@ from functools import lru_cache
 import numpy as np
 
 KIND_GATE, KIND_UP, KIND_DOWN = 0, 1, 2
+KIND_HEAD = 3  # the target's output head [V][H] (layer 0, expert 0)
 SHARED_EXPERT_ID = 0xFFFF
 WEIGHT_STD = 0.02
 PLANTED_LOGIT = 8.0  # exceeds every N(0,1) draw of a 151936-wide row with probability ~1e-10
@@ -181,6 +182,12 @@ def shared_tensors(wl: Workload, layer: int) -> dict | None:
             "gate": weight_bf16(wl.seed, layer, KIND_GATE, SHARED_EXPERT_ID, i, s.hidden),
             "up": weight_bf16(wl.seed, layer, KIND_UP, SHARED_EXPERT_ID, i, s.hidden),
             "down": weight_bf16(wl.seed, layer, KIND_DOWN, SHARED_EXPERT_ID, s.hidden, i)}
+
+
+def head_weight(wl: Workload) -> np.ndarray:
+    """bf16 bits [V][H] of the target's output head (the same counter-based stream as the
+    experts' weights, tensor kind KIND_HEAD)."""
+    return weight_bf16(wl.seed, 0, KIND_HEAD, 0, wl.vocab, wl.shape.hidden)
 
 
 # ----------------------------------------------------------------------------------------------

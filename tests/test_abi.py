@@ -136,6 +136,42 @@ def test_accept_prefix_validation(b):
     assert f(lg, 17, 151936, dr, 16, tg, tg, ws, need, None) == -6
 
 
+def test_lm_head_accept_validation(b):
+    f = b.lib.lm_head_accept
+    V, H = 151936, 2048
+    need = b.lib.lm_head_accept_workspace_size(16, H, V)
+    assert need > 0
+    assert b.lib.lm_head_accept_workspace_size(0, H, V) == 0
+    assert b.lib.lm_head_accept_workspace_size(17, H, V) == 0
+    assert b.lib.lm_head_accept_workspace_size(4, H, 0) == 0
+    h, w, dr, tg, ac, ws = (FAKE, FAKE + 0x10000000, FAKE + 0x60000000, FAKE + 0x61000000, FAKE + 0x62000000,
+                            FAKE + 0x63000000)
+    ok = (h, 16, H, w, V, 1, dr, 15, tg, ac, ws, need, None)
+
+    def call(**kw):
+        names = ("h", "n", "H", "w", "V", "layout", "dr", "nd", "tg", "ac", "ws", "wsb", "s")
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[k] for k in names])
+
+    # every call below fails a host-side check: none reaches a launch
+    assert call(h=None) == -1
+    assert call(dr=None) == -1
+    assert call(n=0) == -2
+    assert call(n=17) == -2
+    assert call(nd=17) == -2
+    assert call(H=2000) == -2       # not a multiple of 128
+    assert call(H=4096) == -2       # above the largest supported hidden size
+    assert call(V=0) == -2
+    assert call(V=1 << 21, H=2048) == -2  # 32-bit offsets into the head
+    assert call(layout=0) == -3
+    assert call(h=h + 4) == -4
+    assert call(wsb=need - 1) == -5
+    assert call(tg=h + 64) == -6
+    assert call(ac=tg) == -6
+    assert call(ws=w + 4096) == -6
+
+
 def test_pack_weights_validation(b):
     f = b.lib.moe_pack_weights
     src, dst, ss, ds = FAKE, FAKE + 0x10000000, FAKE + 0x20000000, FAKE + 0x30000000

@@ -1,0 +1,147 @@
+"""GPU parity of the output head with fused argmax and acceptance (lm_head_accept, through the C
+ABI) against the CPU oracle on the same seeded inputs. Run on an MI355X: ``pytest -m gpu``.
+
+Bars: accepted lengths bit-exact; target ids bit-exact except where the oracle's logits put
+another row within the GPU's error bound of the maximum. The bound for row v is
+GAMMA * sum_c |W[v, c] h[c]|: the hidden states enter MFMA as bf16 hi + lo pairs (relative
+residual below 2^-15) and products of bf16 values are exact in fp32, so the error is at most the
+residual plus fp32 accumulation over 2 H terms, (2^-15 + 2 H 2^-24) * sum |W h|, H <= 2048.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_decoding_moe_amd.workloads import gen
+
+pytestmark = pytest.mark.gpu
+
+GAMMA = 2.0 ** -15 + 2 * 2048 * 2.0 ** -24
+
+
+@pytest.fixture(scope="session")
+def B():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    torch.cuda.set_device(0)
+    from speculative_decoding_moe_amd import binding
+    return binding
+
+
+def _wl(H, V, n, seed=77):
+    return gen.Workload("head", gen.LayerShape(H, 16, 2, 128, 0), k=n, seed=seed, vocab=V, n_target=n)
+
+
+def run_head(B, h, w_tiled, V, draft, ws_fill=None):
+    n = h.shape[0]
+    hd = torch.from_numpy(np.ascontiguousarray(h, dtype=np.float32)).cuda()
+    dr = torch.from_numpy(np.asarray(draft, dtype=np.int32)).cuda() if len(draft) else None
+    tg = torch.full((max(n, 4),), -1, dtype=torch.int32, device="cuda")
+    ac = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(B.lm_head_accept_workspace_size(n, h.shape[1], V), dtype=torch.uint8, device="cuda")
+    if ws_fill is not None:
+        ws.fill_(ws_fill)
+    B.lm_head_accept(hd, w_tiled, V, dr, tg, ac, ws, n_draft=len(draft))
+    torch.cuda.synchronize()
+    return tg[:n].cpu().numpy().astype(np.int64), int(ac[0].item())
+
+
+def check_targets(h, w_bits, got):
+    """got equals the oracle's ids, or lies within the error bound of each row's maximum."""
+    L = oracle.head_logits(h, w_bits)
+    ref = oracle.argmax_first(L)
+    if np.array_equal(got, ref):
+        return ref
+    W = oracle.decode_bf16(w_bits)
+    for i in np.nonzero(got != ref)[0]:
+        g, t = int(got[i]), int(ref[i])
+        assert 0 <= g < w_bits.shape[0], (i, g)
+        bound = GAMMA * (np.abs(W[t] * h[i]).sum() + np.abs(W[g] * h[i]).sum())
+        assert L[i, t] - L[i, g] <= bound, f"row {i}: GPU {g} vs oracle {t}, gap {L[i, t] - L[i, g]:.3e} > {bound:.3e}"
+    return ref
+
+
+def _head(B, wl):
+    from speculative_decoding_moe_amd.workloads import device
+    w = device.head_tensor(wl)
+    return w, B.pack_head(w)
+
+
+@pytest.mark.parametrize("H,V,n", [
+    (256, 1000, 4),     # ragged vocab: 8 padding rows, odd tile count
+    (128, 17, 1),       # one window (seven idle waves), two tiles, the second holds one row
+    (1024, 33, 16),     # three tiles: an item whose second tile is past the head
+    (512, 70001, 9),    # many items per workgroup and a ragged tail
+])
+def test_head_parity_small(B, H, V, n):
+    wl = _wl(H, V, n)
+    wdev, wt = _head(B, wl)
+    w_bits = gen.head_weight(wl)
+    assert np.array_equal(wdev.cpu().numpy().view(np.uint16), w_bits)
+    h = gen.hidden_states(wl, rep=3, k=n)
+    ref = oracle.argmax_first(oracle.head_logits(h, w_bits))
+    L = min(n, 3)
+    draft = np.concatenate([ref[:L], (ref[L:n] + 1) % V]) if n > L else ref[:n].copy()
+    got, a = run_head(B, h, wt, V, draft)
+    check_targets(h, w_bits, got)
+    assert a == oracle.accept_length(draft, got)
+
+
+def test_head_full_size_and_acceptance(B):
+    """The benchmark's head: V 151936, H 2048, 16 positions; drafts agree for 5 positions."""
+    wl = _wl(2048, 151936, 16, seed=1002)
+    _, wt = _head(B, wl)
+    w_bits = gen.head_weight(wl)
+    h = gen.hidden_states(wl, rep=11, k=16)
+    ref = oracle.argmax_first(oracle.head_logits(h, w_bits))
+    draft = ref[:15].copy()
+    draft[5] = (draft[5] + 1) % wl.vocab
+    got, a = run_head(B, h, wt, wl.vocab, draft)
+    check_targets(h, w_bits, got)
+    assert a == oracle.accept_length(draft, got)
+    got2, a2 = run_head(B, h, wt, wl.vocab, draft[:0])
+    assert np.array_equal(got, got2) and a2 == 0
+
+
+def test_head_padding_rows_never_win(B):
+    """Positive weights and negative hidden states make every real logit negative, so the zero
+    rows that pad the head to a multiple of 16 would win if they were not masked."""
+    V, H, n = 1000, 256, 4
+    wl = _wl(H, V, n, seed=5)
+    w_bits = (gen.head_weight(wl) & np.uint16(0x7FFF)).astype(np.uint16)
+    wt = B.pack_head(torch.from_numpy(w_bits.view(np.int16)).cuda())
+    h = -np.abs(gen.hidden_states(wl, rep=1, k=n)) - 0.1
+    got, a = run_head(B, h, wt, V, [])
+    assert np.all(got < V)
+    check_targets(h, w_bits, got)
+    assert a == 0
+
+
+def test_head_exact_ties_pick_lowest_row(B):
+    """Rows planted along each position's dominant coordinate win; identical copies of them at
+    higher rows (in other items and workgroups) lose the tie."""
+    V, H, n = 40000, 512, 4
+    wl = _wl(H, V, n, seed=6)
+    w_bits = gen.head_weight(wl).copy()
+    rng = np.random.default_rng(8)
+    h = (0.01 * np.abs(rng.standard_normal((n, H)))).astype(np.float32)
+    planted, coords = [31, 20000, 7, 39999], [3, 100, 511, 7]
+    for i, (v, c) in enumerate(zip(planted, coords)):
+        h[i, c] += 10.0
+        w_bits[v] = gen.f32_to_bf16_bits(np.eye(H, dtype=np.float32)[c])
+    for src, dst in ((31, 33), (31, 32768), (20000, 20001), (7, 39998)):
+        w_bits[dst] = w_bits[src]
+    wt = B.pack_head(torch.from_numpy(w_bits.view(np.int16)).cuda())
+    got, a = run_head(B, h, wt, V, planted[:2] + [0])
+    assert list(got[:3]) == planted[:3]
+    check_targets(h, w_bits, got)
+    assert a == 2
+
+
+def test_head_deterministic_with_stale_workspace(B):
+    wl = _wl(512, 70001, 16, seed=9)
+    _, wt = _head(B, wl)
+    h = gen.hidden_states(wl, rep=2, k=16)
+    base = run_head(B, h, wt, wl.vocab, [1, 2, 3], ws_fill=0)
+    for fill in (0xFF, 0x7F, None):
+        g = run_head(B, h, wt, wl.vocab, [1, 2, 3], ws_fill=fill)
+        assert np.array_equal(g[0], base[0]) and g[1] == base[1]
