@@ -33,6 +33,7 @@
 // whole 32-value block and its single scale byte).
 #include <hip/hip_runtime.h>
 #include <algorithm>
+#include <atomic>
 #include <stdint.h>
 #include <string.h>
 
@@ -664,9 +665,10 @@ __device__ __forceinline__ void gu_load_xb(u32x4 (&xb)[WPW][4][2], const u32x4* 
 //    f = (b - n_sh) mod G, i.e. the workgroups that took a shared item start the routed deal last.
 //    With at least 6 rounds of items S = n / G - 2 and the rest is claimed; with fewer, every
 //    round is static.
-//  * Claimed part: items S G .. n-1, split into NGRP interleaved pools (item S G + p + NGRP c for
-//    pool p and counter value c). Workgroup b draws from pool (b / 8) mod NGRP, so every pool is
-//    served by workgroups on all XCDs: the XCDs of this part stream at noticeably different rates,
+//  * Claimed part: items S G .. n-1, split into P = min(NGRP, G / 8) interleaved pools (item
+//    S G + p + P c for pool p and counter value c). Workgroup b draws from pool (b / 8) mod P, so
+//    every pool has members (workgroup 8 p is one) and is served by workgroups on all XCDs
+//    (consecutive workgroups go to different XCDs): the XCDs of this part stream at noticeably different rates,
 //    which a fully static deal turns into a tail, and claiming lets the faster ones take more.
 //    Device-scope atomics on one address serialise (about 30 ns each), hence several pools, and
 //    only the last rounds are claimed.
@@ -676,9 +678,9 @@ __device__ __forceinline__ void gu_load_xb(u32x4 (&xb)[WPW][4][2], const u32x4* 
 constexpr int NGRP = 8;          // claim pools
 constexpr int CTR_STRIDE = 64;   // uint32 words between pool counters (256 B)
 struct Sched {
-  int G, S, f, pool;  // workgroups, static rounds, first item, pool
-  bool claims;        // whether the last rounds are claimed
-  uint32_t* ctr;      // this workgroup's pool counter
+  int G, S, f, pool, npool;  // workgroups, static rounds, first item, pool, pools
+  bool claims;               // whether the last rounds are claimed
+  uint32_t* ctr;             // this workgroup's pool counter
 };
 __device__ __forceinline__ Sched make_sched(int n, int G, int b, int n_sh, uint32_t* ctr_base) {
   Sched q;
@@ -686,7 +688,8 @@ __device__ __forceinline__ Sched make_sched(int n, int G, int b, int n_sh, uint3
   q.claims = n >= 6 * G;
   q.S = q.claims ? n / G - 2 : (n + G - 1) / G;
   q.f = (b - n_sh + G) % G;
-  q.pool = (b >> 3) % NGRP;
+  q.npool = min(NGRP, max(1, G >> 3));
+  q.pool = (b >> 3) % q.npool;
   q.ctr = ctr_base + q.pool * CTR_STRIDE;
   return q;
 }
@@ -694,7 +697,7 @@ __device__ __forceinline__ bool is_static(const Sched& q, int h) { return !q.cla
 // item of step h if it is static (h < S)
 __device__ __forceinline__ int static_item(const Sched& q, int h) { return h * q.G + q.f; }
 // item for counter value c of this workgroup's pool
-__device__ __forceinline__ int pool_item(const Sched& q, uint32_t c) { return q.S * q.G + q.pool + NGRP * (int)c; }
+__device__ __forceinline__ int pool_item(const Sched& q, uint32_t c) { return q.S * q.G + q.pool + q.npool * (int)c; }
 __device__ __forceinline__ uint32_t claim_raw(uint32_t* ctr) {
   return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1234,18 +1237,28 @@ __global__ void __launch_bounds__(1024) k_accept_final(const float* pv, const in
 // ------------------------------------------------------------------------------------------
 // The head is one [V x H] matrix read once for the whole block ("Speculating on a Strix Halo",
 // "What the pieces cost"; "Should we shrink the vocab?"). An item is 32 head rows (two 16-row
-// tiles of the tiled bf16 layout, 64 H bytes); workgroup b takes items b, b + G, ... with the
-// next item's loads in flight while the current one is multiplied (wave w owns H windows
-// w WPW .. w WPW + WPW - 1, the block's hidden states enter MFMA as bf16 hi + lo fragments that
-// every workgroup builds once). The logits never leave the chip: after the cross-wave sum each
-// thread owns one fixed (tile, row, position) slot and keeps the best (logit, row) seen in it;
-// the workgroup reduces its slots once at the end into one partial per position, and
-// k_accept_final reduces the partials and scans the accepted prefix.
+// tiles of the tiled bf16 layout, 64 H bytes); items are scheduled as in the gate/up kernel
+// (make_sched: static rounds, then the last rounds claimed from pools) with the next item's
+// loads in flight while the current one is multiplied. Wave w owns H windows w WPW ..
+// w WPW + WPW - 1; the block's hidden states enter MFMA as bf16 hi + lo fragments that every
+// workgroup builds once. The logits never leave the chip: after the cross-wave sum each thread
+// owns one fixed (tile, row, position) slot and keeps the best (logit, row) seen in it; the
+// workgroup reduces its slots once at the end into one partial per position, and k_accept_final
+// reduces the partials and scans the accepted prefix.
+//
+// No earlier kernel of the call can reset the claim pools, so each pool counter is 64-bit with
+// a per-call epoch above the count: its owner (workgroup 8 p of pool p) stores (epoch, 0) when
+// it starts, and a claim that returns another epoch means the pool is not set up yet and ends
+// that workgroup's claiming. The owner claims until its pool is exhausted, so no item is ever
+// left out whatever the workspace held; a stale counter can at worst repeat an item, which a
+// maximum absorbs.
 struct HeadSmem {
   float red[2][NW * 2 * 256];  // per-wave partial tiles, double-buffered across items
   float bv[NW][KMAX];
   int bi[NW][KMAX];
+  int claim[4];                // ring of scheduled item indices: item h sits in claim[h % 4]
 };
+constexpr int HEAD_CTR_STRIDE = 32;  // uint64 words between pool counters (256 B)
 
 // B fragments of this wave's H windows from the fp32 hidden states (bf16 K order). Every lane
 // loads unconditionally (clamped to position 0 / window 0) so that all loads are in flight at
@@ -1286,11 +1299,15 @@ __device__ __forceinline__ void head_xb(u32x4 (&xb)[WPW][4][2], const float* h, 
 
 // Cross-wave sum of one item's two tiles, then each thread's running best for its slot:
 // tile tl = tid / 256, row r = 4 (p / 64) + p % 4 and position c = (p / 4) % 16 of p = tid % 256.
-__device__ __forceinline__ void head_epilogue(float* red, const f32x4 (&acc)[GU_MX_RT][2], int item, int V,
-                                              int n, int wave, int lane, int tid, float& bv, int& bi) {
+// Reads the item index two steps ahead from the ring after the barrier.
+__device__ __forceinline__ void head_epilogue(HeadSmem& S, int buf, const f32x4 (&acc)[GU_MX_RT][2], int item,
+                                              int V, int n, int wave, int lane, int tid, float& bv, int& bi,
+                                              int ring, int* next) {
+  float* red = S.red[buf];
   *reinterpret_cast<f32x4*>(&red[(wave * 2 + 0) * 256 + lane * 4]) = acc[0][0];
   *reinterpret_cast<f32x4*>(&red[(wave * 2 + 1) * 256 + lane * 4]) = acc[0][1];
   __syncthreads();  // one barrier per item: the other buffer takes the next item's tiles
+  *next = __builtin_amdgcn_readfirstlane(S.claim[ring]);
   const int tl = tid >> 8, p = tid & 255;
   float v = 0.f;
 #pragma unroll
@@ -1300,9 +1317,15 @@ __device__ __forceinline__ void head_epilogue(float* red, const f32x4 (&acc)[GU_
   if (c < n && row < V) argmax_merge(bv, bi, v, row);
 }
 
+// item of a claimed head ticket, or n (past the end) when the ticket predates this call's epoch
+__device__ __forceinline__ int head_pool_item(const Sched& q, uint64_t v, uint32_t epoch, int n) {
+  const uint32_t c = (uint32_t)v;
+  return ((uint32_t)(v >> 32) == epoch && c < (uint32_t)n) ? min(pool_item(q, c), n) : n;
+}
+
 template <int WPW>
 __global__ void __launch_bounds__(NTH) k_head(const float* h, const uint8_t* w, int H, int V, int n,
-                                              int n_items, float* pv, int* pi) {
+                                              int n_items, float* pv, int* pi, uint64_t* ctr, uint32_t epoch) {
   __shared__ HeadSmem S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1315,34 +1338,51 @@ __global__ void __launch_bounds__(NTH) k_head(const float* h, const uint8_t* w, 
   // second-tile loads of an odd last item fall past the second resource's range and read zeros
   const rsrc_t r0 = buf_rsrc(w, ntile * tile), r1 = buf_rsrc(w + tile, (ntile - 1u) * tile);
   const uint32_t vb = (uint32_t)(256 * wsafe + lane) * 16u;
+  const Sched q = make_sched(n_items, G, b, 0, nullptr);
+  uint64_t* const pctr = ctr + q.pool * HEAD_CTR_STRIDE;
+  if (tid == 0 && q.claims && b == 8 * q.pool)  // the pool's owner sets it up for this call
+    __hip_atomic_store(pctr, (uint64_t)epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   u32x4 xb[WPW][4][2];
   head_xb<WPW>(xb, h, H, n, win0, active, lane);
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  int i0 = b;
+  const int i0 = static_item(q, 0);
   if (i0 < n_items) {
+    // step h: item h is in T[h % 2] with its loads in flight; the loads of item h + 1 are
+    // issued; thread 0 stores item h + 2 into the ring (static, or claimed two steps earlier)
+    // and claims item h + 4 when that one is claimed (stand-in item 0 past the end)
     GUItem<WPW> T0, T1;
-    gu_load_bf16<WPW>(T0, r0, r1, (uint32_t)i0 * 2u * tile, vb);
-    for (;;) {
-      const int i1 = i0 + G;  // item 0 stands in past the end (the same bytes for every workgroup)
-      gu_load_bf16<WPW>(T1, r0, r1, (uint32_t)(i1 < n_items ? i1 : 0) * 2u * tile, vb);
+    int c0 = i0, n1 = static_item(q, 1), n2;
+    uint64_t ca = 0, cb = 0;
+    gu_load_bf16<WPW>(T0, r0, r1, (uint32_t)c0 * 2u * tile, vb);
+    for (int st = 0;; st += 2) {
+      gu_load_bf16<WPW>(T1, r0, r1, (uint32_t)(n1 < n_items ? n1 : 0) * 2u * tile, vb);
+      if (tid == 0) {
+        S.claim[(st + 2) & 3] = is_static(q, st + 2) ? static_item(q, st + 2) : head_pool_item(q, ca, epoch, n_items);
+        if (!is_static(q, st + 4))
+          ca = __hip_atomic_fetch_add(pctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       __builtin_amdgcn_sched_barrier(0);
       {
         f32x4 acc[GU_MX_RT][2];
         gu_math_bf16<WPW>(acc, T0, xb);
-        head_epilogue(S.red[0], acc, i0, V, n, wave, lane, tid, bv, bi);
+        head_epilogue(S, 0, acc, c0, V, n, wave, lane, tid, bv, bi, (st + 2) & 3, &n2);
       }
-      if (i1 >= n_items) break;
-      const int i2 = i1 + G;
-      gu_load_bf16<WPW>(T0, r0, r1, (uint32_t)(i2 < n_items ? i2 : 0) * 2u * tile, vb);
+      if (n1 >= n_items) break;
+      gu_load_bf16<WPW>(T0, r0, r1, (uint32_t)(n2 < n_items ? n2 : 0) * 2u * tile, vb);
+      if (tid == 0) {
+        S.claim[(st + 3) & 3] = is_static(q, st + 3) ? static_item(q, st + 3) : head_pool_item(q, cb, epoch, n_items);
+        if (!is_static(q, st + 5))
+          cb = __hip_atomic_fetch_add(pctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       __builtin_amdgcn_sched_barrier(0);
       {
         f32x4 acc[GU_MX_RT][2];
         gu_math_bf16<WPW>(acc, T1, xb);
-        head_epilogue(S.red[1], acc, i1, V, n, wave, lane, tid, bv, bi);
+        head_epilogue(S, 1, acc, n1, V, n, wave, lane, tid, bv, bi, (st + 3) & 3, &n1);
       }
-      if (i2 >= n_items) break;
-      i0 = i2;
+      if (n2 >= n_items) break;
+      c0 = n2;
     }
   }
   // the four row slots of a position sit in lanes 4c .. 4c + 3 of each wave
@@ -1620,9 +1660,10 @@ int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const in
 
 constexpr int HEAD_GMAX = 1024;  // largest grid the head workspace provides for
 
+// workspace: partial maxima pv [n][G] fp32, their rows pi [n][G], then the claim pool counters
 size_t lm_head_accept_workspace_size(int32_t n_target, int32_t hidden, int32_t vocab) {
   if (n_target < 1 || n_target > KMAX || hidden < 1 || vocab < 1) return 0;
-  return 2 * align256((size_t)n_target * HEAD_GMAX * 4);
+  return 2 * align256((size_t)n_target * HEAD_GMAX * 4) + (size_t)NGRP * HEAD_CTR_STRIDE * 8;
 }
 
 int lm_head_accept(const float* h, int32_t n_target, int32_t hidden, const void* w_head, int32_t vocab,
@@ -1650,13 +1691,19 @@ int lm_head_accept(const float* h, int32_t n_target, int32_t hidden, const void*
     return MOE_ERR_ALIAS;
   const int G = std::min(num_cus(), HEAD_GMAX);
   const int n_items = (int)((v16 / 16 + 1) / 2);
+  const size_t part = align256((size_t)n_target * HEAD_GMAX * 4);
   float* pv = (float*)workspace;
-  int* pi = (int*)((uint8_t*)workspace + need / 2);
+  int* pi = (int*)((uint8_t*)workspace + part);
+  uint64_t* ctr = (uint64_t*)((uint8_t*)workspace + 2 * part);
+  // a fresh epoch per call tags this call's claim pools (zero is never used)
+  static std::atomic<uint32_t> calls{0};
+  uint32_t epoch = ++calls;
+  if (epoch == 0) epoch = ++calls;
   hipStream_t s = (hipStream_t)hip_stream;
   (void)hipGetLastError();
   const uint8_t* w = (const uint8_t*)w_head;
-  if (hidden <= NW * WIN) k_head<1><<<G, NTH, 0, s>>>(h, w, hidden, vocab, n_target, n_items, pv, pi);
-  else                    k_head<2><<<G, NTH, 0, s>>>(h, w, hidden, vocab, n_target, n_items, pv, pi);
+  if (hidden <= NW * WIN) k_head<1><<<G, NTH, 0, s>>>(h, w, hidden, vocab, n_target, n_items, pv, pi, ctr, epoch);
+  else                    k_head<2><<<G, NTH, 0, s>>>(h, w, hidden, vocab, n_target, n_items, pv, pi, ctr, epoch);
   k_accept_final<<<1, 1024, 0, s>>>(pv, pi, G, n_target, draft_ids, n_draft, target_ids, accepted);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
