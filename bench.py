@@ -198,6 +198,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer mxfp4 stack measurement")
+    ap.add_argument("--no-head", action="store_true", help="skip the output-head (lm_head_accept) measurement")
     ap.add_argument("--profile-run", action="store_true",
                     help="counter-collection run: warmup + steps without events, then a plain copy of "
                          "known size for calibrating HBM traffic counters; prints one JSON line")
@@ -446,6 +447,42 @@ def main():
                  "ms_per_layer": round(st_ms / sw.n_layers, 5)}
         print("[bench] stack done", file=sys.stderr, flush=True)
 
+    # ---- output head with fused argmax + greedy acceptance (16 positions, 15 drafts) ----
+    head = None
+    if not args.no_head:
+        print("[bench] filling the output head", file=sys.stderr, flush=True)
+        hw = gen.Workload("head", s, k=16, seed=wl.seed, vocab=V, n_target=16)
+        w_rm = device.head_tensor(hw, dev)
+        heads = [binding.pack_head(w_rm) for _ in range(2)]  # 2 x 622 MB: no call finds it in the LLC
+        del w_rm
+        hhs = [torch.from_numpy(gen.hidden_states(hw, rep=p, k=16)).to(dev) for p in range(4)]
+        hdr = drs[0][:15].contiguous()
+        htg = torch.empty((16,), dtype=torch.int32, device=dev)
+        hac = torch.empty((4,), dtype=torch.int32, device=dev)
+        hws = torch.empty(binding.lm_head_accept_workspace_size(16, s.hidden, V), dtype=torch.uint8, device=dev)
+        for r in range(5):
+            binding.lm_head_accept(hhs[r % 4], heads[r % 2], V, hdr, htg, hac, hws)
+        a_, b_ = ev.create(2)
+        torch.cuda.synchronize()
+        hreps = 40
+        ev.record(a_, stream)
+        for r in range(hreps):
+            binding.lm_head_accept(hhs[r % 4], heads[r % 2], V, hdr, htg, hac, hws)
+        ev.record(b_, stream)
+        torch.cuda.synchronize()
+        h_us = ev.ms(a_, b_) * 1e3 / hreps
+        ev.destroy([a_, b_])
+        hbytes = (V + 15) // 16 * 16 * s.hidden * 2 + 16 * s.hidden * 4
+        head = {"workload": f"output head bf16 {V} x {s.hidden}, 16 positions, fused argmax + greedy acceptance "
+                            "(lm_head_accept: head kernel + final reduction)",
+                "us_per_call": round(h_us, 2), "bytes_per_call": hbytes,
+                "GBps": round(hbytes / (h_us * 1e-6) / 1e9, 1),
+                "frac_of_peak": round(hbytes / (h_us * 1e-6) / 1e9 / 8000.0, 4),
+                "frac_of_achievable": (round(hbytes / (h_us * 1e-6) / 1e9 / roofline["achievable_read_GBps"], 4)
+                                       if roofline.get("achievable_read_GBps") else None)}
+        del heads
+        print("[bench] head done", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {args.cpu_samples} steps", file=sys.stderr, flush=True)
@@ -468,6 +505,7 @@ def main():
         "sweep_sigma": sweep_sigma,
         "sweep_fit": fit,
         "stack40_mxfp4": stack,
+        "lm_head": head,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
