@@ -31,6 +31,7 @@ METRIC = "MoE verify-block latency (ms) and achieved HBM GB/s vs k=1..16, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 GATEUP_SRC = os.path.join(ROOT, "speculative_decoding_moe_amd", "csrc", "moe_verify.hip")
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_gateup_verify_k16_bf16_traffic.txt")
+HEAD_PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_head_v151936_h2048_traffic.txt")
 
 
 class HipEvents:
@@ -84,14 +85,15 @@ def gateup_bytes(shape, U):
     return (U * 2 * H * I + 2 * H * Is) * 2
 
 
-def traffic_from_profile():
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter summary, or None when the
-    summary is missing or was taken on different kernel source."""
-    if not os.path.exists(PMC_SUMMARY):
+def traffic_from_profile(summary=None):
+    """HBM bytes per launch from a committed rocprofv3 counter summary (the gate/up one by default),
+    or None when the summary is missing or was taken on different kernel source."""
+    summary = PMC_SUMMARY if summary is None else summary
+    if not os.path.exists(summary):
         return None
     src_hash = hashlib.sha256(open(GATEUP_SRC, "rb").read()).hexdigest()
     fields = {}
-    for line in open(PMC_SUMMARY):
+    for line in open(summary):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
@@ -270,6 +272,19 @@ def main():
             step(i)
         torch.cuda.synchronize()
         Uall = nw_all[:max(nsteps, args.warmup), 0].cpu().numpy().astype(np.int64)
+        # the output head: 4 calls on 2 packed copies
+        hw = gen.Workload("head", s, k=16, seed=wl.seed, vocab=V, n_target=16)
+        w_rm = device.head_tensor(hw, dev)
+        heads = [binding.pack_head(w_rm) for _ in range(2)]
+        del w_rm
+        hh = torch.from_numpy(gen.hidden_states(hw, rep=0, k=16)).to(dev)
+        htg = torch.empty((16,), dtype=torch.int32, device=dev)
+        hac = torch.empty((4,), dtype=torch.int32, device=dev)
+        hws = torch.empty(binding.lm_head_accept_workspace_size(16, s.hidden, V), dtype=torch.uint8, device=dev)
+        for r in range(4):
+            binding.lm_head_accept(hh, heads[r % 2], V, drs[0][:15].contiguous(), htg, hac, hws)
+        torch.cuda.synchronize()
+        del heads
         copy_mib = 512
         src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -279,6 +294,7 @@ def main():
         print(json.dumps({"profile_run": True, "launches": int(len(Uall)),
                           "gateup_bytes_mean": float(np.mean([gateup_bytes(s, u) for u in Uall])),
                           "layer_bytes_mean": float(np.mean([layer_bytes(s, u, k) for u in Uall])),
+                          "head_bytes": (V + 15) // 16 * 16 * s.hidden * 2 + 16 * s.hidden * 4,
                           "copy_bytes": copy_mib << 20, "copy_launches": 3}), flush=True)
         return
 
@@ -479,7 +495,8 @@ def main():
                 "GBps": round(hbytes / (h_us * 1e-6) / 1e9, 1),
                 "frac_of_peak": round(hbytes / (h_us * 1e-6) / 1e9 / 8000.0, 4),
                 "frac_of_achievable": (round(hbytes / (h_us * 1e-6) / 1e9 / roofline["achievable_read_GBps"], 4)
-                                       if roofline.get("achievable_read_GBps") else None)}
+                                       if roofline.get("achievable_read_GBps") else None),
+                "traffic": traffic_from_profile(HEAD_PMC_SUMMARY)}
         del heads
         print("[bench] head done", file=sys.stderr, flush=True)
 

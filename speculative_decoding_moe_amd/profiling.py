@@ -100,8 +100,12 @@ def traffic(fetch_dir, write_dir, run_json, cmd_fetch, cmd_write, kernel, source
             f"fetch_scale_bytes_per_unit: {fscale:.4f}", f"write_scale_bytes_per_unit: {wscale:.4f}",
             f"fetch_bytes_per_launch: {fb:.0f}", f"write_bytes_per_launch: {wb:.0f}",
             f"traffic_bytes_per_launch: {fb + wb:.0f}"]
+    alg = None
     if "gateup_bytes_mean" in run and "gateup" in kernel:
         alg = float(run["gateup_bytes_mean"])
+    elif "head_bytes" in run and "head" in kernel:
+        alg = float(run["head_bytes"])
+    if alg:
         out += [f"algorithmic_bytes_per_launch: {alg:.0f}", f"traffic_over_algorithmic: {(fb + wb) / alg:.4f}"]
     return "\n".join(out)
 
