@@ -242,6 +242,58 @@ def accept_length(draft: np.ndarray, target_ids: np.ndarray) -> int:
     return a
 
 
+def softmax_temp(logits_row: np.ndarray, temperature: float) -> np.ndarray:
+    """p = softmax(l / T) in float64 (the maximum subtracted first; -inf logits give 0)."""
+    z = np.asarray(logits_row, dtype=np.float64) / float(temperature)
+    z = z - z.max()
+    e = np.exp(z)
+    return e / e.sum()
+
+
+def sample_inverse_cdf(weights: np.ndarray, u: float) -> int:
+    """The smallest index x whose running sum of the non-negative weights exceeds u times their
+    total (u in [0, 1)); an index of zero weight is never returned."""
+    c = np.cumsum(np.asarray(weights, dtype=np.float64))
+    return int(np.searchsorted(c, float(u) * c[-1], side="right"))
+
+
+def speculative_accept(target_logits: np.ndarray, draft_logits: np.ndarray, draft: np.ndarray,
+                       temperature: float, u_accept: np.ndarray, u_sample: np.ndarray):
+    """Lossless acceptance of a draft block at temperature T: the committed tokens are
+    distributed exactly as the target's own samples ([SH1] 'Speculative decoding', which relies
+    on its reference 2, Leviathan et al., for the rule restated here).
+
+    With p_i = softmax(target_logits[i] / T) and q_i = softmax(draft_logits[i] / T), draft d_i is
+    kept while u_accept[i] * q_i(d_i) < p_i(d_i) (probability min(1, p_i(d_i) / q_i(d_i))). At the
+    first rejection a, the target's own token is drawn from the residual max(0, p_a - q_a)
+    (renormalised) with u_sample[a]; if every draft is kept, from p_n (n = len(draft)) with
+    u_sample[n] when that row exists. Returns (a, token), token -1 when there is no row to draw
+    from. A residual with no mass (p_a = q_a, reachable only through rounding or a draft that q_a
+    gives probability zero) is read as its limit, p_a itself."""
+    n = len(draft)
+    for i in range(n):
+        p = softmax_temp(target_logits[i], temperature)
+        q = softmax_temp(draft_logits[i], temperature)
+        d = int(draft[i])
+        if not (float(u_accept[i]) * q[d] < p[d]):
+            r = np.maximum(p - q, 0.0)
+            return i, sample_inverse_cdf(r if r.sum() > 0 else p, u_sample[i])
+    if len(target_logits) > n:
+        return n, sample_inverse_cdf(softmax_temp(target_logits[n], temperature), u_sample[n])
+    return n, -1
+
+
+def accept_histogram(accepted: np.ndarray, n_draft: int):
+    """Cycle statistics of accepted lengths ([SH2] 'Why drafter performance doesn't really
+    matter' counts cycles by accepted length; [MI] plots the per-position marginal): hist[j] = the
+    number of cycles that accepted exactly j drafts (0 <= j <= n_draft), and survival[i] = the
+    number that accepted at least i + 1 (the marginal P(accept >= i + 1) times the cycle count)."""
+    a = np.asarray(accepted, dtype=np.int64)
+    hist = np.array([int(np.sum(a == j)) for j in range(n_draft + 1)], dtype=np.int64)
+    survival = np.array([int(np.sum(a >= i + 1)) for i in range(n_draft)], dtype=np.int64)
+    return hist, survival
+
+
 def committed_tokens(draft: np.ndarray, target_ids: np.ndarray) -> list:
     """The accepted draft prefix plus the target's own token after it, when there is one:
     tau = a + 1 tokens per cycle ([SH1] 'Speculative decoding')."""

@@ -417,6 +417,129 @@ def test_head_accept_planted_winners_ties_and_prefix():
     assert oracle.head_accept(h, w, np.array([], dtype=np.int64))[1] == 0
 
 
+# ---------------------------------------------------------------- stochastic acceptance
+def test_softmax_temp_closed_forms_and_library():
+    from scipy.special import softmax
+    rng = np.random.default_rng(41)
+    l = rng.standard_normal(50)
+    for T in (0.3, 1.0, 2.5):
+        np.testing.assert_allclose(oracle.softmax_temp(l, T), softmax(l / T), rtol=1e-13, atol=0)
+    np.testing.assert_allclose(oracle.softmax_temp(np.full(8, 3.0), 0.7), np.full(8, 1 / 8), rtol=1e-15)
+    p = oracle.softmax_temp(np.array([0.0, -np.inf, 1.0]), 1.0)
+    assert p[1] == 0.0 and abs(p[2] / p[0] - math.e) < 1e-12
+
+
+def test_sample_inverse_cdf_brute_force():
+    rng = np.random.default_rng(42)
+    for _ in range(300):
+        w = rng.random(7) * (rng.random(7) < 0.7)
+        if w.sum() == 0:
+            continue
+        u = float(rng.random())
+        run, x = 0.0, None
+        for i, wi in enumerate(w):
+            run += wi
+            if run > u * w.sum():
+                x = i
+                break
+        got = oracle.sample_inverse_cdf(w, u)
+        assert got == x and w[got] > 0
+    # exact boundaries: u = 0 skips leading zero weights; a running sum equal to u * total is not
+    # yet past it
+    assert oracle.sample_inverse_cdf(np.array([0.0, 0.0, 2.0, 1.0]), 0.0) == 2
+    assert oracle.sample_inverse_cdf(np.array([1.0, 1.0, 2.0]), 0.5) == 2
+    assert oracle.sample_inverse_cdf(np.array([1.0, 0.0, 3.0]), 0.25) == 2
+
+
+def _boundary(f, lo=0.0, hi=1.0, iters=60):
+    """Smallest u in [lo, hi] with f(u) true, for f monotone (false then true); hi if never."""
+    if not f(hi):
+        return hi
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        lo, hi = (lo, mid) if f(mid) else (mid, hi)
+    return hi
+
+
+def test_speculative_accept_is_lossless():
+    """The first committed token is distributed exactly as the target's p_0, and when every draft
+    is kept the bonus token as p_n: the acceptance region and the sampled token's regions are
+    measured by bisection on the oracle's own decisions, then combined over d_0 ~ q_0."""
+    rng = np.random.default_rng(43)
+    V, n, T = 6, 2, 0.8
+    tl = rng.standard_normal((n + 1, V)) * 1.5
+    dl = tl[:n] + rng.standard_normal((n, V))          # a drafter close to the target
+    p0 = oracle.softmax_temp(tl[0], T)
+    q0 = oracle.softmax_temp(dl[0], T)
+
+    def run(d0, ua0, us0, us_bonus=0.5):
+        return oracle.speculative_accept(tl, dl, np.array([d0, 0]), T, np.array([ua0, 0.0]),
+                                         np.array([us0, 0.5, us_bonus]))
+
+    dist = np.zeros(V)
+    for d in range(V):
+        alpha = _boundary(lambda u: run(d, u, 0.5)[0] == 0)   # accept while u < alpha
+        dist[d] += q0[d] * alpha
+        if alpha < 1.0:
+            edges = [0.0] + [_boundary(lambda u, x=x: run(d, 1.0 - 1e-12, u)[1] >= x) for x in range(1, V)] + [1.0]
+            dist += q0[d] * (1.0 - alpha) * np.diff(edges)
+    np.testing.assert_allclose(dist, p0, rtol=0, atol=1e-12)
+    pn = oracle.softmax_temp(tl[n], T)
+    same = oracle.speculative_accept(tl, tl[:n], np.array([0, 1]), T, np.zeros(n), np.zeros(n + 1))
+    assert same[0] == n
+    edges = [0.0] + [_boundary(lambda u, x=x: oracle.speculative_accept(tl, tl[:n], np.array([0, 1]), T, np.zeros(n),
+                                                                      np.array([0.0, 0.0, u]))[1] >= x)
+                     for x in range(1, V)] + [1.0]
+    np.testing.assert_allclose(np.diff(edges), pn, rtol=0, atol=1e-12)
+
+
+def test_speculative_accept_special_cases():
+    rng = np.random.default_rng(44)
+    V, n = 30, 4
+    tl = rng.standard_normal((n + 1, V))
+    # a drafter equal to the target keeps every draft for any u < 1
+    a, tok = oracle.speculative_accept(tl, tl[:n], rng.integers(0, V, n), 1.0, np.full(n, 0.999999), np.zeros(n + 1))
+    assert a == n and tok == oracle.sample_inverse_cdf(oracle.softmax_temp(tl[n], 1.0), 0.0)
+    # a draft the target gives probability zero is always rejected; the residual is then p itself
+    # when the drafter is one-hot on it
+    tz = tl.copy()
+    tz[1, 7] = -np.inf
+    dl = np.full((n, V), -np.inf)
+    dl[:, 7] = 0.0
+    dl[0] = tl[0]
+    draft = np.array([3, 7, 7, 7])
+    for u in (0.0, 0.5, 0.9):
+        a, tok = oracle.speculative_accept(tz, dl, draft, 1.0, np.array([0.0, u, u, u]), np.full(n + 1, u))
+        assert a == 1 and tok == oracle.sample_inverse_cdf(oracle.softmax_temp(tz[1], 1.0), u) and tok != 7
+    # the low-temperature limit is greedy acceptance of the drafter's own argmax, and the token at
+    # the first disagreement is the target's argmax
+    sep = np.argsort(rng.random((n + 1, V)), axis=1).astype(np.float64)   # distinct integer logits
+    tgt = oracle.argmax_first(sep)
+    dsep = sep[:n].copy()
+    dsep[2, (tgt[2] + 1) % V] = V + 5.0                                    # the drafter disagrees at 2
+    draft = oracle.argmax_first(dsep)
+    a, tok = oracle.speculative_accept(sep, dsep, draft, 1e-3, np.full(n, 0.5), np.full(n + 1, 0.5))
+    assert a == oracle.accept_length(draft, tgt) == 2 and tok == tgt[2]
+    # a rejection whose residual has no mass draws from the target itself
+    a, tok = oracle.speculative_accept(sep, sep[:n] * 0.5, draft, 1e-3, np.full(n, 0.5), np.full(n + 1, 0.5))
+    assert a == 2 and tok == tgt[2]
+    # no bonus row: every draft kept gives no token
+    assert oracle.speculative_accept(tl[:n], tl[:n], np.zeros(n, dtype=np.int64), 1.0, np.zeros(n),
+                                     np.zeros(n)) == (n, -1)
+
+
+def test_accept_histogram_brute_force():
+    rng = np.random.default_rng(45)
+    a = rng.integers(0, 17, size=500)
+    hist, surv = oracle.accept_histogram(a, 16)
+    assert hist.sum() == 500 and len(hist) == 17 and len(surv) == 16
+    for j in range(17):
+        assert hist[j] == sum(1 for v in a if v == j)
+    for i in range(16):
+        assert surv[i] == sum(1 for v in a if v >= i + 1)
+    assert surv[0] == 500 - hist[0]
+
+
 def _read_golden(name):
     rows = []
     with open(os.path.join(GOLDEN, name)) as f:
