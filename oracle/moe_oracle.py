@@ -269,13 +269,14 @@ def speculative_accept(target_logits: np.ndarray, draft_logits: np.ndarray, draf
     (renormalised) with u_sample[a]; if every draft is kept, from p_n (n = len(draft)) with
     u_sample[n] when that row exists. Returns (a, token), token -1 when there is no row to draw
     from. A residual with no mass (p_a = q_a, reachable only through rounding or a draft that q_a
-    gives probability zero) is read as its limit, p_a itself."""
+    gives probability zero) is read as its limit, p_a itself. A draft id outside [0, V) has
+    target probability zero and is rejected."""
     n = len(draft)
     for i in range(n):
         p = softmax_temp(target_logits[i], temperature)
         q = softmax_temp(draft_logits[i], temperature)
         d = int(draft[i])
-        if not (float(u_accept[i]) * q[d] < p[d]):
+        if not (0 <= d < len(p)) or not (float(u_accept[i]) * q[d] < p[d]):
             r = np.maximum(p - q, 0.0)
             return i, sample_inverse_cdf(r if r.sum() > 0 else p, u_sample[i])
     if len(target_logits) > n:

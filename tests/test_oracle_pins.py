@@ -523,6 +523,8 @@ def test_speculative_accept_special_cases():
     # a rejection whose residual has no mass draws from the target itself
     a, tok = oracle.speculative_accept(sep, sep[:n] * 0.5, draft, 1e-3, np.full(n, 0.5), np.full(n + 1, 0.5))
     assert a == 2 and tok == tgt[2]
+    # an id outside the vocabulary is rejected
+    assert oracle.speculative_accept(tl, tl[:n], np.array([0, V, 1, 2]), 1.0, np.zeros(n), np.zeros(n + 1))[0] == 1
     # no bonus row: every draft kept gives no token
     assert oracle.speculative_accept(tl[:n], tl[:n], np.zeros(n, dtype=np.int64), 1.0, np.zeros(n),
                                      np.zeros(n)) == (n, -1)
