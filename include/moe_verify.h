@@ -204,6 +204,47 @@ int lm_head_accept(const float* h, int32_t n_target, int32_t hidden, const void*
                    int32_t layout, const int32_t* draft_ids, int32_t n_draft, int32_t* target_ids,
                    int32_t* accepted, void* workspace, size_t ws_bytes, void* hip_stream);
 
+/* Bytes of device workspace accept_sample needs (0 if the sizes are invalid). Host only. */
+size_t accept_sample_workspace_size(int32_t n_target, int32_t n_draft, int32_t vocab);
+
+/* Lossless acceptance at temperature T: the committed tokens are distributed exactly as the
+ * target's own samples ("Speculating on a Strix Halo", section "Speculative decoding", which
+ * cites Leviathan et al. for the rule). With p_i = softmax(target_logits[i] / T) and
+ * q_i = softmax(draft_logits[i] / T), draft i is kept while u_accept[i] * q_i(d_i) < p_i(d_i);
+ * at the first rejection a, the token is drawn from the renormalised residual max(0, p_a - q_a)
+ * (from p_a if the residual has no mass) as the smallest index whose running weight exceeds
+ * u_sample[a] times the total; if every draft is kept, from p_{n_draft} with u_sample[n_draft]
+ * when n_target > n_draft, else no token.
+ *   target_logits fp32 [n_target][vocab], draft_logits fp32 [n_draft][vocab] (the drafter's
+ *                 logits at each draft position), draft_ids int32 [n_draft] (ids outside
+ *                 [0, vocab) are rejected)
+ *   u_accept fp32 [n_draft], u_sample fp32 [n_target]: uniforms in [0, 1) drawn by the caller
+ *   accepted int32 [1] out: a; token int32 [1] out: the target's own token, or -1 when every
+ *                 draft is kept and n_target == n_draft
+ * draft_logits, draft_ids and u_accept may be NULL when n_draft == 0. Limits: 1 <= n_target <=
+ * 64, 0 <= n_draft <= n_target, 1 <= vocab <= 2^24, 0 < temperature < inf. Logit arrays and the
+ * workspace 16-byte aligned, the rest 4-byte aligned; outputs may not overlap inputs, each other
+ * or the workspace. Logits must be finite except -inf entries (probability zero); u outside
+ * [0, 1) and non-finite logits give unspecified results (the token is still an index of positive
+ * weight when any exists). Computed in fp32 with base-2 exponents; decisions within fp32
+ * rounding of a boundary may differ from exact arithmetic. Returns MOE_OK or an MOE_ERR_* code. */
+int accept_sample(const float* target_logits, int32_t n_target, int32_t vocab, const float* draft_logits,
+                  const int32_t* draft_ids, int32_t n_draft, float temperature, const float* u_accept,
+                  const float* u_sample, int32_t* accepted, int32_t* token, void* workspace, size_t ws_bytes,
+                  void* hip_stream);
+
+/* Acceptance statistics over many cycles: the histogram of accepted lengths ("Speculating on a
+ * Strix Halo (part 2)", section "Why drafter performance doesn't really matter", counts cycles
+ * by accepted length) and the per-position marginal as counts (the DFlash-on-MI355X article
+ * plots P(accept >= i + 1) per position).
+ *   accepted int32 [n_cycles]; hist int64 [n_draft + 1] out: cycles that accepted exactly j;
+ *   survival int64 [n_draft] out (may be NULL when n_draft == 0): cycles that accepted at least
+ *   i + 1. Values outside [0, n_draft] are not counted. 0 <= n_draft <= 64, n_cycles >= 0;
+ *   accepted 4-byte and the outputs 8-byte aligned, no overlaps. Returns MOE_OK or an
+ *   MOE_ERR_* code. */
+int accept_histogram(const int32_t* accepted, int32_t n_cycles, int32_t n_draft, int64_t* hist, int64_t* survival,
+                     void* hip_stream);
+
 /* Static description of a status code. Host only. */
 const char* moe_status_string(int status);
 

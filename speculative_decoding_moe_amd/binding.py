@@ -21,7 +21,8 @@ MOE_PRE_RMSNORM, MOE_RESIDUAL = 1, 2
 
 EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "moe_verify_block_timed",
            "moe_pack_weights", "accept_prefix_workspace_size", "accept_prefix",
-           "lm_head_accept_workspace_size", "lm_head_accept", "moe_status_string")
+           "lm_head_accept_workspace_size", "lm_head_accept", "accept_sample_workspace_size",
+           "accept_sample", "accept_histogram", "moe_status_string")
 
 
 class MoeLayerStruct(ctypes.Structure):
@@ -64,6 +65,12 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lm_head_accept_workspace_size.restype = sz
     lib.lm_head_accept.argtypes = [vp, i32, i32, vp, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     lib.lm_head_accept.restype = ctypes.c_int
+    lib.accept_sample_workspace_size.argtypes = [i32, i32, i32]
+    lib.accept_sample_workspace_size.restype = sz
+    lib.accept_sample.argtypes = [vp, i32, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+    lib.accept_sample.restype = ctypes.c_int
+    lib.accept_histogram.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.accept_histogram.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     return lib
@@ -219,4 +226,28 @@ def lm_head_accept(h, w_head_tiled, vocab, draft_ids, target_ids, accepted, work
     st = lib.lm_head_accept(_ptr(h), n_target, hidden, _ptr(w_head_tiled), int(vocab), MOE_LAYOUT_TILED,
                             _ptr(draft_ids), nd, _ptr(target_ids), _ptr(accepted), _ptr(workspace), ws_bytes,
                             _stream_handle() if stream is None else stream)
+    _check(st)
+
+
+def accept_sample_workspace_size(n_target: int, n_draft: int, vocab: int) -> int:
+    return int(lib.accept_sample_workspace_size(int(n_target), int(n_draft), int(vocab)))
+
+
+def accept_sample(target_logits, draft_logits, draft_ids, temperature, u_accept, u_sample, accepted, token,
+                  workspace, stream=None) -> None:
+    """Lossless acceptance at temperature T (library call): accepted[0] = a, token[0] = the
+    target's own token (or -1). draft_logits / draft_ids / u_accept may be None with no drafts."""
+    n_target, vocab = int(target_logits.shape[0]), int(target_logits.shape[1])
+    n_draft = 0 if draft_ids is None else int(draft_ids.shape[0])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.accept_sample(_ptr(target_logits), n_target, vocab, _ptr(draft_logits), _ptr(draft_ids), n_draft,
+                           float(temperature), _ptr(u_accept), _ptr(u_sample), _ptr(accepted), _ptr(token),
+                           _ptr(workspace), ws_bytes, _stream_handle() if stream is None else stream)
+    _check(st)
+
+
+def accept_histogram(accepted, n_draft, hist, survival, stream=None) -> None:
+    """Histogram of accepted lengths and the per-position survival counts (library call)."""
+    st = lib.accept_histogram(_ptr(accepted), int(accepted.numel()), int(n_draft), _ptr(hist), _ptr(survival),
+                              _stream_handle() if stream is None else stream)
     _check(st)

@@ -1408,6 +1408,305 @@ __global__ void __launch_bounds__(NTH) k_head(const float* h, const uint8_t* w, 
 }
 
 // ------------------------------------------------------------------------------------------
+// accept_sample: lossless acceptance at temperature T, and acceptance statistics
+// ------------------------------------------------------------------------------------------
+// The committed tokens are distributed exactly as the target's own samples at any temperature
+// ("Speculating on a Strix Halo", "Speculative decoding", whose reference 2 gives the rule):
+// with p_i = softmax(target_i / T) and q_i = softmax(draft_i / T), draft d_i is kept while
+// u_accept[i] q_i(d_i) < p_i(d_i); at the first rejection a the token is drawn from the
+// renormalised residual max(0, p_a - q_a) (p_a itself if that has no mass); when every draft is
+// kept, from p_n. Logits are scaled to base-2 exponents z = l log2(e) / T once.
+//   k_lse_partial     (chunk, row): chunk maximum and sum of 2^(z - max), target and draft rows
+//   k_sample_partial  chunk c: every workgroup merges the row partials and takes the accept
+//                     decisions (identical data and code, so identical results); then the weights
+//                     of its chunk of the row to sample are summed with the fixed-order block scan
+//   k_sample_final    one workgroup: the chunk whose running total first exceeds u W, then the
+//                     element inside it, with the same scan, so the chunk totals agree bit for bit
+constexpr int SAMPLE_NTH = 1024;  // threads of the sampling workgroups: 8 values each per chunk
+static_assert(SAMPLE_NTH * 8 == AM_CHUNK, "one chunk per sampling workgroup");
+enum { SAMPLE_NONE = 0, SAMPLE_RESIDUAL = 1, SAMPLE_TARGET = 2 };
+struct SamplePlan {
+  int a, mode, row, pad;
+  float mt, st, md, sd, u;
+};
+
+// (max, sum) pairs of 2^(z - max) partial sums, combined; an empty side (max -inf) adds nothing
+__device__ __forceinline__ void lse_merge(float& m, float& s, float mo, float so) {
+  const float mm = fmaxf(m, mo);
+  if (mm == -INFINITY) return;
+  s = (m == -INFINITY ? 0.f : s * __builtin_amdgcn_exp2f(m - mm)) +
+      (mo == -INFINITY ? 0.f : so * __builtin_amdgcn_exp2f(mo - mm));
+  m = mm;
+}
+__device__ __forceinline__ void wave_lse(float& m, float& s) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float mo = __shfl_xor(m, off), so = __shfl_xor(s, off);
+    lse_merge(m, s, mo, so);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_lse_partial(const float* tl, const float* dl, int n_t, int V, int nchunks,
+                                                     float zscale, float2* ms) {
+  __shared__ float sm[4], ss[4];
+  const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  const float* r = row < n_t ? tl + (size_t)row * V : dl + (size_t)(row - n_t) * V;
+  const int base = chunk * AM_CHUNK, end = min(base + AM_CHUNK, V);
+  constexpr int PER = AM_CHUNK / (4 * 256);
+  float z[PER * 4];
+  if ((V & 3) == 0) {
+    f32x4 v[PER];
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int i = base + 4 * (tid + 256 * m);
+      v[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + (i < end ? i : base)));
+    }
+#pragma unroll
+    for (int m = 0; m < PER; ++m) {
+      const int i = base + 4 * (tid + 256 * m);
+      const float e[4] = {v[m].x, v[m].y, v[m].z, v[m].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) z[4 * m + j] = (i + j < end) ? e[j] * zscale : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < PER; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + 4 * (tid + 256 * m) + j;
+        z[4 * m + j] = i < end ? r[i] * zscale : -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PER * 4; ++i) mx = fmaxf(mx, z[i]);
+  float sum = 0.f;
+  if (mx != -INFINITY) {
+#pragma unroll
+    for (int i = 0; i < PER * 4; ++i) sum += __builtin_amdgcn_exp2f(z[i] - mx);
+  }
+  wave_lse(mx, sum);
+  if ((tid & 63) == 0) { sm[tid >> 6] = mx; ss[tid >> 6] = sum; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) lse_merge(mx, sum, sm[w], ss[w]);
+    ms[(size_t)row * nchunks + chunk] = make_float2(mx, sum);
+  }
+}
+
+// Inclusive prefix sums of one value per thread over the 1024 threads, in a fixed order (wave
+// scans, then the wave totals); every caller sees identical bits for identical inputs.
+__device__ __forceinline__ float block_scan_1024(float v, float* lds16, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float o = __shfl_up(v, off);
+    if (lane >= off) v += o;
+  }
+  if (lane == 63) lds16[wave] = v;
+  __syncthreads();
+  float before = 0.f;
+  for (int w = 0; w < wave; ++w) before += lds16[w];
+  __syncthreads();
+  return before + v;
+}
+
+struct SampleSmem {
+  float m[128], s[128];  // merged (max, sum) per row: target rows, then draft rows
+  float scan[16];
+  SamplePlan plan;
+  int best;
+};
+
+// The weights of chunk c of the plan's row, thread t holding elements 8t .. 8t+7 of the chunk:
+// residual max(0, p - q) (w) and target p (p); elements past V weigh zero.
+__device__ __forceinline__ void sample_weights(const float* tl, const float* dl, int V, float zscale,
+                                               const SamplePlan& P, int c, int tid, float (&w)[8], float (&p)[8]) {
+  const int x0 = c * AM_CHUNK + 8 * tid;
+  const bool res = P.mode == SAMPLE_RESIDUAL;
+  const float* rt = tl + (size_t)P.row * V;
+  const float* rd = res ? dl + (size_t)P.row * V : rt;  // a target row stands in when unused
+  float lt[8], ld[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int x = x0 + j < V ? x0 + j : 0;
+    lt[j] = rt[x];
+    ld[j] = rd[x];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool in = x0 + j < V;
+    const float pt = in ? __builtin_amdgcn_exp2f(lt[j] * zscale - P.mt) / P.st : 0.f;
+    const float pd = (in && res) ? __builtin_amdgcn_exp2f(ld[j] * zscale - P.md) / P.sd : 0.f;
+    p[j] = pt;
+    w[j] = fmaxf(pt - pd, 0.f);
+  }
+}
+
+// Merge the row partials, take the accept decisions, and fill the plan (every workgroup alike).
+__device__ void sample_plan(const float* tl, const float* dl, int n_t, int V, int nchunks, float zscale,
+                            const int32_t* draft, int n_d, const float* u_acc, const float* u_smp,
+                            const float2* ms, SampleSmem& S, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int R = n_t + n_d;
+  for (int row = wave; row < R; row += SAMPLE_NTH / 64) {
+    float m = -INFINITY, s = 0.f;
+    for (int c = lane; c < nchunks; c += 64) {
+      const float2 v = ms[(size_t)row * nchunks + c];
+      lse_merge(m, s, v.x, v.y);
+    }
+    wave_lse(m, s);
+    if (lane == 0) { S.m[row] = m; S.s[row] = s; }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    bool miss = false;
+    if (lane < n_d) {
+      const int d = draft[lane];
+      const bool valid = d >= 0 && d < V;
+      const int dd = valid ? d : 0;
+      const float p = __builtin_amdgcn_exp2f(tl[(size_t)lane * V + dd] * zscale - S.m[lane]) / S.s[lane];
+      const float q = __builtin_amdgcn_exp2f(dl[(size_t)lane * V + dd] * zscale - S.m[n_t + lane]) / S.s[n_t + lane];
+      miss = !(valid && u_acc[lane] * q < p);
+    }
+    const unsigned long long mm = __ballot(miss);
+    if (lane == 0) {
+      SamplePlan P;
+      P.a = mm ? __builtin_ctzll(mm) : n_d;
+      P.pad = 0;
+      if (P.a < n_d) { P.mode = SAMPLE_RESIDUAL; P.row = P.a; }
+      else if (n_d < n_t) { P.mode = SAMPLE_TARGET; P.row = n_d; }
+      else { P.mode = SAMPLE_NONE; P.row = 0; }
+      P.mt = S.m[P.row]; P.st = S.s[P.row];
+      P.md = P.mode == SAMPLE_RESIDUAL ? S.m[n_t + P.row] : 0.f;
+      P.sd = P.mode == SAMPLE_RESIDUAL ? S.s[n_t + P.row] : 1.f;
+      P.u = P.mode == SAMPLE_NONE ? 0.f : u_smp[P.row];
+      S.plan = P;
+    }
+  }
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(SAMPLE_NTH) k_sample_partial(const float* tl, const float* dl, int n_t, int V,
+                                                               int nchunks, float zscale, const int32_t* draft,
+                                                               int n_d, const float* u_acc, const float* u_smp,
+                                                               const float2* ms, float2* csum, SamplePlan* plan,
+                                                               int32_t* accepted, int32_t* token) {
+  __shared__ SampleSmem S;
+  const int tid = threadIdx.x, c = blockIdx.x;
+  sample_plan(tl, dl, n_t, V, nchunks, zscale, draft, n_d, u_acc, u_smp, ms, S, tid);
+  const SamplePlan P = S.plan;
+  if (c == 0 && tid == 0) {
+    *plan = P;
+    accepted[0] = P.a;
+    if (P.mode == SAMPLE_NONE) token[0] = -1;
+  }
+  if (P.mode == SAMPLE_NONE) return;  // uniform across the grid
+  float w[8], p[8];
+  sample_weights(tl, dl, V, zscale, P, c, tid, w, p);
+  float tw = 0.f, tp = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { tw += w[j]; tp += p[j]; }
+  const float sw = block_scan_1024(tw, S.scan, tid);
+  const float sp = block_scan_1024(tp, S.scan, tid);
+  if (tid == SAMPLE_NTH - 1) csum[c] = make_float2(sw, sp);
+}
+
+__global__ void __launch_bounds__(SAMPLE_NTH) k_sample_final(const float* tl, const float* dl, int V, int nchunks,
+                                                             float zscale, const float2* csum, const SamplePlan* plan,
+                                                             int32_t* token) {
+  __shared__ SampleSmem S;
+  __shared__ float2 cs[2048];
+  __shared__ int sel_chunk;
+  __shared__ float sel_base;
+  __shared__ int use_res, lastw;
+  const int tid = threadIdx.x;
+  const SamplePlan P = *plan;
+  if (P.mode == SAMPLE_NONE) return;
+  for (int c = tid; c < nchunks; c += SAMPLE_NTH) cs[c] = csum[c];
+  __syncthreads();
+  if (tid == 0) {
+    // the residual unless it has no mass; then the running chunk totals in chunk order
+    float totw = 0.f;
+    for (int c = 0; c < nchunks; ++c) totw += cs[c].x;
+    const bool res = P.mode == SAMPLE_RESIDUAL && totw > 0.f;
+    float tot = 0.f;
+    for (int c = 0; c < nchunks; ++c) tot += res ? cs[c].x : cs[c].y;
+    const float target = P.u * tot;
+    float run = 0.f;
+    int sel = -1, last = 0;
+    float base = 0.f, lastbase = 0.f;
+    for (int c = 0; c < nchunks; ++c) {
+      const float wc = res ? cs[c].x : cs[c].y;
+      if (wc > 0.f) { last = c; lastbase = run; }
+      if (sel < 0 && run + wc > target) { sel = c; base = run; }
+      run += wc;
+    }
+    if (sel < 0) { sel = last; base = lastbase; }  // u at or past the top: the last weighted chunk
+    sel_chunk = sel;
+    sel_base = base;
+    use_res = res;
+    S.best = 0x7fffffff;
+    lastw = -1;
+  }
+  __syncthreads();
+  const int c = sel_chunk;
+  float w[8], p[8];
+  sample_weights(tl, dl, V, zscale, P, c, tid, w, p);
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = use_res ? w[j] : p[j];
+  float tv = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) tv += v[j];
+  const float incl = block_scan_1024(tv, S.scan, tid);
+  // totals of the chunk's earlier threads and of the whole chunk, as k_sample_partial summed them
+  float tot = 0.f;
+  for (int cc = 0; cc < nchunks; ++cc) tot += use_res ? cs[cc].x : cs[cc].y;
+  const float target = P.u * tot;
+  const float run0 = sel_base + (incl - tv);  // running total before this thread's elements
+  int first = 0x7fffffff, lastnz = -1;
+  float run = run0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    run += v[j];
+    if (v[j] > 0.f) lastnz = j;
+    if (first == 0x7fffffff && v[j] > 0.f && run > target) first = j;
+  }
+  const int x0 = c * AM_CHUNK + 8 * tid;
+  if (first != 0x7fffffff) atomicMin(&S.best, x0 + first);
+  __syncthreads();
+  if (S.best == 0x7fffffff) {  // no crossing (rounding at the top): the chunk's last weighted element
+    if (lastnz >= 0) atomicMax(&lastw, x0 + lastnz);
+    __syncthreads();
+    if (tid == 0) token[0] = lastw;
+    return;
+  }
+  if (tid == 0) token[0] = S.best;
+}
+
+// Cycle statistics: hist[j] = cycles that accepted exactly j drafts, survival[i] = cycles that
+// accepted at least i + 1 (values outside [0, n_draft] are not counted). One workgroup.
+__global__ void __launch_bounds__(1024) k_accept_hist(const int32_t* acc, int n_cycles, int n_draft, int64_t* hist,
+                                                      int64_t* survival) {
+  __shared__ unsigned long long h[65];
+  const int tid = threadIdx.x;
+  if (tid <= n_draft) h[tid] = 0ull;
+  __syncthreads();
+  for (int i = tid; i < n_cycles; i += 1024) {
+    const int a = acc[i];
+    if (a >= 0 && a <= n_draft) atomicAdd(&h[a], 1ull);
+  }
+  __syncthreads();
+  if (tid <= n_draft) hist[tid] = (int64_t)h[tid];
+  if (tid < n_draft) {
+    unsigned long long sv = 0;
+    for (int j = tid + 1; j <= n_draft; ++j) sv += h[j];
+    survival[tid] = (int64_t)sv;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------------------
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -1441,6 +1740,8 @@ Layout make_layout(const moe_layer* L, int k) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
@@ -1705,6 +2006,71 @@ int lm_head_accept(const float* h, int32_t n_target, int32_t hidden, const void*
   if (hidden <= NW * WIN) k_head<1><<<G, NTH, 0, s>>>(h, w, hidden, vocab, n_target, n_items, pv, pi, ctr, epoch);
   else                    k_head<2><<<G, NTH, 0, s>>>(h, w, hidden, vocab, n_target, n_items, pv, pi, ctr, epoch);
   k_accept_final<<<1, 1024, 0, s>>>(pv, pi, G, n_target, draft_ids, n_draft, target_ids, accepted);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+// workspace: row partials ms [n_target + n_draft][nchunks] float2, chunk sums [nchunks] float2,
+// the plan
+size_t accept_sample_workspace_size(int32_t n_target, int32_t n_draft, int32_t vocab) {
+  if (n_target < 1 || n_target > 64 || n_draft < 0 || n_draft > n_target || vocab < 1 || vocab > (1 << 24)) return 0;
+  const size_t nch = ((size_t)vocab + AM_CHUNK - 1) / AM_CHUNK;
+  return align256((size_t)(n_target + n_draft) * nch * 8) + align256(nch * 8) + align256(sizeof(SamplePlan));
+}
+
+int accept_sample(const float* target_logits, int32_t n_target, int32_t vocab, const float* draft_logits,
+                  const int32_t* draft_ids, int32_t n_draft, float temperature, const float* u_accept,
+                  const float* u_sample, int32_t* accepted, int32_t* token, void* workspace, size_t ws_bytes,
+                  void* hip_stream) {
+  if (!target_logits || !u_sample || !accepted || !token || !workspace ||
+      (n_draft > 0 && (!draft_logits || !draft_ids || !u_accept)))
+    return MOE_ERR_NULL;
+  if (n_target < 1 || n_target > 64 || n_draft < 0 || n_draft > n_target || vocab < 1 || vocab > (1 << 24) ||
+      !(temperature > 0.f) || !(temperature < INFINITY))
+    return MOE_ERR_SHAPE;
+  if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits)) || !aligned16(workspace) ||
+      (draft_ids && !aligned4(draft_ids)) || (u_accept && !aligned4(u_accept)) || !aligned4(u_sample) ||
+      !aligned4(accepted) || !aligned4(token))
+    return MOE_ERR_ALIGN;
+  const size_t need = accept_sample_workspace_size(n_target, n_draft, vocab);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const size_t tb = (size_t)n_target * vocab * 4, db = (size_t)n_draft * vocab * 4;
+  const void* outs[3] = {accepted, token, workspace};
+  const size_t osz[3] = {4, 4, need};
+  const void* ins[5] = {target_logits, draft_logits, draft_ids, u_accept, u_sample};
+  const size_t isz[5] = {tb, db, (size_t)n_draft * 4, (size_t)n_draft * 4, (size_t)n_target * 4};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (ins[i] && overlaps(outs[o], osz[o], ins[i], isz[i])) return MOE_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlaps(outs[o], osz[o], outs[o2], osz[o2])) return MOE_ERR_ALIAS;
+  }
+  const int nch = (vocab + AM_CHUNK - 1) / AM_CHUNK;
+  uint8_t* ws = (uint8_t*)workspace;
+  float2* ms = (float2*)ws;
+  float2* csum = (float2*)(ws + align256((size_t)(n_target + n_draft) * nch * 8));
+  SamplePlan* plan = (SamplePlan*)(ws + align256((size_t)(n_target + n_draft) * nch * 8) + align256((size_t)nch * 8));
+  const float zscale = 1.4426950408889634f / temperature;  // log2(e) / T
+  hipStream_t s = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  k_lse_partial<<<dim3(nch, n_target + n_draft), 256, 0, s>>>(target_logits, draft_logits, n_target, vocab, nch,
+                                                             zscale, ms);
+  k_sample_partial<<<nch, SAMPLE_NTH, 0, s>>>(target_logits, draft_logits, n_target, vocab, nch, zscale, draft_ids,
+                                              n_draft, u_accept, u_sample, ms, csum, plan, accepted, token);
+  k_sample_final<<<1, SAMPLE_NTH, 0, s>>>(target_logits, draft_logits, vocab, nch, zscale, csum, plan, token);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int accept_histogram(const int32_t* accepted, int32_t n_cycles, int32_t n_draft, int64_t* hist, int64_t* survival,
+                     void* hip_stream) {
+  if (!accepted || !hist || (n_draft > 0 && !survival)) return MOE_ERR_NULL;
+  if (n_cycles < 0 || n_draft < 0 || n_draft > 64) return MOE_ERR_SHAPE;
+  if (!aligned4(accepted) || !aligned8(hist) || (survival && !aligned8(survival))) return MOE_ERR_ALIGN;
+  const size_t ab = (size_t)n_cycles * 4, hb = (size_t)(n_draft + 1) * 8, sb = (size_t)n_draft * 8;
+  if (overlaps(hist, hb, accepted, ab) || (survival && (overlaps(survival, sb, accepted, ab) ||
+                                                        overlaps(survival, sb, hist, hb))))
+    return MOE_ERR_ALIAS;
+  (void)hipGetLastError();
+  k_accept_hist<<<1, 1024, 0, (hipStream_t)hip_stream>>>(accepted, n_cycles, n_draft, hist, survival);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -172,6 +172,61 @@ def test_lm_head_accept_validation(b):
     assert call(ws=w + 4096) == -6
 
 
+def test_accept_sample_validation(b):
+    f = b.lib.accept_sample
+    V, nt, nd = 151936, 17, 16
+    need = b.lib.accept_sample_workspace_size(nt, nd, V)
+    assert need > 0
+    assert b.lib.accept_sample_workspace_size(0, 0, V) == 0
+    assert b.lib.accept_sample_workspace_size(65, 0, V) == 0
+    assert b.lib.accept_sample_workspace_size(4, 5, V) == 0
+    assert b.lib.accept_sample_workspace_size(4, 4, (1 << 24) + 1) == 0
+    tl, dl, di, ua, us, ac, tk, ws = (FAKE, FAKE + 0x10000000, FAKE + 0x20000000, FAKE + 0x21000000,
+                                      FAKE + 0x22000000, FAKE + 0x23000000, FAKE + 0x24000000, FAKE + 0x30000000)
+    ok = dict(tl=tl, nt=nt, V=V, dl=dl, di=di, nd=nd, T=1.0, ua=ua, us=us, ac=ac, tk=tk, ws=ws, wsb=need, s=None)
+    names = ("tl", "nt", "V", "dl", "di", "nd", "T", "ua", "us", "ac", "tk", "ws", "wsb", "s")
+
+    def call(**kw):
+        args = dict(ok)
+        args.update(kw)
+        return f(*[args[k] for k in names])
+
+    # every call below fails a host-side check: none reaches a launch
+    assert call(tl=None) == -1
+    assert call(us=None) == -1
+    assert call(dl=None) == -1
+    assert call(di=None) == -1
+    assert call(ua=None) == -1
+    assert call(tk=None) == -1
+    assert call(nt=0) == -2
+    assert call(nt=65) == -2
+    assert call(nd=18) == -2
+    assert call(V=0) == -2
+    assert call(T=0.0) == -2
+    assert call(T=-1.0) == -2
+    assert call(T=float("inf")) == -2
+    assert call(T=float("nan")) == -2
+    assert call(tl=tl + 4) == -4
+    assert call(ac=ac + 2) == -4
+    assert call(wsb=need - 1) == -5
+    assert call(tk=tl + 64) == -6
+    assert call(tk=ac) == -6
+    assert call(ac=ws + 64) == -6
+
+
+def test_accept_histogram_validation(b):
+    f = b.lib.accept_histogram
+    a, h, sv = FAKE, FAKE + 0x1000, FAKE + 0x2000
+    assert f(None, 10, 4, h, sv, None) == -1
+    assert f(a, 10, 4, None, sv, None) == -1
+    assert f(a, 10, 4, h, None, None) == -1
+    assert f(a, -1, 4, h, sv, None) == -2
+    assert f(a, 10, 65, h, sv, None) == -2
+    assert f(a, 10, 4, h + 4, sv, None) == -4
+    assert f(a, 10, 4, a + 8, sv, None) == -6
+    assert f(a, 10, 4, h, h + 8, None) == -6
+
+
 def test_pack_weights_validation(b):
     f = b.lib.moe_pack_weights
     src, dst, ss, ds = FAKE, FAKE + 0x10000000, FAKE + 0x20000000, FAKE + 0x30000000
