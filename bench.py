@@ -201,6 +201,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer mxfp4 stack measurement")
     ap.add_argument("--no-head", action="store_true", help="skip the output-head (lm_head_accept) measurement")
+    ap.add_argument("--no-sample", action="store_true", help="skip the accept_sample / statistics measurement")
     ap.add_argument("--profile-run", action="store_true",
                     help="counter-collection run: warmup + steps without events, then a plain copy of "
                          "known size for calibrating HBM traffic counters; prints one JSON line")
@@ -500,6 +501,55 @@ def main():
         del heads
         print("[bench] head done", file=sys.stderr, flush=True)
 
+    # ---- lossless acceptance at temperature + acceptance statistics (17 target, 16 draft rows) ----
+    samp = None
+    if not args.no_sample:
+        print("[bench] timing accept_sample", file=sys.stderr, flush=True)
+        g = torch.Generator(device=dev)
+        g.manual_seed(wl.seed)
+        nt_, nd_, temp = NT, NT - 1, 1.0
+        # synthetic cycles: target logits 2 N(0,1), a drafter 0.5 N(0,1) away, drafts drawn from it
+        tls = [torch.randn((nt_, V), generator=g, device=dev) * 2.0 for _ in range(4)]
+        dls = [(t[:nd_] + 0.5 * torch.randn((nd_, V), generator=g, device=dev)).contiguous() for t in tls]
+        dds = [torch.multinomial(torch.softmax(d / temp, dim=1), 1, generator=g).view(-1).to(torch.int32).contiguous()
+               for d in dls]
+        ncyc = 512
+        uas = torch.rand((ncyc, nd_), generator=g, device=dev)
+        uss = torch.rand((ncyc, nt_), generator=g, device=dev)
+        sacc = torch.zeros((ncyc,), dtype=torch.int32, device=dev)
+        stok = torch.zeros((ncyc,), dtype=torch.int32, device=dev)
+        sws = torch.empty(binding.accept_sample_workspace_size(nt_, nd_, V), dtype=torch.uint8, device=dev)
+
+        def scall(c):
+            i = c % 4
+            binding.accept_sample(tls[i], dls[i], dds[i], temp, uas[c], uss[c], sacc[c:c + 1], stok[c:c + 1], sws)
+
+        for c in range(5):
+            scall(c)
+        a_, b_ = ev.create(2)
+        torch.cuda.synchronize()
+        ev.record(a_, stream)
+        for c in range(ncyc):
+            scall(c)
+        ev.record(b_, stream)
+        torch.cuda.synchronize()
+        s_us = ev.ms(a_, b_) * 1e3 / ncyc
+        ev.destroy([a_, b_])
+        hist = torch.empty((nd_ + 1,), dtype=torch.int64, device=dev)
+        surv = torch.empty((nd_,), dtype=torch.int64, device=dev)
+        binding.accept_histogram(sacc, nd_, hist, surv)
+        torch.cuda.synchronize()
+        sbytes = (nt_ + nd_) * V * 4
+        hh, sv = hist.cpu().numpy(), surv.cpu().numpy()
+        samp = {"workload": f"accept_sample: {nt_} target + {nd_} draft rows x {V} fp32 logits, T = {temp}, "
+                            f"synthetic drafter (target + 0.5 N(0,1) logits, drafts drawn from it), {ncyc} cycles",
+                "us_per_call": round(s_us, 2), "bytes_per_call": sbytes,
+                "GBps": round(sbytes / (s_us * 1e-6) / 1e9, 1),
+                "tau_mean": round(float((np.arange(nd_ + 1) * hh).sum() / ncyc + 1.0), 3),
+                "hist_accepted": [int(v) for v in hh],
+                "marginal_accept": [round(float(v) / ncyc, 4) for v in sv]}
+        print("[bench] sample done", file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {args.cpu_samples} steps", file=sys.stderr, flush=True)
@@ -523,6 +573,7 @@ def main():
         "sweep_fit": fit,
         "stack40_mxfp4": stack,
         "lm_head": head,
+        "accept_sample": samp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

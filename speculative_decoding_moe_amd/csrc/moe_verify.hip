@@ -1438,12 +1438,39 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float mo, float so
       (mo == -INFINITY ? 0.f : so * __builtin_amdgcn_exp2f(mo - mm));
   m = mm;
 }
+// DPP lane moves of fp32 values (CTRL: the DPP control; lanes outside ROWMASK keep 0)
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWMASK, 0xf, true));
+}
+// Wave-uniform maximum and sum over the 64 lanes (every lane of a 16-lane row gets the row result
+// from four full-row permutations, then the four row results in a fixed order).
+__device__ __forceinline__ float wave_max_f32(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp_f32<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48))));
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  x += dpp_f32<0xB1>(x);
+  x += dpp_f32<0x4E>(x);
+  x += dpp_f32<0x141>(x);
+  x += dpp_f32<0x140>(x);
+  return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
+}
+// wave-uniform merge of the lanes' (max, sum) pairs: the maximum first, then one rescale per lane
 __device__ __forceinline__ void wave_lse(float& m, float& s) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float mo = __shfl_xor(m, off), so = __shfl_xor(s, off);
-    lse_merge(m, s, mo, so);
-  }
+  const float mm = wave_max_f32(m);
+  const float t = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f(m - mm);
+  s = wave_sum_f32(t);
+  m = mm;
 }
 
 __global__ void __launch_bounds__(256) k_lse_partial(const float* tl, const float* dl, int n_t, int V, int nchunks,
@@ -1495,28 +1522,53 @@ __global__ void __launch_bounds__(256) k_lse_partial(const float* tl, const floa
 }
 
 // Inclusive prefix sums of one value per thread over the 1024 threads, in a fixed order (wave
-// scans, then the wave totals); every caller sees identical bits for identical inputs.
+// scans, then the wave totals scanned by one wave); every caller sees identical bits for
+// identical inputs.
+__device__ __forceinline__ float wave_scan_incl(float v, int lane) {
+  (void)lane;
+  v += dpp_f32<0x111>(v);       // row_shr:1 (lanes without a source add 0)
+  v += dpp_f32<0x112>(v);       // row_shr:2
+  v += dpp_f32<0x114>(v);       // row_shr:4
+  v += dpp_f32<0x118>(v);       // row_shr:8: inclusive scans of each 16-lane row
+  v += dpp_f32<0x142, 0xa>(v);  // row_bcast:15: row 0's total into row 1, row 2's into row 3
+  v += dpp_f32<0x143, 0xc>(v);  // row_bcast:31: the total of rows 0-1 into rows 2 and 3
+  return v;
+}
 __device__ __forceinline__ float block_scan_1024(float v, float* lds16, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
+  v = wave_scan_incl(v, lane);
   if (lane == 63) lds16[wave] = v;
   __syncthreads();
-  float before = 0.f;
-  for (int w = 0; w < wave; ++w) before += lds16[w];
+  if (wave == 0) {
+    float t = lane < 16 ? lds16[lane] : 0.f;
+    t = wave_scan_incl(t, lane);
+    const float ex = __shfl_up(t, 1);
+    if (lane < 16) lds16[16 + lane] = lane ? ex : 0.f;  // totals of the earlier waves
+  }
   __syncthreads();
+  const float before = lds16[16 + wave];
+  __syncthreads();  // lds16 may be rewritten by the next scan
   return before + v;
 }
 
 struct SampleSmem {
   float m[128], s[128];  // merged (max, sum) per row: target rows, then draft rows
-  float scan[16];
+  float scan[32];
   SamplePlan plan;
   int best;
 };
+
+// Loads of the 8 consecutive elements 8t .. 8t+7 of chunk c of one row (clamped past V).
+__device__ __forceinline__ void load8(const float* row, int V, int x0, float (&v)[8]) {
+  if ((V & 3) == 0 && x0 + 8 <= V) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(row + x0);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(row + x0 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = row[x0 + j < V ? x0 + j : 0];
+  }
+}
 
 // The weights of chunk c of the plan's row, thread t holding elements 8t .. 8t+7 of the chunk:
 // residual max(0, p - q) (w) and target p (p); elements past V weigh zero.
@@ -1527,12 +1579,8 @@ __device__ __forceinline__ void sample_weights(const float* tl, const float* dl,
   const float* rt = tl + (size_t)P.row * V;
   const float* rd = res ? dl + (size_t)P.row * V : rt;  // a target row stands in when unused
   float lt[8], ld[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int x = x0 + j < V ? x0 + j : 0;
-    lt[j] = rt[x];
-    ld[j] = rd[x];
-  }
+  load8(rt, V, x0, lt);
+  load8(rd, V, x0, ld);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const bool in = x0 + j < V;
@@ -1544,30 +1592,57 @@ __device__ __forceinline__ void sample_weights(const float* tl, const float* dl,
 }
 
 // Merge the row partials, take the accept decisions, and fill the plan (every workgroup alike).
+// The logits at the drafted ids and every row's partials are requested together.
 __device__ void sample_plan(const float* tl, const float* dl, int n_t, int V, int nchunks, float zscale,
                             const int32_t* draft, int n_d, const float* u_acc, const float* u_smp,
                             const float2* ms, SampleSmem& S, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
   const int R = n_t + n_d;
-  for (int row = wave; row < R; row += SAMPLE_NTH / 64) {
-    float m = -INFINITY, s = 0.f;
-    for (int c = lane; c < nchunks; c += 64) {
-      const float2 v = ms[(size_t)row * nchunks + c];
-      lse_merge(m, s, v.x, v.y);
-    }
-    wave_lse(m, s);
-    if (lane == 0) { S.m[row] = m; S.s[row] = s; }
+  // wave 0: the drafted ids' logits (lane i < n_d)
+  float lt_d = 0.f, ld_d = 0.f, ua = 0.f;
+  bool valid = false;
+  if (wave == 0 && lane < n_d) {
+    const int d = draft[lane];
+    valid = d >= 0 && d < V;
+    const int dd = valid ? d : 0;
+    lt_d = tl[(size_t)lane * V + dd];
+    ld_d = dl[(size_t)lane * V + dd];
+    ua = u_acc[lane];
+  }
+  // every wave: rows wave, wave + 16, ... (at most 8), chunks lane, lane + 64, ...
+  constexpr int RPW = 128 / (SAMPLE_NTH / 64);
+  float2 v[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const int row = min(wave + 16 * j, R - 1), c = min(lane, nchunks - 1);
+    v[j] = ms[(size_t)row * nchunks + c];
+  }
+  float m[RPW], sm[RPW];
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    const bool live = wave + 16 * j < R && lane < nchunks;
+    m[j] = live ? v[j].x : -INFINITY;
+    sm[j] = live ? v[j].y : 0.f;
+  }
+  for (int c = lane + 64; c < nchunks; c += 64)  // vocabularies beyond 64 chunks
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+      if (wave + 16 * j < R) {
+        const float2 o = ms[(size_t)(wave + 16 * j) * nchunks + c];
+        lse_merge(m[j], sm[j], o.x, o.y);
+      }
+#pragma unroll
+  for (int j = 0; j < RPW; ++j) {
+    wave_lse(m[j], sm[j]);
+    if (lane == 0 && wave + 16 * j < R) { S.m[wave + 16 * j] = m[j]; S.s[wave + 16 * j] = sm[j]; }
   }
   __syncthreads();
   if (wave == 0) {
     bool miss = false;
     if (lane < n_d) {
-      const int d = draft[lane];
-      const bool valid = d >= 0 && d < V;
-      const int dd = valid ? d : 0;
-      const float p = __builtin_amdgcn_exp2f(tl[(size_t)lane * V + dd] * zscale - S.m[lane]) / S.s[lane];
-      const float q = __builtin_amdgcn_exp2f(dl[(size_t)lane * V + dd] * zscale - S.m[n_t + lane]) / S.s[n_t + lane];
-      miss = !(valid && u_acc[lane] * q < p);
+      const float p = __builtin_amdgcn_exp2f(lt_d * zscale - S.m[lane]) / S.s[lane];
+      const float q = __builtin_amdgcn_exp2f(ld_d * zscale - S.m[n_t + lane]) / S.s[n_t + lane];
+      miss = !(valid && ua * q < p);
     }
     const unsigned long long mm = __ballot(miss);
     if (lane == 0) {
@@ -1616,38 +1691,55 @@ __global__ void __launch_bounds__(SAMPLE_NTH) k_sample_final(const float* tl, co
                                                              float zscale, const float2* csum, const SamplePlan* plan,
                                                              int32_t* token) {
   __shared__ SampleSmem S;
-  __shared__ float2 cs[2048];
-  __shared__ int sel_chunk;
-  __shared__ float sel_base;
-  __shared__ int use_res, lastw;
-  const int tid = threadIdx.x;
+  __shared__ int sel_chunk, use_res, lastw;
+  __shared__ float sel_base, sel_target;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const SamplePlan P = *plan;
   if (P.mode == SAMPLE_NONE) return;
-  for (int c = tid; c < nchunks; c += SAMPLE_NTH) cs[c] = csum[c];
-  __syncthreads();
-  if (tid == 0) {
-    // the residual unless it has no mass; then the running chunk totals in chunk order
+  if (wave == 0) {
+    // residual chunk totals unless they have no mass; running totals by a wave scan per 64 chunks
     float totw = 0.f;
-    for (int c = 0; c < nchunks; ++c) totw += cs[c].x;
+    for (int c0 = 0; c0 < nchunks; c0 += 64) {
+      const float x = c0 + lane < nchunks ? csum[c0 + lane].x : 0.f;
+      totw += __shfl(wave_scan_incl(x, lane), 63);
+    }
     const bool res = P.mode == SAMPLE_RESIDUAL && totw > 0.f;
     float tot = 0.f;
-    for (int c = 0; c < nchunks; ++c) tot += res ? cs[c].x : cs[c].y;
+    for (int c0 = 0; c0 < nchunks; c0 += 64) {
+      const float2 cv = c0 + lane < nchunks ? csum[c0 + lane] : make_float2(0.f, 0.f);
+      tot += __shfl(wave_scan_incl(res ? cv.x : cv.y, lane), 63);
+    }
     const float target = P.u * tot;
-    float run = 0.f;
-    int sel = -1, last = 0;
-    float base = 0.f, lastbase = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-      const float wc = res ? cs[c].x : cs[c].y;
-      if (wc > 0.f) { last = c; lastbase = run; }
-      if (sel < 0 && run + wc > target) { sel = c; base = run; }
-      run += wc;
+    int sel = -1, last = -1;
+    float base = 0.f, lastbase = 0.f, run = 0.f;
+    for (int c0 = 0; c0 < nchunks && sel < 0; c0 += 64) {
+      const float2 cv = c0 + lane < nchunks ? csum[c0 + lane] : make_float2(0.f, 0.f);
+      const float wc = res ? cv.x : cv.y;
+      const float incl = run + wave_scan_incl(wc, lane);
+      const float excl = incl - wc;
+      const unsigned long long cross = __ballot(wc > 0.f && incl > target);
+      const unsigned long long nz = __ballot(wc > 0.f);
+      if (cross) {
+        const int l = __builtin_ctzll(cross);
+        sel = c0 + l;
+        base = __shfl(excl, l);
+      }
+      if (nz) {
+        const int l = 63 - __builtin_clzll(nz);
+        last = c0 + l;
+        lastbase = __shfl(excl, l);
+      }
+      run = __shfl(incl, 63);
     }
     if (sel < 0) { sel = last; base = lastbase; }  // u at or past the top: the last weighted chunk
-    sel_chunk = sel;
-    sel_base = base;
-    use_res = res;
-    S.best = 0x7fffffff;
-    lastw = -1;
+    if (lane == 0) {
+      sel_chunk = sel;
+      sel_base = base;
+      sel_target = target;
+      use_res = res;
+      S.best = 0x7fffffff;
+      lastw = -1;
+    }
   }
   __syncthreads();
   const int c = sel_chunk;
@@ -1660,13 +1752,9 @@ __global__ void __launch_bounds__(SAMPLE_NTH) k_sample_final(const float* tl, co
 #pragma unroll
   for (int j = 0; j < 8; ++j) tv += v[j];
   const float incl = block_scan_1024(tv, S.scan, tid);
-  // totals of the chunk's earlier threads and of the whole chunk, as k_sample_partial summed them
-  float tot = 0.f;
-  for (int cc = 0; cc < nchunks; ++cc) tot += use_res ? cs[cc].x : cs[cc].y;
-  const float target = P.u * tot;
-  const float run0 = sel_base + (incl - tv);  // running total before this thread's elements
+  const float target = sel_target;
   int first = 0x7fffffff, lastnz = -1;
-  float run = run0;
+  float run = sel_base + (incl - tv);  // running total before this thread's elements
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     run += v[j];
@@ -1675,14 +1763,10 @@ __global__ void __launch_bounds__(SAMPLE_NTH) k_sample_final(const float* tl, co
   }
   const int x0 = c * AM_CHUNK + 8 * tid;
   if (first != 0x7fffffff) atomicMin(&S.best, x0 + first);
+  if (lastnz >= 0) atomicMax(&lastw, x0 + lastnz);
   __syncthreads();
-  if (S.best == 0x7fffffff) {  // no crossing (rounding at the top): the chunk's last weighted element
-    if (lastnz >= 0) atomicMax(&lastw, x0 + lastnz);
-    __syncthreads();
-    if (tid == 0) token[0] = lastw;
-    return;
-  }
-  if (tid == 0) token[0] = S.best;
+  // no crossing inside the chunk (rounding at its top): its last weighted element
+  if (tid == 0) token[0] = S.best != 0x7fffffff ? S.best : lastw;
 }
 
 // Cycle statistics: hist[j] = cycles that accepted exactly j drafts, survival[i] = cycles that
