@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 #include <stdint.h>
 #include <string.h>
 
@@ -109,6 +110,80 @@ __device__ __forceinline__ u32x4 dec_fp4x8(uint32_t c, float scale) {
   return r;
 }
 __device__ __forceinline__ float e8m0_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
+
+// ---- MX-fp8 operands of the scaled matrix-core instruction (mxfp4 layers) ----
+// v_mfma_scale_f32_16x16x128_f8f6f4 multiplies a 16x128 A by a 128x16 B with one e8m0 scale per
+// 32 values along K for each row of A and each column of B. A (fp4 codes): lane l holds row
+// l % 16, K = 32 (l / 16) .. +31, low nibble first, the tiled mxfp4 layout's lane block. B
+// (fp8 e4m3): lane l = c + 16 q holds column c at K = 16 q + j in bytes j < 16 and at
+// K = 64 + 16 q + j in bytes 16 + j. The scale of (row or column c, 32-block b) is the selected
+// byte of lane c + 16 b's scale register. Activations enter as hi + lo fp8 pairs, each with its
+// own block scale (the lo part quantises the residual of the hi part).
+typedef int v8i __attribute__((ext_vector_type(8)));
+constexpr int MXW = 4096 + 256;  // bytes per 128-wide window: hi [64][32], lo [64][32], scales [64] u32
+
+// e8m0 exponent for a block whose largest magnitude is m: the smallest e with m 2^-e <= 448 (the
+// largest e4m3 value), clamped to [-127, 127]; an all-zero block takes -127.
+__device__ __forceinline__ int mx8_exp(float m) {
+  if (!(m > 0.f)) return -127;
+  int e = (int)((__float_as_uint(m) >> 23) & 0xFFu) - 127 - 8;
+  if (ldexpf(m, -e) > 448.f) ++e;
+  return max(-127, min(127, e));
+}
+// four values to e4m3 (round to nearest even), packed low to high
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+// N values (a multiple of 4) as hi and lo fp8 words with their exponents; the block maximum is
+// taken over the values and, when PARTNER is set, over the same computation in lane ^ 16.
+template <int N, bool PARTNER>
+__device__ __forceinline__ void mx8_quant(const float (&v)[N], uint32_t (&hi)[N / 4], uint32_t (&lo)[N / 4],
+                                          int& eh, int& el) {
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < N; ++j) m = fmaxf(m, fabsf(v[j]));
+  if (PARTNER) m = fmaxf(m, __shfl_xor(m, 16));
+  eh = mx8_exp(m);
+#pragma unroll
+  for (int g = 0; g < N / 4; ++g)
+    hi[g] = fp8x4(ldexpf(v[4 * g], -eh), ldexpf(v[4 * g + 1], -eh), ldexpf(v[4 * g + 2], -eh),
+                  ldexpf(v[4 * g + 3], -eh));
+  float r[N];
+#pragma unroll
+  for (int g = 0; g < N / 4; ++g) {
+    r[4 * g + 0] = v[4 * g + 0] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hi[g], 0), eh);
+    r[4 * g + 1] = v[4 * g + 1] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hi[g], 1), eh);
+    r[4 * g + 2] = v[4 * g + 2] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hi[g], 2), eh);
+    r[4 * g + 3] = v[4 * g + 3] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hi[g], 3), eh);
+  }
+  float mr = 0.f;
+#pragma unroll
+  for (int j = 0; j < N; ++j) mr = fmaxf(mr, fabsf(r[j]));
+  if (PARTNER) mr = fmaxf(mr, __shfl_xor(mr, 16));
+  el = mx8_exp(mr);
+#pragma unroll
+  for (int g = 0; g < N / 4; ++g)
+    lo[g] = fp8x4(ldexpf(r[4 * g], -el), ldexpf(r[4 * g + 1], -el), ldexpf(r[4 * g + 2], -el),
+                  ldexpf(r[4 * g + 3], -el));
+}
+// store 16 quantised values of (column c, 32-block blk, half h) of one window and, for h == 0,
+// the block's scale pair (hi exponent in byte 0, lo in byte 1)
+__device__ __forceinline__ void mx8_store16(uint8_t* win, int c, int blk, int h, const uint32_t (&hi)[4],
+                                            const uint32_t (&lo)[4], int eh, int el) {
+  const int L = c + 16 * (2 * (blk & 1) + h), off = 16 * (blk >> 1);
+  *reinterpret_cast<u32x4*>(win + L * 32 + off) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  *reinterpret_cast<u32x4*>(win + 2048 + L * 32 + off) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  if (h == 0)
+    *reinterpret_cast<uint32_t*>(win + 4096 + (c + 16 * blk) * 4) = (uint32_t)(eh + 127) | ((uint32_t)(el + 127) << 8);
+}
+__device__ __forceinline__ f32x4 mfma_mx(u32x4 a, uint32_t sa, u32x4 b0, u32x4 b1, uint32_t sb, int sel, f32x4 acc) {
+  const v8i A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  if (sel == 0) return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 0, 0, (int)sa, 0, (int)sb);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc, 4, 0, 0, (int)sa, 1, (int)sb);
+}
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
@@ -202,6 +277,31 @@ __device__ __forceinline__ void write_xfrag(const float* x, u32x4* dst, int H, i
   dst[((size_t)s * 2 + 1) * 64 + lane] = l;
 }
 
+// window w of the raw block as MX-fp8 hi + lo B fragments with their scales (mxfp4 layers): lane
+// l = c + 16 b quantises block b (32 values) of token c and stores its two 16-value halves where
+// the instruction's B layout puts them
+__device__ __forceinline__ void write_xmx(const float* x, uint8_t* dst, int H, int k, int w, int lane) {
+  const int c = lane & 15, b = lane >> 4;
+  float v[32];
+  const float* src = x + (size_t)(c < k ? c : 0) * H + w * WIN + 32 * b;
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const float4 f = *reinterpret_cast<const float4*>(src + 4 * g);
+    v[4 * g + 0] = c < k ? f.x : 0.f;
+    v[4 * g + 1] = c < k ? f.y : 0.f;
+    v[4 * g + 2] = c < k ? f.z : 0.f;
+    v[4 * g + 3] = c < k ? f.w : 0.f;
+  }
+  uint32_t hi[8], lo[8];
+  int eh, el;
+  mx8_quant<32, false>(v, hi, lo, eh, el);
+  uint8_t* win = dst + (size_t)w * MXW;
+  const uint32_t h0[4] = {hi[0], hi[1], hi[2], hi[3]}, h1[4] = {hi[4], hi[5], hi[6], hi[7]};
+  const uint32_t l0[4] = {lo[0], lo[1], lo[2], lo[3]}, l1[4] = {lo[4], lo[5], lo[6], lo[7]};
+  mx8_store16(win, c, b, 0, h0, l0, eh, el);
+  mx8_store16(win, c, b, 1, h1, l1, eh, el);
+}
+
 struct RouterSmem {
   float red[NW * 256];
   float rsq[NW][64];
@@ -249,12 +349,16 @@ __device__ void router_item(const Args& a, RouterSmem& S, int r, int wave, int l
       for (int qq = 0; qq < 4; ++qq) s += S.rsq[w][tid + 16 * qq];
     a.psq[hsi * KMAX + tid] = s;
   }
-  // B-operand fragments of the raw block: k-steps s = r + nr * (tid / 64) + 8 nr * i. mxfp4
-  // layers with a shared expert also get the bf16 fragment order for the shared expert's tiles.
+  // B-operand fragments of the raw block, spread over the router's waves: bf16 hi/lo k-steps
+  // (bf16 layers, and the shared expert of mxfp4 layers), MX-fp8 windows (mxfp4 routed experts)
   const int nr = a.ntile_e * a.hs;
-  for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) {
-    write_xfrag<NAT>(a.x, a.xfrag, H, k, s, lane);
-    if (!NAT && a.Is > 0) write_xfrag<true>(a.x, a.xfrag_nat, H, k, s, lane);
+  if (NAT) {
+    for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) write_xfrag<true>(a.x, a.xfrag, H, k, s, lane);
+  } else {
+    for (int w = r + nr * (tid >> 6); w < H / WIN; w += nr * NW)
+      write_xmx(a.x, reinterpret_cast<uint8_t*>(a.xfrag), H, k, w, lane);
+    if (a.Is > 0)
+      for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) write_xfrag<true>(a.x, a.xfrag_nat, H, k, s, lane);
   }
 }
 
@@ -555,8 +659,10 @@ __device__ __forceinline__ void gu_load_mx(GUItem<WPW>& T, const GURes& R, const
 }
 
 // Cross-wave reduction, SwiGLU with the RMSNorm factor and the routing weight, hi/lo split, and
-// the store as down-projection B fragments (rows row0 .. row0 + 16 ntile of expert slot `u`).
-template <bool NAT>
+// the store as down-projection B fragments (rows row0 .. row0 + 16 ntile of expert slot `u`):
+// bf16 hi/lo fragments, or (MX8: routed items of mxfp4 layers, 32 rows = one 32-value block of
+// the down projection's reduction dimension) MX-fp8 hi/lo operands with their block scales.
+template <bool NAT, bool MX8 = false>
 __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 (&acc)[GU_MX_RT][2],
                                             int ntile, int u, int row0, bool routed, int wave,
                                             int lane, int tid, int ring = -1, int* next = nullptr) {
@@ -583,6 +689,22 @@ __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 
   if (ring >= 0) {  // the next item index, read before this epilogue's stores are issued
     *next = __builtin_amdgcn_readfirstlane(S.claim[ring]);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (MX8) {
+    // thread (half h, column c) -> rows 16 h .. 16 h + 15 of the block; the block maximum pairs
+    // the two halves (lanes c and c + 16 of wave 0)
+    if (tid < 2 * KMAX) {
+      const int c = tid & 15, h = tid >> 4;
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = S.act[h][(c + 16 * (j >> 2)) * 4 + (j & 3)];
+      uint32_t hi[4], lo[4];
+      int eh, el;
+      mx8_quant<16, true>(v, hi, lo, eh, el);
+      uint8_t* win = reinterpret_cast<uint8_t*>(a.afrag) + ((size_t)u * (a.I / WIN) + row0 / WIN) * MXW;
+      mx8_store16(win, c, (row0 % WIN) / 32, h, hi, lo, eh, el);
+    }
+    return;
   }
   // thread (tile, half, column c) -> rows R .. R+7 of the expert's intermediate dimension
   if (tid < ntile * 2 * KMAX) {
@@ -623,9 +745,33 @@ __device__ __forceinline__ void gu_math_bf16(f32x4 (&acc)[GU_MX_RT][2], const GU
       }
 }
 
+// MX-fp8 B operands of this wave's H windows (mxfp4 routed experts): hi and lo halves, scales
 template <int WPW>
-__device__ __forceinline__ void gu_math_mx(f32x4 (&acc)[GU_MX_RT][2], const GUItem<WPW>& T,
-                                           const u32x4 (&xb)[WPW][4][2]) {
+struct XMX {
+  u32x4 hi[WPW][2], lo[WPW][2];
+  uint32_t sc[WPW];
+};
+template <int WPW>
+__device__ __forceinline__ void gu_load_xmx(XMX<WPW>& xm, const u32x4* xf, int win0, bool active, int lane) {
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(xf);
+#pragma unroll
+  for (int wi = 0; wi < WPW; ++wi) {
+    const uint8_t* w = base + (size_t)(active ? win0 + wi : 0) * MXW;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const u32x4 h = *reinterpret_cast<const u32x4*>(w + lane * 32 + 16 * hh);
+      const u32x4 l = *reinterpret_cast<const u32x4*>(w + 2048 + lane * 32 + 16 * hh);
+      xm.hi[wi][hh] = active ? h : u32x4{0u, 0u, 0u, 0u};  // inactive waves multiply by zero
+      xm.lo[wi][hh] = active ? l : u32x4{0u, 0u, 0u, 0u};
+    }
+    xm.sc[wi] = *reinterpret_cast<const uint32_t*>(w + 4096 + lane * 4);
+  }
+}
+
+// mxfp4 item: per (tile, window, matrix) one lane block of fp4 codes and its scale against the
+// window's fp8 hi and lo operands: two scaled matrix-core instructions
+template <int WPW>
+__device__ __forceinline__ void gu_math_mx(f32x4 (&acc)[GU_MX_RT][2], const GUItem<WPW>& T, const XMX<WPW>& xm) {
 #pragma unroll
   for (int tl = 0; tl < GU_MX_RT; ++tl) acc[tl][0] = acc[tl][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -635,14 +781,9 @@ __device__ __forceinline__ void gu_math_mx(f32x4 (&acc)[GU_MX_RT][2], const GUIt
 #pragma unroll
       for (int mat = 0; mat < 2; ++mat) {
         const u32x4 c = T.v[(tl * WPW + wi) * 2 + mat];
-        const float sc = e8m0_scale(T.sc[(tl * WPW + wi) * 2 + mat]);
-        const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4 av = dec_fp4x8(cw[j], sc);
-          acc[tl][mat] = mfma16(av, xb[wi][j][0], acc[tl][mat]);
-          acc[tl][mat] = mfma16(av, xb[wi][j][1], acc[tl][mat]);
-        }
+        const uint32_t sa = T.sc[(tl * WPW + wi) * 2 + mat];
+        acc[tl][mat] = mfma_mx(c, sa, xm.hi[wi][0], xm.hi[wi][1], xm.sc[wi], 0, acc[tl][mat]);
+        acc[tl][mat] = mfma_mx(c, sa, xm.lo[wi][0], xm.lo[wi][1], xm.sc[wi], 1, acc[tl][mat]);
       }
 }
 
@@ -754,8 +895,8 @@ __device__ __forceinline__ void gu_load(GUItem<WPW>& T, const GURes& R, const GU
 
 template <int WPW, bool MX>
 __device__ __forceinline__ void gu_math(f32x4 (&acc)[GU_MX_RT][2], const GUItem<WPW>& T,
-                                        const u32x4 (&xb)[WPW][4][2]) {
-  if (MX) gu_math_mx<WPW>(acc, T, xb);
+                                        const u32x4 (&xb)[WPW][4][2], const XMX<WPW>& xm) {
+  if constexpr (MX) gu_math_mx<WPW>(acc, T, xm);
   else gu_math_bf16<WPW>(acc, T, xb);
 }
 
@@ -851,32 +992,52 @@ __device__ __forceinline__ void dn_load_b(u32x4 (&bf)[4][2], rsrc_t raf, uint32_
     for (int hl = 0; hl < 2; ++hl) bf[j][hl] = bld16_cached(raf, vb + (uint32_t)((j * 2 + hl) * 1024), soff);
 }
 
+// B operands of a wave's window for one expert slot: bf16 hi/lo fragments (4 k-steps), or the
+// MX-fp8 hi/lo operands and their scale word (mxfp4 routed experts)
+struct DBF {
+  u32x4 f[4][2];
+};
+struct DBM {
+  u32x4 hi[2], lo[2];
+  uint32_t sc;
+};
+template <bool MX>
+using DnB = std::conditional_t<MX, DBM, DBF>;
+
+template <int NWIN, bool MX>
+__device__ __forceinline__ void dn_load_bb(DnB<MX>& B, rsrc_t raf, int u, int I, int wave, int lane) {
+  if constexpr (MX) {
+    const uint32_t soff = (uint32_t)((u * (I / WIN) + wave % NWIN) * MXW);
+    const uint32_t vb = (uint32_t)lane * 32u;
+    B.hi[0] = bld16_cached(raf, vb, soff);
+    B.hi[1] = bld16_cached(raf, vb + 16u, soff);
+    B.lo[0] = bld16_cached(raf, vb + 2048u, soff);
+    B.lo[1] = bld16_cached(raf, vb + 2064u, soff);
+    B.sc = __builtin_amdgcn_raw_buffer_load_b32(raf, (uint32_t)(4096 + lane * 4), soff, 0);
+  } else {
+    dn_load_b<NWIN>(B.f, raf, (uint32_t)(u * (I / 32) * 2048), wave, lane);
+  }
+}
+
 template <int NWIN, bool MX>
 __device__ __forceinline__ void dn_math(f32x4 (&acc)[DnShape<NWIN>::TPW_MX], const DNItem<NWIN>& T,
-                                        const u32x4 (&bf)[4][2]) {
+                                        const DnB<MX>& B) {
   using SH = DnShape<NWIN>;
 #pragma unroll
   for (int tl = 0; tl < SH::TPW_MX; ++tl) acc[tl] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (MX) {
+  if constexpr (MX) {  // per tile: the lane's fp4 block and scale against the fp8 hi and lo operands
 #pragma unroll
     for (int tl = 0; tl < SH::TPW_MX; ++tl) {
-      const u32x4 c = T.v[tl];
-      const float s = e8m0_scale(T.sc[tl]);
-      const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x4 av = dec_fp4x8(cw[j], s);
-        acc[tl] = mfma16(av, bf[j][0], acc[tl]);
-        acc[tl] = mfma16(av, bf[j][1], acc[tl]);
-      }
+      acc[tl] = mfma_mx(T.v[tl], T.sc[tl], B.hi[0], B.hi[1], B.sc, 0, acc[tl]);
+      acc[tl] = mfma_mx(T.v[tl], T.sc[tl], B.lo[0], B.lo[1], B.sc, 1, acc[tl]);
     }
   } else {
 #pragma unroll
     for (int tl = 0; tl < SH::TPW_BF; ++tl)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[tl] = mfma16(T.v[tl * 4 + j], bf[j][0], acc[tl]);
-        acc[tl] = mfma16(T.v[tl * 4 + j], bf[j][1], acc[tl]);
+        acc[tl] = mfma16(T.v[tl * 4 + j], B.f[j][0], acc[tl]);
+        acc[tl] = mfma16(T.v[tl * 4 + j], B.f[j][1], acc[tl]);
       }
   }
 }
@@ -983,10 +1144,13 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
   route(a, S, wave, lane, tid);
   const int U = __builtin_amdgcn_readfirstlane(S.nw);
 
-  // B fragments of this wave's H windows (the raw block), used by every item; the shared
-  // expert's tiles are bf16 and take the bf16 K order
+  // B operands of this wave's H windows (the raw block), used by every item: bf16 hi/lo
+  // fragments (bf16 layers and the shared expert's bf16 tiles), MX-fp8 hi/lo operands (mxfp4
+  // routed experts)
   u32x4 xb[WPW][4][2];
-  gu_load_xb<WPW>(xb, (MX && b < n_sh) ? a.xfrag_nat : a.xfrag, win0, active, lane);
+  XMX<WPW> xm;
+  if (!MX || b < n_sh) gu_load_xb<WPW>(xb, MX ? a.xfrag_nat : a.xfrag, win0, active, lane);
+  if (MX && b >= n_sh) gu_load_xmx<WPW>(xm, a.xfrag, win0, active, lane);
 
   const int ipe = I / (16 * (MX ? GU_MX_RT : 1));
   const int n_gu = U * ipe;
@@ -994,7 +1158,7 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
     f32x4 acc[GU_MX_RT][2];
     gu_math_bf16<WPW>(acc, Ts, xb);
     gu_epilogue<true>(a, S, acc, 1, U, b * 16, false, wave, lane, tid);
-    if (MX) gu_load_xb<WPW>(xb, a.xfrag, win0, active, lane);
+    if (MX) gu_load_xmx<WPW>(xm, a.xfrag, win0, active, lane);
   }
   // Routed items (see make_sched). Step h: item h is in T[h % 2] with its loads in flight; the
   // loads of item h + 1 are issued; thread 0 stores item h + 2 into the ring (static, or claimed
@@ -1019,8 +1183,8 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
     __builtin_amdgcn_sched_barrier(0);
     {
       f32x4 acc[GU_MX_RT][2];
-      gu_math<WPW, MX>(acc, T0, xb);
-      gu_epilogue<NAT>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid, (h + 2) & 3, &n2);
+      gu_math<WPW, MX>(acc, T0, xb, xm);
+      gu_epilogue<NAT, MX>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid, (h + 2) & 3, &n2);
     }
     if (n1 >= n_gu) break;
     d0 = gu_desc<MX>(a, wk, n2, n_gu, ipe);
@@ -1032,8 +1196,8 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
     __builtin_amdgcn_sched_barrier(0);
     {
       f32x4 acc[GU_MX_RT][2];
-      gu_math<WPW, MX>(acc, T1, xb);
-      gu_epilogue<NAT>(a, S, acc, d1.ntile, d1.u, d1.row0, true, wave, lane, tid, (h + 3) & 3, &n1);
+      gu_math<WPW, MX>(acc, T1, xb, xm);
+      gu_epilogue<NAT, MX>(a, S, acc, d1.ntile, d1.u, d1.row0, true, wave, lane, tid, (h + 3) & 3, &n1);
     }
     if (n2 >= n_gu) break;
   }
@@ -1056,7 +1220,7 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   const uint32_t E = a.E;
   const rsrc_t rw = buf_rsrc(a.wd, MX ? E * H * (I / 2) : E * H * I * 2);
   const rsrc_t rs = buf_rsrc(a.sd, MX ? E * H * (I / 32) : 0);
-  const rsrc_t raf = buf_rsrc(a.afrag, (uint32_t)a.umax * (I / 32) * 2048);
+  const rsrc_t raf = buf_rsrc(a.afrag, MX ? (uint32_t)a.umax * (I / WIN) * MXW : (uint32_t)a.umax * (I / 32) * 2048);
   if (b < n_sh) dn_load_bf16<NWIN>(Ts, buf_rsrc(a.shd, H * Is * 2), (uint32_t)(b * 16 * SH::TPI_BF * Is * 2), Is, wave, lane);
 
   // the routing tables, up to umax entries regardless of U, in one memory round trip
@@ -1070,10 +1234,10 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   const int ipe = H / (16 * (MX ? SH::TPI_MX : SH::TPI_BF));
   const int n_dn = U * ipe;
   if (b < n_sh) {
-    u32x4 bf[4][2];
-    dn_load_b<NWIN>(bf, buf_rsrc(a.afrag_sh, (Is / 32) * 2048), 0u, wave, lane);
+    DBF bs;
+    dn_load_b<NWIN>(bs.f, buf_rsrc(a.afrag_sh, (Is / 32) * 2048), 0u, wave, lane);
     f32x4 acc[SH::TPW_MX];
-    dn_math<NWIN, false>(acc, Ts, bf);
+    dn_math<NWIN, false>(acc, Ts, bs);
     dn_store_partial<NWIN>(S, acc, SH::TPW_BF, wave, lane);
     dn_epilogue<NWIN>(a, S, SH::TPI_BF, SH::TPW_BF, U, false, b * 16 * SH::TPI_BF, tid);
   }
@@ -1084,16 +1248,16 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   if (q0 >= n_dn) return;  // every later item is past the end too
   const Woken wk = load_woken(S, lane);
   DNItem<NWIN> T0, T1;
-  u32x4 b0[4][2], b1[4][2];
+  DnB<MX> b0, b1;
   DNDesc e0 = dn_desc<NWIN, MX>(a, wk, q0, n_dn, ipe), e1;
   dn_load<NWIN, MX>(T0, rw, rs, e0, I, wave, lane);
-  dn_load_b<NWIN>(b0, raf, (uint32_t)(e0.u * (I / 32) * 2048), wave, lane);
+  dn_load_bb<NWIN, MX>(b0, raf, e0.u, I, wave, lane);
   int n1 = static_item(q, 1), n2;  // items h + 1 and h + 2
   uint32_t ca = 0, cb = 0;         // claims in flight (thread 0): items h + 2 / h + 3
   for (int h = 0;; h += 2) {
     e1 = dn_desc<NWIN, MX>(a, wk, n1, n_dn, ipe);  // a valid stand-in past the end
     dn_load<NWIN, MX>(T1, rw, rs, e1, I, wave, lane);
-    dn_load_b<NWIN>(b1, raf, (uint32_t)(e1.u * (I / 32) * 2048), wave, lane);
+    dn_load_bb<NWIN, MX>(b1, raf, e1.u, I, wave, lane);
     if (tid == 0) {
       S.claim[(h + 2) & 3] = is_static(q, h + 2) ? static_item(q, h + 2) : pool_item(q, ca);
       if (!is_static(q, h + 4)) ca = claim_raw(q.ctr);
@@ -1108,7 +1272,7 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
     if (n1 >= n_dn) break;
     e0 = dn_desc<NWIN, MX>(a, wk, n2, n_dn, ipe);
     dn_load<NWIN, MX>(T0, rw, rs, e0, I, wave, lane);
-    dn_load_b<NWIN>(b0, raf, (uint32_t)(e0.u * (I / 32) * 2048), wave, lane);
+    dn_load_bb<NWIN, MX>(b0, raf, e0.u, I, wave, lane);
     if (tid == 0) {
       S.claim[(h + 3) & 3] = is_static(q, h + 3) ? static_item(q, h + 3) : pool_item(q, cb);
       if (!is_static(q, h + 5)) cb = claim_raw(q.ctr);
