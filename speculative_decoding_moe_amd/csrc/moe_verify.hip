@@ -5,14 +5,16 @@
 // stream-ordered launches; the kernel boundaries publish each phase's results to every CU:
 //
 //   k_router    (expert tile, H slice) items: fp32 MFMA partial logits and sums of squares; the
-//               block is also packed as bf16 hi/lo MFMA B-operand fragments.
+//               block is also packed as the experts' B operands (bf16 hi/lo fragments, or MX-fp8
+//               hi/lo operands for mxfp4 routed experts).
 //   k_gateup    every workgroup first computes the routing in LDS: RMSNorm factor, logits, top-K
 //               per token (ties to the lower expert), softmax over the K, the woken-expert union
 //               (wave ballot + prefix count) and the weight table. Then (woken expert, row tile)
-//               items, assigned statically and balanced: the expert's gate and up rows are
-//               streamed from HBM once (128-bit nontemporal loads, the next item prefetched) and
-//               applied to all 16 token columns with MFMA; SwiGLU, the routing weight and the
-//               hi/lo split are fused into the epilogue, which writes the down B operand.
+//               items, assigned statically and balanced, the last rounds claimed: the expert's
+//               gate and up rows are streamed from HBM once (128-bit nontemporal loads, the next
+//               item prefetched) and applied to all 16 token columns on the matrix cores; SwiGLU,
+//               the routing weight and the hi/lo split are fused into the epilogue, which writes
+//               the down B operand.
 //   k_down      (woken expert, row group) items: W_down streamed once, partial rows per (token,
 //               slot).
 //   k_combine   y[t] = sum_j P[t, j] + P[t, shared] (+ x[t]), fixed slot order.
@@ -24,13 +26,14 @@
 // Tokens are the MFMA N dimension (16 columns; unused columns are explicit zeros written every
 // call), expert rows the M dimension, the hidden / intermediate size the K dimension. MFMA work
 // is free next to the HBM stream, so every expert is applied to all 16 columns; columns of tokens
-// not routed to it carry weight 0. Activations enter MFMA as bf16 hi + lo pairs (~2^-17 relative).
+// not routed to it carry weight 0. Activations enter as hi + lo pairs: bf16 (~2^-17 relative)
+// against bf16 weights, MX-fp8 (e4m3 with a scale per 32 values) against mxfp4 weights.
 //
-// K-index mapping of every MFMA tile: the reduction dimension is cut into windows of 128; in
+// K-index mapping of the bf16 MFMA tiles: the reduction dimension is cut into windows of 128; in
 // window w, k-step j (0..3), lane l = c + 16 q (c = row or token column, q = 0..3) holds the 8
-// values at 128 w + 32 j + 8 q + (0..7) for bf16 layers (a lane quad reads 64 contiguous bytes
-// per row and instruction) and at 128 w + 32 q + 8 j + (0..7) for mxfp4 layers (a lane holds one
-// whole 32-value block and its single scale byte).
+// values at 128 w + 32 j + 8 q + (0..7) (a lane quad reads 64 contiguous bytes per row and
+// instruction). mxfp4 weights go to the scaled instruction whole: in window w lane l holds the
+// 32-value block 4 w + q of row c and its scale byte (see the MX-fp8 helpers for the B side).
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <atomic>
@@ -99,16 +102,6 @@ __device__ __forceinline__ void pack8(const uint32_t (&v)[8], u32x4& o) {
   o.x = v[0] | (v[1] << 16); o.y = v[2] | (v[3] << 16); o.z = v[4] | (v[5] << 16); o.w = v[6] | (v[7] << 16);
 }
 
-// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) -> eight bf16 scaled by
-// `scale` (a power of two built from the e8m0 byte).
-__device__ __forceinline__ u32x4 dec_fp4x8(uint32_t c, float scale) {
-  u32x4 r;
-  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 0));
-  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 1));
-  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 2));
-  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3));
-  return r;
-}
 __device__ __forceinline__ float e8m0_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
 
 // ---- MX-fp8 operands of the scaled matrix-core instruction (mxfp4 layers) ----
@@ -188,8 +181,7 @@ __device__ __forceinline__ f32x4 mfma_mx(u32x4 a, uint32_t sa, u32x4 b0, u32x4 b
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 // Offset (in values) of lane quad q, k-step j inside a 128-wide window.
-template <bool NAT>
-__device__ __forceinline__ int kofs(int j, int q) { return NAT ? 32 * j + 8 * q : 32 * q + 8 * j; }
+__device__ __forceinline__ int kofs(int j, int q) { return 32 * j + 8 * q; }
 
 // (value, index) maximum with equal values going to the lower index.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float ov, int oi) {
@@ -225,8 +217,9 @@ struct Args {
                       // apart (zeroed by the router)
   int32_t* tab_woken; // [umax] woken expert ids, ascending
   int8_t* tab_slot;   // [umax][16] slot of token t for woken expert u, or -1
-  u32x4* xfrag;   // (H/32) k-steps x {hi, lo} x 64 lanes, the layer's K order
-  u32x4* xfrag_nat;  // the same in the bf16 K order (mxfp4 layers with a shared expert)
+  u32x4* xfrag;   // the block's B operands: bf16 layers (H/32) k-steps x {hi, lo} x 64 lanes;
+                  // mxfp4 layers (H/128) MX-fp8 windows of MXW bytes
+  u32x4* xfrag_sh;   // bf16 hi/lo fragments for the shared expert of mxfp4 layers
   float* plog;    // [hs][16][E] partial raw logits
   float* psq;     // [hs][16] partial sums of squares
   u32x4* afrag;   // [umax][(I/32) x {hi, lo} x 64 lanes]
@@ -254,13 +247,12 @@ struct alignas(16) Smem {
 // ------------------------------------------------------------------------------------------
 // router item (expert tile, H slice) with fp32 MFMA 16x16x4
 // ------------------------------------------------------------------------------------------
-// k-step s of the block as bf16 hi/lo MFMA B fragments in the K order of NAT
-template <bool NAT>
+// k-step s of the block as bf16 hi/lo MFMA B fragments
 __device__ __forceinline__ void write_xfrag(const float* x, u32x4* dst, int H, int k, int s, int lane) {
   const int t = lane & 15, qq = lane >> 4, w = s >> 2, j = s & 3;
   uint32_t hi[8], lo[8];
   if (t < k) {
-    const float* src = x + (size_t)t * H + w * WIN + kofs<NAT>(j, qq);
+    const float* src = x + (size_t)t * H + w * WIN + kofs(j, qq);
     const float4 v0 = *reinterpret_cast<const float4*>(src);
     const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
     const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -307,7 +299,7 @@ struct RouterSmem {
   float rsq[NW][64];
 };
 
-template <bool NAT>
+template <bool MX>
 __device__ void router_item(const Args& a, RouterSmem& S, int r, int wave, int lane, int tid) {
   const int H = a.H, E = a.E, k = a.k;
   const int tile = r % a.ntile_e, hsi = r / a.ntile_e;
@@ -352,13 +344,13 @@ __device__ void router_item(const Args& a, RouterSmem& S, int r, int wave, int l
   // B-operand fragments of the raw block, spread over the router's waves: bf16 hi/lo k-steps
   // (bf16 layers, and the shared expert of mxfp4 layers), MX-fp8 windows (mxfp4 routed experts)
   const int nr = a.ntile_e * a.hs;
-  if (NAT) {
-    for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) write_xfrag<true>(a.x, a.xfrag, H, k, s, lane);
+  if (!MX) {
+    for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) write_xfrag(a.x, a.xfrag, H, k, s, lane);
   } else {
     for (int w = r + nr * (tid >> 6); w < H / WIN; w += nr * NW)
       write_xmx(a.x, reinterpret_cast<uint8_t*>(a.xfrag), H, k, w, lane);
     if (a.Is > 0)
-      for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) write_xfrag<true>(a.x, a.xfrag_nat, H, k, s, lane);
+      for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) write_xfrag(a.x, a.xfrag_sh, H, k, s, lane);
   }
 }
 
@@ -662,7 +654,7 @@ __device__ __forceinline__ void gu_load_mx(GUItem<WPW>& T, const GURes& R, const
 // the store as down-projection B fragments (rows row0 .. row0 + 16 ntile of expert slot `u`):
 // bf16 hi/lo fragments, or (MX8: routed items of mxfp4 layers, 32 rows = one 32-value block of
 // the down projection's reduction dimension) MX-fp8 hi/lo operands with their block scales.
-template <bool NAT, bool MX8 = false>
+template <bool MX8 = false>
 __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 (&acc)[GU_MX_RT][2],
                                             int ntile, int u, int row0, bool routed, int wave,
                                             int lane, int tid, int ring = -1, int* next = nullptr) {
@@ -717,7 +709,7 @@ __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 
     }
     const int R = row0 + 16 * tl + 8 * half;
     const int w = R / WIN, o = R % WIN;
-    const int j = NAT ? o / 32 : (o % 32) / 8, q = NAT ? (o % 32) / 8 : o / 32;
+    const int j = o / 32, q = (o % 32) / 8;
     const int s = w * 4 + j;
     const int I = routed ? a.I : a.Is;
     u32x4* dst = routed ? a.afrag + (size_t)u * (I / 32) * 128 : a.afrag_sh;
@@ -1104,18 +1096,17 @@ __global__ void __launch_bounds__(256) k_combine(Args a) {
 // ------------------------------------------------------------------------------------------
 // kernels
 // ------------------------------------------------------------------------------------------
-template <bool NAT>
+template <bool MX>
 __global__ void __launch_bounds__(NTH) k_router(Args a) {
   __shared__ RouterSmem S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   if (blockIdx.x == 0 && tid < 2 * NGRP) a.ctr[tid * CTR_STRIDE] = 0u;  // this layer's pools start at 0
-  router_item<NAT>(a, S, blockIdx.x, wave, lane, tid);
+  router_item<MX>(a, S, blockIdx.x, wave, lane, tid);
 }
 
 template <int WPW, bool MX>
 __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
-  constexpr bool NAT = !MX;  // K mapping of this layer's fragments
   __shared__ Smem S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
@@ -1149,7 +1140,7 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
   // routed experts)
   u32x4 xb[WPW][4][2];
   XMX<WPW> xm;
-  if (!MX || b < n_sh) gu_load_xb<WPW>(xb, MX ? a.xfrag_nat : a.xfrag, win0, active, lane);
+  if (!MX || b < n_sh) gu_load_xb<WPW>(xb, MX ? a.xfrag_sh : a.xfrag, win0, active, lane);
   if (MX && b >= n_sh) gu_load_xmx<WPW>(xm, a.xfrag, win0, active, lane);
 
   const int ipe = I / (16 * (MX ? GU_MX_RT : 1));
@@ -1157,7 +1148,7 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
   if (b < n_sh) {
     f32x4 acc[GU_MX_RT][2];
     gu_math_bf16<WPW>(acc, Ts, xb);
-    gu_epilogue<true>(a, S, acc, 1, U, b * 16, false, wave, lane, tid);
+    gu_epilogue(a, S, acc, 1, U, b * 16, false, wave, lane, tid);
     if (MX) gu_load_xmx<WPW>(xm, a.xfrag, win0, active, lane);
   }
   // Routed items (see make_sched). Step h: item h is in T[h % 2] with its loads in flight; the
@@ -1184,7 +1175,7 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
     {
       f32x4 acc[GU_MX_RT][2];
       gu_math<WPW, MX>(acc, T0, xb, xm);
-      gu_epilogue<NAT, MX>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid, (h + 2) & 3, &n2);
+      gu_epilogue<MX>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid, (h + 2) & 3, &n2);
     }
     if (n1 >= n_gu) break;
     d0 = gu_desc<MX>(a, wk, n2, n_gu, ipe);
@@ -1197,7 +1188,7 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
     {
       f32x4 acc[GU_MX_RT][2];
       gu_math<WPW, MX>(acc, T1, xb, xm);
-      gu_epilogue<NAT, MX>(a, S, acc, d1.ntile, d1.u, d1.row0, true, wave, lane, tid, (h + 3) & 3, &n1);
+      gu_epilogue<MX>(a, S, acc, d1.ntile, d1.u, d1.row0, true, wave, lane, tid, (h + 3) & 3, &n1);
     }
     if (n2 >= n_gu) break;
   }
@@ -1438,7 +1429,7 @@ __device__ __forceinline__ void head_xb(u32x4 (&xb)[WPW][4][2], const float* h, 
   for (int wi = 0; wi < WPW; ++wi)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float* src = row + wi * WIN + kofs<true>(j, q);
+      const float* src = row + wi * WIN + kofs(j, q);
       v[wi][j][0] = *reinterpret_cast<const float4*>(src);
       v[wi][j][1] = *reinterpret_cast<const float4*>(src + 4);
     }
@@ -1960,7 +1951,7 @@ __global__ void __launch_bounds__(1024) k_accept_hist(const int32_t* acc, int n_
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t ctr, tab_n, tab_woken, tab_slot, xfrag, xfrag_nat, plog, psq, afrag, afrag_sh, part, total;
+  size_t ctr, tab_n, tab_woken, tab_slot, xfrag, xfrag_sh, plog, psq, afrag, afrag_sh, part, total;
   int umax, hs;
 };
 
@@ -1977,7 +1968,7 @@ Layout make_layout(const moe_layer* L, int k) {
   o.tab_woken = off; off = align256(off + (size_t)o.umax * 4);
   o.tab_slot = off;  off = align256(off + (size_t)o.umax * KMAX);
   o.xfrag = off;    off = align256(off + H * 64);
-  o.xfrag_nat = off; off = align256(off + H * 64);
+  o.xfrag_sh = off; off = align256(off + H * 64);
   o.plog = off;     off = align256(off + (size_t)o.hs * KMAX * E * 4);
   o.psq = off;      off = align256(off + (size_t)o.hs * KMAX * 4);
   o.afrag = off;    off = align256(off + (size_t)o.umax * I * 64);
@@ -2040,7 +2031,7 @@ bool launch_layer(const Args& a, hipStream_t s, void* const* ev) {
   // one workgroup per CU; never fewer workgroups than shared-expert items (one each)
   const int cus = std::max(num_cus(), std::max(a.Is / 16, a.H / 64));
   if (!mark(ev, 0, s)) return false;
-  k_router<!MX><<<a.ntile_e * a.hs, NTH, 0, s>>>(a);
+  k_router<MX><<<a.ntile_e * a.hs, NTH, 0, s>>>(a);
   if (!mark(ev, 1, s)) return false;
   k_gateup<WPW, MX><<<cus, NTH, 0, s>>>(a);
   if (!mark(ev, 2, s)) return false;
@@ -2117,7 +2108,7 @@ static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint
   a.shg = (const uint8_t*)L->sh_gate; a.shu = (const uint8_t*)L->sh_up; a.shd = (const uint8_t*)L->sh_down;
   a.tab_n = (int32_t*)(ws + lay.tab_n); a.ctr = (uint32_t*)(ws + lay.ctr); a.tab_woken = (int32_t*)(ws + lay.tab_woken);
   a.tab_slot = (int8_t*)(ws + lay.tab_slot);
-  a.xfrag = (u32x4*)(ws + lay.xfrag); a.xfrag_nat = (u32x4*)(ws + lay.xfrag_nat); a.plog = (float*)(ws + lay.plog); a.psq = (float*)(ws + lay.psq);
+  a.xfrag = (u32x4*)(ws + lay.xfrag); a.xfrag_sh = (u32x4*)(ws + lay.xfrag_sh); a.plog = (float*)(ws + lay.plog); a.psq = (float*)(ws + lay.psq);
   a.afrag = (u32x4*)(ws + lay.afrag); a.afrag_sh = (u32x4*)(ws + lay.afrag_sh); a.part = (float*)(ws + lay.part);
   a.H = L->hidden; a.E = L->n_experts; a.K = L->top_k; a.I = L->inter; a.Is = L->shared_inter; a.k = k;
   a.hs = lay.hs; a.ntile_e = (L->n_experts + 15) / 16; a.umax = lay.umax;
