@@ -54,7 +54,7 @@ constexpr int MAX_K = 16;
 constexpr int MAX_U = KMAX * MAX_K;  // woken experts at most
 constexpr int HS_MAX = 4;            // H slices of the router at most
 static_assert(MAX_E <= NTH, "routing assigns one expert per thread");
-constexpr int GU_MX_RT = 2;       // gate/up row tiles per mxfp4 item (bf16: 1)
+constexpr int GU_MX_RT = 2;  // gate/up row tiles per mxfp4 item (bf16: 1); even, <= 4
 constexpr int AM_CHUNK = 8192;    // argmax values per workgroup
 
 
@@ -665,8 +665,8 @@ __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 
       *reinterpret_cast<f32x4*>(&S.red[((wave * GU_MX_RT + tl) * 2 + 1) * 256 + lane * 4]) = acc[tl][1];
     }
   __syncthreads();
-  if (tid < ntile * 256) {
-    const int tl = tid >> 8, p = tid & 255;
+  for (int i = tid; i < ntile * 256; i += NTH) {
+    const int tl = i >> 8, p = i & 255;
     float g = 0.f, up = 0.f;
 #pragma unroll
     for (int wv = 0; wv < NW; ++wv) {
@@ -683,18 +683,18 @@ __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (MX8) {
-    // thread (half h, column c) -> rows 16 h .. 16 h + 15 of the block; the block maximum pairs
-    // the two halves (lanes c and c + 16 of wave 0)
-    if (tid < 2 * KMAX) {
-      const int c = tid & 15, h = tid >> 4;
+    // thread (block bb, half h, column c) -> rows 32 bb + 16 h .. + 15 of the item; the block
+    // maximum pairs the two halves (lanes c and c + 16 of the same wave)
+    if (tid < 16 * ntile) {
+      const int c = tid & 15, h = (tid >> 4) & 1, bb = tid >> 5;
       float v[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = S.act[h][(c + 16 * (j >> 2)) * 4 + (j & 3)];
+      for (int j = 0; j < 16; ++j) v[j] = S.act[2 * bb + h][(c + 16 * (j >> 2)) * 4 + (j & 3)];
       uint32_t hi[4], lo[4];
       int eh, el;
       mx8_quant<16, true>(v, hi, lo, eh, el);
       uint8_t* win = reinterpret_cast<uint8_t*>(a.afrag) + ((size_t)u * (a.I / WIN) + row0 / WIN) * MXW;
-      mx8_store16(win, c, (row0 % WIN) / 32, h, hi, lo, eh, el);
+      mx8_store16(win, c, (row0 % WIN) / 32 + bb, h, hi, lo, eh, el);
     }
     return;
   }
