@@ -1151,46 +1151,53 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
     gu_epilogue(a, S, acc, 1, U, b * 16, false, wave, lane, tid);
     if (MX) gu_load_xmx<WPW>(xm, a.xfrag, win0, active, lane);
   }
-  // Routed items (see make_sched). Step h: item h is in T[h % 2] with its loads in flight; the
-  // loads of item h + 1 are issued; thread 0 stores item h + 2 into the ring (static, or claimed
-  // two steps earlier) and claims item h + 4 when that one is claimed; the epilogue reads item
-  // h + 2 back for the next step.
+  // Routed items (see make_sched), D items deep: at step h item h is multiplied while the loads
+  // of items h + 1 .. h + D - 1 are in flight (those of item h + D - 1 issued at the top of the
+  // step). Thread 0 stores the index of item h + D into the LDS ring (static, or claimed two steps
+  // earlier) and claims item h + D + 2 when that one is claimed; the epilogue reads item h + D back
+  // for the next step's loads. Claims whose step would be negative are taken before the loop.
+  // Two in flight: for mxfp4 items (70 KB) four were measured slower (more stand-in loads when a
+  // workgroup has few items, and no gain in the steady state).
+  constexpr int D = 2;
   const Sched q = make_sched(n_gu, G, b, n_sh, a.ctr);
   const int r0 = static_item(q, 0);
   if (r0 >= n_gu) return;  // every later item is past the end too
   const Woken wk = load_woken(S, lane);
-  GUItem<WPW> T0, T1;
-  GUDesc d0 = gu_desc<MX>(a, wk, r0, n_gu, ipe), d1;
-  gu_load<WPW, MX>(T0, R, d0, H, vbc, vbs);
-  int n1 = static_item(q, 1), n2;  // items h + 1 and h + 2
-  uint32_t ca = 0, cb = 0;         // claims in flight (thread 0): items h + 2 / h + 3
-  for (int h = 0;; h += 2) {
-    d1 = gu_desc<MX>(a, wk, n1, n_gu, ipe);  // a valid stand-in past the end
-    gu_load<WPW, MX>(T1, R, d1, H, vbc, vbs);
-    if (tid == 0) {
-      S.claim[(h + 2) & 3] = is_static(q, h + 2) ? static_item(q, h + 2) : pool_item(q, ca);
-      if (!is_static(q, h + 4)) ca = claim_raw(q.ctr);
+  GUItem<WPW> T[D];
+  GUDesc dd[D];
+  int nx[D];
+#pragma unroll
+  for (int j = 0; j + 1 < D; ++j) {
+    nx[j] = static_item(q, j);
+    dd[j] = gu_desc<MX>(a, wk, nx[j], n_gu, ipe);  // a valid stand-in past the end
+    gu_load<WPW, MX>(T[j], R, dd[j], H, vbc, vbs);
+  }
+  int nload = static_item(q, D - 1);  // item of the next step whose loads are issued
+  uint32_t cl[2] = {0u, 0u};          // claims in flight (thread 0)
+  if (tid == 0 && q.claims)
+    for (int X = max(q.S, D); X < D + 2; ++X) cl[(X - D) & 1] = claim_raw(q.ctr);
+  for (int h = 0;; h += D) {
+    bool done = false;
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+      const int st = h + r;
+      const int jl = (r + D - 1) % D;  // buffer of item st + D - 1
+      nx[jl] = nload;
+      dd[jl] = gu_desc<MX>(a, wk, nload, n_gu, ipe);
+      gu_load<WPW, MX>(T[jl], R, dd[jl], H, vbc, vbs);
+      if (tid == 0) {
+        S.claim[(st + D) & 3] = is_static(q, st + D) ? static_item(q, st + D) : pool_item(q, cl[st & 1]);
+        if (!is_static(q, st + D + 2)) cl[st & 1] = claim_raw(q.ctr);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f32x4 acc[GU_MX_RT][2];
+        gu_math<WPW, MX>(acc, T[r], xb, xm);
+        gu_epilogue<MX>(a, S, acc, dd[r].ntile, dd[r].u, dd[r].row0, true, wave, lane, tid, (st + D) & 3, &nload);
+      }
+      if (nx[(r + 1) % D] >= n_gu) { done = true; break; }  // the next step's item is past the end
     }
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      f32x4 acc[GU_MX_RT][2];
-      gu_math<WPW, MX>(acc, T0, xb, xm);
-      gu_epilogue<MX>(a, S, acc, d0.ntile, d0.u, d0.row0, true, wave, lane, tid, (h + 2) & 3, &n2);
-    }
-    if (n1 >= n_gu) break;
-    d0 = gu_desc<MX>(a, wk, n2, n_gu, ipe);
-    gu_load<WPW, MX>(T0, R, d0, H, vbc, vbs);
-    if (tid == 0) {
-      S.claim[(h + 3) & 3] = is_static(q, h + 3) ? static_item(q, h + 3) : pool_item(q, cb);
-      if (!is_static(q, h + 5)) cb = claim_raw(q.ctr);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      f32x4 acc[GU_MX_RT][2];
-      gu_math<WPW, MX>(acc, T1, xb, xm);
-      gu_epilogue<MX>(a, S, acc, d1.ntile, d1.u, d1.row0, true, wave, lane, tid, (h + 3) & 3, &n1);
-    }
-    if (n2 >= n_gu) break;
+    if (done) break;
   }
 }
 
