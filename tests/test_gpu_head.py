@@ -71,6 +71,8 @@ def _head(B, wl):
     (128, 17, 1),       # one window (seven idle waves), two tiles, the second holds one row
     (1024, 33, 16),     # three tiles: an item whose second tile is past the head
     (512, 70001, 9),    # many items per workgroup and a ragged tail
+    (128, 5, 3),        # fewer rows than one tile
+    (2048, 16, 16),     # exactly one tile, all positions
 ])
 def test_head_parity_small(B, H, V, n):
     wl = _wl(H, V, n)

@@ -185,3 +185,21 @@ def test_accept_histogram_matches_oracle(B):
         assert np.array_equal(hist.cpu().numpy(), ref_h)
         if n_draft:
             assert np.array_equal(surv.cpu().numpy(), ref_s)
+
+
+@pytest.mark.parametrize("V", [1, 2, 5])
+def test_accept_sample_tiny_vocabularies(B, V):
+    """Vocabularies smaller than one float4 and than one chunk's first wave: with V = 1 every
+    draft of id 0 is kept and the token is 0."""
+    rng = np.random.default_rng(11 + V)
+    n = 3
+    tl = rng.standard_normal((n + 1, V)).astype(np.float32)
+    dl = (tl[:n] + rng.standard_normal((n, V)) * 0.3).astype(np.float32)
+    for rep in range(6):
+        draft = rng.integers(0, V, n).astype(np.int32)
+        ua = rng.random(n).astype(np.float32)
+        us = rng.random(n + 1).astype(np.float32)
+        got = run_sample(B, tl, dl, draft, 1.0, ua, us)
+        check_sample(tl, dl, draft, 1.0, ua, us, got)
+        if V == 1:
+            assert got == (n, 0)
