@@ -13,7 +13,8 @@
  *   moe_verify_block -- one MoE layer over a block of k <= 16 tokens: fp32 router logits,
  *                       top-K with softmax renormalised over the K, woken-expert union, grouped
  *                       SwiGLU experts (bf16 or mxfp4 weights), weighted combine with the shared
- *                       expert, optional RMSNorm pre-norm and residual add;
+ *                       expert, optional RMSNorm pre-norm and residual add; also the blocks of
+ *                       many sequences verified together (up to 1024 tokens, bf16 weights);
  *   accept_prefix    -- per-position target argmax and greedy longest-prefix acceptance;
  *   moe_pack_weights -- rearranges row-major expert matrices into the tiled layout the verify
  *                       block streams (done once, when the weights are loaded).
@@ -83,7 +84,8 @@ enum {
 enum {
   MOE_PRE_RMSNORM = 1u, /* x_hat = x / sqrt(mean(x^2) + rms_eps) (unit gain) before the router
                            and the experts, as in a pre-norm stack of MoE layers              */
-  MOE_RESIDUAL = 2u     /* add the un-normalised input x to the MoE output                    */
+  MOE_RESIDUAL = 2u,    /* add the un-normalised input x to the MoE output                    */
+  MOE_GATHER = 4u       /* use the gathered path (below) for any k; implied for k > 16         */
 };
 
 /* One MoE layer (a host struct, read only during the call; the arrays are device memory).
@@ -118,22 +120,31 @@ typedef struct moe_layer {
   const void* sh_down;
 } moe_layer;
 
-/* Bytes of device workspace moe_verify_block needs for blocks of up to k_max tokens
- * (0 if the layer description is invalid). Host only. */
+/* Bytes of device workspace moe_verify_block needs for calls of up to k_max tokens, on either
+ * path, 1 <= k_max <= 1024 (0 if the layer description is invalid, k_max is out of range, or
+ * k_max > 16 with mxfp4 weights). Host only. */
 size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max);
 
 /* One MoE layer over a verify block.
  *   x        fp32 [k][H]  block hidden states (input; not modified)
- *   k        1 <= k <= 16 block tokens (a block carries 1 known token and up to 15 drafted
- *            ones: "Speculating on a Strix Halo", section "Speculative decoding")
- *   flags    MOE_PRE_RMSNORM | MOE_RESIDUAL
+ *   k        1 <= k <= 1024 tokens. One sequence's block carries 1 known token and up to 15
+ *            drafted ones ("Speculating on a Strix Halo", section "Speculative decoding"); the
+ *            blocks of several sequences may be stacked into one call, since every token routes
+ *            on its own. With k > 16 (or MOE_GATHER) the call takes the gathered path: the
+ *            tokens are sorted by expert (a deterministic counting sort) and each woken expert
+ *            is applied to its own tokens only, 32 token columns per weight pass. That is the
+ *            regime of batched serving, where the verify step becomes compute-heavy
+ *            (DFlash-on-MI355X article, section "Results: Throughput and Speedup"). The
+ *            gathered path takes bf16 layers (an mxfp4 layer returns MOE_ERR_DTYPE there).
+ *   flags    MOE_PRE_RMSNORM | MOE_RESIDUAL | MOE_GATHER
  *   y        fp32 [k][H]  output; must not overlap x or the workspace
  *   topk_ids int32 [k][K] or NULL: each token's experts, descending router logit, equal logits
  *            to the lower expert index
  *   topk_w   fp32  [k][K] or NULL: the matching weights, softmax over the K selected logits
  *   n_woken  int32 [1]    or NULL: size of the union of the block's routed experts (shared
  *            expert not counted)
- *   workspace, ws_bytes: device scratch of at least moe_verify_workspace_size(layer, k) bytes;
+ *   workspace, ws_bytes: device scratch of at least moe_verify_workspace_size(layer, k) bytes
+ *            (k_max = 1024 with bf16 weights: about 80 MB at H 2048, E 256, K 8, I 512);
  *            its contents need no initialisation and are overwritten.
  * Returns MOE_OK or an MOE_ERR_* code (nothing is enqueued on error). */
 int moe_verify_block(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
@@ -142,8 +153,9 @@ int moe_verify_block(const moe_layer* layer, const float* x, int32_t k, uint32_t
 
 /* moe_verify_block with per-kernel timing, for profiling: the same computation and launches;
  * additionally records events[i] (hipEvent_t created and owned by the caller; any entry may be
- * NULL) on hip_stream at the kernel boundaries: [0] before the router kernel, [1] after it,
- * [2] after the gate/up kernel, [3] after the down kernel, [4] after the combine. A failing
+ * NULL) on hip_stream at the kernel boundaries: [0] before the router kernel, [1] after it
+ * (gathered path: after the router, top-K and permutation kernels), [2] after the gate/up
+ * kernel, [3] after the down kernel, [4] after the combine. A failing
  * event record returns MOE_ERR_HIP. */
 int moe_verify_block_timed(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
                            int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,

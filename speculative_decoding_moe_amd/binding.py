@@ -17,7 +17,7 @@ MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_ALIGN = -1, -2, -3, -4
 MOE_ERR_WORKSPACE, MOE_ERR_ALIAS, MOE_ERR_HIP, MOE_ERR_ARG = -5, -6, -7, -8
 MOE_W_BF16, MOE_W_MXFP4 = 0, 1
 MOE_LAYOUT_TILED = 1
-MOE_PRE_RMSNORM, MOE_RESIDUAL = 1, 2
+MOE_PRE_RMSNORM, MOE_RESIDUAL, MOE_GATHER = 1, 2, 4
 
 EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "moe_verify_block_timed",
            "moe_pack_weights", "accept_prefix_workspace_size", "accept_prefix",

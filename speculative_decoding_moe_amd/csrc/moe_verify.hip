@@ -1953,6 +1953,608 @@ __global__ void __launch_bounds__(1024) k_accept_hist(const int32_t* acc, int n_
 }
 
 // ------------------------------------------------------------------------------------------
+// Gathered path: many sequences verified together (up to BT_MAX tokens per call). Each token
+// still routes on its own ("Speculating on a Strix Halo", section "What the pieces cost"), but
+// with hundreds of tokens nearly every expert wakes, each for a few dozen of them, so the
+// experts' B operands become per-expert token gathers (tokens sorted by expert, "Speculating on
+// a Strix Halo", section "The verify's own cost"):
+//
+//   k_brouter   (16-token tile, 16-expert tile) items, fp32 MFMA over the full H: raw logits,
+//               the RMSNorm factor, and each token's bf16 hi/lo B fragments (token-major).
+//   k_btopk     one wave per token: top-K (ties to the lower expert), softmax over the K.
+//   k_bperm     one workgroup: per-expert token bitmasks (LDS), counts, a scan over experts for
+//               the list offsets, then each (token, slot) pair's list position = expert offset
+//               + number of the expert's tokens below it. The list (tokens by expert, then
+//               token) is deterministic; the shared expert follows as slot U with every token.
+//   k_bexp<GU>  (woken slot u, column group, row block) items over a flat sequence of window
+//               ticks. Per tick every wave streams two 16-row A bands of one 128-wide window
+//               (gate + up rows: two K halves of 64-row items; down: two row tiles of 256-row
+//               items); the item's gathered token columns for that tick are loaded by all
+//               threads and staged through a two-slot LDS ring. Weights are requested BD - 1
+//               ticks ahead; the gate/up epilogue fuses the K-half reduction, SwiGLU with the
+//               RMSNorm factor and the routing weight, and stores the down B operands per list
+//               position; the down epilogue stores fp32 partial rows per list position.
+//   k_bcombine  y[t] = sum_j P[pos(t, j)] + P[shared(t)] (+ x[t]), fixed slot order.
+// ------------------------------------------------------------------------------------------
+constexpr int BT_MAX = 1024;      // tokens per gathered call
+constexpr int BTW = BT_MAX / 32;  // token-mask words per expert
+constexpr int BCG = 2;            // 16-token column tiles per gathered item
+constexpr int BD = 3;             // weight ticks in flight (loads issued BD - 1 ticks ahead)
+constexpr int BPERM_NTH = 1024;
+
+struct BArgs {
+  const float* x;
+  float* y;
+  int32_t* out_ids;
+  float* out_w;
+  int32_t* out_n;
+  const float* wr;
+  const uint8_t* wg;
+  const uint8_t* wu;
+  const uint8_t* wd;
+  const uint8_t* shg;
+  const uint8_t* shu;
+  const uint8_t* shd;
+  float* logits;    // [T][E] raw router logits (un-normalised input)
+  float* rinv;      // [T] RMSNorm factor (1 without pre-norm)
+  uint8_t* xg;      // [T][H/128][512 B] bf16 hi/lo B fragments of each token, k-step j, half hl,
+                    // lane quad q at ((j * 2 + hl) * 4 + q) * 16
+  int32_t* ids;     // [T][K]
+  float* wts;       // [T][K]
+  int32_t* tab;     // [0] U, [1] gate/up items, [2] down items
+  int32_t* ut;      // 5 arrays of E + 2: slot u -> expert (-1: shared), list offset, count,
+                    // gate/up item prefix, down item prefix (entry U + 1: totals)
+  int32_t* blist;   // [T K + T] token at list position p (positions T K + t: the shared expert)
+  float* bw;        // [T K + T] routing weight at position p (1 for the shared expert)
+  float* brv;       // [T K + T] RMSNorm factor of the token at position p
+  int32_t* bpos;    // [T][K] list position of (token, slot)
+  uint8_t* af;      // [(T K + T + 16)][I/128][512 B] down B operands per list position
+  float* part;      // [T K + T][H] fp32 partial rows per list position
+  int H, E, K, I, Is, T, pre_norm, residual;
+  float eps;
+};
+
+__device__ __forceinline__ int* ut_arr(const BArgs& a, int which) { return a.ut + which * (a.E + 2); }
+
+struct BRouterSmem {
+  float red[NW * 256];
+  float rsq[NW][64];
+};
+
+__global__ void __launch_bounds__(NTH) k_brouter(BArgs a) {
+  __shared__ BRouterSmem S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.H, E = a.E, T = a.T;
+  const int nte = (E + 15) / 16;
+  const int tt = blockIdx.x / nte, et = blockIdx.x % nte;
+  const int cpw = H / NW;  // a multiple of 16
+  const int c0 = wave * cpw;
+  const int row = lane & 15, q = lane >> 4;
+  const int e = et * 16 + row, t = tt * 16 + row;
+  const float* wrow = a.wr + (size_t)(e < E ? e : 0) * H;
+  const float* xrow = a.x + (size_t)(t < T ? t : 0) * H;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  for (int m = 0; m < cpw / 16; ++m) {
+    const int h = c0 + 16 * m + 4 * q;
+    float4 wv = *reinterpret_cast<const float4*>(wrow + h);
+    float4 xv = *reinterpret_cast<const float4*>(xrow + h);
+    if (e >= E) wv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t >= T) xv = make_float4(0.f, 0.f, 0.f, 0.f);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.x, xv.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.y, xv.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.z, xv.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.w, xv.w, acc, 0, 0, 0);
+    ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+  }
+  *reinterpret_cast<f32x4*>(&S.red[wave * 256 + lane * 4]) = acc;
+  S.rsq[wave][lane] = ss;
+  __syncthreads();
+  if (tid < 256) {  // D[i][j] in lane j + 16 (i / 4), element i % 4; i = expert, j = token
+    float d = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) d += S.red[w * 256 + tid];
+    const int l = tid >> 2, v = tid & 3;
+    const int tok = tt * 16 + (l & 15), ei = et * 16 + 4 * (l >> 4) + v;
+    if (tok < T && ei < E) a.logits[(size_t)tok * E + ei] = d;
+  }
+  if (et == 0 && tid < 16) {
+    float s = 0.f;
+    for (int w = 0; w < NW; ++w)
+      for (int qq = 0; qq < 4; ++qq) s += S.rsq[w][tid + 16 * qq];
+    const int tok = tt * 16 + tid;
+    if (tok < T) a.rinv[tok] = a.pre_norm ? 1.0f / sqrtf(s / (float)H + a.eps) : 1.0f;
+  }
+  // B fragments of the tile's tokens, windows et, et + nte, ... (256 threads per window)
+  const int nwt = H / WIN;
+  for (int w = et + nte * (tid >> 8); w < nwt; w += 2 * nte) {
+    const int r = tid & 255, c = r & 15, j = (r >> 4) & 3, qq = r >> 6;
+    const int tok = tt * 16 + c;
+    if (tok < T) {
+      const float* src = a.x + (size_t)tok * H + w * WIN + kofs(j, qq);
+      const float4 v0 = *reinterpret_cast<const float4*>(src);
+      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) split_bf16(f[i], hi[i], lo[i]);
+      u32x4 hv, lv;
+      pack8(hi, hv);
+      pack8(lo, lv);
+      uint8_t* dst = a.xg + ((size_t)tok * nwt + w) * 512;
+      *reinterpret_cast<u32x4*>(dst + ((j * 2 + 0) * 4 + qq) * 16) = hv;
+      *reinterpret_cast<u32x4*>(dst + ((j * 2 + 1) * 4 + qq) * 16) = lv;
+    }
+  }
+}
+
+// one wave per token: top-K over the scaled logits, softmax over the K
+__global__ void __launch_bounds__(NTH) k_btopk(BArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * NW + (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int E = a.E, K = a.K;
+  const float rv = a.rinv[t];
+  const float* lg = a.logits + (size_t)t * E;
+  int my_e = 0;
+  uint32_t my_key = 0;
+  if (E <= 256) {  // experts 4 lane + m
+    uint64_t c[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = 4 * lane + m;
+      const float v = lg[e < E ? e : E - 1];
+      c[m] = topk_comp(e < E ? okey32(rv * v) : 0u, e);
+    }
+    sort_desc<4>(c);
+    topk_sorted<4, false>(c, K, lane, my_e, my_key);
+  } else {  // experts 8 lane + m
+    uint64_t c[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int e = 8 * lane + m;
+      const float v = lg[e < E ? e : E - 1];
+      c[m] = topk_comp(e < E ? okey32(rv * v) : 0u, e);
+    }
+    sort_desc<8>(c);
+    topk_sorted<8, false>(c, K, lane, my_e, my_key);
+  }
+  const float my_val = okey32_value(my_key);
+  const float m0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_val), 0));
+  const float ex = expf(my_val - m0);
+  float sum = 0.f;
+  for (int j = 0; j < K; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+  if (lane < K) {
+    const float w = ex / sum;
+    a.ids[t * K + lane] = my_e;
+    a.wts[t * K + lane] = w;
+    if (a.out_ids) a.out_ids[t * K + lane] = my_e;
+    if (a.out_w) a.out_w[t * K + lane] = w;
+  }
+}
+
+// exclusive prefix over the workgroup's threads (BPERM_NTH) of four counters at once; tot gets
+// the sums
+__device__ __forceinline__ int4 block_excl_scan4(int4 v, int4* wsum, int tid, int4& tot) {
+  const int lane = tid & 63, wave = tid >> 6;
+  int4 inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ax = __shfl_up(inc.x, o), ay = __shfl_up(inc.y, o), az = __shfl_up(inc.z, o),
+              aw = __shfl_up(inc.w, o);
+    if (lane >= o) { inc.x += ax; inc.y += ay; inc.z += az; inc.w += aw; }
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int4 base = {0, 0, 0, 0};
+  tot = base;
+  for (int w = 0; w < BPERM_NTH / 64; ++w) {
+    const int4 s = wsum[w];
+    if (w < wave) { base.x += s.x; base.y += s.y; base.z += s.z; base.w += s.w; }
+    tot.x += s.x; tot.y += s.y; tot.z += s.z; tot.w += s.w;
+  }
+  return int4{base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z, base.w + inc.w - v.w};
+}
+
+struct PermSmem {
+  uint32_t msk[MAX_E * BTW];
+  uint16_t wpre[MAX_E * BTW];  // the expert's tokens in the words before this one
+  int eoff[MAX_E];
+  int4 wsum[BPERM_NTH / 64];
+};
+
+__global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
+  __shared__ PermSmem S;
+  const int tid = threadIdx.x;
+  const int T = a.T, E = a.E, K = a.K, H = a.H;
+  const int tw = (T + 31) / 32, n = T * K;
+  for (int i = tid; i < E * tw; i += BPERM_NTH) S.msk[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += BPERM_NTH) {
+    const int t = i / K, e = a.ids[i];
+    atomicOr(&S.msk[e * tw + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E)
+    for (int w = 0; w < tw; ++w) {
+      S.wpre[tid * tw + w] = (uint16_t)cnt;
+      cnt += __popc(S.msk[tid * tw + w]);
+    }
+  const int ncg = (cnt + 16 * BCG - 1) / (16 * BCG);  // column groups
+  const int nrb_gu = a.I / 64, nrb_dn = (H + 255) / 256;
+  int4 tot;
+  const int4 pre = block_excl_scan4(int4{cnt, cnt > 0 ? 1 : 0, ncg * nrb_gu, ncg * nrb_dn}, S.wsum, tid, tot);
+  const int U = tot.y;
+  int* ue = ut_arr(a, 0);
+  int* uoff = ut_arr(a, 1);
+  int* ucnt = ut_arr(a, 2);
+  int* gpre = ut_arr(a, 3);
+  int* dpre = ut_arr(a, 4);
+  if (tid < E) {
+    S.eoff[tid] = pre.x;
+    if (cnt > 0) {
+      const int u = pre.y;
+      ue[u] = tid; uoff[u] = pre.x; ucnt[u] = cnt; gpre[u] = pre.z; dpre[u] = pre.w;
+    }
+  }
+  if (tid == 0) {  // the shared expert is slot U, over every token
+    const int ncs = a.Is ? (T + 16 * BCG - 1) / (16 * BCG) : 0;
+    ue[U] = -1; uoff[U] = n; ucnt[U] = a.Is ? T : 0; gpre[U] = tot.z; dpre[U] = tot.w;
+    ue[U + 1] = -1; uoff[U + 1] = n + T; ucnt[U + 1] = 0;
+    gpre[U + 1] = tot.z + ncs * nrb_gu;
+    dpre[U + 1] = tot.w + ncs * nrb_dn;
+    a.tab[0] = U; a.tab[1] = gpre[U + 1]; a.tab[2] = dpre[U + 1];
+    if (a.out_n) a.out_n[0] = U;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += BPERM_NTH) {
+    const int t = i / K, e = a.ids[i], w = t >> 5;
+    const int p = S.eoff[e] + S.wpre[e * tw + w] + __popc(S.msk[e * tw + w] & ((1u << (t & 31)) - 1u));
+    a.blist[p] = t;
+    a.bw[p] = a.wts[i];
+    a.brv[p] = a.rinv[t];
+    a.bpos[i] = p;
+  }
+  if (a.Is)
+    for (int t = tid; t < T; t += BPERM_NTH) {
+      a.blist[n + t] = t;
+      a.bw[n + t] = 1.0f;
+      a.brv[n + t] = a.rinv[t];
+    }
+}
+
+// A operands of one tick for one wave: two 16-row bands x four k-steps of one window
+struct BWin {
+  u32x4 v[8];  // [band * 4 + j]
+};
+
+// wave-uniform description of a gathered item for one wave
+struct BItem {
+  int u, off, cnt, col0;  // slot, list offset, tokens, first column (rank) of the item
+  int rb;                 // row block
+  bool shared;
+  uint32_t aoff;          // byte offset of the wave's first A band in its tensor
+};
+
+template <bool GU>
+struct BSmem {
+  static constexpr int NKH = GU ? 2 : 1;
+  u32x4 ring[2][NKH * BCG * 8 * 64];  // [slot][((kh * BCG + ct) * 8 + jh) * 64 + lane]
+  float red[GU ? 4 * 2 * BCG * 256 : 1];
+  float act[GU ? 4 * BCG * 256 : 1];
+  int ue[MAX_E + 2], uoff[MAX_E + 2], ucnt[MAX_E + 2], pre[MAX_E + 2];
+};
+
+template <bool GU>
+__device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int U, int idx, int wave) {
+  // slot: the largest u <= U with pre[u] <= idx (every slot below U + 1 with items has pre
+  // strictly increasing)
+  int lo = 0, hi = U;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (S.pre[mid] <= idx) lo = mid; else hi = mid - 1;
+  }
+  BItem d;
+  d.u = lo;
+  const int loc = idx - S.pre[lo];
+  const int nrb = GU ? a.I / 64 : (a.H + 255) / 256;
+  const int cg = loc / nrb;
+  d.rb = loc - cg * nrb;
+  d.col0 = cg * BCG * 16;
+  d.off = S.uoff[lo];
+  d.cnt = S.ucnt[lo];
+  const int e = S.ue[lo];
+  d.shared = e < 0;
+  const uint32_t eb = d.shared ? 0u : (uint32_t)e;
+  if (GU) {  // wave (rt, kh): rows rb 64 + 16 rt of gate and up
+    const uint32_t row = eb * (uint32_t)a.I + (uint32_t)(d.rb * 64 + 16 * (wave & 3));
+    d.aoff = row * (uint32_t)(a.H * 2);
+  } else {   // wave w: row tiles rb 256 + 32 w (+ 16)
+    const uint32_t row = eb * (uint32_t)a.H + (uint32_t)(d.rb * 256 + 32 * wave);
+    d.aoff = row * (uint32_t)(a.I * 2);
+  }
+  d.u = __builtin_amdgcn_readfirstlane(d.u);
+  d.off = __builtin_amdgcn_readfirstlane(d.off);
+  d.cnt = __builtin_amdgcn_readfirstlane(d.cnt);
+  d.col0 = __builtin_amdgcn_readfirstlane(d.col0);
+  d.rb = __builtin_amdgcn_readfirstlane(d.rb);
+  d.aoff = __builtin_amdgcn_readfirstlane(d.aoff);
+  return d;
+}
+
+// B chunks of one tick held by one thread: (kh, ct) for the thread's (k-step half jh, lane)
+template <bool GU>
+struct BReg {
+  u32x4 v[(GU ? 2 : 1) * BCG];
+};
+
+template <bool GU>
+__global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
+  constexpr int NKH = GU ? 2 : 1;
+  __shared__ BSmem<GU> S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.H, I = a.I;
+  const int U = __builtin_amdgcn_readfirstlane(a.tab[0]);
+  const int n_items = __builtin_amdgcn_readfirstlane(a.tab[GU ? 1 : 2]);
+  for (int i = tid; i <= U + 1; i += NTH) {
+    S.ue[i] = ut_arr(a, 0)[i];
+    S.uoff[i] = ut_arr(a, 1)[i];
+    S.ucnt[i] = ut_arr(a, 2)[i];
+    S.pre[i] = ut_arr(a, GU ? 3 : 4)[i];
+  }
+  // items m G + slot(b): the workgroups of one XCD (b mod 8) take consecutive items, which share
+  // their gathered columns in that XCD's L2
+  const int G = gridDim.x, b = blockIdx.x;
+  const int slotb = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+  const int n_my = slotb < n_items ? (n_items - slotb + G - 1) / G : 0;
+  if (n_my == 0) return;  // uniform over the workgroup
+  __syncthreads();
+
+  const int nwt = H / WIN;                       // windows of the A reduction (gate/up: H)
+  const int ns = GU ? (nwt + 1) / 2 : I / WIN;   // ticks per item
+  const int ticks = n_my * ns;
+  const int kh = GU ? (wave >> 2) : 0;
+  const uint32_t E = a.E;
+  const uint32_t abytes = GU ? E * (uint32_t)I * H * 2 : E * (uint32_t)H * I * 2;
+  const uint32_t sbytes = GU ? (uint32_t)a.Is * H * 2 : (uint32_t)H * a.Is * 2;
+  const rsrc_t r0 = buf_rsrc(GU ? a.wg : a.wd, abytes), r1 = buf_rsrc(a.wu, GU ? abytes : 0);
+  const rsrc_t s0 = buf_rsrc(GU ? a.shg : a.shd, sbytes), s1 = buf_rsrc(a.shu, GU ? sbytes : 0);
+  const uint32_t band2 = GU ? 0u : (uint32_t)(16 * I * 2);  // down: second tile 16 rows below
+  const uint32_t vl = (uint32_t)lane * 16u;
+  // B staging: thread (jh, ln) = (tid / 64, tid % 64), column c = ln % 16, quad q = ln / 16
+  const int jh = tid >> 6, ln = tid & 63, bc = ln & 15, bq = ln >> 4;
+  const int npos = a.T * a.K + a.T;
+  const rsrc_t rx = buf_rsrc(GU ? (const void*)a.xg : (const void*)a.af,
+                             GU ? (uint32_t)a.T * H * 4 : (uint32_t)(npos + 16) * I * 4);
+
+  auto item_of = [&](int m) {
+    const int mm = m < n_my ? m : n_my - 1;  // past the end: the last item again (valid loads)
+    return b_item<GU>(a, S, U, mm * G + slotb, wave);
+  };
+  auto load_a = [&](BWin& W, const BItem& d, int step) {
+    const int w = GU ? kh * ns + step : step;
+    const uint32_t so = d.aoff + (uint32_t)w * 4096u;
+    const rsrc_t ra = d.shared ? s0 : r0, rb2 = d.shared ? s1 : r1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      W.v[j] = bld16(ra, vl + j * 1024, so);
+      W.v[4 + j] = GU ? bld16(rb2, vl + j * 1024, so) : bld16(ra, vl + j * 1024, so + band2);
+    }
+  };
+  // gathered B chunks of one tick (tokens of the item's columns, or list positions for down)
+  auto load_b = [&](BReg<GU>& R, const BItem& d, const int (&src)[BCG], int step) {
+#pragma unroll
+    for (int h = 0; h < NKH; ++h) {
+      const int w = GU ? h * ns + step : step;
+      const int nw = GU ? nwt : I / WIN;
+#pragma unroll
+      for (int ct = 0; ct < BCG; ++ct) {
+        const bool ok = src[ct] >= 0 && w < nw;
+        const uint32_t o = (uint32_t)(((ok ? src[ct] : 0) * nw + (w < nw ? w : 0)) * 512 + (jh * 4 + bq) * 16);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
+        R.v[h * BCG + ct] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_b = [&](const BReg<GU>& R, int slot) {
+#pragma unroll
+    for (int h = 0; h < NKH; ++h)
+#pragma unroll
+      for (int ct = 0; ct < BCG; ++ct) S.ring[slot][((h * BCG + ct) * 8 + jh) * 64 + ln] = R.v[h * BCG + ct];
+  };
+  // the thread's B source per column tile of an item: the token (gate/up) or the list position
+  // (down) of column bc, -1 past the item's tokens
+  auto src_of = [&](const BItem& d, int (&src)[BCG]) {
+#pragma unroll
+    for (int ct = 0; ct < BCG; ++ct) {
+      const int r = d.col0 + 16 * ct + bc;
+      const int p = d.off + (r < d.cnt ? r : 0);
+      src[ct] = r < d.cnt ? (GU ? a.blist[p] : p) : -1;
+    }
+  };
+
+  // Cursors: the A and B loads of tick t + BD - 1 are issued at tick t (B is stored into the LDS
+  // ring at the end of tick t + BD - 2), math at tick t. Vector memory results complete in issue
+  // order, so every load whose result steers later loads (the column sources) is issued one
+  // item ahead, and a wait for it never drains loads that were issued for later ticks.
+  BWin W[BD];
+  BReg<GU> R[BD];
+  int ma = 0, sa = 0;  // load cursor (item, step)
+  BItem da = item_of(0);
+  int srca[BCG], srcn[BCG];
+  src_of(da, srca);
+  src_of(item_of(1), srcn);
+  auto advance = [&]() {
+    if (++sa == ns) {
+      sa = 0;
+      ++ma;
+      da = item_of(ma);
+#pragma unroll
+      for (int ct = 0; ct < BCG; ++ct) srca[ct] = srcn[ct];
+      src_of(item_of(ma + 1), srcn);
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < BD - 1; ++j) {
+    load_a(W[j], da, sa);
+    load_b(R[j], da, srca, sa);
+    advance();
+  }
+  store_b(R[0], 0);
+  __syncthreads();
+
+  int mc = 0, sc = 0;  // math cursor
+  BItem dc = item_of(0);
+  f32x4 acc[2][BCG];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int ct = 0; ct < BCG; ++ct) acc[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // per-column epilogue factors of the math cursor's item (gate/up): RMSNorm factor and weight,
+  // requested when the item's math starts and used at its last tick
+  float crv[BCG], cw[BCG];
+  auto col_factors = [&](const BItem& d) {
+    if (!GU) return;
+#pragma unroll
+    for (int ct = 0; ct < BCG; ++ct) {
+      const int r = d.col0 + 16 * ct + (lane & 15);
+      const int p = d.off + (r < d.cnt ? r : 0);
+      crv[ct] = a.brv[p];
+      cw[ct] = a.bw[p];
+    }
+  };
+  col_factors(dc);
+
+  for (int t0 = 0;; t0 += BD) {
+#pragma unroll
+    for (int r = 0; r < BD; ++r) {
+      const int t = t0 + r;
+      const int ib = (r + BD - 1) % BD;  // buffers of tick t + BD - 1
+      load_a(W[ib], da, sa);
+      load_b(R[ib], da, srca, sa);
+      advance();
+      __builtin_amdgcn_sched_barrier(0);
+      // math of tick t
+      {
+        const u32x4* ring = S.ring[t & 1];
+#pragma unroll
+        for (int ct = 0; ct < BCG; ++ct)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x4 bh = ring[((kh * BCG + ct) * 8 + j * 2 + 0) * 64 + lane];
+            const u32x4 bl = ring[((kh * BCG + ct) * 8 + j * 2 + 1) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              acc[i][ct] = mfma16(W[r].v[i * 4 + j], bh, acc[i][ct]);
+              acc[i][ct] = mfma16(W[r].v[i * 4 + j], bl, acc[i][ct]);
+            }
+          }
+      }
+      if (sc + 1 == ns) {  // the item's last tick: epilogue (uniform over the workgroup)
+        if constexpr (GU) {
+          const int rt = wave & 3;
+          if (kh == 1)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int ct = 0; ct < BCG; ++ct)
+                *reinterpret_cast<f32x4*>(&S.red[((rt * 2 + i) * BCG + ct) * 256 + lane * 4]) = acc[i][ct];
+          __syncthreads();
+          if (kh == 0) {
+#pragma unroll
+            for (int ct = 0; ct < BCG; ++ct) {
+              const f32x4 g2 = *reinterpret_cast<const f32x4*>(&S.red[((rt * 2 + 0) * BCG + ct) * 256 + lane * 4]);
+              const f32x4 u2 = *reinterpret_cast<const f32x4*>(&S.red[((rt * 2 + 1) * BCG + ct) * 256 + lane * 4]);
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const float g = (acc[0][ct][v] + g2[v]) * crv[ct];
+                const float up = (acc[1][ct][v] + u2[v]) * crv[ct];
+                // row 4 (lane / 16) + v, column lane % 16
+                S.act[(rt * BCG + ct) * 256 + (4 * (lane >> 4) + v) * 16 + (lane & 15)] = silu(g) * up * cw[ct];
+              }
+            }
+          }
+          __syncthreads();
+          if (tid < 4 * BCG * 2 * 16) {  // (rt, ct, half, column): 8 rows as down B operands
+            const int c = tid & 15, half = (tid >> 4) & 1, ct = (tid >> 5) % BCG, rt2 = tid / (32 * BCG);
+            const int rnk = dc.col0 + 16 * ct + c;
+            if (rnk < dc.cnt) {
+              uint32_t hi[8], lo[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                split_bf16(S.act[(rt2 * BCG + ct) * 256 + (8 * half + i) * 16 + c], hi[i], lo[i]);
+              u32x4 hv, lv;
+              pack8(hi, hv);
+              pack8(lo, lv);
+              const int R0 = dc.rb * 64 + 16 * rt2 + 8 * half;  // intermediate row
+              const int w = R0 / WIN, o = R0 % WIN, j = o / 32, qd = (o % 32) / 8;
+              const int p = dc.off + rnk;
+              uint8_t* dst = a.af + ((size_t)p * (I / WIN) + w) * 512;
+              *reinterpret_cast<u32x4*>(dst + ((j * 2 + 0) * 4 + qd) * 16) = hv;
+              *reinterpret_cast<u32x4*>(dst + ((j * 2 + 1) * 4 + qd) * 16) = lv;
+            }
+          }
+        } else {
+          // lane: column lane % 16, rows 4 (lane / 16) .. + 3 of each of the wave's two tiles
+#pragma unroll
+          for (int ct = 0; ct < BCG; ++ct) {
+            const int rnk = dc.col0 + 16 * ct + (lane & 15);
+            if (rnk < dc.cnt) {
+              float* dst = a.part + (size_t)(dc.off + rnk) * H;
+#pragma unroll
+              for (int i = 0; i < 2; ++i) {
+                const int row = dc.rb * 256 + 32 * wave + 16 * i + 4 * (lane >> 4);
+                if (row < H) *reinterpret_cast<f32x4*>(dst + row) = acc[i][ct];
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int ct = 0; ct < BCG; ++ct) acc[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sc = 0;
+        ++mc;
+        if (mc < n_my) {
+          dc = item_of(mc);
+          col_factors(dc);
+        }
+      } else {
+        ++sc;
+      }
+      if (t + 1 == ticks) return;
+      store_b(R[(r + 1) % BD], (t + 1) & 1);  // B of tick t + 1 (loads issued at tick t - 1)
+      __syncthreads();
+    }
+  }
+}
+
+// y[t][h] = sum_j P[pos(t, j)][h] + P[T K + t][h] (+ x[t][h]); one thread per four outputs
+__global__ void __launch_bounds__(256) k_bcombine(BArgs a) {
+  const int H = a.H, K = a.K, H4 = H / 4;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= a.T * H4) return;
+  const int t = idx / H4, c = idx % H4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < K; ++j) {
+    const float4 v = reinterpret_cast<const float4*>(a.part + (size_t)a.bpos[t * K + j] * H)[c];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  if (a.Is > 0) {
+    const float4 v = reinterpret_cast<const float4*>(a.part + (size_t)(a.T * K + t) * H)[c];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  if (a.residual) {
+    const float4 v = reinterpret_cast<const float4*>(a.x + (size_t)t * H)[c];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(a.y + (size_t)t * H)[c] = acc;
+}
+
+// ------------------------------------------------------------------------------------------
 // host side
 // ------------------------------------------------------------------------------------------
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -1981,6 +2583,33 @@ Layout make_layout(const moe_layer* L, int k) {
   o.afrag = off;    off = align256(off + (size_t)o.umax * I * 64);
   o.afrag_sh = off; off = align256(off + Is * 64);
   o.part = off;     off = align256(off + (size_t)k * (K + 1) * H * 4);
+  o.total = off;
+  return o;
+}
+
+// workspace of the gathered path for T tokens
+struct BLayout {
+  size_t tab, ut, logits, rinv, xg, ids, wts, blist, bw, brv, bpos, af, part, total;
+};
+
+BLayout make_blayout(const moe_layer* L, int T) {
+  BLayout o;
+  const size_t H = L->hidden, E = L->n_experts, K = L->top_k, I = L->inter;
+  const size_t n = (size_t)T * K + T;  // list positions: routed pairs, then the shared expert
+  size_t off = 0;
+  o.tab = off;    off = align256(off + 16);
+  o.ut = off;     off = align256(off + 5 * (E + 2) * 4);
+  o.logits = off; off = align256(off + (size_t)T * E * 4);
+  o.rinv = off;   off = align256(off + (size_t)T * 4);
+  o.xg = off;     off = align256(off + (size_t)T * H * 4);
+  o.ids = off;    off = align256(off + (size_t)T * K * 4);
+  o.wts = off;    off = align256(off + (size_t)T * K * 4);
+  o.blist = off;  off = align256(off + n * 4);
+  o.bw = off;     off = align256(off + n * 4);
+  o.brv = off;    off = align256(off + n * 4);
+  o.bpos = off;   off = align256(off + (size_t)T * K * 4);
+  o.af = off;     off = align256(off + (n + 16) * I * 4);
+  o.part = off;   off = align256(off + n * H * 4);
   o.total = off;
   return o;
 }
@@ -2078,8 +2707,72 @@ const char* moe_status_string(int status) {
 }
 
 size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max) {
-  if (check_layer(layer) != MOE_OK || k_max < 1 || k_max > KMAX) return 0;
-  return make_layout(layer, k_max).total;
+  if (check_layer(layer) != MOE_OK || k_max < 1 || k_max > BT_MAX) return 0;
+  const size_t small = make_layout(layer, std::min(k_max, (int32_t)KMAX)).total;
+  if (layer->wdtype != MOE_W_BF16) return k_max > KMAX ? 0 : small;
+  return std::max(small, make_blayout(layer, k_max).total);
+}
+
+// the gathered path (k > 16 tokens, or MOE_GATHER): bf16 layers
+static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t flags, float* y,
+                       int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace, size_t ws_bytes,
+                       void* hip_stream, void* const* events) {
+  if (L->wdtype != MOE_W_BF16) return MOE_ERR_DTYPE;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || (topk_ids && !aligned16(topk_ids)) ||
+      (topk_w && !aligned16(topk_w)) || (n_woken && !aligned16(n_woken)))
+    return MOE_ERR_ALIGN;
+  const BLayout lay = make_blayout(L, T);
+  if (ws_bytes < lay.total) return MOE_ERR_WORKSPACE;
+  const size_t xy_bytes = (size_t)T * L->hidden * 4;
+  const size_t ids_bytes = (size_t)T * L->top_k * 4;
+  if (overlaps(x, xy_bytes, y, xy_bytes) || overlaps(y, xy_bytes, workspace, lay.total)) return MOE_ERR_ALIAS;
+  if (overlaps(x, xy_bytes, workspace, lay.total)) return MOE_ERR_ALIAS;
+  if (topk_ids && (overlaps(topk_ids, ids_bytes, workspace, lay.total) || overlaps(topk_ids, ids_bytes, y, xy_bytes)))
+    return MOE_ERR_ALIAS;
+  if (topk_w && (overlaps(topk_w, ids_bytes, workspace, lay.total) || overlaps(topk_w, ids_bytes, y, xy_bytes)))
+    return MOE_ERR_ALIAS;
+  if (n_woken && (overlaps(n_woken, 4, workspace, lay.total) || overlaps(n_woken, 4, y, xy_bytes)))
+    return MOE_ERR_ALIAS;
+
+  uint8_t* ws = (uint8_t*)workspace;
+  BArgs a;
+  a.x = x; a.y = y; a.out_ids = topk_ids; a.out_w = topk_w; a.out_n = n_woken;
+  a.wr = L->router_w;
+  a.wg = (const uint8_t*)L->w_gate; a.wu = (const uint8_t*)L->w_up; a.wd = (const uint8_t*)L->w_down;
+  a.shg = (const uint8_t*)L->sh_gate; a.shu = (const uint8_t*)L->sh_up; a.shd = (const uint8_t*)L->sh_down;
+  a.logits = (float*)(ws + lay.logits); a.rinv = (float*)(ws + lay.rinv); a.xg = ws + lay.xg;
+  a.ids = (int32_t*)(ws + lay.ids); a.wts = (float*)(ws + lay.wts); a.tab = (int32_t*)(ws + lay.tab);
+  a.ut = (int32_t*)(ws + lay.ut); a.blist = (int32_t*)(ws + lay.blist); a.bw = (float*)(ws + lay.bw);
+  a.brv = (float*)(ws + lay.brv); a.bpos = (int32_t*)(ws + lay.bpos); a.af = ws + lay.af;
+  a.part = (float*)(ws + lay.part);
+  a.H = L->hidden; a.E = L->n_experts; a.K = L->top_k; a.I = L->inter; a.Is = L->shared_inter; a.T = T;
+  a.pre_norm = (flags & MOE_PRE_RMSNORM) ? 1 : 0; a.residual = (flags & MOE_RESIDUAL) ? 1 : 0;
+  a.eps = L->rms_eps;
+
+  hipStream_t s = (hipStream_t)hip_stream;
+  (void)hipGetLastError();  // clear a stale error so the check below reports this launch
+  const int cus = num_cus();
+  const int nte = (a.E + 15) / 16, ntt = (T + 15) / 16;
+  bool ok = mark(events, 0, s);
+  if (ok) {
+    k_brouter<<<ntt * nte, NTH, 0, s>>>(a);
+    k_btopk<<<(T + NW - 1) / NW, NTH, 0, s>>>(a);
+    k_bperm<<<1, BPERM_NTH, 0, s>>>(a);
+    ok = mark(events, 1, s);
+  }
+  if (ok) {
+    k_bexp<true><<<cus, NTH, 0, s>>>(a);
+    ok = mark(events, 2, s);
+  }
+  if (ok) {
+    k_bexp<false><<<cus, NTH, 0, s>>>(a);
+    ok = mark(events, 3, s);
+  }
+  if (ok) {
+    k_bcombine<<<(T * a.H / 4 + 255) / 256, 256, 0, s>>>(a);
+    ok = mark(events, 4, s);
+  }
+  return (ok && hipGetLastError() == hipSuccess) ? MOE_OK : MOE_ERR_HIP;
 }
 
 static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint32_t flags, float* y,
@@ -2088,8 +2781,10 @@ static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint
   int st = check_layer(L);
   if (st != MOE_OK) return st;
   if (!x || !y || !workspace) return MOE_ERR_NULL;
-  if (k < 1 || k > KMAX) return MOE_ERR_SHAPE;
-  if (flags & ~(uint32_t)(MOE_PRE_RMSNORM | MOE_RESIDUAL)) return MOE_ERR_ARG;
+  if (k < 1 || k > BT_MAX) return MOE_ERR_SHAPE;
+  if (flags & ~(uint32_t)(MOE_PRE_RMSNORM | MOE_RESIDUAL | MOE_GATHER)) return MOE_ERR_ARG;
+  if (k > KMAX || (flags & MOE_GATHER))
+    return gather_impl(L, x, k, flags, y, topk_ids, topk_w, n_woken, workspace, ws_bytes, hip_stream, events);
   if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || (topk_ids && !aligned16(topk_ids)) ||
       (topk_w && !aligned16(topk_w)) || (n_woken && !aligned16(n_woken)))
     return MOE_ERR_ALIGN;

@@ -79,6 +79,8 @@ WORKLOADS = {
                               LayerShape(2048, 256, 8, 512, 512, wdtype="mxfp4"), k=16,
                               seed=1004, n_layers=40, vocab=151936, n_target=17, n_draft=16,
                               accept_p=0.7, pre_norm=True, residual=True),
+    # 32 sequences verified together, 16 independent block tokens each
+    "batched": Workload("batched", _L1, k=512, seed=1005),
 }
 
 

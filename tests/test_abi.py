@@ -57,7 +57,7 @@ def _layer(b, **over):
 def _call(b, L, k=16, flags=0, x=FAKE + 0x10000000, y=FAKE + 0x20000000, ids=None, w=None, n=None,
           ws=FAKE + 0x40000000, ws_bytes=None):
     if ws_bytes is None:
-        ws_bytes = b.lib.moe_verify_workspace_size(ctypes.byref(L), k) if 1 <= k <= 16 else 1 << 30
+        ws_bytes = b.lib.moe_verify_workspace_size(ctypes.byref(L), k) if 1 <= k <= 1024 else 1 << 30
     return b.lib.moe_verify_block(ctypes.byref(L), x, k, flags, y, ids, w, n, ws, ws_bytes, None)
 
 
@@ -68,7 +68,14 @@ def test_workspace_size(b):
     assert 0 < n1 < n16
     assert n16 % 256 == 0
     assert b.lib.moe_verify_workspace_size(ctypes.byref(L), 0) == 0
-    assert b.lib.moe_verify_workspace_size(ctypes.byref(L), 17) == 0
+    # the gathered path (k > 16) grows with k, up to 1024 tokens
+    n17 = b.lib.moe_verify_workspace_size(ctypes.byref(L), 17)
+    n1024 = b.lib.moe_verify_workspace_size(ctypes.byref(L), 1024)
+    assert n16 <= n17 < n1024 and n1024 % 256 == 0
+    assert b.lib.moe_verify_workspace_size(ctypes.byref(L), 1025) == 0
+    mx = _layer(b, wdtype=1, s_gate=FAKE + 0x7000, s_up=FAKE + 0x8000, s_down=FAKE + 0x9000)
+    assert b.lib.moe_verify_workspace_size(ctypes.byref(mx), 16) > 0
+    assert b.lib.moe_verify_workspace_size(ctypes.byref(mx), 17) == 0
     assert b.lib.moe_verify_workspace_size(None, 4) == 0
     assert b.lib.moe_verify_workspace_size(ctypes.byref(_layer(b, hidden=100)), 4) == 0
 
@@ -92,8 +99,8 @@ def test_bad_call_arguments_rejected(b):
     assert _call(b, L, y=None) == -1
     assert _call(b, L, ws=None) == -1
     assert _call(b, L, k=0) == -2
-    assert _call(b, L, k=17) == -2
-    assert _call(b, L, flags=4) == -8
+    assert _call(b, L, k=1025) == -2
+    assert _call(b, L, flags=8) == -8
     assert _call(b, L, x=FAKE + 0x10000004) == -4
     assert _call(b, L, ids=FAKE + 0x30000002) == -4
     need = b.lib.moe_verify_workspace_size(ctypes.byref(L), 16)
@@ -103,6 +110,26 @@ def test_bad_call_arguments_rejected(b):
     assert _call(b, L, y=FAKE + 0x40000000 + 256) == -6
     assert _call(b, L, x=FAKE + 0x40000000 + 4096) == -6
     assert _call(b, L, ids=FAKE + 0x40000000 + 512) == -6
+
+
+def test_gathered_path_validation(b):
+    """Calls of more than 16 tokens (or MOE_GATHER) take the gathered path; every case here is
+    rejected before any HIP call."""
+    L = _layer(b)
+    need = b.lib.moe_verify_workspace_size(ctypes.byref(L), 100)
+    assert need > b.lib.moe_verify_workspace_size(ctypes.byref(L), 16)
+    assert _call(b, L, k=100, ws_bytes=need - 1) == -5
+    assert _call(b, L, k=8, flags=4, ws_bytes=0) == -5
+    assert _call(b, L, k=100, x=FAKE + 0x10000004) == -4
+    assert _call(b, L, k=100, ids=FAKE + 0x30000002) == -4
+    assert _call(b, L, k=100, y=FAKE + 0x10000000 + 4096) == -6          # y overlaps x
+    assert _call(b, L, k=100, y=FAKE + 0x40000000 + 256) == -6           # y overlaps the workspace
+    assert _call(b, L, k=100, ids=FAKE + 0x40000000 + need - 64) == -6   # ids overlap the workspace
+    assert _call(b, L, k=100, flags=1 | 2 | 8) == -8
+    # mxfp4 layers: the gathered path takes bf16 weights only
+    mx = _layer(b, wdtype=1, s_gate=FAKE + 0x7000, s_up=FAKE + 0x8000, s_down=FAKE + 0x9000)
+    assert _call(b, mx, k=17, ws_bytes=1 << 30) == -3
+    assert _call(b, mx, k=16, flags=4, ws_bytes=1 << 30) == -3
 
 
 def test_mxfp4_layer_needs_h_multiple_of_256(b):
