@@ -202,6 +202,8 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer mxfp4 stack measurement")
     ap.add_argument("--no-head", action="store_true", help="skip the output-head (lm_head_accept) measurement")
     ap.add_argument("--no-sample", action="store_true", help="skip the accept_sample / statistics measurement")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the many-sequence (gathered path) measurement")
     ap.add_argument("--profile-run", action="store_true",
                     help="counter-collection run: warmup + steps without events, then a plain copy of "
                          "known size for calibrating HBM traffic counters; prints one JSON line")
@@ -420,6 +422,55 @@ def main():
         fit["same_U_check_ms"] = {"k1_U8": sweep_k[0]["ms"], "k16_sigma0_U8": sweep_sigma[0]["ms"]}
         print("[bench] sweeps done", file=sys.stderr, flush=True)
 
+    # ---- many sequences verified together: the gathered path at 4..64 sequences x 16 tokens ----
+    batched = None
+    if not args.no_batched:
+        print("[bench] timing the gathered path", file=sys.stderr, flush=True)
+        bw_ = gen.WORKLOADS["batched"]
+        tmax = 1024
+        bws = torch.empty(layers[0].workspace_size(tmax), dtype=torch.uint8, device=dev)
+        by = torch.empty((tmax, s.hidden), dtype=torch.float32, device=dev)
+        bids = torch.empty((tmax, K), dtype=torch.int32, device=dev)
+        bwt = torch.empty((tmax, K), dtype=torch.float32, device=dev)
+        rows = []
+        for T in (64, 128, 256, 512, 1024):
+            blocks = [torch.from_numpy(gen.hidden_states(bw_, rep=400 + p, k=T)).to(dev) for p in range(2)]
+            reps = 8
+            nw = torch.zeros((reps + 1, 4), dtype=torch.int32, device=dev)
+            evs = ev.create(5 * reps)
+            for i in range(3):
+                binding.moe_verify_block(layers[i % R], blocks[i % 2], 0, by[:T], bids[:T], bwt[:T], nw[reps], bws)
+            torch.cuda.synchronize()
+            for i in range(reps):
+                binding.moe_verify_block_timed(layers[i % R], blocks[i % 2], 0, by[:T], evs[5 * i:5 * i + 5],
+                                               bids[:T], bwt[:T], nw[i], bws)
+            torch.cuda.synchronize()
+            seg = np.array([[ev.ms(evs[5 * i + j], evs[5 * i + j + 1]) for j in range(4)] for i in range(reps)])
+            tot = np.array([ev.ms(evs[5 * i], evs[5 * i + 4]) for i in range(reps)])
+            ev.destroy(evs)
+            Us = nw[:reps, 0].cpu().numpy().astype(np.float64)
+            Um = float(Us.mean())
+            t_ms = float(tot.mean())
+            byt = float(np.mean([layer_bytes(s, u, T) for u in Us]))
+            gub = float(np.mean([gateup_bytes(s, u) for u in Us]))
+            dnb = gub / 2
+            flops = 2.0 * 3 * s.hidden * s.inter * T * K + 2.0 * 3 * s.hidden * s.shared_inter * T
+            sm = seg.mean(axis=0)
+            rows.append({"tokens": T, "sequences": T // 16, "U_mean": round(Um, 2), "ms": round(t_ms, 4),
+                         "tokens_per_s": round(T / (t_ms * 1e-3)), "GBps": round(byt / (t_ms * 1e-3) / 1e9, 1),
+                         "expert_TFLOPs": round(flops / (t_ms * 1e-3) / 1e12, 1),
+                         "kernels_us": {"route": round(sm[0] * 1e3, 2), "gateup": round(sm[1] * 1e3, 2),
+                                        "down": round(sm[2] * 1e3, 2), "combine": round(sm[3] * 1e3, 2)},
+                         "gateup_GBps": round(gub / (sm[1] * 1e-3) / 1e9, 1),
+                         "down_GBps": round(dnb / (sm[2] * 1e-3) / 1e9, 1)})
+            del blocks
+        batched = {"workload": "gathered path: 4..64 sequences x 16 independent N(0,1) tokens through the k = 16 "
+                               "layer (bf16); event times per call, route = router + top-K + permutation",
+                   "points": rows,
+                   "single_block_k16_ms": sweep_k[-1]["ms"] if sweep_k else None}
+        del bws, by
+        print("[bench] gathered path done", file=sys.stderr, flush=True)
+
     # ---- 40-layer mxfp4 stack: one verify pass (pre-norm, residual) + acceptance ----
     stack = None
     if not args.no_stack:
@@ -571,6 +622,7 @@ def main():
         "sweep_k": sweep_k,
         "sweep_sigma": sweep_sigma,
         "sweep_fit": fit,
+        "batched": batched,
         "stack40_mxfp4": stack,
         "lm_head": head,
         "accept_sample": samp,

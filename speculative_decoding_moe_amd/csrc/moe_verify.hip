@@ -2166,15 +2166,30 @@ struct PermSmem {
 
 __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
   __shared__ PermSmem S;
+  constexpr int PPT = BT_MAX * MAX_K / BPERM_NTH;  // (token, slot) pairs per thread at most
   const int tid = threadIdx.x;
   const int T = a.T, E = a.E, K = a.K, H = a.H;
   const int tw = (T + 31) / 32, n = T * K;
+  // the thread's pairs i = tid + BPERM_NTH m, all requested at once (one memory round trip)
+  int pte[PPT];  // token << 16 | expert
+  float pw[PPT], pr[PPT];
+#pragma unroll
+  for (int m = 0; m < PPT; ++m) {
+    const int i = tid + BPERM_NTH * m;
+    const int ic = i < n ? i : 0;
+    const int t = ic / K;
+    pte[m] = (t << 16) | a.ids[ic];
+    pw[m] = a.wts[ic];
+    pr[m] = a.rinv[t];
+  }
   for (int i = tid; i < E * tw; i += BPERM_NTH) S.msk[i] = 0u;
   __syncthreads();
-  for (int i = tid; i < n; i += BPERM_NTH) {
-    const int t = i / K, e = a.ids[i];
-    atomicOr(&S.msk[e * tw + (t >> 5)], 1u << (t & 31));
-  }
+#pragma unroll
+  for (int m = 0; m < PPT; ++m)
+    if (tid + BPERM_NTH * m < n) {
+      const int t = pte[m] >> 16, e = pte[m] & 0xFFFF;
+      atomicOr(&S.msk[e * tw + (t >> 5)], 1u << (t & 31));
+    }
   __syncthreads();
   int cnt = 0;
   if (tid < E)
@@ -2209,13 +2224,17 @@ __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
     if (a.out_n) a.out_n[0] = U;
   }
   __syncthreads();
-  for (int i = tid; i < n; i += BPERM_NTH) {
-    const int t = i / K, e = a.ids[i], w = t >> 5;
-    const int p = S.eoff[e] + S.wpre[e * tw + w] + __popc(S.msk[e * tw + w] & ((1u << (t & 31)) - 1u));
-    a.blist[p] = t;
-    a.bw[p] = a.wts[i];
-    a.brv[p] = a.rinv[t];
-    a.bpos[i] = p;
+#pragma unroll
+  for (int m = 0; m < PPT; ++m) {
+    const int i = tid + BPERM_NTH * m;
+    if (i < n) {
+      const int t = pte[m] >> 16, e = pte[m] & 0xFFFF, w = t >> 5;
+      const int p = S.eoff[e] + S.wpre[e * tw + w] + __popc(S.msk[e * tw + w] & ((1u << (t & 31)) - 1u));
+      a.blist[p] = t;
+      a.bw[p] = pw[m];
+      a.brv[p] = pr[m];
+      a.bpos[i] = p;
+    }
   }
   if (a.Is)
     for (int t = tid; t < T; t += BPERM_NTH) {
@@ -2235,6 +2254,7 @@ struct BItem {
   int u, off, cnt, col0;  // slot, list offset, tokens, first column (rank) of the item
   int rb;                 // row block
   bool shared;
+  bool cached;            // the slot's weights are read by several column groups
   uint32_t aoff;          // byte offset of the wave's first A band in its tensor
 };
 
@@ -2259,12 +2279,15 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
   BItem d;
   d.u = lo;
   const int loc = idx - S.pre[lo];
-  const int nrb = GU ? a.I / 64 : (a.H + 255) / 256;
-  const int cg = loc / nrb;
-  d.rb = loc - cg * nrb;
-  d.col0 = cg * BCG * 16;
   d.off = S.uoff[lo];
   d.cnt = S.ucnt[lo];
+  // column groups fastest: the items that read the same weights are consecutive, so they run
+  // together on one XCD (see the item order in k_bexp) and all but the first read hit its L2
+  const int ncg = (d.cnt + 16 * BCG - 1) / (16 * BCG);
+  const int cg = loc % ncg;
+  d.rb = loc / ncg;
+  d.col0 = cg * BCG * 16;
+  d.cached = ncg > 1;
   const int e = S.ue[lo];
   d.shared = e < 0;
   const uint32_t eb = d.shared ? 0u : (uint32_t)e;
@@ -2281,6 +2304,8 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
   d.col0 = __builtin_amdgcn_readfirstlane(d.col0);
   d.rb = __builtin_amdgcn_readfirstlane(d.rb);
   d.aoff = __builtin_amdgcn_readfirstlane(d.aoff);
+  d.cached = __builtin_amdgcn_readfirstlane((int)d.cached) != 0;
+  d.shared = __builtin_amdgcn_readfirstlane((int)d.shared) != 0;
   return d;
 }
 
@@ -2338,10 +2363,18 @@ __global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
     const int w = GU ? kh * ns + step : step;
     const uint32_t so = d.aoff + (uint32_t)w * 4096u;
     const rsrc_t ra = d.shared ? s0 : r0, rb2 = d.shared ? s1 : r1;
+    if (d.cached) {  // read again by the slot's other column groups: keep in L2
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      W.v[j] = bld16(ra, vl + j * 1024, so);
-      W.v[4 + j] = GU ? bld16(rb2, vl + j * 1024, so) : bld16(ra, vl + j * 1024, so + band2);
+      for (int j = 0; j < 4; ++j) {
+        W.v[j] = bld16_cached(ra, vl + j * 1024, so);
+        W.v[4 + j] = GU ? bld16_cached(rb2, vl + j * 1024, so) : bld16_cached(ra, vl + j * 1024, so + band2);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        W.v[j] = bld16(ra, vl + j * 1024, so);
+        W.v[4 + j] = GU ? bld16(rb2, vl + j * 1024, so) : bld16(ra, vl + j * 1024, so + band2);
+      }
     }
   };
   // gathered B chunks of one tick (tokens of the item's columns, or list positions for down)
@@ -2352,10 +2385,11 @@ __global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
       const int nw = GU ? nwt : I / WIN;
 #pragma unroll
       for (int ct = 0; ct < BCG; ++ct) {
+        // padding columns and windows past the reduction read past the resource: zeros, with no
+        // memory access (every offset of a real column is far below 2^31)
         const bool ok = src[ct] >= 0 && w < nw;
-        const uint32_t o = (uint32_t)(((ok ? src[ct] : 0) * nw + (w < nw ? w : 0)) * 512 + (jh * 4 + bq) * 16);
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
-        R.v[h * BCG + ct] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+        const uint32_t o = ok ? (uint32_t)((src[ct] * nw + w) * 512 + (jh * 4 + bq) * 16) : 0x80000000u;
+        R.v[h * BCG + ct] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
       }
     }
   };
@@ -2442,6 +2476,7 @@ __global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
         const u32x4* ring = S.ring[t & 1];
 #pragma unroll
         for (int ct = 0; ct < BCG; ++ct)
+          if (ct == 0 || dc.col0 + 16 * ct < dc.cnt)  // a column tile of padding only: skipped
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const u32x4 bh = ring[((kh * BCG + ct) * 8 + j * 2 + 0) * 64 + lane];
