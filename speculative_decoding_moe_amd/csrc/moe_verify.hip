@@ -1962,9 +1962,10 @@ __global__ void __launch_bounds__(1024) k_accept_hist(const int32_t* acc, int n_
 //   k_brouter   (16-token tile, 16-expert tile) items, fp32 MFMA over the full H: raw logits,
 //               the RMSNorm factor, and each token's bf16 hi/lo B fragments (token-major).
 //   k_btopk     one wave per token: top-K (ties to the lower expert), softmax over the K.
-//   k_bperm     one workgroup: per-expert token bitmasks (LDS), counts, a scan over experts for
-//               the list offsets, then each (token, slot) pair's list position = expert offset
-//               + number of the expert's tokens below it. The list (tokens by expert, then
+//   k_bperm     eight workgroups, each: per-expert token bitmasks (LDS), counts, a scan over
+//               experts for the list offsets, then the list position of each (token, slot) pair
+//               of one eighth of the experts = expert offset + number of the expert's tokens
+//               below it. The list (tokens by expert, then
 //               token) is deterministic; the shared expert follows as slot U with every token.
 //   k_bexp<GU>  (woken slot u, column group, row block) items over a flat sequence of window
 //               ticks. Per tick every wave streams two 16-row A bands of one 128-wide window
@@ -1981,6 +1982,7 @@ constexpr int BTW = BT_MAX / 32;  // token-mask words per expert
 constexpr int BCG = 2;            // 16-token column tiles per gathered item
 constexpr int BD = 3;             // weight ticks in flight (loads issued BD - 1 ticks ahead)
 constexpr int BPERM_NTH = 1024;
+constexpr int BPERM_G = 8;        // permutation workgroups (each places the pairs of 1/8 of the experts)
 
 struct BArgs {
   const float* x;
@@ -2171,16 +2173,13 @@ __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
   const int T = a.T, E = a.E, K = a.K, H = a.H;
   const int tw = (T + 31) / 32, n = T * K;
   // the thread's pairs i = tid + BPERM_NTH m, all requested at once (one memory round trip)
+  const int g = blockIdx.x, ng = gridDim.x;
   int pte[PPT];  // token << 16 | expert
-  float pw[PPT], pr[PPT];
 #pragma unroll
   for (int m = 0; m < PPT; ++m) {
     const int i = tid + BPERM_NTH * m;
     const int ic = i < n ? i : 0;
-    const int t = ic / K;
-    pte[m] = (t << 16) | a.ids[ic];
-    pw[m] = a.wts[ic];
-    pr[m] = a.rinv[t];
+    pte[m] = ((ic / K) << 16) | a.ids[ic];
   }
   for (int i = tid; i < E * tw; i += BPERM_NTH) S.msk[i] = 0u;
   __syncthreads();
@@ -2207,14 +2206,14 @@ __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
   int* ucnt = ut_arr(a, 2);
   int* gpre = ut_arr(a, 3);
   int* dpre = ut_arr(a, 4);
-  if (tid < E) {
-    S.eoff[tid] = pre.x;
+  if (tid < E) S.eoff[tid] = pre.x;
+  if (g == 0 && tid < E) {
     if (cnt > 0) {
       const int u = pre.y;
       ue[u] = tid; uoff[u] = pre.x; ucnt[u] = cnt; gpre[u] = pre.z; dpre[u] = pre.w;
     }
   }
-  if (tid == 0) {  // the shared expert is slot U, over every token
+  if (g == 0 && tid == 0) {  // the shared expert is slot U, over every token
     const int ncs = a.Is ? (T + 16 * BCG - 1) / (16 * BCG) : 0;
     ue[U] = -1; uoff[U] = n; ucnt[U] = a.Is ? T : 0; gpre[U] = tot.z; dpre[U] = tot.w;
     ue[U + 1] = -1; uoff[U + 1] = n + T; ucnt[U + 1] = 0;
@@ -2224,20 +2223,23 @@ __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
     if (a.out_n) a.out_n[0] = U;
   }
   __syncthreads();
+  // this workgroup's pairs: experts e with e mod ng == g (the scattered stores spread over ng CUs)
 #pragma unroll
   for (int m = 0; m < PPT; ++m) {
     const int i = tid + BPERM_NTH * m;
-    if (i < n) {
-      const int t = pte[m] >> 16, e = pte[m] & 0xFFFF, w = t >> 5;
+    const int t = pte[m] >> 16, e = pte[m] & 0xFFFF;
+    if (i < n && e % ng == g) {
+      const float wt = a.wts[i], rv = a.rinv[t];
+      const int w = t >> 5;
       const int p = S.eoff[e] + S.wpre[e * tw + w] + __popc(S.msk[e * tw + w] & ((1u << (t & 31)) - 1u));
       a.blist[p] = t;
-      a.bw[p] = pw[m];
-      a.brv[p] = pr[m];
+      a.bw[p] = wt;
+      a.brv[p] = rv;
       a.bpos[i] = p;
     }
   }
   if (a.Is)
-    for (int t = tid; t < T; t += BPERM_NTH) {
+    for (int t = tid + BPERM_NTH * g; t < T; t += BPERM_NTH * ng) {
       a.blist[n + t] = t;
       a.bw[n + t] = 1.0f;
       a.brv[n + t] = a.rinv[t];
@@ -2792,7 +2794,7 @@ static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t f
   if (ok) {
     k_brouter<<<ntt * nte, NTH, 0, s>>>(a);
     k_btopk<<<(T + NW - 1) / NW, NTH, 0, s>>>(a);
-    k_bperm<<<1, BPERM_NTH, 0, s>>>(a);
+    k_bperm<<<BPERM_G, BPERM_NTH, 0, s>>>(a);
     ok = mark(events, 1, s);
   }
   if (ok) {
