@@ -204,6 +204,8 @@ def main():
     ap.add_argument("--no-sample", action="store_true", help="skip the accept_sample / statistics measurement")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the many-sequence (gathered path) measurement")
+    ap.add_argument("--batched-tokens", type=int, default=0,
+                    help="measure the gathered path at this token count only (for profiling)")
     ap.add_argument("--profile-run", action="store_true",
                     help="counter-collection run: warmup + steps without events, then a plain copy of "
                          "known size for calibrating HBM traffic counters; prints one JSON line")
@@ -288,6 +290,17 @@ def main():
             binding.lm_head_accept(hh, heads[r % 2], V, drs[0][:15].contiguous(), htg, hac, hws)
         torch.cuda.synchronize()
         del heads
+        # the gathered path: 4 calls of 512 tokens (32 sequences x 16) on the rotating copies
+        bt = 512
+        bx = torch.from_numpy(gen.hidden_states(gen.WORKLOADS["batched"], rep=400, k=bt)).to(dev)
+        bws = torch.empty(layers[0].workspace_size(bt), dtype=torch.uint8, device=dev)
+        by = torch.empty((bt, s.hidden), dtype=torch.float32, device=dev)
+        bnw = torch.zeros((4, 4), dtype=torch.int32, device=dev)
+        for r in range(4):
+            binding.moe_verify_block(layers[r % R], bx, 0, by, None, None, bnw[r], bws)
+        torch.cuda.synchronize()
+        bU = bnw[:, 0].cpu().numpy().astype(np.int64)
+        del bws, by
         copy_mib = 512
         src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -298,6 +311,8 @@ def main():
                           "gateup_bytes_mean": float(np.mean([gateup_bytes(s, u) for u in Uall])),
                           "layer_bytes_mean": float(np.mean([layer_bytes(s, u, k) for u in Uall])),
                           "head_bytes": (V + 15) // 16 * 16 * s.hidden * 2 + 16 * s.hidden * 4,
+                          "bexp_gateup_bytes": float(np.mean([gateup_bytes(s, u) for u in bU])),
+                          "bexp_down_bytes": float(np.mean([gateup_bytes(s, u) / 2 for u in bU])),
                           "copy_bytes": copy_mib << 20, "copy_launches": 3}), flush=True)
         return
 
@@ -433,7 +448,7 @@ def main():
         bids = torch.empty((tmax, K), dtype=torch.int32, device=dev)
         bwt = torch.empty((tmax, K), dtype=torch.float32, device=dev)
         rows = []
-        for T in (64, 128, 256, 512, 1024):
+        for T in ((args.batched_tokens,) if args.batched_tokens else (64, 128, 256, 512, 1024)):
             blocks = [torch.from_numpy(gen.hidden_states(bw_, rep=400 + p, k=T)).to(dev) for p in range(2)]
             reps = 8
             nw = torch.zeros((reps + 1, 4), dtype=torch.int32, device=dev)
