@@ -479,8 +479,31 @@ def main():
                          "gateup_GBps": round(gub / (sm[1] * 1e-3) / 1e9, 1),
                          "down_GBps": round(dnb / (sm[2] * 1e-3) / 1e9, 1)})
             del blocks
+        # greedy acceptance of 32 sequences at once: 32 x 17 rows x V logits
+        ns = 32
+        blg = torch.randn((ns, NT, V), device=dev, generator=torch.Generator(device=dev).manual_seed(wl.seed))
+        bdr = torch.randint(0, V, (ns, NT - 1), dtype=torch.int32, device=dev)
+        btg = torch.empty((ns, NT), dtype=torch.int32, device=dev)
+        bac = torch.empty((ns,), dtype=torch.int32, device=dev)
+        baws = torch.empty(binding.accept_prefix_batch_workspace_size(ns, NT, V), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            binding.accept_prefix_batch(blg, bdr, btg, bac, baws)
+        a_, b_ = ev.create(2)
+        torch.cuda.synchronize()
+        ev.record(a_, stream)
+        for _ in range(20):
+            binding.accept_prefix_batch(blg, bdr, btg, bac, baws)
+        ev.record(b_, stream)
+        torch.cuda.synchronize()
+        acc_us = ev.ms(a_, b_) * 1e3 / 20
+        ev.destroy([a_, b_])
+        accept_batch = {"workload": f"accept_prefix_batch: {ns} sequences x {NT} rows x {V} fp32 logits",
+                        "us_per_call": round(acc_us, 2),
+                        "GBps": round(ns * NT * V * 4 / (acc_us * 1e-6) / 1e9, 1)}
+        del blg
         batched = {"workload": "gathered path: 4..64 sequences x 16 independent N(0,1) tokens through the k = 16 "
                                "layer (bf16); event times per call, route = router + top-K + permutation",
+                   "accept_32_sequences": accept_batch,
                    "points": rows,
                    "single_block_k16_ms": sweep_k[-1]["ms"] if sweep_k else None}
         del bws, by

@@ -192,6 +192,26 @@ int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const in
                   int32_t n_draft, int32_t* target_ids, int32_t* accepted, void* workspace,
                   size_t ws_bytes, void* hip_stream);
 
+/* Bytes of device workspace accept_prefix_batch needs (0 if the sizes are invalid). Host only. */
+size_t accept_prefix_batch_workspace_size(int32_t n_seq, int32_t n_target, int32_t vocab);
+
+/* accept_prefix for many sequences verified together (the blocks of one moe_verify_block call
+ * over several sequences): sequence s is judged exactly as accept_prefix judges one block, in
+ * two launches for all of them. Draft counts may differ per sequence: a cycle need not draft a
+ * full block ("Speculating on a Strix Halo (part 2)", section "llama curiosities").
+ *   logits      fp32 [n_seq][n_target][vocab]
+ *   draft_ids   int32 [n_seq][n_draft_max] (may be NULL when n_draft_max == 0)
+ *   n_draft     int32 [n_seq] or NULL: sequence s compares its first n_draft[s] drafts (device
+ *               values are clamped to [0, n_draft_max]); NULL: every sequence has n_draft_max
+ *   target_ids  int32 [n_seq][n_target] out: per-row argmax, equal values to the lowest index
+ *   accepted    int32 [n_seq] out: each sequence's accepted length
+ * Limits: 1 <= n_seq <= 1024, 1 <= n_target <= 64, n_seq * n_target <= 65535,
+ * 0 <= n_draft_max <= n_target, 1 <= vocab <= 2^24. Returns MOE_OK or an MOE_ERR_* code. */
+int accept_prefix_batch(const float* logits, int32_t n_seq, int32_t n_target, int32_t vocab,
+                        const int32_t* draft_ids, int32_t n_draft_max, const int32_t* n_draft,
+                        int32_t* target_ids, int32_t* accepted, void* workspace, size_t ws_bytes,
+                        void* hip_stream);
+
 /* Bytes of device workspace lm_head_accept needs (0 if the sizes are invalid). Host only. */
 size_t lm_head_accept_workspace_size(int32_t n_target, int32_t hidden, int32_t vocab);
 

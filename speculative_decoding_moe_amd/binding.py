@@ -21,6 +21,7 @@ MOE_PRE_RMSNORM, MOE_RESIDUAL, MOE_GATHER = 1, 2, 4
 
 EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "moe_verify_block_timed",
            "moe_pack_weights", "accept_prefix_workspace_size", "accept_prefix",
+           "accept_prefix_batch_workspace_size", "accept_prefix_batch",
            "lm_head_accept_workspace_size", "lm_head_accept", "accept_sample_workspace_size",
            "accept_sample", "accept_histogram", "moe_status_string")
 
@@ -61,6 +62,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.accept_prefix_workspace_size.restype = sz
     lib.accept_prefix.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     lib.accept_prefix.restype = ctypes.c_int
+    lib.accept_prefix_batch_workspace_size.argtypes = [i32, i32, i32]
+    lib.accept_prefix_batch_workspace_size.restype = sz
+    lib.accept_prefix_batch.argtypes = [vp, i32, i32, i32, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.accept_prefix_batch.restype = ctypes.c_int
     lib.lm_head_accept_workspace_size.argtypes = [i32, i32, i32]
     lib.lm_head_accept_workspace_size.restype = sz
     lib.lm_head_accept.argtypes = [vp, i32, i32, vp, i32, i32, vp, i32, vp, vp, vp, sz, vp]
@@ -186,6 +191,23 @@ def moe_verify_block_timed(layer: MoeLayer, x, flags: int, y, events, topk_ids=N
 
 def accept_prefix_workspace_size(n_target: int, vocab: int) -> int:
     return int(lib.accept_prefix_workspace_size(int(n_target), int(vocab)))
+
+
+def accept_prefix_batch_workspace_size(n_seq: int, n_target: int, vocab: int) -> int:
+    return int(lib.accept_prefix_batch_workspace_size(int(n_seq), int(n_target), int(vocab)))
+
+
+def accept_prefix_batch(logits, draft_ids, target_ids, accepted, workspace, n_draft=None, stream=None) -> None:
+    """accept_prefix for n_seq sequences at once (library call): logits [n_seq][n_target][V],
+    draft_ids [n_seq][n_draft_max] or None, n_draft: optional int32 device tensor [n_seq] of
+    per-sequence draft counts; target_ids [n_seq][n_target] and accepted [n_seq] are outputs."""
+    n_seq, n_target, vocab = (int(v) for v in logits.shape)
+    nd_max = int(draft_ids.shape[1]) if draft_ids is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.accept_prefix_batch(_ptr(logits), n_seq, n_target, vocab, _ptr(draft_ids), nd_max, _ptr(n_draft),
+                                 _ptr(target_ids), _ptr(accepted), _ptr(workspace), ws_bytes,
+                                 _stream_handle() if stream is None else stream)
+    _check(st)
 
 
 def accept_prefix(logits, draft_ids, target_ids, accepted, workspace, n_draft=None, stream=None) -> None:

@@ -1366,14 +1366,24 @@ __global__ void __launch_bounds__(256) k_argmax_partial(const float* logits, int
   }
 }
 
-// One workgroup of 16 waves: wave w reduces rows w, w + 16, ... (lane l takes chunks l, l + 64,
+// One workgroup of 16 waves per sequence (workgroup s: sequence s, its rows, drafts and results
+// at s times the strides): wave w reduces rows w, w + 16, ... (lane l takes chunks l, l + 64,
 // ...); then wave 0 compares the drafts with the targets, one position per lane, and the first
 // mismatch (a ballot) is the accepted length. The draft ids are requested before the partials.
+// A sequence's draft count is n_draft, or n_draft_seq[s] clamped to [0, n_draft] when given.
 __global__ void __launch_bounds__(1024) k_accept_final(const float* pv, const int* pi, int nchunks,
                                                        int n_target, const int32_t* draft, int n_draft,
-                                                       int32_t* target_ids, int32_t* accepted) {
+                                                       int32_t* target_ids, int32_t* accepted,
+                                                       const int32_t* n_draft_seq = nullptr) {
   __shared__ int tgt[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sq = blockIdx.x;
+  pv += (size_t)sq * n_target * nchunks;
+  pi += (size_t)sq * n_target * nchunks;
+  target_ids += (size_t)sq * n_target;
+  accepted += sq;
+  if (draft) draft += (size_t)sq * n_draft;
+  if (n_draft_seq) n_draft = min(max(n_draft_seq[sq], 0), n_draft);
   const int32_t d = (tid < n_draft) ? draft[tid] : 0;  // n_draft <= n_target <= 64
   for (int row = wave; row < n_target; row += 16) {
     float bv = -INFINITY;
@@ -2909,6 +2919,44 @@ size_t accept_prefix_workspace_size(int32_t n_target, int32_t vocab) {
   if (n_target < 1 || n_target > 64 || vocab < 1 || vocab > (1 << 24)) return 0;
   const size_t nchunks = ((size_t)vocab + AM_CHUNK - 1) / AM_CHUNK;
   return align256((size_t)n_target * nchunks * 4) * 2;
+}
+
+size_t accept_prefix_batch_workspace_size(int32_t n_seq, int32_t n_target, int32_t vocab) {
+  if (n_seq < 1 || n_seq > 1024 || n_target < 1 || n_target > 64 || n_seq * n_target > 65535 || vocab < 1 ||
+      vocab > (1 << 24))
+    return 0;
+  const size_t nchunks = ((size_t)vocab + AM_CHUNK - 1) / AM_CHUNK;
+  return align256((size_t)n_seq * n_target * nchunks * 4) * 2;
+}
+
+int accept_prefix_batch(const float* logits, int32_t n_seq, int32_t n_target, int32_t vocab,
+                        const int32_t* draft_ids, int32_t n_draft_max, const int32_t* n_draft,
+                        int32_t* target_ids, int32_t* accepted, void* workspace, size_t ws_bytes,
+                        void* hip_stream) {
+  if (!logits || !target_ids || !accepted || !workspace || (n_draft_max > 0 && !draft_ids)) return MOE_ERR_NULL;
+  if (n_seq < 1 || n_seq > 1024 || n_target < 1 || n_target > 64 || n_seq * n_target > 65535 || vocab < 1 ||
+      vocab > (1 << 24) || n_draft_max < 0 || n_draft_max > n_target)
+    return MOE_ERR_SHAPE;
+  if (!aligned16(logits) || !aligned16(target_ids) || !aligned16(accepted) || !aligned16(workspace) ||
+      (draft_ids && !aligned16(draft_ids)) || (n_draft && !aligned16(n_draft)))
+    return MOE_ERR_ALIGN;
+  const size_t need = accept_prefix_batch_workspace_size(n_seq, n_target, vocab);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const size_t lbytes = (size_t)n_seq * n_target * vocab * 4;
+  const size_t tbytes = (size_t)n_seq * n_target * 4, abytes = (size_t)n_seq * 4;
+  if (overlaps(target_ids, tbytes, logits, lbytes) || overlaps(accepted, abytes, logits, lbytes) ||
+      overlaps(target_ids, tbytes, workspace, need) || overlaps(accepted, abytes, workspace, need) ||
+      overlaps(accepted, abytes, target_ids, tbytes))
+    return MOE_ERR_ALIAS;
+  const int nchunks = (vocab + AM_CHUNK - 1) / AM_CHUNK;
+  float* pv = (float*)workspace;
+  int* pi = (int*)((uint8_t*)workspace + need / 2);
+  hipStream_t s = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  k_argmax_partial<<<dim3(nchunks, n_seq * n_target), 256, 0, s>>>(logits, vocab, nchunks, pv, pi);
+  k_accept_final<<<n_seq, 1024, 0, s>>>(pv, pi, nchunks, n_target, n_draft_max > 0 ? draft_ids : nullptr,
+                                        n_draft_max, target_ids, accepted, n_draft);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const int32_t* draft_ids,

@@ -163,6 +163,31 @@ def test_accept_prefix_validation(b):
     assert f(lg, 17, 151936, dr, 16, tg, tg, ws, need, None) == -6
 
 
+def test_accept_prefix_batch_validation(b):
+    f = b.lib.accept_prefix_batch
+    ws = FAKE + 0x50000000
+    need = b.lib.accept_prefix_batch_workspace_size(32, 17, 151936)
+    assert need >= 32 * b.lib.accept_prefix_workspace_size(17, 151936) - 32 * 512
+    assert b.lib.accept_prefix_batch_workspace_size(0, 17, 10) == 0
+    assert b.lib.accept_prefix_batch_workspace_size(1025, 17, 10) == 0
+    assert b.lib.accept_prefix_batch_workspace_size(1024, 64, 10) == 0   # more than 65535 rows
+    assert b.lib.accept_prefix_batch_workspace_size(4, 65, 10) == 0
+    assert b.lib.accept_prefix_batch_workspace_size(4, 17, 0) == 0
+    lg, dr, nd, tg, ac = FAKE, FAKE + 0x20000000, FAKE + 0x21000000, FAKE + 0x22000000, FAKE + 0x23000000
+    assert f(None, 32, 17, 151936, dr, 16, nd, tg, ac, ws, need, None) == -1
+    assert f(lg, 32, 17, 151936, None, 16, nd, tg, ac, ws, need, None) == -1
+    assert f(lg, 32, 17, 151936, dr, 16, nd, None, ac, ws, need, None) == -1
+    assert f(lg, 0, 17, 151936, dr, 16, nd, tg, ac, ws, need, None) == -2
+    assert f(lg, 32, 17, 151936, dr, 18, nd, tg, ac, ws, need, None) == -2
+    assert f(lg, 32, 17, 151936, dr, -1, nd, tg, ac, ws, need, None) == -2
+    assert f(lg, 1024, 64, 151936, dr, 16, nd, tg, ac, ws, need, None) == -2
+    assert f(lg, 32, 17, 151936, dr, 16, nd + 4, tg, ac, ws, need, None) == -4
+    assert f(lg, 32, 17, 151936, dr, 16, nd, tg, ac, ws, need - 1, None) == -5
+    assert f(lg, 32, 17, 151936, dr, 16, nd, lg + 4096, ac, ws, need, None) == -6   # targets inside the logits
+    assert f(lg, 32, 17, 151936, dr, 16, nd, tg, tg + 64, ws, need, None) == -6     # accepted inside the targets
+    assert f(lg, 32, 17, 151936, dr, 16, nd, tg, ws + 256, ws, need, None) == -6    # accepted inside the workspace
+
+
 def test_lm_head_accept_validation(b):
     f = b.lib.lm_head_accept
     V, H = 151936, 2048

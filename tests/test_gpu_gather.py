@@ -227,3 +227,71 @@ def test_gather_determinism_and_stale_workspace(B):
     run(B, layer, gen.hidden_states(wl, rep=10, k=1024), ws=ws)
     g = run(B, layer, x, ws=ws)
     assert np.array_equal(g["y"], base["y"])
+
+
+# ---- greedy acceptance for many sequences (accept_prefix_batch) -------------------------------
+def run_accept_batch(B, logits, drafts, n_draft=None):
+    S, NT, V = logits.shape
+    print(f"[accept_batch] n_seq={S} n_target={NT} vocab={V}", flush=True)
+    lg = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).cuda()
+    dr = torch.from_numpy(np.ascontiguousarray(drafts, dtype=np.int32)).cuda() if drafts is not None else None
+    nd = torch.from_numpy(np.asarray(n_draft, dtype=np.int32)).cuda() if n_draft is not None else None
+    tg = torch.full((S, NT), -1, dtype=torch.int32, device="cuda")
+    ac = torch.full((S,), -1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(B.accept_prefix_batch_workspace_size(S, NT, V), dtype=torch.uint8, device="cuda")
+    B.accept_prefix_batch(lg, dr, tg, ac, ws, n_draft=nd)
+    torch.cuda.synchronize()
+    return tg.cpu().numpy().astype(np.int64), ac.cpu().numpy().astype(np.int64)
+
+
+def test_accept_prefix_batch_32_sequences(B):
+    """32 sequences x 17 rows x 151936: geometric drafts per sequence, each sequence with its own
+    draft count; the drafts past a sequence's count are its targets (a kernel that read them
+    would accept too much)."""
+    wl = gen.WORKLOADS["verify"]
+    S = 32
+    logits = np.stack([gen.target_logits(wl, rep=500 + s)[0] for s in range(S)])
+    t_ref = np.stack([oracle.argmax_first(logits[s]) for s in range(S)])
+    rng = np.random.default_rng(12)
+    n_d = rng.integers(0, 17, size=S)
+    drafts = t_ref[:, :16].copy()
+    for s in range(S):
+        planted = gen.target_logits(wl, rep=500 + s)[1]
+        d, _ = gen.draft_ids(wl, planted, rep=600 + s)
+        drafts[s, :n_d[s]] = d[:n_d[s]]
+    tg, ac = run_accept_batch(B, logits, drafts, n_d)
+    assert np.array_equal(tg, t_ref)
+    for s in range(S):
+        assert ac[s] == oracle.accept_length(drafts[s, :n_d[s]], t_ref[s]), s
+    # every sequence with the full count, and the same as accept_prefix one sequence at a time
+    tg2, ac2 = run_accept_batch(B, logits, drafts)
+    assert np.array_equal(tg2, t_ref)
+    for s in (0, 7, 31):
+        lg = torch.from_numpy(logits[s]).cuda()
+        dr = torch.from_numpy(drafts[s].astype(np.int32)).cuda()
+        one_t = torch.empty(17, dtype=torch.int32, device="cuda")
+        one_a = torch.empty(4, dtype=torch.int32, device="cuda")
+        ws = torch.empty(B.accept_prefix_workspace_size(17, wl.vocab), dtype=torch.uint8, device="cuda")
+        B.accept_prefix(lg, dr, one_t, one_a, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(one_t.cpu().numpy(), t_ref[s]) and int(one_a[0].item()) == ac2[s]
+        assert ac2[s] == oracle.accept_length(drafts[s], t_ref[s])
+
+
+def test_accept_prefix_batch_counts_clamped_and_small_vocab(B):
+    """Device draft counts outside [0, n_draft_max] are clamped; 1024 sequences over a tiny
+    vocabulary (17408 rows) with exact ties; no drafts at all."""
+    rng = np.random.default_rng(13)
+    S, NT, V = 1024, 17, 7
+    logits = rng.integers(0, 3, size=(S, NT, V)).astype(np.float32)  # many exact ties
+    t_ref = np.stack([oracle.argmax_first(logits[s]) for s in range(S)])
+    drafts = t_ref[:, :16].copy()
+    drafts[:, 9] = (drafts[:, 9] + 1) % V
+    n_d = rng.integers(-5, 30, size=S)
+    tg, ac = run_accept_batch(B, logits, drafts, n_d)
+    assert np.array_equal(tg, t_ref)
+    for s in range(S):
+        nd = min(max(int(n_d[s]), 0), 16)
+        assert ac[s] == oracle.accept_length(drafts[s, :nd], t_ref[s]), (s, n_d[s])
+    tg, ac = run_accept_batch(B, logits, None)
+    assert np.array_equal(tg, t_ref) and np.all(ac == 0)
