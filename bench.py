@@ -479,6 +479,40 @@ def main():
                          "gateup_GBps": round(gub / (sm[1] * 1e-3) / 1e9, 1),
                          "down_GBps": round(dnb / (sm[2] * 1e-3) / 1e9, 1)})
             del blocks
+        # the same over the 40-layer stack's mxfp4 layer (pre-norm, residual): 4 rotating copies
+        mw = gen.WORKLOADS["stack40_mxfp4"]
+        mbase = device.layer_tensors(mw, 0, dev)
+        mlayers = [device.make_layer(mw, 0, dev, tensors=mbase)] + [
+            device.make_layer(mw, 0, dev, tensors={n: (t.clone() if t is not None else None) for n, t in mbase.items()})
+            for _ in range(3)]
+        del mbase
+        mws = torch.empty(mlayers[0].workspace_size(tmax), dtype=torch.uint8, device=dev)
+        mrows = []
+        for T in ((args.batched_tokens,) if args.batched_tokens else (64, 256, 512, 1024)):
+            blocks = [torch.from_numpy(gen.hidden_states(mw, rep=400 + p, k=T)).to(dev) for p in range(2)]
+            reps = 8
+            nw = torch.zeros((reps + 1, 4), dtype=torch.int32, device=dev)
+            evs = ev.create(5 * reps)
+            for i in range(3):
+                binding.moe_verify_block(mlayers[i % 4], blocks[i % 2], 3, by[:T], bids[:T], bwt[:T], nw[reps], mws)
+            torch.cuda.synchronize()
+            for i in range(reps):
+                binding.moe_verify_block_timed(mlayers[i % 4], blocks[i % 2], 3, by[:T], evs[5 * i:5 * i + 5],
+                                               bids[:T], bwt[:T], nw[i], mws)
+            torch.cuda.synchronize()
+            seg = np.array([[ev.ms(evs[5 * i + j], evs[5 * i + j + 1]) for j in range(4)] for i in range(reps)])
+            tot = np.array([ev.ms(evs[5 * i], evs[5 * i + 4]) for i in range(reps)])
+            ev.destroy(evs)
+            Us = nw[:reps, 0].cpu().numpy().astype(np.float64)
+            t_ms = float(tot.mean())
+            byt = float(np.mean([layer_bytes(mw.shape, u, T) for u in Us]))
+            sm = seg.mean(axis=0)
+            mrows.append({"tokens": T, "sequences": T // 16, "U_mean": round(float(Us.mean()), 2), "ms": round(t_ms, 4),
+                          "tokens_per_s": round(T / (t_ms * 1e-3)), "GBps": round(byt / (t_ms * 1e-3) / 1e9, 1),
+                          "kernels_us": {"route": round(sm[0] * 1e3, 2), "gateup": round(sm[1] * 1e3, 2),
+                                         "down": round(sm[2] * 1e3, 2), "combine": round(sm[3] * 1e3, 2)}})
+            del blocks
+        del mlayers, mws
         # greedy acceptance of 32 sequences at once: 32 x 17 rows x V logits
         ns = 32
         blg = torch.randn((ns, NT, V), device=dev, generator=torch.Generator(device=dev).manual_seed(wl.seed))
@@ -505,6 +539,8 @@ def main():
                                "layer (bf16); event times per call, route = router + top-K + permutation",
                    "accept_32_sequences": accept_batch,
                    "points": rows,
+                   "points_mxfp4": {"workload": "the 40-layer stack's mxfp4 layer (pre-norm, residual, bf16 shared "
+                                                "expert) over 4..64 sequences x 16 tokens", "points": mrows},
                    "single_block_k16_ms": sweep_k[-1]["ms"] if sweep_k else None}
         del bws, by
         print("[bench] gathered path done", file=sys.stderr, flush=True)

@@ -121,8 +121,8 @@ typedef struct moe_layer {
 } moe_layer;
 
 /* Bytes of device workspace moe_verify_block needs for calls of up to k_max tokens, on either
- * path, 1 <= k_max <= 1024 (0 if the layer description is invalid, k_max is out of range, or
- * k_max > 16 with mxfp4 weights). Host only. */
+ * path, 1 <= k_max <= 1024 (0 if the layer description is invalid or k_max is out of range).
+ * Host only. */
 size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max);
 
 /* One MoE layer over a verify block.
@@ -134,8 +134,9 @@ size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max);
  *            tokens are sorted by expert (a deterministic counting sort) and each woken expert
  *            is applied to its own tokens only, 32 token columns per weight pass. That is the
  *            regime of batched serving, where the verify step becomes compute-heavy
- *            (DFlash-on-MI355X article, section "Results: Throughput and Speedup"). The
- *            gathered path takes bf16 layers (an mxfp4 layer returns MOE_ERR_DTYPE there).
+ *            (DFlash-on-MI355X article, section "Results: Throughput and Speedup"). With
+ *            mxfp4 weights the routed experts run on the scaled matrix-core instruction there
+ *            too (MX-fp8 hi/lo activations) and the shared expert in bf16.
  *   flags    MOE_PRE_RMSNORM | MOE_RESIDUAL | MOE_GATHER
  *   y        fp32 [k][H]  output; must not overlap x or the workspace
  *   topk_ids int32 [k][K] or NULL: each token's experts, descending router logit, equal logits

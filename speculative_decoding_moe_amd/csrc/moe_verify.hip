@@ -2007,6 +2007,9 @@ struct BArgs {
   const uint8_t* shg;
   const uint8_t* shu;
   const uint8_t* shd;
+  const uint8_t* sg;  // mxfp4 scales of the routed experts (NULL for bf16 layers)
+  const uint8_t* su;
+  const uint8_t* sd;
   float* logits;    // [T][E] raw router logits (un-normalised input)
   float* rinv;      // [T] RMSNorm factor (1 without pre-norm)
   uint8_t* xg;      // [T][H/128][512 B] bf16 hi/lo B fragments of each token, k-step j, half hl,
@@ -2021,12 +2024,28 @@ struct BArgs {
   float* brv;       // [T K + T] RMSNorm factor of the token at position p
   int32_t* bpos;    // [T][K] list position of (token, slot)
   uint8_t* af;      // [(T K + T + 16)][I/128][512 B] down B operands per list position
+  uint8_t* xgm;     // mxfp4 layers: [T][H/128][MXT] MX-fp8 hi/lo B windows of each token (else NULL)
+  uint8_t* afm;     // mxfp4 layers: [(T K + T + 16)][I/128][MXT] down B windows per list position
   float* part;      // [T K + T][H] fp32 partial rows per list position
   int H, E, K, I, Is, T, pre_norm, residual;
   float eps;
 };
 
 __device__ __forceinline__ int* ut_arr(const BArgs& a, int which) { return a.ut + which * (a.E + 2); }
+
+// Token-major MX-fp8 window of one column (128 values, mxfp4 layers): hi [4 lane quads][32 B] and
+// lo [4][32 B] in the scaled instruction's B-lane byte order (quad q holds K = 16 q + j in bytes
+// j < 16 and K = 64 + 16 q + j in bytes 16 + j), then the scale words of the four 32-blocks (hi
+// exponent in byte 0, lo in byte 1): the column's share of an MXW window, contiguous.
+constexpr int MXT = 272;
+__device__ __forceinline__ void mx8_store16_tok(uint8_t* tw, int blk, int h, const uint32_t (&hi)[4],
+                                                const uint32_t (&lo)[4], int eh, int el) {
+  const int q = 2 * (blk & 1) + h, off = 16 * (blk >> 1);
+  *reinterpret_cast<u32x4*>(tw + q * 32 + off) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  *reinterpret_cast<u32x4*>(tw + 128 + q * 32 + off) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+  if (h == 0)
+    *reinterpret_cast<uint32_t*>(tw + 256 + 4 * blk) = (uint32_t)(eh + 127) | ((uint32_t)(el + 127) << 8);
+}
 
 struct BRouterSmem {
   float red[NW * 256];
@@ -2097,6 +2116,30 @@ __global__ void __launch_bounds__(NTH) k_brouter(BArgs a) {
       uint8_t* dst = a.xg + ((size_t)tok * nwt + w) * 512;
       *reinterpret_cast<u32x4*>(dst + ((j * 2 + 0) * 4 + qq) * 16) = hv;
       *reinterpret_cast<u32x4*>(dst + ((j * 2 + 1) * 4 + qq) * 16) = lv;
+    }
+  }
+  // mxfp4 layers: the MX-fp8 windows of the routed experts' B operands, one wave per window,
+  // lane (column c, 32-block blk)
+  if (a.xgm) {
+    const int c = lane & 15, blk = lane >> 4, tok = tt * 16 + c;
+    for (int w = et + nte * wave; w < nwt; w += nte * NW) {
+      float v[32];
+      const float* src = a.x + (size_t)(tok < T ? tok : 0) * H + w * WIN + 32 * blk;
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const float4 f = *reinterpret_cast<const float4*>(src + 4 * g);
+        v[4 * g + 0] = f.x; v[4 * g + 1] = f.y; v[4 * g + 2] = f.z; v[4 * g + 3] = f.w;
+      }
+      uint32_t hi[8], lo[8];
+      int eh, el;
+      mx8_quant<32, false>(v, hi, lo, eh, el);
+      if (tok < T) {
+        uint8_t* tw = a.xgm + ((size_t)tok * nwt + w) * MXT;
+        const uint32_t h0[4] = {hi[0], hi[1], hi[2], hi[3]}, h1[4] = {hi[4], hi[5], hi[6], hi[7]};
+        const uint32_t l0[4] = {lo[0], lo[1], lo[2], lo[3]}, l1[4] = {lo[4], lo[5], lo[6], lo[7]};
+        mx8_store16_tok(tw, blk, 0, h0, l0, eh, el);
+        mx8_store16_tok(tw, blk, 1, h1, l1, eh, el);
+      }
     }
   }
 }
@@ -2256,9 +2299,32 @@ __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
     }
 }
 
-// A operands of one tick for one wave: two 16-row bands x four k-steps of one window
+// Geometry of one tick of the gathered expert kernels. bf16: one 128-wide window per tick, the
+// B windows as (k-step half jh, lane) pieces of the bf16 hi/lo fragments (8 KiB per 16 columns).
+// mxfp4: two windows per tick (the same bytes of A per tick as bf16), the B windows as MX-fp8
+// hi/lo operands with their scale words (MXW bytes per 16 columns).
+template <bool GU, bool MX>
+struct BGeo {
+  static constexpr int NKH = GU ? 2 : 1;                    // K halves (gate/up)
+  static constexpr int NWT = MX ? 2 : 1;                    // windows per tick
+  static constexpr int NCB = NKH * NWT * BCG;               // 16-column B windows per tick
+  static constexpr int CBB = MX ? MXW : 8192;               // ring bytes per B window
+  static constexpr int NCH = MX ? NCB * 256 / NTH : NCB;    // 16-byte B pieces per thread and tick
+  static constexpr int RING = NCB * CBB;                    // ring bytes per slot
+};
+static_assert(BCG == 2, "the staging maps below assume two column tiles per item");
+
+// A operands of one tick for one wave: bf16, two 16-row bands x four k-steps of one window;
+// mxfp4, two bands x two windows of codes (v[band * 2 + window]) and their scale bytes
 struct BWin {
-  u32x4 v[8];  // [band * 4 + j]
+  u32x4 v[8];
+  uint32_t sc[4];
+};
+
+// B pieces of one tick held by one thread (and, mxfp4, one scale word)
+struct BReg {
+  u32x4 v[4];
+  uint32_t s;
 };
 
 // wave-uniform description of a gathered item for one wave
@@ -2267,19 +2333,21 @@ struct BItem {
   int rb;                 // row block
   bool shared;
   bool cached;            // the slot's weights are read by several column groups
-  uint32_t aoff;          // byte offset of the wave's first A band in its tensor
+  uint32_t aoff;          // byte offset of the wave's first A band (codes for mxfp4) in its tensor
+  uint32_t soff;          // byte offset of its scales (mxfp4)
 };
 
 template <bool GU>
 struct BSmem {
-  static constexpr int NKH = GU ? 2 : 1;
-  u32x4 ring[2][NKH * BCG * 8 * 64];  // [slot][((kh * BCG + ct) * 8 + jh) * 64 + lane]
+  static constexpr int RB = BGeo<GU, false>::RING > BGeo<GU, true>::RING ? BGeo<GU, false>::RING
+                                                                          : BGeo<GU, true>::RING;
+  alignas(16) uint8_t ring[2][RB];
   float red[GU ? 4 * 2 * BCG * 256 : 1];
   float act[GU ? 4 * BCG * 256 : 1];
   int ue[MAX_E + 2], uoff[MAX_E + 2], ucnt[MAX_E + 2], pre[MAX_E + 2];
 };
 
-template <bool GU>
+template <bool GU, bool MX>
 __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int U, int idx, int wave) {
   // slot: the largest u <= U with pre[u] <= idx (every slot below U + 1 with items has pre
   // strictly increasing)
@@ -2294,7 +2362,7 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
   d.off = S.uoff[lo];
   d.cnt = S.ucnt[lo];
   // column groups fastest: the items that read the same weights are consecutive, so they run
-  // together on one XCD (see the item order in k_bexp) and all but the first read hit its L2
+  // together on one XCD (see the item order in bexp_run) and all but the first read hit its L2
   const int ncg = (d.cnt + 16 * BCG - 1) / (16 * BCG);
   const int cg = loc % ncg;
   d.rb = loc / ncg;
@@ -2303,122 +2371,192 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
   const int e = S.ue[lo];
   d.shared = e < 0;
   const uint32_t eb = d.shared ? 0u : (uint32_t)e;
-  if (GU) {  // wave (rt, kh): rows rb 64 + 16 rt of gate and up
-    const uint32_t row = eb * (uint32_t)a.I + (uint32_t)(d.rb * 64 + 16 * (wave & 3));
-    d.aoff = row * (uint32_t)(a.H * 2);
-  } else {   // wave w: row tiles rb 256 + 32 w (+ 16)
-    const uint32_t row = eb * (uint32_t)a.H + (uint32_t)(d.rb * 256 + 32 * wave);
-    d.aoff = row * (uint32_t)(a.I * 2);
-  }
+  // gate/up wave (rt, kh): rows rb 64 + 16 rt of gate and up; down wave w: row tiles rb 256 + 32 w (+ 16)
+  const uint32_t row = GU ? eb * (uint32_t)a.I + (uint32_t)(d.rb * 64 + 16 * (wave & 3))
+                          : eb * (uint32_t)a.H + (uint32_t)(d.rb * 256 + 32 * wave);
+  const uint32_t K = GU ? (uint32_t)a.H : (uint32_t)a.I;  // reduction length of a row
+  d.aoff = MX ? row * (K / 2) : row * (K * 2);
+  d.soff = MX ? row * (K / 32) : 0u;
   d.u = __builtin_amdgcn_readfirstlane(d.u);
   d.off = __builtin_amdgcn_readfirstlane(d.off);
   d.cnt = __builtin_amdgcn_readfirstlane(d.cnt);
   d.col0 = __builtin_amdgcn_readfirstlane(d.col0);
   d.rb = __builtin_amdgcn_readfirstlane(d.rb);
   d.aoff = __builtin_amdgcn_readfirstlane(d.aoff);
+  d.soff = __builtin_amdgcn_readfirstlane(d.soff);
   d.cached = __builtin_amdgcn_readfirstlane((int)d.cached) != 0;
   d.shared = __builtin_amdgcn_readfirstlane((int)d.shared) != 0;
   return d;
 }
 
-// B chunks of one tick held by one thread: (kh, ct) for the thread's (k-step half jh, lane)
-template <bool GU>
-struct BReg {
-  u32x4 v[(GU ? 2 : 1) * BCG];
-};
-
-template <bool GU>
-__global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
-  constexpr int NKH = GU ? 2 : 1;
-  __shared__ BSmem<GU> S;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = a.H, I = a.I;
-  const int U = __builtin_amdgcn_readfirstlane(a.tab[0]);
-  const int n_items = __builtin_amdgcn_readfirstlane(a.tab[GU ? 1 : 2]);
-  for (int i = tid; i <= U + 1; i += NTH) {
-    S.ue[i] = ut_arr(a, 0)[i];
-    S.uoff[i] = ut_arr(a, 1)[i];
-    S.ucnt[i] = ut_arr(a, 2)[i];
-    S.pre[i] = ut_arr(a, GU ? 3 : 4)[i];
-  }
-  // items m G + slot(b): the workgroups of one XCD (b mod 8) take consecutive items, which share
-  // their gathered columns in that XCD's L2
+// One phase of a gathered expert kernel: items base .. base + n_items - 1 of one format, dealt
+// m G + position, where a workgroup's position is its XCD-grouped slot (the 32 workgroups of an
+// XCD take consecutive items, which share their gathered columns and repeated weights in that
+// XCD's L2) rotated by rot, so a phase that follows another starts its deal after the
+// workgroups the first one loaded.
+template <bool GU, bool MX>
+__device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_items, int rot, int tid,
+                         int lane, int wave) {
+  using GE = BGeo<GU, MX>;
   const int G = gridDim.x, b = blockIdx.x;
   const int slotb = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-  const int n_my = slotb < n_items ? (n_items - slotb + G - 1) / G : 0;
+  const int pos = (slotb - rot % G + G) % G;
+  const int n_my = pos < n_items ? (n_items - pos + G - 1) / G : 0;
   if (n_my == 0) return;  // uniform over the workgroup
-  __syncthreads();
 
-  const int nwt = H / WIN;                       // windows of the A reduction (gate/up: H)
-  const int ns = GU ? (nwt + 1) / 2 : I / WIN;   // ticks per item
+  const int H = a.H, I = a.I;
+  const int nwt = H / WIN;                     // windows of a token row (gate/up B source)
+  const int nwk = GU ? nwt : I / WIN;          // windows of the A reduction
+  const int nwh = GU ? (nwk + 1) / 2 : nwk;    // windows per K half
+  const int ns = (nwh + GE::NWT - 1) / GE::NWT;  // ticks per item
   const int ticks = n_my * ns;
   const int kh = GU ? (wave >> 2) : 0;
   const uint32_t E = a.E;
-  const uint32_t abytes = GU ? E * (uint32_t)I * H * 2 : E * (uint32_t)H * I * 2;
-  const uint32_t sbytes = GU ? (uint32_t)a.Is * H * 2 : (uint32_t)H * a.Is * 2;
-  const rsrc_t r0 = buf_rsrc(GU ? a.wg : a.wd, abytes), r1 = buf_rsrc(a.wu, GU ? abytes : 0);
-  const rsrc_t s0 = buf_rsrc(GU ? a.shg : a.shd, sbytes), s1 = buf_rsrc(a.shu, GU ? sbytes : 0);
-  const uint32_t band2 = GU ? 0u : (uint32_t)(16 * I * 2);  // down: second tile 16 rows below
+  const uint32_t anum = GU ? E * (uint32_t)I * H : E * (uint32_t)H * I;  // values of a routed tensor
+  const rsrc_t r0 = buf_rsrc(GU ? a.wg : a.wd, MX ? anum / 2 : anum * 2);
+  const rsrc_t r1 = buf_rsrc(a.wu, GU ? (MX ? anum / 2 : anum * 2) : 0);
+  const rsrc_t q0 = buf_rsrc(GU ? a.sg : a.sd, MX ? anum / 32 : 0);
+  const rsrc_t q1 = buf_rsrc(a.su, (GU && MX) ? anum / 32 : 0);
+  const uint32_t snum = (uint32_t)a.Is * H;  // values of a shared-expert tensor (bf16)
+  const rsrc_t s0 = buf_rsrc(GU ? a.shg : a.shd, snum * 2), s1 = buf_rsrc(a.shu, GU ? snum * 2 : 0);
   const uint32_t vl = (uint32_t)lane * 16u;
-  // B staging: thread (jh, ln) = (tid / 64, tid % 64), column c = ln % 16, quad q = ln / 16
-  const int jh = tid >> 6, ln = tid & 63, bc = ln & 15, bq = ln >> 4;
   const int npos = a.T * a.K + a.T;
-  const rsrc_t rx = buf_rsrc(GU ? (const void*)a.xg : (const void*)a.af,
-                             GU ? (uint32_t)a.T * H * 4 : (uint32_t)(npos + 16) * I * 4);
+  const int bwr = GU ? nwt : I / WIN;  // windows per B source row
+  const uint8_t* bsrc = MX ? (GU ? a.xgm : a.afm) : (GU ? a.xg : a.af);
+  const rsrc_t rx = buf_rsrc(bsrc, (uint32_t)(GU ? a.T : npos + 16) * (uint32_t)bwr * (MX ? MXT : 512));
+  // B staging. bf16: thread (jh, ln) = (tid / 64, tid % 64) holds piece (jh, q = ln / 16) of
+  // column ln % 16 for every (K half, column tile). mxfp4: thread tid holds piece tid % 16 of
+  // column (tid / 16) % 16 of column tile (tid / 256) % 2 for the B windows (tid / 256) + 2 m,
+  // and, below NCB 64, scale word tid % 4 of column (tid / 4) % 16 of B window tid / 64.
+  const int jh = tid >> 6, ln = tid & 63, bc = ln & 15, bq = ln >> 4;
+  const int mc = (tid >> 4) & 15, mch = tid & 15, mct = (tid >> 8) & 1;
+  const int scb = tid >> 6, sc_c = (tid >> 2) & 15, sblk = tid & 3;
 
   auto item_of = [&](int m) {
     const int mm = m < n_my ? m : n_my - 1;  // past the end: the last item again (valid loads)
-    return b_item<GU>(a, S, U, mm * G + slotb, wave);
+    return b_item<GU, MX>(a, S, U, base + mm * G + pos, wave);
+  };
+  // window of B window-slot (K half h, tick window v) at tick step, and whether it exists
+  auto win_of = [&](int h, int v, int step, bool& ok) {
+    const int wl = step * GE::NWT + v;
+    const int w = (GU ? h * nwh : 0) + wl;
+    ok = wl < nwh && w < nwk;
+    return w;
   };
   auto load_a = [&](BWin& W, const BItem& d, int step) {
-    const int w = GU ? kh * ns + step : step;
-    const uint32_t so = d.aoff + (uint32_t)w * 4096u;
-    const rsrc_t ra = d.shared ? s0 : r0, rb2 = d.shared ? s1 : r1;
-    if (d.cached) {  // read again by the slot's other column groups: keep in L2
+    if constexpr (!MX) {
+      const int w = GU ? kh * ns + step : step;
+      const uint32_t so = d.aoff + (uint32_t)w * 4096u;
+      const rsrc_t ra = d.shared ? s0 : r0, rb2 = d.shared ? s1 : r1;
+      const uint32_t band2 = (uint32_t)(16 * I * 2);  // down: the second tile, 16 rows below
+      if (d.cached) {  // read again by the slot's other column groups: keep in L2
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        W.v[j] = bld16_cached(ra, vl + j * 1024, so);
-        W.v[4 + j] = GU ? bld16_cached(rb2, vl + j * 1024, so) : bld16_cached(ra, vl + j * 1024, so + band2);
+        for (int j = 0; j < 4; ++j) {
+          W.v[j] = bld16_cached(ra, vl + j * 1024, so);
+          W.v[4 + j] = GU ? bld16_cached(rb2, vl + j * 1024, so) : bld16_cached(ra, vl + j * 1024, so + band2);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          W.v[j] = bld16(ra, vl + j * 1024, so);
+          W.v[4 + j] = GU ? bld16(rb2, vl + j * 1024, so) : bld16(ra, vl + j * 1024, so + band2);
+        }
+      }
+    } else {
+      // band i: gate / up rows (gate/up), or row tile i (down); a window past the reduction
+      // reads the half's first window (finite codes and scales, multiplied by zero B)
+      const uint32_t c2 = GU ? 0u : (uint32_t)(16 * (I / 2)), s2 = GU ? 0u : (uint32_t)(16 * (I / 32));
+#pragma unroll
+      for (int v = 0; v < GE::NWT; ++v) {
+        bool ok;
+        int w = win_of(kh, v, step, ok);
+        if (!ok) w = GU ? kh * nwh : 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const rsrc_t rc = (GU && i) ? r1 : r0, rs = (GU && i) ? q1 : q0;
+          const uint32_t co = d.aoff + (uint32_t)w * 1024u + (i ? c2 : 0u);
+          const uint32_t sco = d.soff + (uint32_t)w * 64u + (i ? s2 : 0u);
+          if (d.cached) {
+            W.v[i * 2 + v] = bld16_cached(rc, vl, co);
+            W.sc[i * 2 + v] = __builtin_amdgcn_raw_buffer_load_b8(rs, (uint32_t)lane, sco, 0);
+          } else {
+            W.v[i * 2 + v] = bld16(rc, vl, co);
+            W.sc[i * 2 + v] = bld1(rs, (uint32_t)lane, sco);
+          }
+        }
+      }
+    }
+  };
+  // gathered B pieces of one tick; padding columns and missing windows read past the resource
+  // (zeros, with no memory access: every real offset is far below 2^31)
+  auto load_b = [&](BReg& R, const int (&src)[2], int step) {
+    if constexpr (!MX) {
+#pragma unroll
+      for (int h = 0; h < GE::NKH; ++h) {
+        bool okw;
+        const int w = win_of(h, 0, step, okw);
+#pragma unroll
+        for (int ct = 0; ct < BCG; ++ct) {
+          const bool ok = src[ct] >= 0 && okw;
+          const uint32_t o = ok ? (uint32_t)((src[ct] * bwr + w) * 512 + (jh * 4 + bq) * 16) : 0x80000000u;
+          R.v[h * BCG + ct] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
+        }
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        W.v[j] = bld16(ra, vl + j * 1024, so);
-        W.v[4 + j] = GU ? bld16(rb2, vl + j * 1024, so) : bld16(ra, vl + j * 1024, so + band2);
+      for (int m = 0; m < GE::NCH; ++m) {
+        const int hv = ((tid >> 8) + 2 * m) >> 1;  // B window index / BCG
+        bool okw;
+        const int w = win_of(hv / GE::NWT, hv % GE::NWT, step, okw);
+        const bool ok = src[0] >= 0 && okw;
+        const uint32_t o = ok ? (uint32_t)((src[0] * bwr + w) * MXT + mch * 16) : 0x80000000u;
+        R.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
+      }
+      {
+        const int hv = scb >> 1;
+        bool okw;
+        const int w = win_of(hv / GE::NWT, hv % GE::NWT, step, okw);
+        const bool ok = tid < GE::NCB * 64 && src[1] >= 0 && okw;
+        const uint32_t o = ok ? (uint32_t)((src[1] * bwr + w) * MXT + 256 + sblk * 4) : 0x80000000u;
+        R.s = __builtin_amdgcn_raw_buffer_load_b32(rx, o, 0, 0);
       }
     }
   };
-  // gathered B chunks of one tick (tokens of the item's columns, or list positions for down)
-  auto load_b = [&](BReg<GU>& R, const BItem& d, const int (&src)[BCG], int step) {
+  auto store_b = [&](const BReg& R, int slot) {
+    uint8_t* ring = S.ring[slot];
+    if constexpr (!MX) {
 #pragma unroll
-    for (int h = 0; h < NKH; ++h) {
-      const int w = GU ? h * ns + step : step;
-      const int nw = GU ? nwt : I / WIN;
+      for (int h = 0; h < GE::NKH; ++h)
 #pragma unroll
-      for (int ct = 0; ct < BCG; ++ct) {
-        // padding columns and windows past the reduction read past the resource: zeros, with no
-        // memory access (every offset of a real column is far below 2^31)
-        const bool ok = src[ct] >= 0 && w < nw;
-        const uint32_t o = ok ? (uint32_t)((src[ct] * nw + w) * 512 + (jh * 4 + bq) * 16) : 0x80000000u;
-        R.v[h * BCG + ct] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
+        for (int ct = 0; ct < BCG; ++ct)
+          reinterpret_cast<u32x4*>(ring)[((h * BCG + ct) * 8 + jh) * 64 + ln] = R.v[h * BCG + ct];
+    } else {
+#pragma unroll
+      for (int m = 0; m < GE::NCH; ++m) {
+        const int cb = (tid >> 8) + 2 * m;
+        const int part = mch >> 3, k8 = mch & 7;  // hi / lo, then (lane quad, 16-byte half)
+        const int o = cb * MXW + part * 2048 + (mc + 16 * (k8 >> 1)) * 32 + 16 * (k8 & 1);
+        *reinterpret_cast<u32x4*>(ring + o) = R.v[m];
       }
+      if (tid < GE::NCB * 64)
+        *reinterpret_cast<uint32_t*>(ring + scb * MXW + 4096 + (sc_c + 16 * sblk) * 4) = R.s;
     }
   };
-  auto store_b = [&](const BReg<GU>& R, int slot) {
+  // the thread's B sources for an item: the token (gate/up) or list position (down) of each of
+  // its columns, -1 past the item's tokens
+  auto src_of = [&](const BItem& d, int (&src)[2]) {
+    int r[2];
+    if constexpr (!MX) {
+      r[0] = d.col0 + bc;
+      r[1] = d.col0 + 16 + bc;
+    } else {
+      r[0] = d.col0 + 16 * mct + mc;
+      r[1] = d.col0 + 16 * (scb & 1) + sc_c;
+    }
 #pragma unroll
-    for (int h = 0; h < NKH; ++h)
-#pragma unroll
-      for (int ct = 0; ct < BCG; ++ct) S.ring[slot][((h * BCG + ct) * 8 + jh) * 64 + ln] = R.v[h * BCG + ct];
-  };
-  // the thread's B source per column tile of an item: the token (gate/up) or the list position
-  // (down) of column bc, -1 past the item's tokens
-  auto src_of = [&](const BItem& d, int (&src)[BCG]) {
-#pragma unroll
-    for (int ct = 0; ct < BCG; ++ct) {
-      const int r = d.col0 + 16 * ct + bc;
-      const int p = d.off + (r < d.cnt ? r : 0);
-      src[ct] = r < d.cnt ? (GU ? a.blist[p] : p) : -1;
+    for (int k = 0; k < 2; ++k) {
+      const int p = d.off + (r[k] < d.cnt ? r[k] : 0);
+      src[k] = r[k] < d.cnt ? (GU ? a.blist[p] : p) : -1;
     }
   };
 
@@ -2427,10 +2565,10 @@ __global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
   // order, so every load whose result steers later loads (the column sources) is issued one
   // item ahead, and a wait for it never drains loads that were issued for later ticks.
   BWin W[BD];
-  BReg<GU> R[BD];
+  BReg R[BD];
   int ma = 0, sa = 0;  // load cursor (item, step)
   BItem da = item_of(0);
-  int srca[BCG], srcn[BCG];
+  int srca[2], srcn[2];
   src_of(da, srca);
   src_of(item_of(1), srcn);
   auto advance = [&]() {
@@ -2438,21 +2576,21 @@ __global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
       sa = 0;
       ++ma;
       da = item_of(ma);
-#pragma unroll
-      for (int ct = 0; ct < BCG; ++ct) srca[ct] = srcn[ct];
+      srca[0] = srcn[0];
+      srca[1] = srcn[1];
       src_of(item_of(ma + 1), srcn);
     }
   };
 #pragma unroll
   for (int j = 0; j < BD - 1; ++j) {
     load_a(W[j], da, sa);
-    load_b(R[j], da, srca, sa);
+    load_b(R[j], srca, sa);
     advance();
   }
   store_b(R[0], 0);
   __syncthreads();
 
-  int mc = 0, sc = 0;  // math cursor
+  int mcur = 0, scur = 0;  // math cursor
   BItem dc = item_of(0);
   f32x4 acc[2][BCG];
 #pragma unroll
@@ -2480,27 +2618,46 @@ __global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
       const int t = t0 + r;
       const int ib = (r + BD - 1) % BD;  // buffers of tick t + BD - 1
       load_a(W[ib], da, sa);
-      load_b(R[ib], da, srca, sa);
+      load_b(R[ib], srca, sa);
       advance();
       __builtin_amdgcn_sched_barrier(0);
       // math of tick t
       {
-        const u32x4* ring = S.ring[t & 1];
+        const uint8_t* ring = S.ring[t & 1];
 #pragma unroll
         for (int ct = 0; ct < BCG; ++ct)
-          if (ct == 0 || dc.col0 + 16 * ct < dc.cnt)  // a column tile of padding only: skipped
+          if (ct == 0 || dc.col0 + 16 * ct < dc.cnt) {  // a column tile of padding only: skipped
+            if constexpr (!MX) {
+              const u32x4* rg = reinterpret_cast<const u32x4*>(ring);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x4 bh = ring[((kh * BCG + ct) * 8 + j * 2 + 0) * 64 + lane];
-            const u32x4 bl = ring[((kh * BCG + ct) * 8 + j * 2 + 1) * 64 + lane];
+              for (int j = 0; j < 4; ++j) {
+                const u32x4 bh = rg[((kh * BCG + ct) * 8 + j * 2 + 0) * 64 + lane];
+                const u32x4 bl = rg[((kh * BCG + ct) * 8 + j * 2 + 1) * 64 + lane];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-              acc[i][ct] = mfma16(W[r].v[i * 4 + j], bh, acc[i][ct]);
-              acc[i][ct] = mfma16(W[r].v[i * 4 + j], bl, acc[i][ct]);
+                for (int i = 0; i < 2; ++i) {
+                  acc[i][ct] = mfma16(W[r].v[i * 4 + j], bh, acc[i][ct]);
+                  acc[i][ct] = mfma16(W[r].v[i * 4 + j], bl, acc[i][ct]);
+                }
+              }
+            } else {
+#pragma unroll
+              for (int v = 0; v < GE::NWT; ++v) {
+                const uint8_t* cbp = ring + ((kh * GE::NWT + v) * BCG + ct) * MXW;
+                const u32x4 bh0 = *reinterpret_cast<const u32x4*>(cbp + lane * 32);
+                const u32x4 bh1 = *reinterpret_cast<const u32x4*>(cbp + lane * 32 + 16);
+                const u32x4 bl0 = *reinterpret_cast<const u32x4*>(cbp + 2048 + lane * 32);
+                const u32x4 bl1 = *reinterpret_cast<const u32x4*>(cbp + 2048 + lane * 32 + 16);
+                const uint32_t bsc = *reinterpret_cast<const uint32_t*>(cbp + 4096 + lane * 4);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                  acc[i][ct] = mfma_mx(W[r].v[i * 2 + v], W[r].sc[i * 2 + v], bh0, bh1, bsc, 0, acc[i][ct]);
+                  acc[i][ct] = mfma_mx(W[r].v[i * 2 + v], W[r].sc[i * 2 + v], bl0, bl1, bsc, 1, acc[i][ct]);
+                }
+              }
             }
           }
       }
-      if (sc + 1 == ns) {  // the item's last tick: epilogue (uniform over the workgroup)
+      if (scur + 1 == ns) {  // the item's last tick: epilogue (uniform over the workgroup)
         if constexpr (GU) {
           const int rt = wave & 3;
           if (kh == 1)
@@ -2525,23 +2682,42 @@ __global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
             }
           }
           __syncthreads();
-          if (tid < 4 * BCG * 2 * 16) {  // (rt, ct, half, column): 8 rows as down B operands
-            const int c = tid & 15, half = (tid >> 4) & 1, ct = (tid >> 5) % BCG, rt2 = tid / (32 * BCG);
-            const int rnk = dc.col0 + 16 * ct + c;
-            if (rnk < dc.cnt) {
-              uint32_t hi[8], lo[8];
+          if constexpr (!MX) {
+            if (tid < 4 * BCG * 2 * 16) {  // (rt, ct, half, column): 8 rows as down B operands
+              const int c = tid & 15, half = (tid >> 4) & 1, ct = (tid >> 5) % BCG, rt2 = tid / (32 * BCG);
+              const int rnk = dc.col0 + 16 * ct + c;
+              if (rnk < dc.cnt) {
+                uint32_t hi[8], lo[8];
 #pragma unroll
-              for (int i = 0; i < 8; ++i)
-                split_bf16(S.act[(rt2 * BCG + ct) * 256 + (8 * half + i) * 16 + c], hi[i], lo[i]);
-              u32x4 hv, lv;
-              pack8(hi, hv);
-              pack8(lo, lv);
-              const int R0 = dc.rb * 64 + 16 * rt2 + 8 * half;  // intermediate row
-              const int w = R0 / WIN, o = R0 % WIN, j = o / 32, qd = (o % 32) / 8;
-              const int p = dc.off + rnk;
-              uint8_t* dst = a.af + ((size_t)p * (I / WIN) + w) * 512;
-              *reinterpret_cast<u32x4*>(dst + ((j * 2 + 0) * 4 + qd) * 16) = hv;
-              *reinterpret_cast<u32x4*>(dst + ((j * 2 + 1) * 4 + qd) * 16) = lv;
+                for (int i = 0; i < 8; ++i)
+                  split_bf16(S.act[(rt2 * BCG + ct) * 256 + (8 * half + i) * 16 + c], hi[i], lo[i]);
+                u32x4 hv, lv;
+                pack8(hi, hv);
+                pack8(lo, lv);
+                const int R0 = dc.rb * 64 + 16 * rt2 + 8 * half;  // intermediate row
+                const int w = R0 / WIN, o = R0 % WIN, j = o / 32, qd = (o % 32) / 8;
+                uint8_t* dst = a.af + ((size_t)(dc.off + rnk) * (I / WIN) + w) * 512;
+                *reinterpret_cast<u32x4*>(dst + ((j * 2 + 0) * 4 + qd) * 16) = hv;
+                *reinterpret_cast<u32x4*>(dst + ((j * 2 + 1) * 4 + qd) * 16) = lv;
+              }
+            }
+          } else {
+            // (ct, 32-row block bb, half h, column c): 16 rows quantised as MX-fp8 hi/lo, the
+            // block maximum shared by the two halves (lanes c and c + 16 of one wave)
+            if (tid < BCG * 2 * 2 * 16) {
+              const int c = tid & 15, h = (tid >> 4) & 1, bb = (tid >> 5) & 1, ct = tid >> 6;
+              float v[16];
+#pragma unroll
+              for (int j = 0; j < 16; ++j) v[j] = S.act[((2 * bb + h) * BCG + ct) * 256 + j * 16 + c];
+              uint32_t hi[4], lo[4];
+              int eh, el;
+              mx8_quant<16, true>(v, hi, lo, eh, el);
+              const int rnk = dc.col0 + 16 * ct + c;
+              if (rnk < dc.cnt) {
+                const int R0 = dc.rb * 64 + 32 * bb;  // intermediate row of the block
+                uint8_t* tw = a.afm + ((size_t)(dc.off + rnk) * (I / WIN) + R0 / WIN) * MXT;
+                mx8_store16_tok(tw, (R0 % WIN) / 32, h, hi, lo, eh, el);
+              }
             }
           }
         } else {
@@ -2563,19 +2739,45 @@ __global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int ct = 0; ct < BCG; ++ct) acc[i][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sc = 0;
-        ++mc;
-        if (mc < n_my) {
-          dc = item_of(mc);
+        scur = 0;
+        ++mcur;
+        if (mcur < n_my) {
+          dc = item_of(mcur);
           col_factors(dc);
         }
       } else {
-        ++sc;
+        ++scur;
       }
       if (t + 1 == ticks) return;
       store_b(R[(r + 1) % BD], (t + 1) & 1);  // B of tick t + 1 (loads issued at tick t - 1)
       __syncthreads();
     }
+  }
+}
+
+// Gathered gate/up (GU) or down items. bf16 layers: one phase over every item. mxfp4 layers: the
+// shared expert's items (bf16) first, then the routed experts' (mxfp4), in one launch.
+template <bool GU, bool MXL>
+__global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
+  __shared__ BSmem<GU> S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int U = __builtin_amdgcn_readfirstlane(a.tab[0]);
+  for (int i = tid; i <= U + 1; i += NTH) {
+    S.ue[i] = ut_arr(a, 0)[i];
+    S.uoff[i] = ut_arr(a, 1)[i];
+    S.ucnt[i] = ut_arr(a, 2)[i];
+    S.pre[i] = ut_arr(a, GU ? 3 : 4)[i];
+  }
+  __syncthreads();
+  const int routed = __builtin_amdgcn_readfirstlane(S.pre[U]);
+  const int total = __builtin_amdgcn_readfirstlane(S.pre[U + 1]);
+  if constexpr (!MXL) {
+    bexp_run<GU, false>(a, S, U, 0, total, 0, tid, lane, wave);
+  } else {
+    bexp_run<GU, false>(a, S, U, routed, total - routed, 0, tid, lane, wave);
+    __syncthreads();  // the next phase reuses the LDS ring
+    bexp_run<GU, true>(a, S, U, 0, routed, total - routed, tid, lane, wave);
   }
 }
 
@@ -2636,7 +2838,7 @@ Layout make_layout(const moe_layer* L, int k) {
 
 // workspace of the gathered path for T tokens
 struct BLayout {
-  size_t tab, ut, logits, rinv, xg, ids, wts, blist, bw, brv, bpos, af, part, total;
+  size_t tab, ut, logits, rinv, xg, ids, wts, blist, bw, brv, bpos, af, part, xgm, afm, total;
 };
 
 BLayout make_blayout(const moe_layer* L, int T) {
@@ -2657,6 +2859,9 @@ BLayout make_blayout(const moe_layer* L, int T) {
   o.bpos = off;   off = align256(off + (size_t)T * K * 4);
   o.af = off;     off = align256(off + (n + 16) * I * 4);
   o.part = off;   off = align256(off + n * H * 4);
+  const bool mx = L->wdtype == MOE_W_MXFP4;  // MX-fp8 B windows of the routed experts
+  o.xgm = off;    off = align256(off + (mx ? (size_t)T * (H / WIN) * MXT : 0));
+  o.afm = off;    off = align256(off + (mx ? (n + 16) * (I / WIN) * MXT : 0));
   o.total = off;
   return o;
 }
@@ -2756,15 +2961,14 @@ const char* moe_status_string(int status) {
 size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max) {
   if (check_layer(layer) != MOE_OK || k_max < 1 || k_max > BT_MAX) return 0;
   const size_t small = make_layout(layer, std::min(k_max, (int32_t)KMAX)).total;
-  if (layer->wdtype != MOE_W_BF16) return k_max > KMAX ? 0 : small;
   return std::max(small, make_blayout(layer, k_max).total);
 }
 
-// the gathered path (k > 16 tokens, or MOE_GATHER): bf16 layers
+// the gathered path (k > 16 tokens, or MOE_GATHER)
 static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t flags, float* y,
                        int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace, size_t ws_bytes,
                        void* hip_stream, void* const* events) {
-  if (L->wdtype != MOE_W_BF16) return MOE_ERR_DTYPE;
+  const bool mx = L->wdtype == MOE_W_MXFP4;
   if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || (topk_ids && !aligned16(topk_ids)) ||
       (topk_w && !aligned16(topk_w)) || (n_woken && !aligned16(n_woken)))
     return MOE_ERR_ALIGN;
@@ -2792,6 +2996,9 @@ static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t f
   a.ut = (int32_t*)(ws + lay.ut); a.blist = (int32_t*)(ws + lay.blist); a.bw = (float*)(ws + lay.bw);
   a.brv = (float*)(ws + lay.brv); a.bpos = (int32_t*)(ws + lay.bpos); a.af = ws + lay.af;
   a.part = (float*)(ws + lay.part);
+  a.sg = L->s_gate; a.su = L->s_up; a.sd = L->s_down;
+  a.xgm = mx ? ws + lay.xgm : nullptr;
+  a.afm = mx ? ws + lay.afm : nullptr;
   a.H = L->hidden; a.E = L->n_experts; a.K = L->top_k; a.I = L->inter; a.Is = L->shared_inter; a.T = T;
   a.pre_norm = (flags & MOE_PRE_RMSNORM) ? 1 : 0; a.residual = (flags & MOE_RESIDUAL) ? 1 : 0;
   a.eps = L->rms_eps;
@@ -2808,11 +3015,13 @@ static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t f
     ok = mark(events, 1, s);
   }
   if (ok) {
-    k_bexp<true><<<cus, NTH, 0, s>>>(a);
+    if (mx) k_bexp<true, true><<<cus, NTH, 0, s>>>(a);
+    else    k_bexp<true, false><<<cus, NTH, 0, s>>>(a);
     ok = mark(events, 2, s);
   }
   if (ok) {
-    k_bexp<false><<<cus, NTH, 0, s>>>(a);
+    if (mx) k_bexp<false, true><<<cus, NTH, 0, s>>>(a);
+    else    k_bexp<false, false><<<cus, NTH, 0, s>>>(a);
     ok = mark(events, 3, s);
   }
   if (ok) {

@@ -74,8 +74,9 @@ def test_workspace_size(b):
     assert n16 <= n17 < n1024 and n1024 % 256 == 0
     assert b.lib.moe_verify_workspace_size(ctypes.byref(L), 1025) == 0
     mx = _layer(b, wdtype=1, s_gate=FAKE + 0x7000, s_up=FAKE + 0x8000, s_down=FAKE + 0x9000)
-    assert b.lib.moe_verify_workspace_size(ctypes.byref(mx), 16) > 0
-    assert b.lib.moe_verify_workspace_size(ctypes.byref(mx), 17) == 0
+    m16 = b.lib.moe_verify_workspace_size(ctypes.byref(mx), 16)
+    m1024 = b.lib.moe_verify_workspace_size(ctypes.byref(mx), 1024)
+    assert 0 < m16 and m1024 > n1024  # the MX-fp8 windows of the gathered path on top
     assert b.lib.moe_verify_workspace_size(None, 4) == 0
     assert b.lib.moe_verify_workspace_size(ctypes.byref(_layer(b, hidden=100)), 4) == 0
 
@@ -118,7 +119,8 @@ def test_gathered_path_validation(b):
     L = _layer(b)
     need = b.lib.moe_verify_workspace_size(ctypes.byref(L), 100)
     assert need > b.lib.moe_verify_workspace_size(ctypes.byref(L), 16)
-    assert _call(b, L, k=100, ws_bytes=need - 1) == -5
+    assert _call(b, L, k=100, ws_bytes=1024) == -5
+    assert _call(b, L, k=1024, ws_bytes=b.lib.moe_verify_workspace_size(ctypes.byref(L), 1024) - 1) == -5
     assert _call(b, L, k=8, flags=4, ws_bytes=0) == -5
     assert _call(b, L, k=100, x=FAKE + 0x10000004) == -4
     assert _call(b, L, k=100, ids=FAKE + 0x30000002) == -4
@@ -126,10 +128,11 @@ def test_gathered_path_validation(b):
     assert _call(b, L, k=100, y=FAKE + 0x40000000 + 256) == -6           # y overlaps the workspace
     assert _call(b, L, k=100, ids=FAKE + 0x40000000 + need - 64) == -6   # ids overlap the workspace
     assert _call(b, L, k=100, flags=1 | 2 | 8) == -8
-    # mxfp4 layers: the gathered path takes bf16 weights only
+    # mxfp4 layers: the gathered path needs its larger workspace (MX-fp8 windows)
     mx = _layer(b, wdtype=1, s_gate=FAKE + 0x7000, s_up=FAKE + 0x8000, s_down=FAKE + 0x9000)
-    assert _call(b, mx, k=17, ws_bytes=1 << 30) == -3
-    assert _call(b, mx, k=16, flags=4, ws_bytes=1 << 30) == -3
+    assert _call(b, mx, k=17, ws_bytes=1024) == -5
+    assert _call(b, mx, k=1024, ws_bytes=b.lib.moe_verify_workspace_size(ctypes.byref(mx), 1024) - 1) == -5
+    assert _call(b, mx, k=16, flags=4, ws_bytes=1024) == -5
 
 
 def test_mxfp4_layer_needs_h_multiple_of_256(b):

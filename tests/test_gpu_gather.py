@@ -295,3 +295,69 @@ def test_accept_prefix_batch_counts_clamped_and_small_vocab(B):
         assert ac[s] == oracle.accept_length(drafts[s, :nd], t_ref[s]), (s, n_d[s])
     tg, ac = run_accept_batch(B, logits, None)
     assert np.array_equal(tg, t_ref) and np.all(ac == 0)
+
+
+# ---- mxfp4 layers on the gathered path -----------------------------------------------------
+MX_TOL = 3e-2
+
+
+def check_outputs_tol(g, x, wl, tokens, flags, tol, compare_delta):
+    rows = np.asarray(tokens)
+    kw = dict(pre_norm=bool(flags & PRE), residual=bool(flags & RES), rms_eps=wl.rms_eps)
+    ref = oracle.moe_block(x[rows], GenLayer(wl, 0), wl.shape.top_k, forced_ids=g["ids"][rows], **kw)
+    gy, ry = g["y"][rows].astype(np.float64), ref["y"]
+    if compare_delta:
+        gy, ry = gy - x[rows], ry - x[rows]
+    rms = float(np.sqrt(np.mean(ry ** 2)))
+    err = float(np.abs(gy - ry).max())
+    assert err <= tol * rms, f"max|dy| {err:.3e} > {tol} x RMS {rms:.3e}"
+    return err / rms
+
+
+@pytest.mark.parametrize("k", [17, 100, 512])
+def test_gather_mxfp4_layer(B, k):
+    """The 40-layer stack's mxfp4 layer (pre-norm, residual, bf16 shared expert) over k tokens:
+    routing of every token, the MoE delta of sampled tokens within 3e-2 x RMS."""
+    wl = gen.WORKLOADS["stack40_mxfp4"]
+    layer = dev_layer(wl)
+    x = gen.hidden_states(wl, rep=700 + k, k=k)
+    g = run(B, layer, x, PRE | RES)
+    check_routing(g, x, wl, flags=PRE)
+    rng = np.random.default_rng(k + 1)
+    sample = sorted(set([0, k - 1] + rng.choice(k, size=min(k, 8), replace=False).tolist()))
+    r = check_outputs_tol(g, x, wl, sample, PRE | RES, MX_TOL, True)
+    print(f"mxfp4 gathered k={k}: U={g['n_woken']} delta err/rms={r:.2e}")
+
+
+def test_gather_mxfp4_matches_single_block_and_rows_independent(B):
+    """k = 16 through both mxfp4 paths (the same ids; both deltas within the bar), and each row
+    of a 300-token call bit-identical to the same tokens in a 37-token call."""
+    wl = gen.WORKLOADS["stack40_mxfp4"]
+    layer = dev_layer(wl)
+    x = gen.hidden_states(wl, rep=31)
+    a = run(B, layer, x, PRE | RES)
+    b = run(B, layer, x, PRE | RES | GATHER)
+    assert np.array_equal(a["ids"], b["ids"]) and a["n_woken"] == b["n_woken"]
+    check_outputs_tol(b, x, wl, np.arange(16), PRE | RES, MX_TOL, True)
+    xb = gen.hidden_states(wl, rep=32, k=300)
+    full = run(B, layer, xb, PRE | RES)
+    sub = np.array([0, 5, 150, 299] + list(range(40, 73)))
+    part = run(B, layer, xb[sub], PRE | RES)
+    for key in ("y", "ids", "w"):
+        assert np.array_equal(part[key], full[key][sub]), key
+
+
+@pytest.mark.parametrize("shape", [
+    gen.LayerShape(hidden=512, n_experts=32, top_k=4, inter=256, shared_inter=256, wdtype="mxfp4"),
+    gen.LayerShape(hidden=768, n_experts=64, top_k=6, inter=128, shared_inter=0, wdtype="mxfp4"),  # 3 windows per K half, one-window down
+    gen.LayerShape(hidden=256, n_experts=512, top_k=16, inter=1024, shared_inter=1024, wdtype="mxfp4"),
+])
+def test_gather_mxfp4_edge_shapes(B, shape):
+    wl = gen.Workload("edge", shape, k=16, seed=4321)
+    from speculative_decoding_moe_amd.workloads import device
+    layer = device.make_layer(wl, 0, "cuda")
+    for k in (1, 33):
+        x = gen.hidden_states(wl, rep=k, k=k)
+        g = run(B, layer, x, GATHER)
+        check_routing(g, x, wl)
+        check_outputs_tol(g, x, wl, np.arange(k) if k < 40 else [0, k - 1], 0, MX_TOL, False)
