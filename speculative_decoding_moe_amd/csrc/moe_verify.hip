@@ -2250,9 +2250,11 @@ __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
       cnt += __popc(S.msk[tid * tw + w]);
     }
   const int ncg = (cnt + 16 * BCG - 1) / (16 * BCG);  // column groups
-  const int nrb_gu = a.I / 64, nrb_dn = (H + 255) / 256;
+  // row blocks per column group: gate/up 64 rows (bf16, and the shared expert) or 128 rows
+  // (mxfp4 routed experts); down 256 rows
+  const int nrb_gu = a.I / 64, nrb_gr = a.xgm ? a.I / 128 : nrb_gu, nrb_dn = (H + 255) / 256;
   int4 tot;
-  const int4 pre = block_excl_scan4(int4{cnt, cnt > 0 ? 1 : 0, ncg * nrb_gu, ncg * nrb_dn}, S.wsum, tid, tot);
+  const int4 pre = block_excl_scan4(int4{cnt, cnt > 0 ? 1 : 0, ncg * nrb_gr, ncg * nrb_dn}, S.wsum, tid, tot);
   const int U = tot.y;
   int* ue = ut_arr(a, 0);
   int* uoff = ut_arr(a, 1);
@@ -2300,13 +2302,18 @@ __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
 }
 
 // Geometry of one tick of the gathered expert kernels. bf16: one 128-wide window per tick, the
-// B windows as (k-step half jh, lane) pieces of the bf16 hi/lo fragments (8 KiB per 16 columns).
-// mxfp4: two windows per tick (the same bytes of A per tick as bf16), the B windows as MX-fp8
-// hi/lo operands with their scale words (MXW bytes per 16 columns).
+// B windows as (k-step half jh, lane) pieces of the bf16 hi/lo fragments (8 KiB per 16 columns);
+// gate/up items are 64 rows, 4 row tiles x 2 K halves. mxfp4: two windows per tick (half the
+// bytes of A per tick of bf16: two ticks of codes, scale bytes and gathered columns is what the
+// registers hold), the B windows as MX-fp8 hi/lo operands with their scale words (MXW bytes per
+// 16 columns); gate/up items are 128 rows, one row tile per wave over the whole reduction, so the
+// gathered columns are half the share of an item's bytes they would be with K halves.
 template <bool GU, bool MX>
 struct BGeo {
-  static constexpr int NKH = GU ? 2 : 1;                    // K halves (gate/up)
+  static constexpr int NKH = (GU && !MX) ? 2 : 1;           // K halves
   static constexpr int NWT = MX ? 2 : 1;                    // windows per tick
+  static constexpr int RBR = GU ? (MX ? 128 : 64) : 256;    // rows per item (gate/up: of each matrix)
+  static constexpr int DEPTH = BD;                          // ticks of loads in flight + 1
   static constexpr int NCB = NKH * NWT * BCG;               // 16-column B windows per tick
   static constexpr int CBB = MX ? MXW : 8192;               // ring bytes per B window
   static constexpr int NCH = MX ? NCB * 256 / NTH : NCB;    // 16-byte B pieces per thread and tick
@@ -2343,7 +2350,7 @@ struct BSmem {
                                                                           : BGeo<GU, true>::RING;
   alignas(16) uint8_t ring[2][RB];
   float red[GU ? 4 * 2 * BCG * 256 : 1];
-  float act[GU ? 4 * BCG * 256 : 1];
+  float act[GU ? 8 * BCG * 256 : 1];
   int ue[MAX_E + 2], uoff[MAX_E + 2], ucnt[MAX_E + 2], pre[MAX_E + 2];
 };
 
@@ -2371,8 +2378,9 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
   const int e = S.ue[lo];
   d.shared = e < 0;
   const uint32_t eb = d.shared ? 0u : (uint32_t)e;
-  // gate/up wave (rt, kh): rows rb 64 + 16 rt of gate and up; down wave w: row tiles rb 256 + 32 w (+ 16)
-  const uint32_t row = GU ? eb * (uint32_t)a.I + (uint32_t)(d.rb * 64 + 16 * (wave & 3))
+  // gate/up wave: rows rb RBR + 16 rt of gate and up, rt = w mod 4 (bf16, K half w / 4) or w
+  // (mxfp4); down wave w: row tiles rb 256 + 32 w (+ 16)
+  const uint32_t row = GU ? eb * (uint32_t)a.I + (uint32_t)(d.rb * BGeo<GU, MX>::RBR + 16 * (MX ? wave : (wave & 3)))
                           : eb * (uint32_t)a.H + (uint32_t)(d.rb * 256 + 32 * wave);
   const uint32_t K = GU ? (uint32_t)a.H : (uint32_t)a.I;  // reduction length of a row
   d.aoff = MX ? row * (K / 2) : row * (K * 2);
@@ -2407,10 +2415,10 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   const int H = a.H, I = a.I;
   const int nwt = H / WIN;                     // windows of a token row (gate/up B source)
   const int nwk = GU ? nwt : I / WIN;          // windows of the A reduction
-  const int nwh = GU ? (nwk + 1) / 2 : nwk;    // windows per K half
-  const int ns = (nwh + GE::NWT - 1) / GE::NWT;  // ticks per item
+  const int nwh = GE::NKH == 2 ? (nwk + 1) / 2 : nwk;  // windows per K half
+  const int ns = (nwh + GE::NWT - 1) / GE::NWT;        // ticks per item
   const int ticks = n_my * ns;
-  const int kh = GU ? (wave >> 2) : 0;
+  const int kh = GE::NKH == 2 ? (wave >> 2) : 0;
   const uint32_t E = a.E;
   const uint32_t anum = GU ? E * (uint32_t)I * H : E * (uint32_t)H * I;  // values of a routed tensor
   const rsrc_t r0 = buf_rsrc(GU ? a.wg : a.wd, MX ? anum / 2 : anum * 2);
@@ -2425,11 +2433,12 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   const uint8_t* bsrc = MX ? (GU ? a.xgm : a.afm) : (GU ? a.xg : a.af);
   const rsrc_t rx = buf_rsrc(bsrc, (uint32_t)(GU ? a.T : npos + 16) * (uint32_t)bwr * (MX ? MXT : 512));
   // B staging. bf16: thread (jh, ln) = (tid / 64, tid % 64) holds piece (jh, q = ln / 16) of
-  // column ln % 16 for every (K half, column tile). mxfp4: thread tid holds piece tid % 16 of
-  // column (tid / 16) % 16 of column tile (tid / 256) % 2 for the B windows (tid / 256) + 2 m,
-  // and, below NCB 64, scale word tid % 4 of column (tid / 4) % 16 of B window tid / 64.
+  // column ln % 16 for every (K half, column tile). mxfp4: thread tid holds piece (tid / 16) % 16
+  // of column tid % 16 of column tile (tid / 256) % 2 for the B windows (tid / 256) + 2 m, and,
+  // below NCB 64, scale word tid % 4 of column (tid / 4) % 16 of B window tid / 64. Sixteen
+  // consecutive lanes always write sixteen columns' pieces 32 bytes apart into the ring.
   const int jh = tid >> 6, ln = tid & 63, bc = ln & 15, bq = ln >> 4;
-  const int mc = (tid >> 4) & 15, mch = tid & 15, mct = (tid >> 8) & 1;
+  const int mc = tid & 15, mch = (tid >> 4) & 15, mct = (tid >> 8) & 1;
   const int scb = tid >> 6, sc_c = (tid >> 2) & 15, sblk = tid & 3;
 
   auto item_of = [&](int m) {
@@ -2439,7 +2448,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   // window of B window-slot (K half h, tick window v) at tick step, and whether it exists
   auto win_of = [&](int h, int v, int step, bool& ok) {
     const int wl = step * GE::NWT + v;
-    const int w = (GU ? h * nwh : 0) + wl;
+    const int w = h * nwh + wl;
     ok = wl < nwh && w < nwk;
     return w;
   };
@@ -2470,18 +2479,18 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
       for (int v = 0; v < GE::NWT; ++v) {
         bool ok;
         int w = win_of(kh, v, step, ok);
-        if (!ok) w = GU ? kh * nwh : 0;
+        if (!ok) w = kh * nwh;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const rsrc_t rc = (GU && i) ? r1 : r0, rs = (GU && i) ? q1 : q0;
           const uint32_t co = d.aoff + (uint32_t)w * 1024u + (i ? c2 : 0u);
           const uint32_t sco = d.soff + (uint32_t)w * 64u + (i ? s2 : 0u);
           if (d.cached) {
-            W.v[i * 2 + v] = bld16_cached(rc, vl, co);
-            W.sc[i * 2 + v] = __builtin_amdgcn_raw_buffer_load_b8(rs, (uint32_t)lane, sco, 0);
+            W.v[i * GE::NWT + v] = bld16_cached(rc, vl, co);
+            W.sc[i * GE::NWT + v] = __builtin_amdgcn_raw_buffer_load_b8(rs, (uint32_t)lane, sco, 0);
           } else {
-            W.v[i * 2 + v] = bld16(rc, vl, co);
-            W.sc[i * 2 + v] = bld1(rs, (uint32_t)lane, sco);
+            W.v[i * GE::NWT + v] = bld16(rc, vl, co);
+            W.sc[i * GE::NWT + v] = bld1(rs, (uint32_t)lane, sco);
           }
         }
       }
@@ -2560,12 +2569,12 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
     }
   };
 
-  // Cursors: the A and B loads of tick t + BD - 1 are issued at tick t (B is stored into the LDS
-  // ring at the end of tick t + BD - 2), math at tick t. Vector memory results complete in issue
+  // Cursors: the A and B loads of tick t + DEPTH - 1 are issued at tick t (B is stored into the
+  // LDS ring at the end of tick t + DEPTH - 2), math at tick t. Vector memory results complete in issue
   // order, so every load whose result steers later loads (the column sources) is issued one
   // item ahead, and a wait for it never drains loads that were issued for later ticks.
-  BWin W[BD];
-  BReg R[BD];
+  BWin W[GE::DEPTH];
+  BReg R[GE::DEPTH];
   int ma = 0, sa = 0;  // load cursor (item, step)
   BItem da = item_of(0);
   int srca[2], srcn[2];
@@ -2582,7 +2591,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
     }
   };
 #pragma unroll
-  for (int j = 0; j < BD - 1; ++j) {
+  for (int j = 0; j < GE::DEPTH - 1; ++j) {
     load_a(W[j], da, sa);
     load_b(R[j], srca, sa);
     advance();
@@ -2612,11 +2621,11 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   };
   col_factors(dc);
 
-  for (int t0 = 0;; t0 += BD) {
+  for (int t0 = 0;; t0 += GE::DEPTH) {
 #pragma unroll
-    for (int r = 0; r < BD; ++r) {
+    for (int r = 0; r < GE::DEPTH; ++r) {
       const int t = t0 + r;
-      const int ib = (r + BD - 1) % BD;  // buffers of tick t + BD - 1
+      const int ib = (r + GE::DEPTH - 1) % GE::DEPTH;  // buffers of tick t + DEPTH - 1
       load_a(W[ib], da, sa);
       load_b(R[ib], srca, sa);
       advance();
@@ -2650,15 +2659,16 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
                 const uint32_t bsc = *reinterpret_cast<const uint32_t*>(cbp + 4096 + lane * 4);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                  acc[i][ct] = mfma_mx(W[r].v[i * 2 + v], W[r].sc[i * 2 + v], bh0, bh1, bsc, 0, acc[i][ct]);
-                  acc[i][ct] = mfma_mx(W[r].v[i * 2 + v], W[r].sc[i * 2 + v], bl0, bl1, bsc, 1, acc[i][ct]);
+                  const int k = i * GE::NWT + v;
+                  acc[i][ct] = mfma_mx(W[r].v[k], W[r].sc[k], bh0, bh1, bsc, 0, acc[i][ct]);
+                  acc[i][ct] = mfma_mx(W[r].v[k], W[r].sc[k], bl0, bl1, bsc, 1, acc[i][ct]);
                 }
               }
             }
           }
       }
       if (scur + 1 == ns) {  // the item's last tick: epilogue (uniform over the workgroup)
-        if constexpr (GU) {
+        if constexpr (GU && !MX) {
           const int rt = wave & 3;
           if (kh == 1)
 #pragma unroll
@@ -2682,42 +2692,49 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
             }
           }
           __syncthreads();
-          if constexpr (!MX) {
-            if (tid < 4 * BCG * 2 * 16) {  // (rt, ct, half, column): 8 rows as down B operands
-              const int c = tid & 15, half = (tid >> 4) & 1, ct = (tid >> 5) % BCG, rt2 = tid / (32 * BCG);
-              const int rnk = dc.col0 + 16 * ct + c;
-              if (rnk < dc.cnt) {
-                uint32_t hi[8], lo[8];
+          if (tid < 4 * BCG * 2 * 16) {  // (rt, ct, half, column): 8 rows as down B operands
+            const int c = tid & 15, half = (tid >> 4) & 1, ct = (tid >> 5) % BCG, rt2 = tid / (32 * BCG);
+            const int rnk = dc.col0 + 16 * ct + c;
+            if (rnk < dc.cnt) {
+              uint32_t hi[8], lo[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                  split_bf16(S.act[(rt2 * BCG + ct) * 256 + (8 * half + i) * 16 + c], hi[i], lo[i]);
-                u32x4 hv, lv;
-                pack8(hi, hv);
-                pack8(lo, lv);
-                const int R0 = dc.rb * 64 + 16 * rt2 + 8 * half;  // intermediate row
-                const int w = R0 / WIN, o = R0 % WIN, j = o / 32, qd = (o % 32) / 8;
-                uint8_t* dst = a.af + ((size_t)(dc.off + rnk) * (I / WIN) + w) * 512;
-                *reinterpret_cast<u32x4*>(dst + ((j * 2 + 0) * 4 + qd) * 16) = hv;
-                *reinterpret_cast<u32x4*>(dst + ((j * 2 + 1) * 4 + qd) * 16) = lv;
-              }
+              for (int i = 0; i < 8; ++i)
+                split_bf16(S.act[(rt2 * BCG + ct) * 256 + (8 * half + i) * 16 + c], hi[i], lo[i]);
+              u32x4 hv, lv;
+              pack8(hi, hv);
+              pack8(lo, lv);
+              const int R0 = dc.rb * 64 + 16 * rt2 + 8 * half;  // intermediate row
+              const int w = R0 / WIN, o = R0 % WIN, j = o / 32, qd = (o % 32) / 8;
+              uint8_t* dst = a.af + ((size_t)(dc.off + rnk) * (I / WIN) + w) * 512;
+              *reinterpret_cast<u32x4*>(dst + ((j * 2 + 0) * 4 + qd) * 16) = hv;
+              *reinterpret_cast<u32x4*>(dst + ((j * 2 + 1) * 4 + qd) * 16) = lv;
             }
-          } else {
-            // (ct, 32-row block bb, half h, column c): 16 rows quantised as MX-fp8 hi/lo, the
-            // block maximum shared by the two halves (lanes c and c + 16 of one wave)
-            if (tid < BCG * 2 * 2 * 16) {
-              const int c = tid & 15, h = (tid >> 4) & 1, bb = (tid >> 5) & 1, ct = tid >> 6;
-              float v[16];
+          }
+        } else if constexpr (GU) {
+          // mxfp4: each wave holds whole sums for its 16 rows; SwiGLU into the act tile, then
+          // (ct, 32-row block bb, half h, column c): 16 rows quantised as MX-fp8 hi/lo, the block
+          // maximum shared by the two halves (lanes c and c + 16 of one wave)
 #pragma unroll
-              for (int j = 0; j < 16; ++j) v[j] = S.act[((2 * bb + h) * BCG + ct) * 256 + j * 16 + c];
-              uint32_t hi[4], lo[4];
-              int eh, el;
-              mx8_quant<16, true>(v, hi, lo, eh, el);
-              const int rnk = dc.col0 + 16 * ct + c;
-              if (rnk < dc.cnt) {
-                const int R0 = dc.rb * 64 + 32 * bb;  // intermediate row of the block
-                uint8_t* tw = a.afm + ((size_t)(dc.off + rnk) * (I / WIN) + R0 / WIN) * MXT;
-                mx8_store16_tok(tw, (R0 % WIN) / 32, h, hi, lo, eh, el);
-              }
+          for (int ct = 0; ct < BCG; ++ct)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float g = acc[0][ct][v] * crv[ct], up = acc[1][ct][v] * crv[ct];
+              S.act[(wave * BCG + ct) * 256 + (4 * (lane >> 4) + v) * 16 + (lane & 15)] = silu(g) * up * cw[ct];
+            }
+          __syncthreads();
+          if (tid < BCG * 4 * 2 * 16) {
+            const int c = tid & 15, h = (tid >> 4) & 1, bb = (tid >> 5) & 3, ct = tid >> 7;
+            float v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = S.act[((2 * bb + h) * BCG + ct) * 256 + j * 16 + c];
+            uint32_t hi[4], lo[4];
+            int eh, el;
+            mx8_quant<16, true>(v, hi, lo, eh, el);
+            const int rnk = dc.col0 + 16 * ct + c;
+            if (rnk < dc.cnt) {
+              const int R0 = dc.rb * 128 + 32 * bb;  // intermediate row of the block
+              uint8_t* tw = a.afm + ((size_t)(dc.off + rnk) * (I / WIN) + R0 / WIN) * MXT;
+              mx8_store16_tok(tw, (R0 % WIN) / 32, h, hi, lo, eh, el);
             }
           }
         } else {
@@ -2749,7 +2766,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
         ++scur;
       }
       if (t + 1 == ticks) return;
-      store_b(R[(r + 1) % BD], (t + 1) & 1);  // B of tick t + 1 (loads issued at tick t - 1)
+      store_b(R[(r + 1) % GE::DEPTH], (t + 1) & 1);  // B of tick t + 1 (loads issued at tick t - 1)
       __syncthreads();
     }
   }
