@@ -101,9 +101,9 @@ def traffic(fetch_dir, write_dir, run_json, cmd_fetch, cmd_write, kernel, source
             f"fetch_bytes_per_launch: {fb:.0f}", f"write_bytes_per_launch: {wb:.0f}",
             f"traffic_bytes_per_launch: {fb + wb:.0f}"]
     alg = None
-    if "bexp_gateup_bytes" in run and "k_bexp<true>" in kernel:
+    if "bexp_gateup_bytes" in run and "k_bexp<true" in kernel:
         alg = float(run["bexp_gateup_bytes"])
-    elif "bexp_down_bytes" in run and "k_bexp<false>" in kernel:
+    elif "bexp_down_bytes" in run and "k_bexp<false" in kernel:
         alg = float(run["bexp_down_bytes"])
     elif "gateup_bytes_mean" in run and "gateup" in kernel:
         alg = float(run["gateup_bytes_mean"])
