@@ -361,3 +361,18 @@ def test_gather_mxfp4_edge_shapes(B, shape):
         g = run(B, layer, x, GATHER)
         check_routing(g, x, wl)
         check_outputs_tol(g, x, wl, np.arange(k) if k < 40 else [0, k - 1], 0, MX_TOL, False)
+
+
+def test_gather_largest_lists(B):
+    """1024 tokens x top-16 of 512 experts (16384 routed pairs, every pair slot of the permutation
+    kernel's threads in use), with and without the shared expert: routing of every token, sampled
+    outputs against the oracle."""
+    from speculative_decoding_moe_amd.workloads import device
+    for Is in (256, 0):
+        shape = gen.LayerShape(hidden=256, n_experts=512, top_k=16, inter=256, shared_inter=Is)
+        wl = gen.Workload("edge", shape, k=16, seed=4322)
+        layer = device.make_layer(wl, 0, "cuda")
+        x = gen.hidden_states(wl, rep=9, k=1024)
+        g = run(B, layer, x)
+        check_routing(g, x, wl)
+        check_outputs(g, x, wl, [0, 1, 511, 1022, 1023])
