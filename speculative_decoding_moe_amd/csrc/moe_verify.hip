@@ -1973,18 +1973,19 @@ __global__ void __launch_bounds__(1024) k_accept_hist(const int32_t* acc, int n_
 //               the RMSNorm factor, and each token's bf16 hi/lo B fragments (token-major).
 //   k_btopk     one wave per token: top-K (ties to the lower expert), softmax over the K.
 //   k_bperm     eight workgroups, each: per-expert token bitmasks (LDS), counts, a scan over
-//               experts for the list offsets, then the list position of each (token, slot) pair
-//               of one eighth of the experts = expert offset + number of the expert's tokens
-//               below it. The list (tokens by expert, then
-//               token) is deterministic; the shared expert follows as slot U with every token.
+//               experts for the list offsets and item counts, then the list position of each
+//               (token, slot) pair of one eighth of the experts = expert offset + number of the
+//               expert's tokens below it. The list (tokens by expert, then token) is
+//               deterministic; the shared expert follows as slot U with every token.
 //   k_bexp<GU>  (woken slot u, column group, row block) items over a flat sequence of window
-//               ticks. Per tick every wave streams two 16-row A bands of one 128-wide window
-//               (gate + up rows: two K halves of 64-row items; down: two row tiles of 256-row
-//               items); the item's gathered token columns for that tick are loaded by all
-//               threads and staged through a two-slot LDS ring. Weights are requested BD - 1
-//               ticks ahead; the gate/up epilogue fuses the K-half reduction, SwiGLU with the
-//               RMSNorm factor and the routing weight, and stores the down B operands per list
-//               position; the down epilogue stores fp32 partial rows per list position.
+//               ticks. Per tick every wave streams two 16-row A bands (gate + up rows of one
+//               tile, or two row tiles of down) of one window (bf16) or two (mxfp4); the item's
+//               gathered token columns for that tick are loaded by all threads and staged
+//               through a two-slot LDS ring. Weights are requested two ticks ahead; the gate/up
+//               epilogue fuses the reduction, SwiGLU with the RMSNorm factor and the routing
+//               weight, and stores the down B operands per list position; the down epilogue
+//               stores fp32 partial rows per list position. mxfp4 layers run the bf16 shared
+//               expert's items first, then the routed experts' mxfp4 items, in the same launch.
 //   k_bcombine  y[t] = sum_j P[pos(t, j)] + P[shared(t)] (+ x[t]), fixed slot order.
 // ------------------------------------------------------------------------------------------
 constexpr int BT_MAX = 1024;      // tokens per gathered call
@@ -2016,7 +2017,8 @@ struct BArgs {
                     // lane quad q at ((j * 2 + hl) * 4 + q) * 16
   int32_t* ids;     // [T][K]
   float* wts;       // [T][K]
-  int32_t* tab;     // [0] U, [1] gate/up items, [2] down items
+  int32_t* tab;     // [0] U, [1] gate/up items, [2] down items (the kernels read [0]; the item
+                    // counts are also the last entries of the prefixes below)
   int32_t* ut;      // 5 arrays of E + 2: slot u -> expert (-1: shared), list offset, count,
                     // gate/up item prefix, down item prefix (entry U + 1: totals)
   int32_t* blist;   // [T K + T] token at list position p (positions T K + t: the shared expert)
