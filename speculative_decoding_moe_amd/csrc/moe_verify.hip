@@ -2,7 +2,8 @@
 //
 // One MoE layer over a speculative block of k <= 16 tokens ("Speculating on a Strix Halo",
 // sections "Speculative decoding", "What the pieces cost", "The verify's own cost") runs as four
-// stream-ordered launches; the kernel boundaries publish each phase's results to every CU:
+// stream-ordered launches (many sequences at once, up to 1024 tokens: the gathered path further
+// down); the kernel boundaries publish each phase's results to every CU:
 //
 //   k_router    (expert tile, H slice) items: fp32 MFMA partial logits and sums of squares; the
 //               block is also packed as the experts' B operands (bf16 hi/lo fragments, or MX-fp8
