@@ -2305,7 +2305,7 @@ __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
 }
 
 // Geometry of one tick of the gathered expert kernels. bf16: one 128-wide window per tick, the
-// B windows as (k-step half jh, lane) pieces of the bf16 hi/lo fragments (8 KiB per 16 columns);
+// B windows as 16 token rows of their 512-byte hi/lo fragment windows, rows BRS bytes apart;
 // gate/up items are 64 rows, 4 row tiles x 2 K halves. mxfp4: two windows per tick (half the
 // bytes of A per tick of bf16: two ticks of codes, scale bytes and gathered columns is what the
 // registers hold), the B windows as MX-fp8 hi/lo operands with their scale words (MXW bytes per
@@ -2318,11 +2318,14 @@ struct BGeo {
   static constexpr int RBR = GU ? (MX ? 128 : 64) : 256;    // rows per item (gate/up: of each matrix)
   static constexpr int DEPTH = BD;                          // ticks of loads in flight + 1
   static constexpr int NCB = NKH * NWT * BCG;               // 16-column B windows per tick
-  static constexpr int CBB = MX ? MXW : 8192;               // ring bytes per B window
+  static constexpr int CBB = MX ? MXW : 16 * 528;           // ring bytes per B window
   static constexpr int NCH = MX ? NCB * 256 / NTH : NCB;    // 16-byte B pieces per thread and tick
   static constexpr int RING = NCB * CBB;                    // ring bytes per slot
 };
 static_assert(BCG == 2, "the staging maps below assume two column tiles per item");
+// bf16 ring rows: a token's 512-byte window plus 16 bytes, so the matrix-core lanes of 16
+// columns (rows BRS apart, same piece) fall in different LDS banks
+constexpr int BRS = 528;
 
 // A operands of one tick for one wave: bf16, two 16-row bands x four k-steps of one window;
 // mxfp4, two bands x two windows of codes (v[band * 2 + window]) and their scale bytes
@@ -2435,12 +2438,13 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   const int bwr = GU ? nwt : I / WIN;  // windows per B source row
   const uint8_t* bsrc = MX ? (GU ? a.xgm : a.afm) : (GU ? a.xg : a.af);
   const rsrc_t rx = buf_rsrc(bsrc, (uint32_t)(GU ? a.T : npos + 16) * (uint32_t)bwr * (MX ? MXT : 512));
-  // B staging. bf16: thread (jh, ln) = (tid / 64, tid % 64) holds piece (jh, q = ln / 16) of
-  // column ln % 16 for every (K half, column tile). mxfp4: thread tid holds piece (tid / 16) % 16
+  // B staging. bf16: thread tid holds 16-byte piece tid % 32 of column tid / 32 for every (K
+  // half, column tile): 32 threads copy one column's 512-byte window, contiguous in memory and
+  // in its ring row. mxfp4: thread tid holds piece (tid / 16) % 16
   // of column tid % 16 of column tile (tid / 256) % 2 for the B windows (tid / 256) + 2 m, and,
   // below NCB 64, scale word tid % 4 of column (tid / 4) % 16 of B window tid / 64. Sixteen
   // consecutive lanes always write sixteen columns' pieces 32 bytes apart into the ring.
-  const int jh = tid >> 6, ln = tid & 63, bc = ln & 15, bq = ln >> 4;
+  const int bc = tid >> 5, bpc = tid & 31;
   const int mc = tid & 15, mch = (tid >> 4) & 15, mct = (tid >> 8) & 1;
   const int scb = tid >> 6, sc_c = (tid >> 2) & 15, sblk = tid & 3;
 
@@ -2510,7 +2514,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
 #pragma unroll
         for (int ct = 0; ct < BCG; ++ct) {
           const bool ok = src[ct] >= 0 && okw;
-          const uint32_t o = ok ? (uint32_t)((src[ct] * bwr + w) * 512 + (jh * 4 + bq) * 16) : 0x80000000u;
+          const uint32_t o = ok ? (uint32_t)((src[ct] * bwr + w) * 512 + bpc * 16) : 0x80000000u;
           R.v[h * BCG + ct] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
         }
       }
@@ -2541,7 +2545,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
       for (int h = 0; h < GE::NKH; ++h)
 #pragma unroll
         for (int ct = 0; ct < BCG; ++ct)
-          reinterpret_cast<u32x4*>(ring)[((h * BCG + ct) * 8 + jh) * 64 + ln] = R.v[h * BCG + ct];
+          *reinterpret_cast<u32x4*>(ring + (h * BCG + ct) * GE::CBB + bc * BRS + bpc * 16) = R.v[h * BCG + ct];
     } else {
 #pragma unroll
       for (int m = 0; m < GE::NCH; ++m) {
@@ -2640,11 +2644,12 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
         for (int ct = 0; ct < BCG; ++ct)
           if (ct == 0 || dc.col0 + 16 * ct < dc.cnt) {  // a column tile of padding only: skipped
             if constexpr (!MX) {
-              const u32x4* rg = reinterpret_cast<const u32x4*>(ring);
+              // lane (column c, quad q) reads piece (2 j + hl) 4 + q of its column's row
+              const uint8_t* rg = ring + (kh * BCG + ct) * GE::CBB + (lane & 15) * BRS + (lane >> 4) * 16;
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const u32x4 bh = rg[((kh * BCG + ct) * 8 + j * 2 + 0) * 64 + lane];
-                const u32x4 bl = rg[((kh * BCG + ct) * 8 + j * 2 + 1) * 64 + lane];
+                const u32x4 bh = *reinterpret_cast<const u32x4*>(rg + (j * 2 + 0) * 64);
+                const u32x4 bl = *reinterpret_cast<const u32x4*>(rg + (j * 2 + 1) * 64);
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
                   acc[i][ct] = mfma16(W[r].v[i * 4 + j], bh, acc[i][ct]);
