@@ -376,3 +376,43 @@ def test_gather_largest_lists(B):
         g = run(B, layer, x)
         check_routing(g, x, wl)
         check_outputs(g, x, wl, [0, 1, 511, 1022, 1023])
+
+
+class _PeriodicRouterLayer(GenLayer):
+    """A generated layer whose router rows repeat with period P, so logits tie exactly."""
+
+    def __init__(self, wl, period):
+        super().__init__(wl, 0)
+        self.period = period
+
+    def router(self):
+        r = gen.router_weight(self.wl, 0)
+        return np.ascontiguousarray(r[np.arange(r.shape[0]) % self.period])
+
+
+@pytest.mark.parametrize("shape,period,k", [
+    (gen.LayerShape(hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512), 5, 300),
+    (gen.LayerShape(hidden=256, n_experts=200, top_k=6, inter=256, shared_inter=0), 3, 77),   # E not a multiple of 16
+    (gen.LayerShape(hidden=256, n_experts=512, top_k=16, inter=256, shared_inter=256), 7, 40),
+])
+def test_gather_exact_router_ties_pick_lower_expert_ids(B, shape, period, k):
+    """Identical router rows give bit-identical logits, so most picks are exact ties: the gathered
+    path's top-K must take equal logits in ascending expert order, exactly as the oracle does."""
+    from speculative_decoding_moe_amd.workloads import device
+    wl = gen.Workload("ties", shape, k=16, seed=99)
+    L = _PeriodicRouterLayer(wl, period)
+    t = device.layer_tensors(wl, 0, "cuda")
+    t["router_w"] = torch.from_numpy(L.router()).cuda()
+    layer = device.make_layer(wl, 0, "cuda", tensors=t)
+    x = gen.hidden_states(wl, rep=60, k=k)
+    g = run(B, layer, x)
+    xh = x.astype(np.float64)
+    logits = oracle.router_logits(xh, L.router())
+    for i in range(k):
+        assert np.array_equal(g["ids"][i], oracle.select_topk(logits[i], shape.top_k)), i
+        np.testing.assert_allclose(g["w"][i], oracle.routing_weights(logits[i], g["ids"][i]), rtol=0, atol=1e-6)
+    assert g["n_woken"] == oracle.woken_experts(g["ids"])[0].size
+    rows = [0, k // 2, k - 1]
+    ref = oracle.moe_block(x[rows], L, shape.top_k)
+    rms = float(np.sqrt(np.mean(ref["y"] ** 2)))
+    assert float(np.abs(g["y"][rows] - ref["y"]).max()) <= BF16_TOL * rms
