@@ -176,6 +176,21 @@ def cpu_baseline(wl, n_samples, one_core_samples=1):
             "value_1core": one, "sample_1core": f"{one_core_samples} step(s) with one BLAS thread"}
 
 
+def context(sweep_k, value):
+    """The pages' own numbers for this path (other hardware and real prompts: context, not
+    targets), beside the same quantities measured here."""
+    out = {"note": "pages' figures were measured on a Strix Halo APU with real prompts; ours on MI355X, "
+                   "synthetic random routing; context only"}
+    if sweep_k:
+        k1, k16 = sweep_k[0], sweep_k[-1]
+        out["verify16_over_decode"] = {"ours": round(k16["ms"] / k1["ms"], 2),
+                                       "pages_pytorch_bf16": 1.6, "pages_llamacpp_q8": [4.2, 4.7]}
+        out["woken_experts_k16"] = {"ours": k16["U_mean"], "pages_real_text": [47, 52],
+                                    "pages_repeated_token": 31, "decode": 8}
+    out["effective_GBps"] = {"ours_step": value, "pages_pytorch_bf16_decode": 47, "pages_llamacpp_q8_decode": 147}
+    return out
+
+
 def fit_line(points):
     """Least squares t = t0 + B / BW over (bytes, seconds) points: t0 in us, BW in GB/s, and the
     residuals in us."""
@@ -701,6 +716,7 @@ def main():
         "lm_head": head,
         "accept_sample": samp,
         "cpu_baseline": cpu,
+        "context": context(sweep_k, value),
     }
     print(json.dumps(out), flush=True)
 
