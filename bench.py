@@ -549,10 +549,34 @@ def main():
         accept_batch = {"workload": f"accept_prefix_batch: {ns} sequences x {NT} rows x {V} fp32 logits",
                         "us_per_call": round(acc_us, 2),
                         "GBps": round(ns * NT * V * 4 / (acc_us * 1e-6) / 1e9, 1)}
-        del blg
+        # acceptance at temperature of the same 32 sequences (a drafter 0.5 N(0,1) away, T = 1)
+        gq = torch.Generator(device=dev).manual_seed(wl.seed + 1)
+        bdl = (blg[:, :NT - 1] + 0.5 * torch.randn((ns, NT - 1, V), device=dev, generator=gq)).contiguous()
+        bua = torch.rand((ns, NT - 1), device=dev, generator=gq)
+        bus = torch.rand((ns, NT), device=dev, generator=gq)
+        btk = torch.empty((ns,), dtype=torch.int32, device=dev)
+        bsws = torch.empty(binding.accept_sample_batch_workspace_size(ns, NT, NT - 1, V), dtype=torch.uint8,
+                           device=dev)
+        for _ in range(3):
+            binding.accept_sample_batch(blg, bdl, bdr, 1.0, bua, bus, bac, btk, bsws)
+        a_, b_ = ev.create(2)
+        torch.cuda.synchronize()
+        ev.record(a_, stream)
+        for _ in range(20):
+            binding.accept_sample_batch(blg, bdl, bdr, 1.0, bua, bus, bac, btk, bsws)
+        ev.record(b_, stream)
+        torch.cuda.synchronize()
+        smp_us = ev.ms(a_, b_) * 1e3 / 20
+        ev.destroy([a_, b_])
+        accept_batch_sample = {"workload": f"accept_sample_batch: {ns} sequences x ({NT} target + {NT - 1} draft) "
+                                           f"rows x {V} fp32 logits, T = 1",
+                               "us_per_call": round(smp_us, 2),
+                               "GBps": round(ns * (2 * NT - 1) * V * 4 / (smp_us * 1e-6) / 1e9, 1)}
+        del blg, bdl
         batched = {"workload": "gathered path: 4..64 sequences x 16 independent N(0,1) tokens through the k = 16 "
                                "layer (bf16); event times per call, route = router + top-K + permutation",
                    "accept_32_sequences": accept_batch,
+                   "accept_sample_32_sequences": accept_batch_sample,
                    "points": rows,
                    "points_mxfp4": {"workload": "the 40-layer stack's mxfp4 layer (pre-norm, residual, bf16 shared "
                                                 "expert) over 4..64 sequences x 16 tokens", "points": mrows},

@@ -266,6 +266,21 @@ int accept_sample(const float* target_logits, int32_t n_target, int32_t vocab, c
                   const float* u_sample, int32_t* accepted, int32_t* token, void* workspace, size_t ws_bytes,
                   void* hip_stream);
 
+/* Bytes of device workspace accept_sample_batch needs (0 if the sizes are invalid). Host only. */
+size_t accept_sample_batch_workspace_size(int32_t n_seq, int32_t n_target, int32_t n_draft, int32_t vocab);
+
+/* accept_sample for many sequences verified together, in three launches for all of them:
+ * sequence s is judged exactly as accept_sample judges one block (same rule, same arithmetic, so
+ * each sequence's result equals that call's).
+ *   target_logits fp32 [n_seq][n_target][vocab]; draft_logits fp32 [n_seq][n_draft][vocab]
+ *   draft_ids int32 [n_seq][n_draft]; u_accept fp32 [n_seq][n_draft]; u_sample fp32 [n_seq][n_target]
+ *   accepted, token int32 [n_seq] out
+ * Limits as accept_sample, and 1 <= n_seq <= 1024. Returns MOE_OK or an MOE_ERR_* code. */
+int accept_sample_batch(const float* target_logits, int32_t n_seq, int32_t n_target, int32_t vocab,
+                        const float* draft_logits, const int32_t* draft_ids, int32_t n_draft, float temperature,
+                        const float* u_accept, const float* u_sample, int32_t* accepted, int32_t* token,
+                        void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Acceptance statistics over many cycles: the histogram of accepted lengths ("Speculating on a
  * Strix Halo (part 2)", section "Why drafter performance doesn't really matter", counts cycles
  * by accepted length) and the per-position marginal as counts (the DFlash-on-MI355X article

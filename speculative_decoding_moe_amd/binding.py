@@ -23,7 +23,8 @@ EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "moe_verify_block_ti
            "moe_pack_weights", "accept_prefix_workspace_size", "accept_prefix",
            "accept_prefix_batch_workspace_size", "accept_prefix_batch",
            "lm_head_accept_workspace_size", "lm_head_accept", "accept_sample_workspace_size",
-           "accept_sample", "accept_histogram", "moe_status_string")
+           "accept_sample", "accept_sample_batch_workspace_size", "accept_sample_batch",
+           "accept_histogram", "moe_status_string")
 
 
 class MoeLayerStruct(ctypes.Structure):
@@ -74,6 +75,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.accept_sample_workspace_size.restype = sz
     lib.accept_sample.argtypes = [vp, i32, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
     lib.accept_sample.restype = ctypes.c_int
+    lib.accept_sample_batch_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.accept_sample_batch_workspace_size.restype = sz
+    lib.accept_sample_batch.argtypes = [vp, i32, i32, i32, vp, vp, i32, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+    lib.accept_sample_batch.restype = ctypes.c_int
     lib.accept_histogram.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.accept_histogram.restype = ctypes.c_int
     lib.moe_status_string.argtypes = [ctypes.c_int]
@@ -253,6 +258,24 @@ def lm_head_accept(h, w_head_tiled, vocab, draft_ids, target_ids, accepted, work
 
 def accept_sample_workspace_size(n_target: int, n_draft: int, vocab: int) -> int:
     return int(lib.accept_sample_workspace_size(int(n_target), int(n_draft), int(vocab)))
+
+
+def accept_sample_batch_workspace_size(n_seq: int, n_target: int, n_draft: int, vocab: int) -> int:
+    return int(lib.accept_sample_batch_workspace_size(int(n_seq), int(n_target), int(n_draft), int(vocab)))
+
+
+def accept_sample_batch(target_logits, draft_logits, draft_ids, temperature, u_accept, u_sample, accepted, token,
+                        workspace, stream=None) -> None:
+    """accept_sample for n_seq sequences at once (library call): target_logits [n_seq][n_target][V],
+    draft_logits [n_seq][n_draft][V], draft_ids / u_accept [n_seq][n_draft], u_sample [n_seq][n_target];
+    accepted and token [n_seq] are outputs. The draft arguments may be None with no drafts."""
+    n_seq, n_target, vocab = (int(v) for v in target_logits.shape)
+    n_draft = 0 if draft_ids is None else int(draft_ids.shape[1])
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.accept_sample_batch(_ptr(target_logits), n_seq, n_target, vocab, _ptr(draft_logits), _ptr(draft_ids),
+                                 n_draft, float(temperature), _ptr(u_accept), _ptr(u_sample), _ptr(accepted),
+                                 _ptr(token), _ptr(workspace), ws_bytes, _stream_handle() if stream is None else stream)
+    _check(st)
 
 
 def accept_sample(target_logits, draft_logits, draft_ids, temperature, u_accept, u_sample, accepted, token,

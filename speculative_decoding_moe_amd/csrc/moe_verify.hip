@@ -1650,6 +1650,12 @@ __global__ void __launch_bounds__(256) k_lse_partial(const float* tl, const floa
                                                      float zscale, float2* ms) {
   __shared__ float sm[4], ss[4];
   const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+  {  // sequence blockIdx.z of a batch: its rows and partials
+    const int sq = blockIdx.z, n_d = gridDim.y - n_t;
+    tl += (size_t)sq * n_t * V;
+    dl += (size_t)sq * n_d * V;
+    ms += (size_t)sq * gridDim.y * nchunks;
+  }
   const float* r = row < n_t ? tl + (size_t)row * V : dl + (size_t)(row - n_t) * V;
   const int base = chunk * AM_CHUNK, end = min(base + AM_CHUNK, V);
   constexpr int PER = AM_CHUNK / (4 * 256);
@@ -1842,6 +1848,19 @@ __global__ void __launch_bounds__(SAMPLE_NTH) k_sample_partial(const float* tl, 
                                                                int32_t* accepted, int32_t* token) {
   __shared__ SampleSmem S;
   const int tid = threadIdx.x, c = blockIdx.x;
+  {  // sequence blockIdx.y of a batch
+    const size_t sq = blockIdx.y;
+    tl += sq * n_t * V;
+    dl += sq * n_d * V;
+    draft += sq * n_d;
+    u_acc += sq * n_d;
+    u_smp += sq * n_t;
+    ms += sq * (n_t + n_d) * nchunks;
+    csum += sq * nchunks;
+    plan += sq;
+    accepted += sq;
+    token += sq;
+  }
   sample_plan(tl, dl, n_t, V, nchunks, zscale, draft, n_d, u_acc, u_smp, ms, S, tid);
   const SamplePlan P = S.plan;
   if (c == 0 && tid == 0) {
@@ -1862,11 +1881,19 @@ __global__ void __launch_bounds__(SAMPLE_NTH) k_sample_partial(const float* tl, 
 
 __global__ void __launch_bounds__(SAMPLE_NTH) k_sample_final(const float* tl, const float* dl, int V, int nchunks,
                                                              float zscale, const float2* csum, const SamplePlan* plan,
-                                                             int32_t* token) {
+                                                             int32_t* token, int n_t = 0, int n_d = 0) {
   __shared__ SampleSmem S;
   __shared__ int sel_chunk, use_res, lastw;
   __shared__ float sel_base, sel_target;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  {  // sequence blockIdx.x of a batch (n_t, n_d: its target and draft row counts)
+    const size_t sq = blockIdx.x;
+    tl += sq * n_t * V;
+    dl += sq * n_d * V;
+    csum += sq * nchunks;
+    plan += sq;
+    token += sq;
+  }
   const SamplePlan P = *plan;
   if (P.mode == SAMPLE_NONE) return;
   if (wave == 0) {
@@ -3317,6 +3344,62 @@ int accept_sample(const float* target_logits, int32_t n_target, int32_t vocab, c
   k_sample_partial<<<nch, SAMPLE_NTH, 0, s>>>(target_logits, draft_logits, n_target, vocab, nch, zscale, draft_ids,
                                               n_draft, u_accept, u_sample, ms, csum, plan, accepted, token);
   k_sample_final<<<1, SAMPLE_NTH, 0, s>>>(target_logits, draft_logits, vocab, nch, zscale, csum, plan, token);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+size_t accept_sample_batch_workspace_size(int32_t n_seq, int32_t n_target, int32_t n_draft, int32_t vocab) {
+  if (n_seq < 1 || n_seq > 1024) return 0;
+  const size_t one = accept_sample_workspace_size(n_target, n_draft, vocab);
+  if (!one) return 0;
+  const size_t nch = ((size_t)vocab + AM_CHUNK - 1) / AM_CHUNK;
+  return align256((size_t)n_seq * (n_target + n_draft) * nch * 8) + align256((size_t)n_seq * nch * 8) +
+         align256((size_t)n_seq * sizeof(SamplePlan));
+}
+
+int accept_sample_batch(const float* target_logits, int32_t n_seq, int32_t n_target, int32_t vocab,
+                        const float* draft_logits, const int32_t* draft_ids, int32_t n_draft, float temperature,
+                        const float* u_accept, const float* u_sample, int32_t* accepted, int32_t* token,
+                        void* workspace, size_t ws_bytes, void* hip_stream) {
+  if (!target_logits || !u_sample || !accepted || !token || !workspace ||
+      (n_draft > 0 && (!draft_logits || !draft_ids || !u_accept)))
+    return MOE_ERR_NULL;
+  if (n_seq < 1 || n_seq > 1024 || n_target < 1 || n_target > 64 || n_draft < 0 || n_draft > n_target ||
+      vocab < 1 || vocab > (1 << 24) || !(temperature > 0.f) || !(temperature < INFINITY))
+    return MOE_ERR_SHAPE;
+  if (!aligned16(target_logits) || (draft_logits && !aligned16(draft_logits)) || !aligned16(workspace) ||
+      (draft_ids && !aligned4(draft_ids)) || (u_accept && !aligned4(u_accept)) || !aligned4(u_sample) ||
+      !aligned4(accepted) || !aligned4(token))
+    return MOE_ERR_ALIGN;
+  const size_t need = accept_sample_batch_workspace_size(n_seq, n_target, n_draft, vocab);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  const size_t S = (size_t)n_seq;
+  const size_t tb = S * n_target * vocab * 4, db = S * n_draft * vocab * 4;
+  const void* outs[3] = {accepted, token, workspace};
+  const size_t osz[3] = {S * 4, S * 4, need};
+  const void* ins[5] = {target_logits, draft_logits, draft_ids, u_accept, u_sample};
+  const size_t isz[5] = {tb, db, S * n_draft * 4, S * n_draft * 4, S * n_target * 4};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (ins[i] && overlaps(outs[o], osz[o], ins[i], isz[i])) return MOE_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlaps(outs[o], osz[o], outs[o2], osz[o2])) return MOE_ERR_ALIAS;
+  }
+  const int nch = (vocab + AM_CHUNK - 1) / AM_CHUNK;
+  uint8_t* ws = (uint8_t*)workspace;
+  const size_t b0 = align256(S * (n_target + n_draft) * nch * 8), b1 = align256(S * nch * 8);
+  float2* ms = (float2*)ws;
+  float2* csum = (float2*)(ws + b0);
+  SamplePlan* plan = (SamplePlan*)(ws + b0 + b1);
+  const float zscale = 1.4426950408889634f / temperature;  // log2(e) / T
+  hipStream_t s = (hipStream_t)hip_stream;
+  (void)hipGetLastError();
+  k_lse_partial<<<dim3(nch, n_target + n_draft, n_seq), 256, 0, s>>>(target_logits, draft_logits, n_target, vocab,
+                                                                     nch, zscale, ms);
+  k_sample_partial<<<dim3(nch, n_seq), SAMPLE_NTH, 0, s>>>(target_logits, draft_logits, n_target, vocab, nch,
+                                                           zscale, draft_ids, n_draft, u_accept, u_sample, ms, csum,
+                                                           plan, accepted, token);
+  k_sample_final<<<n_seq, SAMPLE_NTH, 0, s>>>(target_logits, draft_logits, vocab, nch, zscale, csum, plan, token,
+                                              n_target, n_draft);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -269,6 +269,27 @@ def test_accept_sample_validation(b):
     assert call(ac=ws + 64) == -6
 
 
+def test_accept_sample_batch_validation(b):
+    f = b.lib.accept_sample_batch
+    need = b.lib.accept_sample_batch_workspace_size(32, 17, 16, 151936)
+    assert need >= 32 * 17 * 10 * 8
+    assert b.lib.accept_sample_batch_workspace_size(0, 17, 16, 100) == 0
+    assert b.lib.accept_sample_batch_workspace_size(1025, 17, 16, 100) == 0
+    assert b.lib.accept_sample_batch_workspace_size(4, 17, 18, 100) == 0
+    tl, dl, di, ua, us, ac, tk, ws = (FAKE, FAKE + 0x40000000, FAKE + 0x80000000, FAKE + 0x81000000,
+                                      FAKE + 0x82000000, FAKE + 0x83000000, FAKE + 0x84000000, FAKE + 0x90000000)
+    assert f(None, 32, 17, 151936, dl, di, 16, 1.0, ua, us, ac, tk, ws, need, None) == -1
+    assert f(tl, 32, 17, 151936, None, di, 16, 1.0, ua, us, ac, tk, ws, need, None) == -1
+    assert f(tl, 0, 17, 151936, dl, di, 16, 1.0, ua, us, ac, tk, ws, need, None) == -2
+    assert f(tl, 1025, 17, 151936, dl, di, 16, 1.0, ua, us, ac, tk, ws, need, None) == -2
+    assert f(tl, 32, 17, 151936, dl, di, 16, 0.0, ua, us, ac, tk, ws, need, None) == -2
+    assert f(tl, 32, 17, 151936, dl, di, 16, float("inf"), ua, us, ac, tk, ws, need, None) == -2
+    assert f(tl + 4, 32, 17, 151936, dl, di, 16, 1.0, ua, us, ac, tk, ws, need, None) == -4
+    assert f(tl, 32, 17, 151936, dl, di, 16, 1.0, ua, us, ac, tk, ws, need - 1, None) == -5
+    assert f(tl, 32, 17, 151936, dl, di, 16, 1.0, ua, us, tl + 4096, tk, ws, need, None) == -6  # accepted inside the logits
+    assert f(tl, 32, 17, 151936, dl, di, 16, 1.0, ua, us, ac, ac + 64, ws, need, None) == -6    # token overlaps accepted
+
+
 def test_accept_histogram_validation(b):
     f = b.lib.accept_histogram
     a, h, sv = FAKE, FAKE + 0x1000, FAKE + 0x2000

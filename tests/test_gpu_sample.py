@@ -203,3 +203,49 @@ def test_accept_sample_tiny_vocabularies(B, V):
         check_sample(tl, dl, draft, 1.0, ua, us, got)
         if V == 1:
             assert got == (n, 0)
+
+
+def run_sample_batch(B, tls, dls, drafts, T, uas, uss, ws_fill=None):
+    """accept_sample_batch over stacked sequences; returns [(a, token)] per sequence."""
+    S, nt, V = tls.shape
+    nd = drafts.shape[1] if drafts is not None else 0
+    print(f"[accept_sample_batch] n_seq={S} n_target={nt} n_draft={nd} vocab={V}", flush=True)
+    t = torch.from_numpy(np.ascontiguousarray(tls, dtype=np.float32)).cuda()
+    d = torch.from_numpy(np.ascontiguousarray(dls, dtype=np.float32)).cuda() if nd else None
+    di = torch.from_numpy(np.ascontiguousarray(drafts, dtype=np.int32)).cuda() if nd else None
+    ua = torch.from_numpy(np.ascontiguousarray(uas, dtype=np.float32)).cuda() if nd else None
+    us = torch.from_numpy(np.ascontiguousarray(uss, dtype=np.float32)).cuda()
+    ac = torch.full((S,), -7, dtype=torch.int32, device="cuda")
+    tk = torch.full((S,), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(B.accept_sample_batch_workspace_size(S, nt, nd, V), dtype=torch.uint8, device="cuda")
+    if ws_fill is not None:
+        ws.fill_(ws_fill)
+    B.accept_sample_batch(t, d, di, T, ua, us, ac, tk, ws)
+    torch.cuda.synchronize()
+    return list(zip(ac.cpu().numpy().tolist(), tk.cpu().numpy().tolist()))
+
+
+@pytest.mark.parametrize("S,nt,nd,V,T", [
+    (16, 17, 16, 151936, 0.8),   # 16 sequences of the benchmark's shape
+    (5, 9, 8, 20001, 1.3),       # ragged vocabulary
+    (7, 3, 0, 1001, 1.0),        # no drafts: each token is the target's own sample
+])
+def test_accept_sample_batch_equals_single_calls(B, S, nt, nd, V, T):
+    """Every sequence of one batched call gives exactly what accept_sample gives for it alone, and
+    sampled sequences agree with the oracle (within fp32 rounding of a decision boundary)."""
+    cases = [_case(1000 + 10 * S + s, nt, nd, V, T) for s in range(S)]
+    tls = np.stack([c[0] for c in cases])
+    dls = np.stack([c[1] for c in cases]) if nd else None
+    drafts = np.stack([c[2] for c in cases]) if nd else None
+    uas = np.stack([c[3] for c in cases]) if nd else None
+    uss = np.stack([c[4] for c in cases])
+    got = run_sample_batch(B, tls, dls, drafts, T, uas, uss)
+    for s in range(S):
+        tl, dl, draft, ua, us = cases[s]
+        one = run_sample(B, tl, dl, draft, T, ua, us)
+        assert got[s] == one, (s, got[s], one)
+    for s in (0, S - 1):
+        tl, dl, draft, ua, us = cases[s]
+        check_sample(tl, dl, draft, T, ua, us, got[s])
+    # the workspace left by another call does not matter
+    assert run_sample_batch(B, tls, dls, drafts, T, uas, uss, ws_fill=0xFF) == got
