@@ -895,15 +895,17 @@ __device__ __forceinline__ void gu_math(f32x4 (&acc)[GU_MX_RT][2], const GUItem<
 
 // ------------------------------------------------------------------------------------------
 // down items. NWIN = I / 128 windows; wave w owns window w % NWIN and tile group
-// w / NWIN, with TPW row tiles (bf16) or 2 TPW (mxfp4).
+// w / NWIN, with TPW row tiles. An mxfp4 item has as many rows as a bf16 one (a quarter of its
+// bytes): with 256-row mxfp4 items a k = 16 layer had about 3.2 items per workgroup, too few for
+// the claimed rounds, and its partial last round cost more than the smaller items' extra epilogues.
 // ------------------------------------------------------------------------------------------
 template <int NWIN>
 struct DnShape {
   static constexpr int WPWIN = NW / NWIN;                   // waves per window
   static constexpr int TPI_BF = NWIN == 8 ? 4 : 8;           // row tiles per bf16 item
   static constexpr int TPW_BF = TPI_BF / WPWIN;              // row tiles per wave, bf16
-  static constexpr int TPI_MX = 2 * TPI_BF;
-  static constexpr int TPW_MX = 2 * TPW_BF;
+  static constexpr int TPI_MX = TPI_BF;                      // row tiles per mxfp4 item
+  static constexpr int TPW_MX = TPW_BF;
 };
 
 template <int NWIN>
@@ -1240,50 +1242,54 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
     dn_store_partial<NWIN>(S, acc, SH::TPW_BF, wave, lane);
     dn_epilogue<NWIN>(a, S, SH::TPI_BF, SH::TPW_BF, U, false, b * 16 * SH::TPI_BF, tid);
   }
-  // routed items, scheduled as in the gate/up kernel; the weights and activation fragments of
-  // the next item are requested before this item's math
+  // Routed items, scheduled and pipelined as in the gate/up kernel (D items deep: at step h item
+  // h is multiplied while the weights and activation fragments of items h + 1 .. h + D - 1 are in
+  // flight). Two in flight for both formats: with the 34 KB mxfp4 items, three or four in flight
+  // were measured slower (k = 16: 22.6 and 22.0 us against 19.9).
+  constexpr int D = 2;
   const Sched q = make_sched(n_dn, G, b, n_sh, a.ctr + NGRP * CTR_STRIDE);
   const int q0 = static_item(q, 0);
   if (q0 >= n_dn) return;  // every later item is past the end too
   const Woken wk = load_woken(S, lane);
-  DNItem<NWIN> T0, T1;
-  DnB<MX> b0, b1;
-  DNDesc e0 = dn_desc<NWIN, MX>(a, wk, q0, n_dn, ipe), e1;
-  dn_load<NWIN, MX>(T0, rw, rs, e0, I, wave, lane);
-  dn_load_bb<NWIN, MX>(b0, raf, e0.u, I, wave, lane);
-  int n1 = static_item(q, 1), n2;  // items h + 1 and h + 2
-  uint32_t ca = 0, cb = 0;         // claims in flight (thread 0): items h + 2 / h + 3
-  for (int h = 0;; h += 2) {
-    e1 = dn_desc<NWIN, MX>(a, wk, n1, n_dn, ipe);  // a valid stand-in past the end
-    dn_load<NWIN, MX>(T1, rw, rs, e1, I, wave, lane);
-    dn_load_bb<NWIN, MX>(b1, raf, e1.u, I, wave, lane);
-    if (tid == 0) {
-      S.claim[(h + 2) & 3] = is_static(q, h + 2) ? static_item(q, h + 2) : pool_item(q, ca);
-      if (!is_static(q, h + 4)) ca = claim_raw(q.ctr);
+  DNItem<NWIN> T[D];
+  DnB<MX> Bf[D];
+  DNDesc dd[D];
+  int nx[D];
+#pragma unroll
+  for (int j = 0; j + 1 < D; ++j) {
+    nx[j] = static_item(q, j);
+    dd[j] = dn_desc<NWIN, MX>(a, wk, nx[j], n_dn, ipe);  // a valid stand-in past the end
+    dn_load<NWIN, MX>(T[j], rw, rs, dd[j], I, wave, lane);
+    dn_load_bb<NWIN, MX>(Bf[j], raf, dd[j].u, I, wave, lane);
+  }
+  int nload = static_item(q, D - 1);  // item of the next step whose loads are issued
+  uint32_t cl[2] = {0u, 0u};          // claims in flight (thread 0)
+  if (tid == 0 && q.claims)
+    for (int X = max(q.S, D); X < D + 2; ++X) cl[(X - D) & 1] = claim_raw(q.ctr);
+  for (int h = 0;; h += D) {
+    bool done = false;
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+      const int st = h + r;
+      const int jl = (r + D - 1) % D;  // buffer of item st + D - 1
+      nx[jl] = nload;
+      dd[jl] = dn_desc<NWIN, MX>(a, wk, nload, n_dn, ipe);
+      dn_load<NWIN, MX>(T[jl], rw, rs, dd[jl], I, wave, lane);
+      dn_load_bb<NWIN, MX>(Bf[jl], raf, dd[jl].u, I, wave, lane);
+      if (tid == 0) {
+        S.claim[(st + D) & 3] = is_static(q, st + D) ? static_item(q, st + D) : pool_item(q, cl[st & 1]);
+        if (!is_static(q, st + D + 2)) cl[st & 1] = claim_raw(q.ctr);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f32x4 acc[SH::TPW_MX];
+        dn_math<NWIN, MX>(acc, T[r], Bf[r]);
+        dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
+        dn_epilogue<NWIN>(a, S, dd[r].ntile, TPW, dd[r].u, true, dd[r].row0, tid, (st + D) & 3, &nload);
+      }
+      if (nx[(r + 1) % D] >= n_dn) { done = true; break; }  // the next step's item is past the end
     }
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      f32x4 acc[SH::TPW_MX];
-      dn_math<NWIN, MX>(acc, T0, b0);
-      dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
-      dn_epilogue<NWIN>(a, S, e0.ntile, TPW, e0.u, true, e0.row0, tid, (h + 2) & 3, &n2);
-    }
-    if (n1 >= n_dn) break;
-    e0 = dn_desc<NWIN, MX>(a, wk, n2, n_dn, ipe);
-    dn_load<NWIN, MX>(T0, rw, rs, e0, I, wave, lane);
-    dn_load_bb<NWIN, MX>(b0, raf, e0.u, I, wave, lane);
-    if (tid == 0) {
-      S.claim[(h + 3) & 3] = is_static(q, h + 3) ? static_item(q, h + 3) : pool_item(q, cb);
-      if (!is_static(q, h + 5)) cb = claim_raw(q.ctr);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      f32x4 acc[SH::TPW_MX];
-      dn_math<NWIN, MX>(acc, T1, b1);
-      dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
-      dn_epilogue<NWIN>(a, S, e1.ntile, TPW, e1.u, true, e1.row0, tid, (h + 3) & 3, &n1);
-    }
-    if (n2 >= n_dn) break;
+    if (done) break;
   }
 }
 
@@ -2937,7 +2943,7 @@ int check_layer(const moe_layer* L) {
   if (Is != 0 && Is != I) return MOE_ERR_SHAPE;
   if (L->wdtype != MOE_W_BF16 && L->wdtype != MOE_W_MXFP4) return MOE_ERR_DTYPE;
   if (L->layout != MOE_LAYOUT_TILED) return MOE_ERR_DTYPE;
-  if (L->wdtype == MOE_W_MXFP4 && H % 256) return MOE_ERR_SHAPE;  // mxfp4 down items are 256 rows
+  if (L->wdtype == MOE_W_MXFP4 && H % 256) return MOE_ERR_SHAPE;  // mxfp4 kernels take whole 256-row down blocks
   if (!L->router_w || !L->w_gate || !L->w_up || !L->w_down) return MOE_ERR_NULL;
   if (L->wdtype == MOE_W_MXFP4 && (!L->s_gate || !L->s_up || !L->s_down)) return MOE_ERR_DTYPE;
   if (Is && (!L->sh_gate || !L->sh_up || !L->sh_down)) return MOE_ERR_NULL;
