@@ -82,7 +82,17 @@ def gateup_bytes(shape, U):
     """Algorithmic bytes of the gate/up kernel: gate and up rows of the woken experts and the
     shared expert (bf16)."""
     H, I, Is = shape.hidden, shape.inter, shape.shared_inter
-    return (U * 2 * H * I + 2 * H * Is) * 2
+    if shape.wdtype == "bf16":
+        return (U * 2 * H * I + 2 * H * Is) * 2
+    return U * 2 * H * I * (0.5 + 1.0 / 32.0) + 2 * H * Is * 2
+
+
+def down_bytes(shape, U):
+    """Algorithmic bytes of the down kernel: down rows of the woken experts and the shared expert
+    (bf16)."""
+    H, I, Is = shape.hidden, shape.inter, shape.shared_inter
+    per_expert = H * I * 2 if shape.wdtype == "bf16" else H * I * (0.5 + 1.0 / 32.0)
+    return U * per_expert + H * Is * 2
 
 
 def traffic_from_profile(summary=None):
@@ -316,6 +326,19 @@ def main():
         torch.cuda.synchronize()
         bU = bnw[:, 0].cpu().numpy().astype(np.int64)
         del bws, by
+        # the 40-layer stack's mxfp4 layer: 4 generated layers, each called twice
+        mw = gen.WORKLOADS["stack40_mxfp4"]
+        mlayers = [device.make_layer(mw, li, dev) for li in range(4)]
+        mws = torch.empty(mlayers[0].workspace_size(mw.k), dtype=torch.uint8, device=dev)
+        mbuf = [torch.empty((mw.k, s.hidden), dtype=torch.float32, device=dev) for _ in range(2)]
+        mnw = torch.zeros((8, 4), dtype=torch.int32, device=dev)
+        for r in range(8):
+            mx_in = torch.from_numpy(gen.hidden_states(mw, rep=r)).to(dev)
+            binding.moe_verify_block(mlayers[r % 4], mx_in, binding.MOE_PRE_RMSNORM | binding.MOE_RESIDUAL,
+                                     mbuf[r % 2], None, None, mnw[r], mws)
+        torch.cuda.synchronize()
+        mU = mnw[:, 0].cpu().numpy().astype(np.int64)
+        del mlayers, mws, mbuf
         copy_mib = 512
         src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -328,6 +351,9 @@ def main():
                           "head_bytes": (V + 15) // 16 * 16 * s.hidden * 2 + 16 * s.hidden * 4,
                           "bexp_gateup_bytes": float(np.mean([gateup_bytes(s, u) for u in bU])),
                           "bexp_down_bytes": float(np.mean([gateup_bytes(s, u) / 2 for u in bU])),
+                          "down_bytes_mean": float(np.mean([down_bytes(s, u) for u in Uall])),
+                          "mx_gateup_bytes_mean": float(np.mean([gateup_bytes(mw.shape, u) for u in mU])),
+                          "mx_down_bytes_mean": float(np.mean([down_bytes(mw.shape, u) for u in mU])),
                           "copy_bytes": copy_mib << 20, "copy_launches": 3}), flush=True)
         return
 

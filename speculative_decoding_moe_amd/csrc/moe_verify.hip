@@ -816,12 +816,25 @@ struct Sched {
   bool claims;               // whether the last rounds are claimed
   uint32_t* ctr;             // this workgroup's pool counter
 };
-__device__ __forceinline__ Sched make_sched(int n, int G, int b, int n_sh, uint32_t* ctr_base) {
+// With ipe_xcd > 0 (the down kernel: ipe_xcd items per expert), a static round deals whole
+// experts round-robin over the XCDs (consecutive workgroup ids go to different XCDs): expert
+// block i of the round goes to XCD i mod 8, and its items to consecutive workgroups there. Every
+// item of an expert reads the expert's activation fragments, which are then fetched into one
+// XCD's L2 instead of all eight, and a round with few experts still spans every XCD. Within each
+// XCD the shared-item workgroups start the deal last. Needs G/8 to be a multiple of ipe_xcd.
+__device__ __forceinline__ Sched make_sched(int n, int G, int b, int n_sh, uint32_t* ctr_base,
+                                            int ipe_xcd = 0) {
   Sched q;
   q.G = G;
   q.claims = n >= 6 * G;
   q.S = q.claims ? n / G - 2 : (n + G - 1) / G;
-  q.f = (b - n_sh + G) % G;
+  const int g8 = G >> 3;
+  if (ipe_xcd > 0 && G % 8 == 0 && g8 % ipe_xcd == 0) {
+    const int j = ((b >> 3) - (n_sh + 7) / 8 + g8) % g8;  // slot within the XCD
+    q.f = (((j / ipe_xcd) << 3) + (b & 7)) * ipe_xcd + j % ipe_xcd;
+  } else {
+    q.f = (b - n_sh + G) % G;
+  }
   q.npool = min(NGRP, max(1, G >> 3));
   q.pool = (b >> 3) % q.npool;
   q.ctr = ctr_base + q.pool * CTR_STRIDE;
@@ -1247,7 +1260,7 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   // flight). Two in flight for both formats: with the 34 KB mxfp4 items, three or four in flight
   // were measured slower (k = 16: 22.6 and 22.0 us against 19.9).
   constexpr int D = 2;
-  const Sched q = make_sched(n_dn, G, b, n_sh, a.ctr + NGRP * CTR_STRIDE);
+  const Sched q = make_sched(n_dn, G, b, n_sh, a.ctr + NGRP * CTR_STRIDE, ipe);
   const int q0 = static_item(q, 0);
   if (q0 >= n_dn) return;  // every later item is past the end too
   const Woken wk = load_woken(S, lane);

@@ -100,15 +100,12 @@ def traffic(fetch_dir, write_dir, run_json, cmd_fetch, cmd_write, kernel, source
             f"fetch_scale_bytes_per_unit: {fscale:.4f}", f"write_scale_bytes_per_unit: {wscale:.4f}",
             f"fetch_bytes_per_launch: {fb:.0f}", f"write_bytes_per_launch: {wb:.0f}",
             f"traffic_bytes_per_launch: {fb + wb:.0f}"]
-    alg = None
-    if "bexp_gateup_bytes" in run and "k_bexp<true" in kernel:
-        alg = float(run["bexp_gateup_bytes"])
-    elif "bexp_down_bytes" in run and "k_bexp<false" in kernel:
-        alg = float(run["bexp_down_bytes"])
-    elif "gateup_bytes_mean" in run and "gateup" in kernel:
-        alg = float(run["gateup_bytes_mean"])
-    elif "head_bytes" in run and "head" in kernel:
-        alg = float(run["head_bytes"])
+    # algorithmic bytes per launch that the profiled program reports for each kernel
+    keys = [("k_bexp<true", "bexp_gateup_bytes"), ("k_bexp<false", "bexp_down_bytes"),
+            ("k_gateup<2, true>", "mx_gateup_bytes_mean"), ("k_down<4, true>", "mx_down_bytes_mean"),
+            ("k_gateup<2, false>", "gateup_bytes_mean"), ("k_down<4, false>", "down_bytes_mean"),
+            ("k_head", "head_bytes")]
+    alg = next((float(run[key]) for sub, key in keys if sub in name and key in run), None)
     if alg:
         out += [f"algorithmic_bytes_per_launch: {alg:.0f}", f"traffic_over_algorithmic: {(fb + wb) / alg:.4f}"]
     return "\n".join(out)
