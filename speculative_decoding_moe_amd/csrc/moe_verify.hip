@@ -446,13 +446,67 @@ __device__ __forceinline__ void topk_sorted(uint64_t (&c)[NS], int K, int lane, 
 // ------------------------------------------------------------------------------------------
 // routing (every gate/up workgroup, into LDS)
 // ------------------------------------------------------------------------------------------
-__device__ void route(const Args& a, Smem& S, int wave, int lane, int tid) {
+// The router's H-slice partials of the block, requested before anything else the gate/up kernel
+// loads. Vector-memory results return in issue order, so a workgroup that then requests its
+// shared-expert tile still sums the partials without waiting for that tile. When E is a multiple
+// of 4 a thread loads float4s of (token, 4 experts, slice), at most 16 loads (4 pairs x 4 slices);
+// 64 scalar loads per thread would exceed the 63 loads one wave can have outstanding and cost a
+// second round trip. Addresses are clamped into the slab; the results are used only in route()
+// (selected there), so nothing waits on them before the shared tile is requested.
+struct RoutePart {
+  f32x4 v[4][HS_MAX];  // (pair i: token, expert quad) x slice; pair P = tid + NTH i
+  float q[HS_MAX];     // sums of squares of token tid (tid < KMAX)
+};
+__device__ __forceinline__ RoutePart route_issue(const Args& a, int tid) {
+  RoutePart r;
+  const int E = a.E, hs = a.hs, k = a.k;
+  // buffer loads: one 32-bit lane offset per pair, the slice offset in an SGPR
+  const rsrc_t rl = buf_rsrc(a.plog, (uint32_t)(hs * KMAX * E * 4));
+  const rsrc_t rq = buf_rsrc(a.psq, (uint32_t)(hs * KMAX * 4));
+  if (E % 4 == 0) {
+    const int nq = E >> 2, np = KMAX * nq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int P = tid + NTH * i;
+      const int Pc = P < np ? P : 0, t = Pc / nq, q = Pc % nq;
+      const uint32_t vo = (uint32_t)(((t < k ? t : 0) * E + 4 * q) * 4);
+#pragma unroll
+      for (int h = 0; h < HS_MAX; ++h)
+        r.v[i][h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rl, vo, (uint32_t)((h < hs ? h : 0) * KMAX * E * 4), 0));
+    }
+  }
+  const uint32_t vq = (uint32_t)((tid < KMAX ? tid : 0) * 4);
+#pragma unroll
+  for (int h = 0; h < HS_MAX; ++h)
+    r.q[h] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rq, vq, (uint32_t)((h < hs ? h : 0) * KMAX * 4), 0));
+  return r;
+}
+
+__device__ void route(const Args& a, Smem& S, RoutePart rp, int wave, int lane, int tid) {
   const int E = a.E, K = a.K, k = a.k, hs = a.hs;
-  // Sum the router's H-slice partials into S.red[t * E + e]. Thread e loads all of expert e's
-  // partials unconditionally (clamped addresses, results selected) before the first is used, so
-  // the slab costs one memory round trip.
+  // The partials are opaque to the optimizer from here on (an empty asm that reads and writes
+  // their registers), so no arithmetic on them is hoisted above the caller's later loads; such an
+  // add made the wave wait for the partials before the shared tile was requested.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int h = 0; h < HS_MAX; ++h) asm volatile("" : "+v"(rp.v[i][h]));
+#pragma unroll
+  for (int h = 0; h < HS_MAX; ++h) asm volatile("" : "+v"(rp.q[h]));
+  // Sum the router's H-slice partials into S.red[t * E + e] (slices in ascending order).
   float* lg = S.red;
-  {
+  if (E % 4 == 0) {
+    const int nq = E >> 2, np = KMAX * nq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int P = tid + NTH * i, t = P / nq, q = P % nq;
+      f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < HS_MAX; ++h) sum = h < hs ? sum + rp.v[i][h] : sum;
+      if (P < np && t < k) *reinterpret_cast<f32x4*>(&lg[t * E + 4 * q]) = sum;
+    }
+  } else {  // thread e loads all of expert e's partials at once, then sums them
     const int e = tid < E ? tid : 0;
     float p[KMAX][HS_MAX];
 #pragma unroll
@@ -469,12 +523,9 @@ __device__ void route(const Args& a, Smem& S, int wave, int lane, int tid) {
     }
   }
   if (tid < KMAX) {
-    float p[HS_MAX];
-#pragma unroll
-    for (int h = 0; h < HS_MAX; ++h) p[h] = a.psq[(h < hs ? h : 0) * KMAX + tid];
     float ssq = 0.f;
 #pragma unroll
-    for (int h = 0; h < HS_MAX; ++h) ssq = h < hs ? ssq + p[h] : ssq;
+    for (int h = 0; h < HS_MAX; ++h) ssq = h < hs ? ssq + rp.q[h] : ssq;
     S.rinv[tid] = a.pre_norm ? 1.0f / sqrtf(ssq / (float)a.H + a.eps) : 1.0f;
   }
   for (int i = tid; i < MAX_E; i += NTH) S.flag[i] = 0;
@@ -1146,9 +1197,15 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
   const uint32_t vbb = (uint32_t)(256 * wsafe + lane) * 16u;            // bf16 tiles
   const uint32_t vbc = MX ? (uint32_t)(64 * wsafe + lane) * 16u : vbb;  // this layer's tiles
   const uint32_t vbs = (uint32_t)(64 * wsafe + lane);                   // mxfp4 scales
-  if (b < n_sh)
-    gu_load_bf16<WPW>(Ts, buf_rsrc(a.shg, Is * H * 2), buf_rsrc(a.shu, Is * H * 2), (uint32_t)(b * 16 * H * 2), vbb);
-  route(a, S, wave, lane, tid);
+  const RoutePart rp = route_issue(a, tid);
+  __builtin_amdgcn_sched_barrier(0);  // the partials are requested ahead of the shared tile
+  {  // every workgroup issues the tile's loads (the same count of loads in flight on every path,
+     // so waiting for the partials never waits for the tile); without a shared item the resource
+     // is empty and the loads return zeros without a memory access
+    const uint32_t shb = b < n_sh ? (uint32_t)(Is * H * 2) : 0u;
+    gu_load_bf16<WPW>(Ts, buf_rsrc(a.shg, shb), buf_rsrc(a.shu, shb), b < n_sh ? (uint32_t)(b * 16 * H * 2) : 0u, vbb);
+  }
+  route(a, S, rp, wave, lane, tid);
   const int U = __builtin_amdgcn_readfirstlane(S.nw);
 
   // B operands of this wave's H windows (the raw block), used by every item: bf16 hi/lo
