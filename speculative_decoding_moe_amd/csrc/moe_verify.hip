@@ -399,10 +399,11 @@ __device__ __forceinline__ void sort_desc(uint64_t (&c)[NS]) {
 }
 
 // K rounds over the lanes' sorted candidate lists: each round takes the maximum of the list
-// heads (DPP steps inside 16-lane rows, then the row results), the lowest lane whose head equals
-// it (one ballot) and pops that lane's head. HALF: the wave serves two tokens, lanes 0-31 and
-// 32-63; the DPP steps never cross a half, so each half picks its own token's next expert. Lane
-// j of a half records pick j (expert and key).
+// heads (DPP steps inside 16-lane rows, then a row swap that pairs rows 0-1 and 2-3, and for a
+// whole wave a half swap, so the maximum sits in a VGPR of every lane), the lowest lane whose head
+// equals it (one ballot) and pops that lane's head. HALF: the wave serves two tokens, lanes 0-31
+// and 32-63; no step crosses a half, so each half picks its own token's next expert. Lane j of a
+// half records pick j (expert and key).
 template <int NS, bool HALF>
 __device__ __forceinline__ void topk_sorted(uint64_t (&c)[NS], int K, int lane, int& my_e, uint32_t& my_key) {
   const bool hi = HALF && lane >= 32;
@@ -413,17 +414,18 @@ __device__ __forceinline__ void topk_sorted(uint64_t (&c)[NS], int K, int lane, 
     x = max(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
     x = max(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
     x = max(x, dpp_u32<0x141>(x));  // row_half_mirror
-    x = max(x, dpp_u32<0x140>(x));  // row_mirror
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 0);
-    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 16);
-    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 32);
-    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+    x = max(x, dpp_u32<0x140>(x));  // row_mirror: the row maximum in every lane of the row
+    // v_permlane16_swap: one copy gets rows (0, 0, 2, 2), the other rows (1, 1, 3, 3)
+    const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    uint32_t w = max((uint32_t)r16[0], (uint32_t)r16[1]);  // the half's maximum
+    if constexpr (!HALF) {  // v_permlane32_swap: halves (0, 0) and (1, 1)
+      const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+      w = max((uint32_t)r32[0], (uint32_t)r32[1]);
+    }
     const uint32_t lo = (uint32_t)c[0];
-    uint32_t w, e;
+    uint32_t e;
     int sl;
     if constexpr (HALF) {
-      const uint32_t wa = max(r0, r1), wb = max(r2, r3);
-      w = hi ? wb : wa;
       const uint64_t bm = __ballot(h == w);  // each half holds its own maximum
       const int sla = __builtin_ctz((uint32_t)bm), slb = 32 + __builtin_ctz((uint32_t)(bm >> 32));
       const uint32_t ea = (uint32_t)__builtin_amdgcn_readlane((int)lo, sla);
@@ -431,7 +433,6 @@ __device__ __forceinline__ void topk_sorted(uint64_t (&c)[NS], int K, int lane, 
       sl = hi ? slb : sla;
       e = hi ? eb : ea;
     } else {
-      w = max(max(r0, r1), max(r2, r3));
       sl = __builtin_ctzll(__ballot(h == w));
       e = (uint32_t)__builtin_amdgcn_readlane((int)lo, sl);
     }
@@ -440,6 +441,24 @@ __device__ __forceinline__ void topk_sorted(uint64_t (&c)[NS], int K, int lane, 
 #pragma unroll
     for (int m = 0; m + 1 < NS; ++m) c[m] = pop ? c[m + 1] : c[m];
     c[NS - 1] = pop ? 0ull : c[NS - 1];
+  }
+}
+
+// A lane's NS consecutive logits row[e0 .. e0 + NS - 1] of one token (LDS or global; values past
+// E are read at E - 1 and masked by the caller): float4 reads when E is a multiple of 4 and the
+// lane's run lies inside the row (row starts are then 16-byte aligned), else clamped scalar
+// reads; all issued before any is used.
+template <int NS>
+__device__ __forceinline__ void lane_logits(const float* row, int e0, int E, float (&v)[NS]) {
+  if (E % 4 == 0 && e0 + NS <= E) {
+#pragma unroll
+    for (int m = 0; m < NS; m += 4) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(row + e0 + m);
+      v[m] = q[0]; v[m + 1] = q[1]; v[m + 2] = q[2]; v[m + 3] = q[3];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NS; ++m) v[m] = row[min(e0 + m, E - 1)];
   }
 }
 
@@ -545,12 +564,13 @@ __device__ void route(const Args& a, Smem& S, RoutePart rp, int wave, int lane, 
     const bool live = t < k;
     const float rv = S.rinv[live ? t : wave];
     const int e0 = 8 * (lane & 31);
+    float v[8];
+    lane_logits<8>(lg + t * E, e0, E, v);  // rows past k are in bounds, unused
     uint64_t c[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int e = e0 + m;
-      const float v = lg[t * E + (e < E ? e : E - 1)];  // rows past k are in bounds, unused
-      c[m] = topk_comp((live && e < E) ? okey32(rv * v) : 0u, e);
+      c[m] = topk_comp((live && e < E) ? okey32(rv * v[m]) : 0u, e);
     }
     sort_desc<8>(c);
     int my_e = 0;
@@ -578,22 +598,24 @@ __device__ void route(const Args& a, Smem& S, RoutePart rp, int wave, int lane, 
       int my_e = 0;
       uint32_t my_key = 0;
       if (E <= 256) {  // 4 candidates per lane: experts 4 lane + m
+        float v[4];
+        lane_logits<4>(lg + t * E, 4 * lane, E, v);
         uint64_t c[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int e = 4 * lane + m;
-          const float v = lg[t * E + (e < E ? e : E - 1)];
-          c[m] = topk_comp(e < E ? okey32(rv * v) : 0u, e);
+          c[m] = topk_comp(e < E ? okey32(rv * v[m]) : 0u, e);
         }
         sort_desc<4>(c);
         topk_sorted<4, false>(c, K, lane, my_e, my_key);
       } else {  // 8 candidates per lane: experts 8 lane + m
+        float v[8];
+        lane_logits<8>(lg + t * E, 8 * lane, E, v);
         uint64_t c[8];
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
           const int e = 8 * lane + m;
-          const float v = lg[t * E + (e < E ? e : E - 1)];
-          c[m] = topk_comp(e < E ? okey32(rv * v) : 0u, e);
+          c[m] = topk_comp(e < E ? okey32(rv * v[m]) : 0u, e);
         }
         sort_desc<8>(c);
         topk_sorted<8, false>(c, K, lane, my_e, my_key);
@@ -2261,22 +2283,24 @@ __global__ void __launch_bounds__(NTH) k_btopk(BArgs a) {
   int my_e = 0;
   uint32_t my_key = 0;
   if (E <= 256) {  // experts 4 lane + m
+    float v[4];
+    lane_logits<4>(lg, 4 * lane, E, v);
     uint64_t c[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int e = 4 * lane + m;
-      const float v = lg[e < E ? e : E - 1];
-      c[m] = topk_comp(e < E ? okey32(rv * v) : 0u, e);
+      c[m] = topk_comp(e < E ? okey32(rv * v[m]) : 0u, e);
     }
     sort_desc<4>(c);
     topk_sorted<4, false>(c, K, lane, my_e, my_key);
   } else {  // experts 8 lane + m
+    float v[8];
+    lane_logits<8>(lg, 8 * lane, E, v);
     uint64_t c[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const int e = 8 * lane + m;
-      const float v = lg[e < E ? e : E - 1];
-      c[m] = topk_comp(e < E ? okey32(rv * v) : 0u, e);
+      c[m] = topk_comp(e < E ? okey32(rv * v[m]) : 0u, e);
     }
     sort_desc<8>(c);
     topk_sorted<8, false>(c, K, lane, my_e, my_key);
