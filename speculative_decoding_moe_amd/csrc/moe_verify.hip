@@ -1268,9 +1268,13 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
     gu_load<WPW, MX>(T[j], R, dd[j], H, vbc, vbs);
   }
   int nload = static_item(q, D - 1);  // item of the next step whose loads are issued
-  uint32_t cl[2] = {0u, 0u};          // claims in flight (thread 0)
-  if (tid == 0 && q.claims)
-    for (int X = max(q.S, D); X < D + 2; ++X) cl[(X - D) & 1] = claim_raw(q.ctr);
+  // Claims (thread 0): the claim for item X sits in cl[X & 1]. It is issued behind the loads of
+  // step X - D - 1 (item X - 2 with two in flight), so it returns right after them, and it is read
+  // after the math of step X - D, which waits for those loads anyway: a workgroup holds at most one
+  // claimed item that it has not started loading, which keeps the end spread to about one item.
+  static_assert(D == 2, "the claim timing assumes two items in flight");
+  uint32_t cl[2] = {0u, 0u};
+  if (tid == 0 && !is_static(q, D)) cl[D & 1] = claim_raw(q.ctr);
   for (int h = 0;; h += D) {
     bool done = false;
 #pragma unroll
@@ -1280,14 +1284,13 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
       nx[jl] = nload;
       dd[jl] = gu_desc<MX>(a, wk, nload, n_gu, ipe);
       gu_load<WPW, MX>(T[jl], R, dd[jl], H, vbc, vbs);
-      if (tid == 0) {
-        S.claim[(st + D) & 3] = is_static(q, st + D) ? static_item(q, st + D) : pool_item(q, cl[st & 1]);
-        if (!is_static(q, st + D + 2)) cl[st & 1] = claim_raw(q.ctr);
-      }
+      if (tid == 0 && !is_static(q, st + D + 1)) cl[(st + D + 1) & 1] = claim_raw(q.ctr);
       __builtin_amdgcn_sched_barrier(0);
       {
         f32x4 acc[GU_MX_RT][2];
         gu_math<WPW, MX>(acc, T[r], xb, xm);
+        if (tid == 0)  // item st + D, read back by this step's epilogue after its barriers
+          S.claim[(st + D) & 3] = is_static(q, st + D) ? static_item(q, st + D) : pool_item(q, cl[(st + D) & 1]);
         gu_epilogue<MX>(a, S, acc, dd[r].ntile, dd[r].u, dd[r].row0, true, wave, lane, tid, (st + D) & 3, &nload);
       }
       if (nx[(r + 1) % D] >= n_gu) { done = true; break; }  // the next step's item is past the end
@@ -1355,9 +1358,13 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
     dn_load_bb<NWIN, MX>(Bf[j], raf, dd[j].u, I, wave, lane);
   }
   int nload = static_item(q, D - 1);  // item of the next step whose loads are issued
-  uint32_t cl[2] = {0u, 0u};          // claims in flight (thread 0)
-  if (tid == 0 && q.claims)
-    for (int X = max(q.S, D); X < D + 2; ++X) cl[(X - D) & 1] = claim_raw(q.ctr);
+  // Claims (thread 0): the claim for item X sits in cl[X & 1]. It is issued behind the loads of
+  // step X - D - 1 (item X - 2 with two in flight), so it returns right after them, and it is read
+  // after the math of step X - D, which waits for those loads anyway: a workgroup holds at most one
+  // claimed item that it has not started loading, which keeps the end spread to about one item.
+  static_assert(D == 2, "the claim timing assumes two items in flight");
+  uint32_t cl[2] = {0u, 0u};
+  if (tid == 0 && !is_static(q, D)) cl[D & 1] = claim_raw(q.ctr);
   for (int h = 0;; h += D) {
     bool done = false;
 #pragma unroll
@@ -1368,14 +1375,13 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
       dd[jl] = dn_desc<NWIN, MX>(a, wk, nload, n_dn, ipe);
       dn_load<NWIN, MX>(T[jl], rw, rs, dd[jl], I, wave, lane);
       dn_load_bb<NWIN, MX>(Bf[jl], raf, dd[jl].u, I, wave, lane);
-      if (tid == 0) {
-        S.claim[(st + D) & 3] = is_static(q, st + D) ? static_item(q, st + D) : pool_item(q, cl[st & 1]);
-        if (!is_static(q, st + D + 2)) cl[st & 1] = claim_raw(q.ctr);
-      }
+      if (tid == 0 && !is_static(q, st + D + 1)) cl[(st + D + 1) & 1] = claim_raw(q.ctr);
       __builtin_amdgcn_sched_barrier(0);
       {
         f32x4 acc[SH::TPW_MX];
         dn_math<NWIN, MX>(acc, T[r], Bf[r]);
+        if (tid == 0)  // item st + D, read back by this step's epilogue after its barrier
+          S.claim[(st + D) & 3] = is_static(q, st + D) ? static_item(q, st + D) : pool_item(q, cl[(st + D) & 1]);
         dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
         dn_epilogue<NWIN>(a, S, dd[r].ntile, TPW, dd[r].u, true, dd[r].row0, tid, (st + D) & 3, &nload);
       }
