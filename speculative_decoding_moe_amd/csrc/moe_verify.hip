@@ -162,6 +162,31 @@ __device__ __forceinline__ void mx8_quant(const float (&v)[N], uint32_t (&hi)[N 
     lo[g] = fp8x4(ldexpf(r[4 * g], -el), ldexpf(r[4 * g + 1], -el), ldexpf(r[4 * g + 2], -el),
                   ldexpf(r[4 * g + 3], -el));
 }
+// Four values per lane; the block is the 32 values of an aligned 8-lane group (the maxima by DPP
+// steps on the magnitudes' bit patterns, which order like the magnitudes). The same hi and lo
+// words and exponents as mx8_quant over those 32 values.
+__device__ __forceinline__ void mx8_quant4_g8(const float (&v)[4], uint32_t& hi, uint32_t& lo, int& eh, int& el) {
+  auto gmax8 = [](uint32_t m) {
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+    return max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  };
+  uint32_t m = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) m = max(m, __float_as_uint(fabsf(v[j])));
+  eh = mx8_exp(__uint_as_float(gmax8(m)));
+  hi = fp8x4(ldexpf(v[0], -eh), ldexpf(v[1], -eh), ldexpf(v[2], -eh), ldexpf(v[3], -eh));
+  float r[4];
+  r[0] = v[0] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hi, 0), eh);
+  r[1] = v[1] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hi, 1), eh);
+  r[2] = v[2] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hi, 2), eh);
+  r[3] = v[3] - ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)hi, 3), eh);
+  uint32_t mr = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) mr = max(mr, __float_as_uint(fabsf(r[j])));
+  el = mx8_exp(__uint_as_float(gmax8(mr)));
+  lo = fp8x4(ldexpf(r[0], -el), ldexpf(r[1], -el), ldexpf(r[2], -el), ldexpf(r[3], -el));
+}
 // store 16 quantised values of (column c, 32-block blk, half h) of one window and, for h == 0,
 // the block's scale pair (hi exponent in byte 0, lo in byte 1)
 __device__ __forceinline__ void mx8_store16(uint8_t* win, int c, int blk, int h, const uint32_t (&hi)[4],
@@ -757,18 +782,24 @@ __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (MX8) {
-    // thread (block bb, half h, column c) -> rows 32 bb + 16 h .. + 15 of the item; the block
-    // maximum pairs the two halves (lanes c and c + 16 of the same wave)
-    if (tid < 16 * ntile) {
-      const int c = tid & 15, h = (tid >> 4) & 1, bb = tid >> 5;
-      float v[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v[j] = S.act[2 * bb + h][(c + 16 * (j >> 2)) * 4 + (j & 3)];
-      uint32_t hi[4], lo[4];
+    // thread (block bb, column c, group g) -> rows 32 bb + 4 g .. + 3 of the item: eight threads
+    // of one aligned 8-lane group share a column's 32-row block (two waves per block; the
+    // quantisation took one half-wave per block before, 1.7 us of a k = 16 call)
+    if (tid < 64 * ntile) {
+      const int g = tid & 7, c = (tid >> 3) & 15, bb = tid >> 7, h = g >> 2, q = g & 3;
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(&S.act[2 * bb + h][(c + 16 * q) * 4]);
+      const float v[4] = {x4[0], x4[1], x4[2], x4[3]};
+      uint32_t hi, lo;
       int eh, el;
-      mx8_quant<16, true>(v, hi, lo, eh, el);
+      mx8_quant4_g8(v, hi, lo, eh, el);
       uint8_t* win = reinterpret_cast<uint8_t*>(a.afrag) + ((size_t)u * (a.I / WIN) + row0 / WIN) * MXW;
-      mx8_store16(win, c, (row0 % WIN) / 32 + bb, h, hi, lo, eh, el);
+      const int blk = (row0 % WIN) / 32 + bb;
+      const int L = c + 16 * (2 * (blk & 1) + h), off = 16 * (blk >> 1) + 4 * q;  // as mx8_store16
+      *reinterpret_cast<uint32_t*>(win + L * 32 + off) = hi;
+      *reinterpret_cast<uint32_t*>(win + 2048 + L * 32 + off) = lo;
+      if (g == 0)
+        *reinterpret_cast<uint32_t*>(win + 4096 + (c + 16 * blk) * 4) =
+            (uint32_t)(eh + 127) | ((uint32_t)(el + 127) << 8);
     }
     return;
   }
