@@ -803,26 +803,25 @@ __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 
     }
     return;
   }
-  // thread (tile, half, column c) -> rows R .. R+7 of the expert's intermediate dimension
-  if (tid < ntile * 2 * KMAX) {
-    const int tl = tid / (2 * KMAX), half = (tid / KMAX) & 1, c = tid % KMAX;
-    uint32_t hi[8], lo[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = half * 8 + i;
-      split_bf16(S.act[tl][(c + 16 * (r >> 2)) * 4 + (r & 3)], hi[i], lo[i]);
-    }
+  // thread (tile, half, column c, pair m) -> rows R + 2 m and R + 2 m + 1 of the expert's
+  // intermediate dimension, R = row0 + 16 tile + 8 half: word m of the 16-byte hi and lo
+  // fragments that hold rows R .. R + 7 of column c (128 threads per tile; the split took 32
+  // threads with eight rows each before)
+  if (tid < ntile * 2 * KMAX * 4) {
+    const int m = tid & 3, c = (tid >> 2) & 15, half = (tid >> 6) & 1, tl = tid >> 7;
+    const int r = half * 8 + 2 * m;  // rows r and r + 1 sit side by side in the act tile
+    const float2 v = *reinterpret_cast<const float2*>(&S.act[tl][(c + 16 * (r >> 2)) * 4 + (r & 3)]);
+    uint32_t h0, l0, h1, l1;
+    split_bf16(v.x, h0, l0);
+    split_bf16(v.y, h1, l1);
     const int R = row0 + 16 * tl + 8 * half;
     const int w = R / WIN, o = R % WIN;
     const int j = o / 32, q = (o % 32) / 8;
     const int s = w * 4 + j;
     const int I = routed ? a.I : a.Is;
     u32x4* dst = routed ? a.afrag + (size_t)u * (I / 32) * 128 : a.afrag_sh;
-    u32x4 h, l;
-    pack8(hi, h);
-    pack8(lo, l);
-    dst[((size_t)s * 2 + 0) * 64 + c + 16 * q] = h;
-    dst[((size_t)s * 2 + 1) * 64 + c + 16 * q] = l;
+    reinterpret_cast<uint32_t*>(dst + ((size_t)s * 2 + 0) * 64 + c + 16 * q)[m] = h0 | (h1 << 16);
+    reinterpret_cast<uint32_t*>(dst + ((size_t)s * 2 + 1) * 64 + c + 16 * q)[m] = l0 | (l1 << 16);
   }
 }
 
