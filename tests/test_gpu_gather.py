@@ -190,6 +190,8 @@ def test_gather_identical_tokens_many_column_groups(B):
     gen.LayerShape(hidden=128, n_experts=4, top_k=4, inter=128, shared_inter=128),     # K = E, H of one window
     gen.LayerShape(hidden=384, n_experts=512, top_k=16, inter=256, shared_inter=256),  # largest E and K, odd windows
     gen.LayerShape(hidden=1024, n_experts=64, top_k=6, inter=1024, shared_inter=0),    # I = 1024, no shared expert
+    gen.LayerShape(hidden=256, n_experts=30, top_k=5, inter=128, shared_inter=128),    # E not a multiple of 4
+    gen.LayerShape(hidden=256, n_experts=302, top_k=8, inter=128, shared_inter=0),     # E > 256, not a multiple of 4
 ])
 def test_gather_edge_shapes(B, shape):
     wl = gen.Workload("edge", shape, k=16, seed=4321)

@@ -190,6 +190,10 @@ def test_flags_without_shared_and_prenorm_only(B):
     gen.LayerShape(hidden=256, n_experts=512, top_k=16, inter=256, shared_inter=256),  # largest E and K
     gen.LayerShape(hidden=1024, n_experts=64, top_k=6, inter=1024, shared_inter=0),    # I = 1024
     gen.LayerShape(hidden=512, n_experts=32, top_k=4, inter=256, shared_inter=256, wdtype="mxfp4"),
+    # E not a multiple of 4 (scalar router-partial and candidate reads) or 8, on both top-K forms
+    gen.LayerShape(hidden=256, n_experts=30, top_k=5, inter=128, shared_inter=128),
+    gen.LayerShape(hidden=256, n_experts=302, top_k=8, inter=128, shared_inter=0),
+    gen.LayerShape(hidden=512, n_experts=10, top_k=3, inter=256, shared_inter=0, wdtype="mxfp4"),
 ])
 def test_edge_shapes_parity(B, shape):
     wl = gen.Workload("edge", shape, k=16, seed=4321)
