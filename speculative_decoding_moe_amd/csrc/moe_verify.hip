@@ -1189,27 +1189,38 @@ __device__ void dn_epilogue(const Args& a, Smem& S, int ntile, int tpw, int u, b
   __syncthreads();  // the next item's partial tiles reuse S.red
 }
 
-// y[t][h] = sum_j P[t][j][h] + P[t][K][h] (+ x[t][h]); one thread per four outputs
+// y[t][h] = sum_j P[t][j][h] + P[t][K][h] (+ x[t][h]). Four threads per four outputs: thread g
+// of the quad sums terms g, g + 4, ... (the routed slots, then the shared expert's, then the
+// residual), each term one float4 load, all issued before any is added; a quad reduction by DPP,
+// (s0 + s1) + (s2 + s3), finishes the sum, in the same order on every run. One thread with every
+// term in a loop waited for each load in turn.
+constexpr int CMB_T = 5;  // terms per thread: at most 16 routed + shared + residual = 18 <= 4 x 5
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));  // [1,0,3,2]
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // [2,3,0,1]
+}
 __global__ void __launch_bounds__(256) k_combine(Args a) {
   const int H = a.H, K = a.K, H4 = H / 4;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.k * H4) return;
-  const int t = idx / H4, c = idx % H4;
+  const int o = idx >> 2, g = idx & 3;
+  const bool live = o < a.k * H4;  // every lane takes part in the DPP steps
+  const int oc = live ? o : 0, t = oc / H4, c = oc % H4;
+  const int nr = K + (a.Is > 0 ? 1 : 0);   // partial rows of the token
+  const int n = nr + (a.residual ? 1 : 0);  // terms
   const float4* p = reinterpret_cast<const float4*>(a.part + (size_t)t * (K + 1) * H) + c;
-  float4 acc = p[0];
-  for (int j = 1; j < K; ++j) {
-    const float4 v = p[(size_t)j * H4];
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  const float4* xr = reinterpret_cast<const float4*>(a.x + (size_t)t * H) + c;
+  float4 v[CMB_T];
+#pragma unroll
+  for (int i = 0; i < CMB_T; ++i) {
+    const int j = g + 4 * i, jj = j < n ? j : 0;  // terms past n re-read term 0 and are unused
+    v[i] = *(jj < nr ? p + (size_t)jj * H4 : xr);
   }
-  if (a.Is > 0) {
-    const float4 v = p[(size_t)K * H4];
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-  }
-  if (a.residual) {
-    const float4 v = reinterpret_cast<const float4*>(a.x + (size_t)t * H)[c];
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-  }
-  reinterpret_cast<float4*>(a.y + (size_t)t * H)[c] = acc;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < CMB_T; ++i)
+    if (g + 4 * i < n) { acc.x += v[i].x; acc.y += v[i].y; acc.z += v[i].z; acc.w += v[i].w; }
+  acc.x = quad_sum(acc.x); acc.y = quad_sum(acc.y); acc.z = quad_sum(acc.z); acc.w = quad_sum(acc.w);
+  if (live && g == 0) reinterpret_cast<float4*>(a.y + (size_t)t * H)[c] = acc;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -3113,7 +3124,7 @@ bool launch_layer(const Args& a, hipStream_t s, void* const* ev) {
   if (!mark(ev, 2, s)) return false;
   k_down<NWIN, MX><<<cus, NTH, 0, s>>>(a);
   if (!mark(ev, 3, s)) return false;
-  k_combine<<<(a.k * a.H / 4 + 255) / 256, 256, 0, s>>>(a);
+  k_combine<<<(a.k * a.H + 255) / 256, 256, 0, s>>>(a);  // four threads per float4 of y
   return mark(ev, 4, s);
 }
 
