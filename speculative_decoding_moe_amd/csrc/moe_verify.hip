@@ -1531,15 +1531,53 @@ __global__ void __launch_bounds__(1024) k_accept_final(const float* pv, const in
   if (draft) draft += (size_t)sq * n_draft;
   if (n_draft_seq) n_draft = min(max(n_draft_seq[sq], 0), n_draft);
   const int32_t d = (tid < n_draft) ? draft[tid] : 0;  // n_draft <= n_target <= 64
-  for (int row = wave; row < n_target; row += 16) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int c = lane; c < nchunks; c += 64)
-      argmax_merge(bv, bi, pv[(size_t)row * nchunks + c], pi[(size_t)row * nchunks + c]);
-    wave_argmax(bv, bi);
-    if (lane == 0) {
+  // The merge keeps the maximum under (value descending, index ascending), so the order in which
+  // partials are merged does not change the result; the loads are issued before any merge.
+  if (n_target <= 32 && nchunks <= 32) {
+    // half a wave per row (rows 2w and 2w + 1 in wave w), lane c of the half takes chunk c: every
+    // row in one pass
+    const int row = 2 * wave + (lane >> 5), c = lane & 31;
+    const size_t at = (size_t)min(row, n_target - 1) * nchunks + min(c, nchunks - 1);
+    const float v = pv[at];
+    const int vi = pi[at];
+    const bool ok = row < n_target && c < nchunks;
+    float bv = ok ? v : -INFINITY;
+    int bi = ok ? vi : 0x7fffffff;
+#pragma unroll
+    for (int off = 16; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      argmax_merge(bv, bi, ov, oi);
+    }
+    if (c == 0 && row < n_target) {
       tgt[row] = bi;
       target_ids[row] = bi;
+    }
+  } else {
+    constexpr int MC = 8;  // chunks per lane loaded at once
+    for (int row = wave; row < n_target; row += 16) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      const float* rv = pv + (size_t)row * nchunks;
+      const int* ri = pi + (size_t)row * nchunks;
+      for (int c0 = 0; c0 < nchunks; c0 += 64 * MC) {
+        float v[MC];
+        int vi[MC];
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+          const int c = c0 + lane + 64 * m;
+          v[m] = rv[c < nchunks ? c : 0];
+          vi[m] = ri[c < nchunks ? c : 0];
+        }
+#pragma unroll
+        for (int m = 0; m < MC; ++m)
+          if (c0 + lane + 64 * m < nchunks) argmax_merge(bv, bi, v[m], vi[m]);
+      }
+      wave_argmax(bv, bi);
+      if (lane == 0) {
+        tgt[row] = bi;
+        target_ids[row] = bi;
+      }
     }
   }
   __syncthreads();
