@@ -187,16 +187,10 @@ __device__ __forceinline__ void mx8_quant4_g8(const float (&v)[4], uint32_t& hi,
   el = mx8_exp(__uint_as_float(gmax8(mr)));
   lo = fp8x4(ldexpf(r[0], -el), ldexpf(r[1], -el), ldexpf(r[2], -el), ldexpf(r[3], -el));
 }
-// store 16 quantised values of (column c, 32-block blk, half h) of one window and, for h == 0,
-// the block's scale pair (hi exponent in byte 0, lo in byte 1)
-__device__ __forceinline__ void mx8_store16(uint8_t* win, int c, int blk, int h, const uint32_t (&hi)[4],
-                                            const uint32_t (&lo)[4], int eh, int el) {
-  const int L = c + 16 * (2 * (blk & 1) + h), off = 16 * (blk >> 1);
-  *reinterpret_cast<u32x4*>(win + L * 32 + off) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-  *reinterpret_cast<u32x4*>(win + 2048 + L * 32 + off) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-  if (h == 0)
-    *reinterpret_cast<uint32_t*>(win + 4096 + (c + 16 * blk) * 4) = (uint32_t)(eh + 127) | ((uint32_t)(el + 127) << 8);
-}
+// MXW window layout: the 16 values of (column c, 32-block blk, half h) sit as bytes L 32 + off ..
+// + 15 of the hi part (bytes 2048 + the same of the lo part), L = c + 16 (2 (blk mod 2) + h),
+// off = 16 (blk / 2), value j of the half in byte j; the block's scale pair (hi exponent + 127 in
+// byte 0, lo in byte 1) is the word at 4096 + 4 (c + 16 blk).
 __device__ __forceinline__ f32x4 mfma_mx(u32x4 a, uint32_t sa, u32x4 b0, u32x4 b1, uint32_t sb, int sel, f32x4 acc) {
   const v8i A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
   const v8i B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
@@ -295,29 +289,24 @@ __device__ __forceinline__ void write_xfrag(const float* x, u32x4* dst, int H, i
   dst[((size_t)s * 2 + 1) * 64 + lane] = l;
 }
 
-// window w of the raw block as MX-fp8 hi + lo B fragments with their scales (mxfp4 layers): lane
-// l = c + 16 b quantises block b (32 values) of token c and stores its two 16-value halves where
-// the instruction's B layout puts them
-__device__ __forceinline__ void write_xmx(const float* x, uint8_t* dst, int H, int k, int w, int lane) {
-  const int c = lane & 15, b = lane >> 4;
-  float v[32];
-  const float* src = x + (size_t)(c < k ? c : 0) * H + w * WIN + 32 * b;
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const float4 f = *reinterpret_cast<const float4*>(src + 4 * g);
-    v[4 * g + 0] = c < k ? f.x : 0.f;
-    v[4 * g + 1] = c < k ? f.y : 0.f;
-    v[4 * g + 2] = c < k ? f.z : 0.f;
-    v[4 * g + 3] = c < k ? f.w : 0.f;
-  }
-  uint32_t hi[8], lo[8];
+// window w of the raw block as MX-fp8 hi + lo B fragments with their scales (mxfp4 layers), by a
+// whole workgroup: thread (token c, 32-block b, group g) quantises values 4 g .. 4 g + 3 of block b
+// of token c, the eight threads of an aligned 8-lane group sharing the block maximum, and stores
+// them where the instruction's B layout puts them (one lane per block did the 32 values before)
+__device__ __forceinline__ void write_xmx(const float* x, uint8_t* dst, int H, int k, int w, int tid) {
+  const int c = tid >> 5, b = (tid >> 3) & 3, g = tid & 7;
+  const float4 f = *reinterpret_cast<const float4*>(x + (size_t)(c < k ? c : 0) * H + w * WIN + 32 * b + 4 * g);
+  const float v[4] = {c < k ? f.x : 0.f, c < k ? f.y : 0.f, c < k ? f.z : 0.f, c < k ? f.w : 0.f};
+  uint32_t hi, lo;
   int eh, el;
-  mx8_quant<32, false>(v, hi, lo, eh, el);
+  mx8_quant4_g8(v, hi, lo, eh, el);
   uint8_t* win = dst + (size_t)w * MXW;
-  const uint32_t h0[4] = {hi[0], hi[1], hi[2], hi[3]}, h1[4] = {hi[4], hi[5], hi[6], hi[7]};
-  const uint32_t l0[4] = {lo[0], lo[1], lo[2], lo[3]}, l1[4] = {lo[4], lo[5], lo[6], lo[7]};
-  mx8_store16(win, c, b, 0, h0, l0, eh, el);
-  mx8_store16(win, c, b, 1, h1, l1, eh, el);
+  const int h = g >> 2, q = g & 3;
+  const int L = c + 16 * (2 * (b & 1) + h), off = 16 * (b >> 1) + 4 * q;  // the MXW window layout
+  *reinterpret_cast<uint32_t*>(win + L * 32 + off) = hi;
+  *reinterpret_cast<uint32_t*>(win + 2048 + L * 32 + off) = lo;
+  if (g == 0)
+    *reinterpret_cast<uint32_t*>(win + 4096 + (c + 16 * b) * 4) = (uint32_t)(eh + 127) | ((uint32_t)(el + 127) << 8);
 }
 
 struct RouterSmem {
@@ -373,8 +362,8 @@ __device__ void router_item(const Args& a, RouterSmem& S, int r, int wave, int l
   if (!MX) {
     for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) write_xfrag(a.x, a.xfrag, H, k, s, lane);
   } else {
-    for (int w = r + nr * (tid >> 6); w < H / WIN; w += nr * NW)
-      write_xmx(a.x, reinterpret_cast<uint8_t*>(a.xfrag), H, k, w, lane);
+    static_assert(NTH == 16 * 4 * 8, "one workgroup per MX-fp8 window");
+    for (int w = r; w < H / WIN; w += nr) write_xmx(a.x, reinterpret_cast<uint8_t*>(a.xfrag), H, k, w, tid);
     if (a.Is > 0)
       for (int s = r + nr * (tid >> 6); s < H / 32; s += nr * NW) write_xfrag(a.x, a.xfrag_sh, H, k, s, lane);
   }
@@ -794,7 +783,7 @@ __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 
       mx8_quant4_g8(v, hi, lo, eh, el);
       uint8_t* win = reinterpret_cast<uint8_t*>(a.afrag) + ((size_t)u * (a.I / WIN) + row0 / WIN) * MXW;
       const int blk = (row0 % WIN) / 32 + bb;
-      const int L = c + 16 * (2 * (blk & 1) + h), off = 16 * (blk >> 1) + 4 * q;  // as mx8_store16
+      const int L = c + 16 * (2 * (blk & 1) + h), off = 16 * (blk >> 1) + 4 * q;  // the MXW window layout
       *reinterpret_cast<uint32_t*>(win + L * 32 + off) = hi;
       *reinterpret_cast<uint32_t*>(win + 2048 + L * 32 + off) = lo;
       if (g == 0)
