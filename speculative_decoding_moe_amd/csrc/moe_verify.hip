@@ -2249,59 +2249,99 @@ __device__ __forceinline__ void mx8_store16_tok(uint8_t* tw, int blk, int h, con
     *reinterpret_cast<uint32_t*>(tw + 256 + 4 * blk) = (uint32_t)(eh + 127) | ((uint32_t)(el + 127) << 8);
 }
 
+// The many-token router is an fp32 [T x H] x [H x E] product on fp32 MFMA (16 x 16 x 4). One
+// workgroup takes 16 tokens x ET 16-expert tiles; its BR_NW waves split H (wave w takes the
+// 16-column steps w n / BR_NW .. (w + 1) n / BR_NW - 1 of the n = H / 16), so a token's logits
+// are summed in the same order whatever the call. Lane (row r = lane % 16, quad q = lane / 16)
+// holds, for each step h, columns h + 4 q .. h + 4 q + 3 of token row r and of expert row r of
+// every tile (the same k order for both operands): one token load feeds ET MFMAs. With one tile
+// per wave each MFMA needs two fresh operands from the cache and the loads, not the MFMAs, set the
+// pace; four tiles cut the bytes per MFMA to 5/8 of that, but a workgroup then holds four times
+// the MFMA work, so the launch takes the widest ET (4, 2, 1) that still gives every CU a
+// workgroup. A group's loads are all issued before its first MFMA (one round trip per group).
+constexpr int BR_NW = 16, BR_NTH = 64 * BR_NW;
+
+template <int NG, int ET>
+__device__ __forceinline__ void brouter_steps(const float* const (&wrow)[ET], const bool (&wz)[ET],
+                                              const float* xrow, bool xz, int h, f32x4 (&acc)[ET],
+                                              float& ss) {
+  f32x4 xv[NG], wv[NG][ET];
+#pragma unroll
+  for (int u = 0; u < NG; ++u) {
+    xv[u] = *reinterpret_cast<const f32x4*>(xrow + h + 16 * u);
+#pragma unroll
+    for (int i = 0; i < ET; ++i) wv[u][i] = *reinterpret_cast<const f32x4*>(wrow[i] + h + 16 * u);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the scheduler from moving loads down to their uses
+#pragma unroll
+  for (int u = 0; u < NG; ++u) {
+    if (xz) xv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ss += xv[u][0] * xv[u][0] + xv[u][1] * xv[u][1] + xv[u][2] * xv[u][2] + xv[u][3] * xv[u][3];
+#pragma unroll
+    for (int i = 0; i < ET; ++i) {
+      if (wz[i]) wv[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u][i][j], xv[u][j], acc[i], 0, 0, 0);
+    }
+  }
+}
+
+template <int ET>
 struct BRouterSmem {
-  float red[NW * 256];
-  float rsq[NW][64];
+  float red[BR_NW][ET * 256];
+  float rsq[BR_NW][64];
 };
 
-__global__ void __launch_bounds__(NTH) k_brouter(BArgs a) {
-  __shared__ BRouterSmem S;
+template <int ET>
+__global__ void __launch_bounds__(BR_NTH) k_brouter(BArgs a) {
+  __shared__ BRouterSmem<ET> S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, E = a.E, T = a.T;
-  const int nte = (E + 15) / 16;
+  const int nte = (E + 16 * ET - 1) / (16 * ET);
   const int tt = blockIdx.x / nte, et = blockIdx.x % nte;
-  const int cpw = H / NW;  // a multiple of 16
-  const int c0 = wave * cpw;
   const int row = lane & 15, q = lane >> 4;
-  const int e = et * 16 + row, t = tt * 16 + row;
-  const float* wrow = a.wr + (size_t)(e < E ? e : 0) * H;
-  const float* xrow = a.x + (size_t)(t < T ? t : 0) * H;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float ss = 0.f;
-  for (int m = 0; m < cpw / 16; ++m) {
-    const int h = c0 + 16 * m + 4 * q;
-    float4 wv = *reinterpret_cast<const float4*>(wrow + h);
-    float4 xv = *reinterpret_cast<const float4*>(xrow + h);
-    if (e >= E) wv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t >= T) xv = make_float4(0.f, 0.f, 0.f, 0.f);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.x, xv.x, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.y, xv.y, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.z, xv.z, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wv.w, xv.w, acc, 0, 0, 0);
-    ss += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+  const int t = tt * 16 + row;
+  const float* xrow = a.x + (size_t)(t < T ? t : 0) * H + 4 * q;
+  const float* wrow[ET];
+  bool wz[ET];
+#pragma unroll
+  for (int i = 0; i < ET; ++i) {
+    const int e = et * 16 * ET + 16 * i + row;
+    wz[i] = e >= E;
+    wrow[i] = a.wr + (size_t)(e < E ? e : 0) * H + 4 * q;
   }
-  *reinterpret_cast<f32x4*>(&S.red[wave * 256 + lane * 4]) = acc;
+  f32x4 acc[ET];
+#pragma unroll
+  for (int i = 0; i < ET; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  const int n = H / 16, s0 = wave * n / BR_NW, s1 = (wave + 1) * n / BR_NW;
+  int m = s0;
+  for (; m + 4 <= s1; m += 4) brouter_steps<4, ET>(wrow, wz, xrow, t >= T, 16 * m, acc, ss);
+  for (; m < s1; ++m) brouter_steps<1, ET>(wrow, wz, xrow, t >= T, 16 * m, acc, ss);
+#pragma unroll
+  for (int i = 0; i < ET; ++i) *reinterpret_cast<f32x4*>(&S.red[wave][i * 256 + lane * 4]) = acc[i];
   S.rsq[wave][lane] = ss;
   __syncthreads();
-  if (tid < 256) {  // D[i][j] in lane j + 16 (i / 4), element i % 4; i = expert, j = token
+  if (tid < ET * 256) {  // one output per thread: tile i, D[ei][j] in lane j + 16 (ei / 4), element ei % 4
     float d = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) d += S.red[w * 256 + tid];
-    const int l = tid >> 2, v = tid & 3;
-    const int tok = tt * 16 + (l & 15), ei = et * 16 + 4 * (l >> 4) + v;
+    for (int w = 0; w < BR_NW; ++w) d += S.red[w][tid];
+    const int i = tid >> 8, l = (tid >> 2) & 63, v = tid & 3;
+    const int tok = tt * 16 + (l & 15), ei = et * 16 * ET + 16 * i + 4 * (l >> 4) + v;
     if (tok < T && ei < E) a.logits[(size_t)tok * E + ei] = d;
   }
   if (et == 0 && tid < 16) {
     float s = 0.f;
-    for (int w = 0; w < NW; ++w)
+    for (int w = 0; w < BR_NW; ++w)
       for (int qq = 0; qq < 4; ++qq) s += S.rsq[w][tid + 16 * qq];
     const int tok = tt * 16 + tid;
     if (tok < T) a.rinv[tok] = a.pre_norm ? 1.0f / sqrtf(s / (float)H + a.eps) : 1.0f;
   }
   // B fragments of the tile's tokens, windows et, et + nte, ... (256 threads per window)
   const int nwt = H / WIN;
-  for (int w = et + nte * (tid >> 8); w < nwt; w += 2 * nte) {
+  for (int w = et + nte * (tid >> 8); w < nwt; w += (BR_NTH / 256) * nte) {
     const int r = tid & 255, c = r & 15, j = (r >> 4) & 3, qq = r >> 6;
     const int tok = tt * 16 + c;
     if (tok < T) {
@@ -2324,7 +2364,7 @@ __global__ void __launch_bounds__(NTH) k_brouter(BArgs a) {
   // lane (column c, 32-block blk)
   if (a.xgm) {
     const int c = lane & 15, blk = lane >> 4, tok = tt * 16 + c;
-    for (int w = et + nte * wave; w < nwt; w += nte * NW) {
+    for (int w = et + nte * wave; w < nwt; w += nte * BR_NW) {
       float v[32];
       const float* src = a.x + (size_t)(tok < T ? tok : 0) * H + w * WIN + 32 * blk;
 #pragma unroll
@@ -3232,10 +3272,13 @@ static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t f
   hipStream_t s = (hipStream_t)hip_stream;
   (void)hipGetLastError();  // clear a stale error so the check below reports this launch
   const int cus = num_cus();
-  const int nte = (a.E + 15) / 16, ntt = (T + 15) / 16;
+  const int ntt = (T + 15) / 16;
+  auto nte = [&](int et) { return (a.E + 16 * et - 1) / (16 * et); };
   bool ok = mark(events, 0, s);
   if (ok) {
-    k_brouter<<<ntt * nte, NTH, 0, s>>>(a);
+    if (ntt * nte(4) >= cus) k_brouter<4><<<ntt * nte(4), BR_NTH, 0, s>>>(a);
+    else if (ntt * nte(2) >= cus) k_brouter<2><<<ntt * nte(2), BR_NTH, 0, s>>>(a);
+    else k_brouter<1><<<ntt * nte(1), BR_NTH, 0, s>>>(a);
     k_btopk<<<(T + NW - 1) / NW, NTH, 0, s>>>(a);
     k_bperm<<<BPERM_G, BPERM_NTH, 0, s>>>(a);
     ok = mark(events, 1, s);
