@@ -14,7 +14,8 @@
  *                       top-K with softmax renormalised over the K, woken-expert union, grouped
  *                       SwiGLU experts (bf16 or mxfp4 weights), weighted combine with the shared
  *                       expert, optional RMSNorm pre-norm and residual add; also the blocks of
- *                       many sequences verified together (up to 1024 tokens, bf16 weights);
+ *                       many sequences verified together (up to 1024 tokens, bf16 or mxfp4
+ *                       weights; mxfp4 experts on the scaled matrix-core instruction);
  *   accept_prefix    -- per-position target argmax and greedy longest-prefix acceptance;
  *   moe_pack_weights -- rearranges row-major expert matrices into the tiled layout the verify
  *                       block streams (done once, when the weights are loaded).
@@ -28,6 +29,10 @@
  *   - Device pointers must be 16-byte aligned.
  *   - Results are deterministic: fixed reduction orders, no floating-point atomics.
  *   - Calls that share a workspace must not overlap in time (same stream is always safe).
+ *   - Errors: a launch failure returns MOE_ERR_HIP and clears that error (hipGetLastError). If a
+ *     HIP error from the caller's earlier work is already pending in the calling thread when a
+ *     call starts, the call enqueues nothing, returns MOE_ERR_HIP and leaves that error pending,
+ *     so the caller's own hipGetLastError still reports it.
  */
 #ifndef MOE_VERIFY_H
 #define MOE_VERIFY_H
@@ -48,7 +53,8 @@ enum {
   MOE_ERR_ALIGN = -4,     /* a device pointer is not 16-byte aligned                         */
   MOE_ERR_WORKSPACE = -5, /* workspace smaller than the matching *_workspace_size()          */
   MOE_ERR_ALIAS = -6,     /* output overlaps an input it must not overlap                    */
-  MOE_ERR_HIP = -7,       /* a kernel launch failed (device faults surface at the next sync) */
+  MOE_ERR_HIP = -7,       /* a launch failed, or an earlier HIP error was pending (device
+                             faults surface at the next sync)                             */
   MOE_ERR_ARG = -8        /* unknown flag bits or a bad scalar argument                      */
 };
 

@@ -3163,6 +3163,11 @@ int check_layer(const moe_layer* L) {
   return MOE_OK;
 }
 
+// A HIP error left pending by the caller's earlier work would be reported (and cleared) by the
+// launch check of this call as if it were this call's; such a call enqueues nothing, returns
+// MOE_ERR_HIP and leaves the error pending for the caller to read.
+bool error_pending() { return hipPeekAtLastError() != hipSuccess; }
+
 int num_cus() {
   static int cached[64] = {0};
   int dev = 0;
@@ -3270,7 +3275,7 @@ static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t f
   a.eps = L->rms_eps;
 
   hipStream_t s = (hipStream_t)hip_stream;
-  (void)hipGetLastError();  // clear a stale error so the check below reports this launch
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   const int cus = num_cus();
   const int ntt = (T + 15) / 16;
   auto nte = [&](int et) { return (a.E + 16 * et - 1) / (16 * et); };
@@ -3343,7 +3348,7 @@ static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint
   a.eps = L->rms_eps;
 
   hipStream_t s = (hipStream_t)hip_stream;
-  (void)hipGetLastError();  // clear a stale error so the check below reports this launch
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   const bool mx = L->wdtype == MOE_W_MXFP4;
   bool ok;
   if (L->hidden > 1024) ok = mx ? launch_nwin<2, true>(a, s, events) : launch_nwin<2, false>(a, s, events);
@@ -3383,7 +3388,7 @@ int moe_pack_weights(int32_t wdtype, int32_t n_mats, int32_t rows, int32_t cols,
                                 overlaps(dst, bytes, src_scales, elems / 32)))
     return MOE_ERR_ALIAS;
   hipStream_t s = (hipStream_t)hip_stream;
-  (void)hipGetLastError();
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   const int grid = 2048;
   if (wdtype == MOE_W_BF16)
     k_pack_bf16<<<grid, 256, 0, s>>>((const uint8_t*)src, (uint8_t*)dst, rows, cols, elems / 8);
@@ -3430,7 +3435,7 @@ int accept_prefix_batch(const float* logits, int32_t n_seq, int32_t n_target, in
   float* pv = (float*)workspace;
   int* pi = (int*)((uint8_t*)workspace + need / 2);
   hipStream_t s = (hipStream_t)hip_stream;
-  (void)hipGetLastError();
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   k_argmax_partial<<<dim3(nchunks, n_seq * n_target), 256, 0, s>>>(logits, vocab, nchunks, pv, pi);
   k_accept_final<<<n_seq, 1024, 0, s>>>(pv, pi, nchunks, n_target, n_draft_max > 0 ? draft_ids : nullptr,
                                         n_draft_max, target_ids, accepted, n_draft);
@@ -3457,7 +3462,7 @@ int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const in
   float* pv = (float*)workspace;
   int* pi = (int*)((uint8_t*)workspace + need / 2);
   hipStream_t s = (hipStream_t)hip_stream;
-  (void)hipGetLastError();
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   k_argmax_partial<<<dim3(nchunks, n_target), 256, 0, s>>>(logits, vocab, nchunks, pv, pi);
   k_accept_final<<<1, 1024, 0, s>>>(pv, pi, nchunks, n_target, draft_ids, n_draft, target_ids, accepted);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -3505,7 +3510,7 @@ int lm_head_accept(const float* h, int32_t n_target, int32_t hidden, const void*
   uint32_t epoch = ++calls;
   if (epoch == 0) epoch = ++calls;
   hipStream_t s = (hipStream_t)hip_stream;
-  (void)hipGetLastError();
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   const uint8_t* w = (const uint8_t*)w_head;
   if (hidden <= NW * WIN) k_head<1><<<G, NTH, 0, s>>>(h, w, hidden, vocab, n_target, n_items, pv, pi, ctr, epoch);
   else                    k_head<2><<<G, NTH, 0, s>>>(h, w, hidden, vocab, n_target, n_items, pv, pi, ctr, epoch);
@@ -3555,7 +3560,7 @@ int accept_sample(const float* target_logits, int32_t n_target, int32_t vocab, c
   SamplePlan* plan = (SamplePlan*)(ws + align256((size_t)(n_target + n_draft) * nch * 8) + align256((size_t)nch * 8));
   const float zscale = 1.4426950408889634f / temperature;  // log2(e) / T
   hipStream_t s = (hipStream_t)hip_stream;
-  (void)hipGetLastError();
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   k_lse_partial<<<dim3(nch, n_target + n_draft), 256, 0, s>>>(target_logits, draft_logits, n_target, vocab, nch,
                                                              zscale, ms);
   k_sample_partial<<<nch, SAMPLE_NTH, 0, s>>>(target_logits, draft_logits, n_target, vocab, nch, zscale, draft_ids,
@@ -3609,7 +3614,7 @@ int accept_sample_batch(const float* target_logits, int32_t n_seq, int32_t n_tar
   SamplePlan* plan = (SamplePlan*)(ws + b0 + b1);
   const float zscale = 1.4426950408889634f / temperature;  // log2(e) / T
   hipStream_t s = (hipStream_t)hip_stream;
-  (void)hipGetLastError();
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   k_lse_partial<<<dim3(nch, n_target + n_draft, n_seq), 256, 0, s>>>(target_logits, draft_logits, n_target, vocab,
                                                                      nch, zscale, ms);
   k_sample_partial<<<dim3(nch, n_seq), SAMPLE_NTH, 0, s>>>(target_logits, draft_logits, n_target, vocab, nch,
@@ -3629,7 +3634,7 @@ int accept_histogram(const int32_t* accepted, int32_t n_cycles, int32_t n_draft,
   if (overlaps(hist, hb, accepted, ab) || (survival && (overlaps(survival, sb, accepted, ab) ||
                                                         overlaps(survival, sb, hist, hb))))
     return MOE_ERR_ALIAS;
-  (void)hipGetLastError();
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   k_accept_hist<<<1, 1024, 0, (hipStream_t)hip_stream>>>(accepted, n_cycles, n_draft, hist, survival);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

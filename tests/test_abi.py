@@ -318,3 +318,4 @@ def test_pack_weights_validation(b):
     assert f(0, 4, 512, 2048, src + 8, None, dst, None, None) == -4
     assert f(0, 4, 512, 2048, src, None, src + 4096, None, None) == -6   # dst overlaps src
     assert f(1, 1, 512, 2048, src, ss, dst, ss + 16, None) == -6          # scales overlap
+

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import GenLayer
+from helpers import WS_FILLS, GenLayer, fill_ws
 from speculative_decoding_moe_amd.workloads import gen
 
 pytestmark = pytest.mark.gpu
@@ -55,8 +55,7 @@ def run(B, layer, x, flags=0, ws_fill=None, ws=None):
     nw = torch.empty(4, dtype=torch.int32, device="cuda")
     if ws is None:
         ws = torch.empty(layer.workspace_size(k), dtype=torch.uint8, device="cuda")
-    if ws_fill is not None:
-        ws.fill_(ws_fill)
+    fill_ws(ws, ws_fill)
     B.moe_verify_block(layer, xd, flags, y, ids, w, nw, ws)
     torch.cuda.synchronize()
     return {"y": y.cpu().numpy(), "ids": ids.cpu().numpy().astype(np.int64), "w": w.cpu().numpy(),
@@ -161,7 +160,11 @@ def test_gather_max_tokens_and_rows_independent_of_the_call(B):
     x = gen.hidden_states(wl, rep=1024, k=1024)
     full = run(B, layer, x)
     check_routing(full, x, wl)
-    check_outputs(full, x, wl, [0, 511, 1023])
+    # 40 rows spread over the call: tokens land in every position of their experts' 32-token
+    # column groups (an expert with n tokens takes ceil(n / 32) groups)
+    rows = sorted(set([0, 31, 32, 511, 1023] + np.random.default_rng(40).choice(1024, 40, replace=False).tolist()))
+    r = check_outputs(full, x, wl, rows)
+    print(f"gathered k=1024: {len(rows)} rows against the oracle, err/rms={r:.2e}")
     sub = np.array([3, 100, 511, 512, 700, 1023] + list(range(200, 231)))
     part = run(B, layer, x[sub])
     for key in ("y", "ids", "w"):
@@ -229,6 +232,24 @@ def test_gather_determinism_and_stale_workspace(B):
     run(B, layer, gen.hidden_states(wl, rep=10, k=1024), ws=ws)
     g = run(B, layer, x, ws=ws)
     assert np.array_equal(g["y"], base["y"])
+
+
+@pytest.mark.parametrize("name,flags", [("batched", GATHER), ("stack40_mxfp4", GATHER | PRE | RES)])
+@pytest.mark.parametrize("k", [1, 5])
+def test_gather_stale_signed_zero_and_nan_workspace(B, name, flags, k):
+    """Gathered calls with partial column groups: a workspace of -0 or NaN words (bf16 and fp32
+    patterns) gives the same bits as a zeroed one."""
+    wl = gen.WORKLOADS[name]
+    layer = dev_layer(wl)
+    x = gen.hidden_states(wl, rep=60 + k, k=k)
+    base = run(B, layer, x, flags, ws_fill=0)
+    ws = torch.empty(layer.workspace_size(64), dtype=torch.uint8, device="cuda")
+    for fill in ("neg_zero_bf16", "neg_zero_f32", "nan_bf16", "nan_f32", "ff"):
+        g = run(B, layer, x, flags, ws_fill=WS_FILLS[fill], ws=ws)
+        for key in ("y", "ids", "w"):
+            assert np.array_equal(g[key], base[key]), (fill, key)
+        assert np.all(np.isfinite(g["y"]))
+    check_routing(base, x, wl, flags=flags & PRE)
 
 
 # ---- greedy acceptance for many sequences (accept_prefix_batch) -------------------------------

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+from helpers import WS_FILLS, fill_ws
 from speculative_decoding_moe_amd.workloads import gen
 
 pytestmark = pytest.mark.gpu
@@ -38,8 +39,7 @@ def run_head(B, h, w_tiled, V, draft, ws_fill=None):
     tg = torch.full((max(n, 4),), -1, dtype=torch.int32, device="cuda")
     ac = torch.full((4,), -1, dtype=torch.int32, device="cuda")
     ws = torch.empty(B.lm_head_accept_workspace_size(n, h.shape[1], V), dtype=torch.uint8, device="cuda")
-    if ws_fill is not None:
-        ws.fill_(ws_fill)
+    fill_ws(ws, ws_fill)
     B.lm_head_accept(hd, w_tiled, V, dr, tg, ac, ws, n_draft=len(draft))
     torch.cuda.synchronize()
     return tg[:n].cpu().numpy().astype(np.int64), int(ac[0].item())
@@ -147,3 +147,18 @@ def test_head_deterministic_with_stale_workspace(B):
     for fill in (0xFF, 0x7F, None):
         g = run_head(B, h, wt, wl.vocab, [1, 2, 3], ws_fill=fill)
         assert np.array_equal(g[0], base[0]) and g[1] == base[1]
+
+
+@pytest.mark.parametrize("n", [1, 5])
+def test_head_stale_signed_zero_and_nan_workspace(B, n):
+    """Blocks of fewer than 16 positions (padding columns): -0 and NaN words in the workspace
+    change nothing."""
+    wl = _wl(512, 70001, n, seed=10 + n)
+    _, wt = _head(B, wl)
+    h = gen.hidden_states(wl, rep=4, k=n)
+    draft = [1, 2, 3][:n - 1]
+    base = run_head(B, h, wt, wl.vocab, draft, ws_fill=0)
+    check_targets(h, gen.head_weight(wl), base[0])
+    for fill in ("neg_zero_bf16", "neg_zero_f32", "nan_bf16", "nan_f32"):
+        g = run_head(B, h, wt, wl.vocab, draft, ws_fill=WS_FILLS[fill])
+        assert np.array_equal(g[0], base[0]) and g[1] == base[1], fill

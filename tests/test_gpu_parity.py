@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import GenLayer
+from helpers import WS_FILLS, GenLayer, fill_ws
 from speculative_decoding_moe_amd.workloads import gen
 
 pytestmark = pytest.mark.gpu
@@ -52,8 +52,8 @@ def run_block(B, layer, x, flags=0, ws_fill=None, ws=None):
     nw = torch.empty(4, dtype=torch.int32, device="cuda")
     if ws is None:
         ws = torch.empty(layer.workspace_size(k), dtype=torch.uint8, device="cuda")
-    if ws_fill is not None:
-        ws.fill_(ws_fill)
+    fill_ws(ws, ws_fill)
+    print(f"[block] k={k} flags={flags} E={layer.n_experts} H={layer.hidden} fill={ws_fill}", flush=True)
     B.moe_verify_block(layer, xd, flags, y, ids, w, nw, ws)
     torch.cuda.synchronize()
     return {"y": y.cpu().numpy(), "ids": ids.cpu().numpy().astype(np.int64), "w": w.cpu().numpy(),
@@ -148,13 +148,23 @@ def test_verify_block_parity(B):
     assert 50 <= g["n_woken"] <= 128
 
 
-@pytest.mark.parametrize("k", [2, 3, 7, 9, 15])
+@pytest.mark.parametrize("k", list(range(1, 17)))
 def test_k_sweep_parity(B, k):
     wl = gen.WORKLOADS["verify"]
     x = gen.hidden_states(wl, rep=100 + k, k=k)
     g = run_block(B, dev_layer(wl), x)
     r = check_parity(g, x, wl)
     print(f"verify k={k}: U={g['n_woken']} err/rms={r:.2e}")
+
+
+@pytest.mark.parametrize("k", list(range(1, 17)))
+def test_k_sweep_parity_mxfp4(B, k):
+    """The 40-layer stack's mxfp4 layer (pre-norm, residual) at every block size."""
+    wl = gen.WORKLOADS["stack40_mxfp4"]
+    x = gen.hidden_states(wl, rep=100 + k, k=k)
+    g = run_block(B, dev_layer(wl, 0), x, flags=PRE | RES)
+    r = check_parity(g, x, wl, 0, flags=PRE | RES, tol=MX_TOL, compare_delta=True)
+    print(f"mxfp4 k={k}: U={g['n_woken']} delta err/rms={r:.2e}")
 
 
 @pytest.mark.parametrize("sigma", [0.0, 0.05, 0.1, 0.3, 1.0])
@@ -257,6 +267,25 @@ def test_determinism_and_stale_workspace(B):
         assert g["n_woken"] == base["n_woken"]
 
 
+@pytest.mark.parametrize("name,flags", [("verify", 0), ("stack40_mxfp4", PRE | RES)])
+@pytest.mark.parametrize("k", [1, 5])
+def test_stale_signed_zero_and_nan_workspace(B, name, flags, k):
+    """Blocks with padding columns (k < 16): a workspace filled with -0 or NaN words (bf16 and fp32
+    patterns) gives the same bits as a zeroed one, so no stale word reaches a matrix-core tile."""
+    wl = gen.WORKLOADS[name]
+    x = gen.hidden_states(wl, rep=40 + k, k=k)
+    layer = dev_layer(wl)
+    base = run_block(B, layer, x, flags=flags, ws_fill=0)
+    ws = torch.empty(layer.workspace_size(16), dtype=torch.uint8, device="cuda")
+    for fill in ("neg_zero_bf16", "neg_zero_f32", "nan_bf16", "nan_f32", "ff"):
+        g = run_block(B, layer, x, flags=flags, ws_fill=WS_FILLS[fill], ws=ws)
+        for key in ("y", "ids", "w"):
+            assert np.array_equal(g[key], base[key]), (fill, key)
+        assert g["n_woken"] == base["n_woken"]
+        assert np.all(np.isfinite(g["y"]))
+    check_parity(base, x, wl, 0, flags=flags, tol=MX_TOL if flags else BF16_TOL, compare_delta=bool(flags & RES))
+
+
 def test_block_rows_equal_single_token_runs_and_permutation(B):
     """Batch invariance: each block row is bit-identical to that token run alone (k = 1), and
     permuting the block permutes the rows (the greedy output cannot depend on the block)."""
@@ -303,8 +332,56 @@ def test_stack_teacher_forced_sampled_layers(B):
         cur = y
         del layer
     for li, g in checks.items():
-        r = check_parity(g, g["x"], wl, li, flags=PRE | RES, tol=MX_TOL, compare_delta=True, tokens=[0, 7, 15])
+        r = check_parity(g, g["x"], wl, li, flags=PRE | RES, tol=MX_TOL, compare_delta=True)
         print(f"stack layer {li}: U={g['n_woken']} delta err/rms={r:.2e}")
+
+
+STACK_TIE = 1e-2  # routing margin after several layers: the GPU's stream has drifted from the oracle's
+
+
+def test_stack_final_stream_deep(B):
+    """An 8-layer mxfp4 stack at k = 16, final residual stream against the oracle's own chain.
+    Each layer's ids are checked against the oracle's selection on the oracle's stream; where a
+    token's top-K is a near-tie (within STACK_TIE, as the two streams drift apart by rounding),
+    the oracle continues with the GPU's ids (forced) so the streams stay comparable."""
+    base = gen.WORKLOADS["stack40_mxfp4"]
+    n_layers = 8
+    wl = gen.Workload("stack8", base.shape, k=16, seed=base.seed, n_layers=n_layers, pre_norm=True, residual=True)
+    from speculative_decoding_moe_amd.workloads import device
+    x0 = gen.hidden_states(wl)
+    cur = torch.from_numpy(x0).cuda()
+    ws = None
+    gids = []
+    for li in range(n_layers):
+        layer = device.make_layer(wl, li, "cuda")
+        if ws is None:
+            ws = torch.empty(layer.workspace_size(16), dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(cur)
+        ids = torch.empty((16, 8), dtype=torch.int32, device="cuda")
+        print(f"[stack8] layer {li}", flush=True)
+        B.moe_verify_block(layer, cur, PRE | RES, y, ids, None, None, ws)
+        torch.cuda.synchronize()
+        gids.append(ids.cpu().numpy().astype(np.int64))
+        cur = y
+        del layer
+    gy = cur.cpu().numpy().astype(np.float64)
+    xo = x0.astype(np.float64)
+    forced_layers = 0
+    for li in range(n_layers):
+        L = GenLayer(wl, li)
+        ref = oracle.moe_block(xo, L, 8, pre_norm=True, residual=True, rms_eps=wl.rms_eps)
+        if not np.array_equal(ref["ids"], gids[li]):
+            for t in range(16):
+                if not np.array_equal(ref["ids"][t], gids[li][t]):
+                    assert _valid_topk_within(ref["logits"][t], gids[li][t], STACK_TIE), (li, t)
+            ref = oracle.moe_block(xo, L, 8, pre_norm=True, residual=True, rms_eps=wl.rms_eps, forced_ids=gids[li])
+            forced_layers += 1
+        xo = ref["y"]
+    delta_ref, delta_gpu = xo - x0, gy - x0
+    rms = float(np.sqrt(np.mean(delta_ref ** 2)))
+    err = float(np.abs(delta_gpu - delta_ref).max())
+    print(f"stack8 final stream: delta err/rms={err / rms:.2e}, layers with forced near-tie ids: {forced_layers}")
+    assert err <= MX_TOL * rms, f"{err:.3e} vs {rms:.3e}"
 
 
 def test_stack_full_stream_shallow(B):

@@ -333,6 +333,24 @@ def test_stack_of_one_layer_is_block_plus_residual():
     np.testing.assert_allclose(st[0]["y"], x + blk["y"], rtol=1e-14, atol=1e-15)
 
 
+def test_stack_of_three_layers_equals_explicit_composition():
+    """Chaining pin: x_{l+1} = x_l + MoE_l(RMSNorm(x_l)) composed by hand from the dense textbook
+    MoE of each layer (torch fp64), for three different layers. Feeding a layer its own input
+    instead of the previous output, normalising the residual, or reusing one layer's weights
+    each fails this."""
+    wl = _tiny_with_shared()
+    layers = [GenLayer(wl, li) for li in range(3)]
+    x0 = gen.hidden_states(wl) * 2.0
+    st = oracle.moe_stack(x0, layers, 3)
+    x = x0.astype(np.float64)
+    for li, layer in enumerate(layers):
+        x = _dense_textbook_moe(x, layer, 3, 12, residual=True, pre_norm=True)
+        np.testing.assert_allclose(st[li]["y"], x, rtol=1e-10, atol=1e-12)
+    # the layers differ, so the composition order matters
+    swapped = oracle.moe_stack(x0, [layers[1], layers[0], layers[2]], 3)
+    assert np.abs(swapped[1]["y"] - st[1]["y"]).max() > 1e-6
+
+
 # ---------------------------------------------------------------- acceptance
 def test_argmax_first_brute_force_and_ties():
     rng = np.random.default_rng(6)
