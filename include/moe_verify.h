@@ -168,6 +168,25 @@ int moe_verify_block_timed(const moe_layer* layer, const float* x, int32_t k, ui
                            int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
                            size_t ws_bytes, void* hip_stream, void* const* events /* [5] */);
 
+/* Bytes of the library's own device scratch used by moe_verify_block_noalloc (per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)24 << 20)
+
+/* moe_verify_block for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same computation, kernels and
+ * results as moe_verify_block; the workspace is a fixed device array inside the library
+ * (MOE_NOALLOC_SCRATCH_BYTES, one per GPU, kept until the process ends) instead of a caller
+ * buffer, and the call allocates nothing. The caller passes inputs and outputs only.
+ *   Covers every k <= 16 block of a supported layer (at most about 19 MB of workspace) and
+ *   gathered calls whose moe_verify_workspace_size(layer, k) fits the scratch (about 200 tokens
+ *   on the H 2048 / 256-expert / I 512 layer); larger calls return MOE_ERR_WORKSPACE.
+ *   Every call on one GPU shares that GPU's scratch, which keeps the last call's contents (no
+ *   call depends on them): calls that overlap in time on one GPU (different streams, threads)
+ *   race and must be serialised by the caller; calls on one stream are always safe.
+ *   The scratch's device address is looked up (hipGetSymbolAddress) on the first call on each
+ *   device; a failed lookup returns MOE_ERR_HIP. Other statuses as moe_verify_block. */
+int moe_verify_block_noalloc(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
+                             int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* hip_stream);
+
 /* Rearranges n_mats row-major matrices of rows x cols into MOE_LAYOUT_TILED (a permutation of
  * 16-byte chunks and, for mxfp4, of scale bytes; output sizes equal input sizes).
  *   wdtype      MOE_W_BF16: src, dst bf16 [n_mats][rows][cols]

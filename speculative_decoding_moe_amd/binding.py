@@ -19,7 +19,9 @@ MOE_W_BF16, MOE_W_MXFP4 = 0, 1
 MOE_LAYOUT_TILED = 1
 MOE_PRE_RMSNORM, MOE_RESIDUAL, MOE_GATHER = 1, 2, 4
 
-EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "moe_verify_block_timed",
+NOALLOC_SCRATCH_BYTES = 24 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+
+EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "moe_verify_block_timed", "moe_verify_block_noalloc",
            "moe_pack_weights", "accept_prefix_workspace_size", "accept_prefix",
            "accept_prefix_batch_workspace_size", "accept_prefix_batch",
            "lm_head_accept_workspace_size", "lm_head_accept", "accept_sample_workspace_size",
@@ -57,6 +59,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_block_timed.argtypes = [ctypes.POINTER(MoeLayerStruct), vp, i32, u32, vp, vp, vp, vp, vp, sz,
                                            vp, ctypes.POINTER(vp)]
     lib.moe_verify_block_timed.restype = ctypes.c_int
+    lib.moe_verify_block_noalloc.argtypes = [ctypes.POINTER(MoeLayerStruct), vp, i32, u32, vp, vp, vp, vp, vp]
+    lib.moe_verify_block_noalloc.restype = ctypes.c_int
     lib.moe_pack_weights.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.moe_pack_weights.restype = ctypes.c_int
     lib.accept_prefix_workspace_size.argtypes = [i32, i32]
@@ -261,6 +265,15 @@ def moe_verify_block(layer: MoeLayer, x, flags: int, y, topk_ids=None, topk_w=No
     st = lib.moe_verify_block(ctypes.byref(layer.struct), _ptr(x), k, int(flags), _ptr(y),
                               _ptr(topk_ids), _ptr(topk_w), _ptr(n_woken), _ptr(workspace),
                               ws_bytes, _stream_handle() if stream is None else stream)
+    _check(st)
+
+
+def moe_verify_block_noalloc(layer: MoeLayer, x, flags: int, y, topk_ids=None, topk_w=None, n_woken=None,
+                             stream=None) -> None:
+    """moe_verify_block on the library's own device scratch: allocates nothing (library call)."""
+    k = _check_block_args(layer, x, y, topk_ids, topk_w, n_woken, None)
+    st = lib.moe_verify_block_noalloc(ctypes.byref(layer.struct), _ptr(x), k, int(flags), _ptr(y), _ptr(topk_ids),
+                                      _ptr(topk_w), _ptr(n_woken), _stream_handle() if stream is None else stream)
     _check(st)
 
 

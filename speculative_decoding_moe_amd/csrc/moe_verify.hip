@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <stdint.h>
 #include <string.h>
@@ -3210,6 +3211,36 @@ bool launch_nwin(const Args& a, hipStream_t s, void* const* ev) {
   }
 }
 
+// Scratch of moe_verify_block_noalloc: the workspace lives in this file-scope device array (one
+// copy per GPU, held until the process ends) instead of a caller buffer. In host code `scratch`
+// names a host-side stand-in, never the device copy: its device address is looked up once per
+// device with hipGetSymbolAddress and only that address is passed to kernels.
+__device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's scratch address (looked up on the first call per device), or NULL with
+// *status set to MOE_ERR_HIP.
+void* device_scratch(int* status) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+    *status = MOE_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *status = MOE_ERR_HIP;
+      return nullptr;
+    }
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -3368,6 +3399,23 @@ int moe_verify_block_timed(const moe_layer* L, const float* x, int32_t k, uint32
                            size_t ws_bytes, void* hip_stream, void* const* events) {
   return verify_block_impl(L, x, k, flags, y, topk_ids, topk_w, n_woken, workspace, ws_bytes, hip_stream,
                            events);
+}
+
+int moe_verify_block_noalloc(const moe_layer* L, const float* x, int32_t k, uint32_t flags, float* y,
+                             int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* hip_stream) {
+  const int st = check_layer(L);
+  if (st != MOE_OK) return st;
+  if (!x || !y) return MOE_ERR_NULL;
+  if (k < 1 || k > BT_MAX) return MOE_ERR_SHAPE;
+  if (flags & ~(uint32_t)(MOE_PRE_RMSNORM | MOE_RESIDUAL | MOE_GATHER)) return MOE_ERR_ARG;
+  const size_t need = (k > KMAX || (flags & MOE_GATHER)) ? make_blayout(L, k).total : make_layout(L, k).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
+  int lookup = MOE_OK;
+  void* ws = device_scratch(&lookup);
+  if (!ws) return lookup;
+  return verify_block_impl(L, x, k, flags, y, topk_ids, topk_w, n_woken, ws, MOE_NOALLOC_SCRATCH_BYTES, hip_stream,
+                           nullptr);
 }
 
 int moe_pack_weights(int32_t wdtype, int32_t n_mats, int32_t rows, int32_t cols, const void* src,

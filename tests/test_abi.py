@@ -319,3 +319,23 @@ def test_pack_weights_validation(b):
     assert f(0, 4, 512, 2048, src, None, src + 4096, None, None) == -6   # dst overlaps src
     assert f(1, 1, 512, 2048, src, ss, dst, ss + 16, None) == -6          # scales overlap
 
+
+def test_noalloc_rejects_calls_beyond_its_scratch_and_bad_arguments(b):
+    """Host-side checks of moe_verify_block_noalloc, all before any HIP call."""
+    L = _layer(b)
+    x, y = FAKE + 0x10000000, FAKE + 0x20000000
+    call = lambda L, k, flags=0, x=x, y=y: b.lib.moe_verify_block_noalloc(ctypes.byref(L), x, k, flags, y, None,  # noqa: E731
+                                                                          None, None, None)
+    assert b.lib.moe_verify_workspace_size(ctypes.byref(L), 1024) > b.NOALLOC_SCRATCH_BYTES
+    assert call(L, 1024) == b.MOE_ERR_WORKSPACE          # gathered 1024 tokens: about 104 MB
+    assert call(L, 17) == b.MOE_ERR_WORKSPACE or b.lib.moe_verify_workspace_size(ctypes.byref(L), 17) <= \
+        b.NOALLOC_SCRATCH_BYTES
+    assert call(L, 0) == b.MOE_ERR_SHAPE
+    assert call(L, 1025) == b.MOE_ERR_SHAPE
+    assert call(L, 16, flags=8) == b.MOE_ERR_ARG
+    assert call(L, 16, x=None) == b.MOE_ERR_NULL
+    assert call(L, 16, y=None) == b.MOE_ERR_NULL
+    assert call(_layer(b, inter=384), 16) == b.MOE_ERR_SHAPE
+    # the largest layer's 16-token block fits: its workspace is below the scratch size
+    big = _layer(b, n_experts=512, top_k=16, inter=1024, shared_inter=1024)
+    assert 0 < b.lib.moe_verify_workspace_size(ctypes.byref(big), 16) <= b.NOALLOC_SCRATCH_BYTES
