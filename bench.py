@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE verify-block latency (ms) and achieved HBM GB/s vs k=1..16, 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 GATEUP_SRC = os.path.join(ROOT, "speculative_decoding_moe_amd", "csrc", "moe_verify.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_gateup_verify_k16_bf16_traffic.txt")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_layer_verify_k16_bf16_traffic.txt")
 HEAD_PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_head_v151936_h2048_traffic.txt")
 
 
@@ -95,6 +95,12 @@ def down_bytes(shape, U):
     return U * per_expert + H * Is * 2
 
 
+def expert_bytes(shape, U):
+    """Algorithmic bytes of the one-launch layer kernel (gate/up, down and combine phases): every
+    woken expert's gate, up and down weights once, and the shared expert's."""
+    return gateup_bytes(shape, U) + down_bytes(shape, U)
+
+
 def traffic_from_profile(summary=None):
     """HBM bytes per launch from a committed rocprofv3 counter summary (the gate/up one by default),
     or None when the summary is missing or was taken on different kernel source."""
@@ -115,10 +121,10 @@ def traffic_from_profile(summary=None):
         return None
 
 
-def cpu_baseline(wl, n_samples, one_core_samples=1):
-    """The oracle as it stands, timed on the host for a bounded sample of the same steps, with the
-    BLAS thread pool as configured and with one thread."""
-    import numpy as np  # noqa: F401
+def cpu_baseline(wl, n_samples, one_core_samples=3):
+    """The oracle as it stands, timed on the host for a bounded sample of the same steps (median of
+    the steps' rates), with the BLAS thread pool as configured and with one thread."""
+    import numpy as np
 
     import oracle
     from speculative_decoding_moe_amd.workloads import gen
@@ -145,7 +151,7 @@ def cpu_baseline(wl, n_samples, one_core_samples=1):
     layer = CachedLayer()
 
     def run(n):
-        total_t, total_bytes = 0.0, 0.0
+        times, rates = [], []
         for p in range(n):
             x = gen.hidden_states(wl, rep=p)
             logits, planted = gen.target_logits(wl, rep=p)
@@ -155,19 +161,19 @@ def cpu_baseline(wl, n_samples, one_core_samples=1):
             r = oracle.moe_block(x, layer, wl.shape.top_k)
             tg = oracle.argmax_first(logits)
             oracle.accept_length(draft, tg)
-            total_t += time.perf_counter() - t0
-            total_bytes += layer_bytes(wl.shape, r["n_woken"], wl.k) + logits.nbytes
-        return total_t, total_bytes
+            t = time.perf_counter() - t0
+            times.append(t)
+            rates.append((layer_bytes(wl.shape, r["n_woken"], wl.k) + logits.nbytes) / t / 1e9)
+        return float(np.median(times)), float(np.median(rates))
 
-    total_t, total_bytes = run(n_samples)
+    t_all, v_all = run(n_samples)
     threads = 1
-    one = None
+    t_one = v_one = None
     try:
         from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         with threadpool_limits(limits=1):
-            t1, b1 = run(one_core_samples)
-        one = round(b1 / t1 / 1e9, 4)
+            t_one, v_one = run(one_core_samples)
     except Exception:
         pass
     cpu_model = ""
@@ -178,12 +184,59 @@ def cpu_baseline(wl, n_samples, one_core_samples=1):
                 break
     except OSError:
         pass
-    return {"value": round(total_bytes / total_t / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n_samples} verify steps (k=16 MoE layer + acceptance over 17x151936 logits), "
-                      f"{total_t / n_samples:.2f} s per step on the host, host has {os.cpu_count()} CPUs "
+    return {"value": round(v_all, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"median of {n_samples} verify steps (k=16 MoE layer + acceptance over 17x151936 logits), "
+                      f"{t_all:.3f} s per step on the host, {threads} BLAS threads; host has {os.cpu_count()} CPUs "
                       f"({cpu_model})",
-            "value_1core": one, "sample_1core": f"{one_core_samples} step(s) with one BLAS thread"}
+            "value_1core": round(v_one, 4) if v_one else None,
+            "sample_1core": f"median of {one_core_samples} steps with one BLAS thread, "
+                            f"{t_one:.3f} s per step" if t_one else None}
+
+
+def cpu_stack_sample(n_layers_timed, NT, V):
+    """The oracle on the 40-layer mxfp4 stack + acceptance: a bounded sample of its first layers
+    (each timed call decodes its woken experts' fp4 codes itself), scaled to the stack's 40 layers,
+    plus the acceptance over NT x V logits."""
+    import numpy as np
+
+    import oracle
+    from speculative_decoding_moe_amd.workloads import gen
+    sw = gen.WORKLOADS["stack40_mxfp4"]
+
+    class RawLayer:  # the layer's raw encoded weights, generated before the timed call
+        def __init__(self, li, woken):
+            self.r = gen.router_weight(sw, li)
+            self.sh = gen.shared_tensors(sw, li)
+            self.ex = {int(e): gen.expert_tensors(sw, li, int(e)) for e in woken}
+
+        def router(self):
+            return self.r
+
+        def expert(self, e):
+            return self.ex[int(e)]
+
+        def shared(self):
+            return self.sh
+
+    x = gen.hidden_states(sw).astype(np.float64)
+    per_layer = []
+    for li in range(n_layers_timed):
+        logits = oracle.router_logits(oracle.rms_norm(x, sw.rms_eps), gen.router_weight(sw, li))
+        woken = {int(e) for t in range(x.shape[0]) for e in oracle.select_topk(logits[t], sw.shape.top_k)}
+        layer = RawLayer(li, woken)
+        t0 = time.perf_counter()
+        r = oracle.moe_block(x, layer, sw.shape.top_k, pre_norm=True, residual=True, rms_eps=sw.rms_eps)
+        per_layer.append(time.perf_counter() - t0)
+        x = r["y"]
+    alog, _ = gen.target_logits(gen.WORKLOADS["verify"], rep=0)
+    t0 = time.perf_counter()
+    oracle.argmax_first(alog)
+    t_acc = time.perf_counter() - t0
+    med = float(np.median(per_layer))
+    return {"ms_stack_plus_accept": round((med * sw.n_layers + t_acc) * 1e3, 1), "cores": os.cpu_count(),
+            "sample": f"first {n_layers_timed} of the {sw.n_layers} mxfp4 layers timed (median {med * 1e3:.0f} ms "
+                      f"per layer, woken experts' codes decoded inside), scaled to {sw.n_layers} layers, plus the "
+                      f"acceptance over {NT}x{V} logits ({t_acc * 1e3:.1f} ms)"}
 
 
 def context(sweep_k, value):
@@ -231,9 +284,15 @@ def main():
                     help="skip the many-sequence (gathered path) measurement")
     ap.add_argument("--batched-tokens", type=int, default=0,
                     help="measure the gathered path at this token count only (for profiling)")
-    ap.add_argument("--profile-run", action="store_true",
-                    help="counter-collection run: warmup + steps without events, then a plain copy of "
-                         "known size for calibrating HBM traffic counters; prints one JSON line")
+    ap.add_argument("--profile-run", nargs="?", const="k16", default=None,
+                    choices=["k16", "k1", "k4", "k8", "sigma0", "sigma0.3"],
+                    help="counter-collection run of one layer configuration (k16: the benchmark step, plus "
+                         "the output head, the gathered path and the stack's mxfp4 layer; k1/k4/k8: the k "
+                         "sweep's blocks; sigma0/sigma0.3: correlated k = 16 blocks): warmup + steps without "
+                         "events, then a plain copy of known size for calibrating HBM traffic counters; "
+                         "prints one JSON line")
+    ap.add_argument("--cpu-stack-layers", type=int, default=1,
+                    help="layers of the 40-layer mxfp4 stack the CPU oracle times (scaled to 40)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -293,68 +352,86 @@ def main():
         if timed_events is not None:
             ev.record(timed_events[5], stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    if args.profile_run:
-        for i in range(nsteps):
+    if args.profile_run in (None, "k16"):
+        for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
-        Uall = nw_all[:max(nsteps, args.warmup), 0].cpu().numpy().astype(np.int64)
-        # the output head: 4 calls on 2 packed copies
-        hw = gen.Workload("head", s, k=16, seed=wl.seed, vocab=V, n_target=16)
-        w_rm = device.head_tensor(hw, dev)
-        heads = [binding.pack_head(w_rm) for _ in range(2)]
-        del w_rm
-        hh = torch.from_numpy(gen.hidden_states(hw, rep=0, k=16)).to(dev)
-        htg = torch.empty((16,), dtype=torch.int32, device=dev)
-        hac = torch.empty((4,), dtype=torch.int32, device=dev)
-        hws = torch.empty(binding.lm_head_accept_workspace_size(16, s.hidden, V), dtype=torch.uint8, device=dev)
-        for r in range(4):
-            binding.lm_head_accept(hh, heads[r % 2], V, drs[0][:15].contiguous(), htg, hac, hws)
-        torch.cuda.synchronize()
-        del heads
-        # the gathered path: 4 calls of 512 tokens (32 sequences x 16) on the rotating copies
-        bt = 512
-        bx = torch.from_numpy(gen.hidden_states(gen.WORKLOADS["batched"], rep=400, k=bt)).to(dev)
-        bws = torch.empty(layers[0].workspace_size(bt), dtype=torch.uint8, device=dev)
-        by = torch.empty((bt, s.hidden), dtype=torch.float32, device=dev)
-        bnw = torch.zeros((4, 4), dtype=torch.int32, device=dev)
-        for r in range(4):
-            binding.moe_verify_block(layers[r % R], bx, 0, by, None, None, bnw[r], bws)
-        torch.cuda.synchronize()
-        bU = bnw[:, 0].cpu().numpy().astype(np.int64)
-        del bws, by
-        # the 40-layer stack's mxfp4 layer: 4 generated layers, each called twice
-        mw = gen.WORKLOADS["stack40_mxfp4"]
-        mlayers = [device.make_layer(mw, li, dev) for li in range(4)]
-        mws = torch.empty(mlayers[0].workspace_size(mw.k), dtype=torch.uint8, device=dev)
-        mbuf = [torch.empty((mw.k, s.hidden), dtype=torch.float32, device=dev) for _ in range(2)]
-        mnw = torch.zeros((8, 4), dtype=torch.int32, device=dev)
-        for r in range(8):
-            mx_in = torch.from_numpy(gen.hidden_states(mw, rep=r)).to(dev)
-            binding.moe_verify_block(mlayers[r % 4], mx_in, binding.MOE_PRE_RMSNORM | binding.MOE_RESIDUAL,
-                                     mbuf[r % 2], None, None, mnw[r], mws)
-        torch.cuda.synchronize()
-        mU = mnw[:, 0].cpu().numpy().astype(np.int64)
-        del mlayers, mws, mbuf
+
+    if args.profile_run:
+        cfg = args.profile_run
+        if cfg != "k16":  # one configuration of the sweeps, layer calls only (warm-up included)
+            if cfg.startswith("sigma"):
+                cw = gen.WORKLOADS["correlated"]
+                blocks = [torch.from_numpy(gen.hidden_states(cw, rep=300 + p, sigma=float(cfg[5:]))).to(dev)
+                          for p in range(4)]
+            else:
+                blocks = [torch.from_numpy(gen.hidden_states(wl, rep=200 + p, k=int(cfg[1:]))).to(dev)
+                          for p in range(4)]
+            kk = blocks[0].shape[0]
+            pnw = torch.zeros((nsteps + args.warmup + 1, 4), dtype=torch.int32, device=dev)
+            for i in range(nsteps + args.warmup):
+                binding.moe_verify_block(layers[i % R], blocks[i % 4], 0, y[:kk], ids[:kk], w[:kk], pnw[i], ws)
+            torch.cuda.synchronize()
+            pU = pnw[:nsteps + args.warmup, 0].cpu().numpy().astype(np.int64)
+            layer_b = {"layer_bytes_mean": float(np.mean([expert_bytes(s, u) for u in pU]))}
+        else:
+            for i in range(nsteps):
+                step(i)
+            torch.cuda.synchronize()
+            Uall = nw_all[:max(nsteps, args.warmup), 0].cpu().numpy().astype(np.int64)
+        if cfg == "k16":
+            # the output head: 4 calls on 2 packed copies
+            hw = gen.Workload("head", s, k=16, seed=wl.seed, vocab=V, n_target=16)
+            w_rm = device.head_tensor(hw, dev)
+            heads = [binding.pack_head(w_rm) for _ in range(2)]
+            del w_rm
+            hh = torch.from_numpy(gen.hidden_states(hw, rep=0, k=16)).to(dev)
+            htg = torch.empty((16,), dtype=torch.int32, device=dev)
+            hac = torch.empty((4,), dtype=torch.int32, device=dev)
+            hws = torch.empty(binding.lm_head_accept_workspace_size(16, s.hidden, V), dtype=torch.uint8, device=dev)
+            for r in range(4):
+                binding.lm_head_accept(hh, heads[r % 2], V, drs[0][:15].contiguous(), htg, hac, hws)
+            torch.cuda.synchronize()
+            del heads
+            # the gathered path: 4 calls of 512 tokens (32 sequences x 16) on the rotating copies
+            bt = 512
+            bx = torch.from_numpy(gen.hidden_states(gen.WORKLOADS["batched"], rep=400, k=bt)).to(dev)
+            bws = torch.empty(layers[0].workspace_size(bt), dtype=torch.uint8, device=dev)
+            by = torch.empty((bt, s.hidden), dtype=torch.float32, device=dev)
+            bnw = torch.zeros((4, 4), dtype=torch.int32, device=dev)
+            for r in range(4):
+                binding.moe_verify_block(layers[r % R], bx, 0, by, None, None, bnw[r], bws)
+            torch.cuda.synchronize()
+            bU = bnw[:, 0].cpu().numpy().astype(np.int64)
+            del bws, by
+            # the 40-layer stack's mxfp4 layer: 4 generated layers, each called twice
+            mw = gen.WORKLOADS["stack40_mxfp4"]
+            mlayers = [device.make_layer(mw, li, dev) for li in range(4)]
+            mws = torch.empty(mlayers[0].workspace_size(mw.k), dtype=torch.uint8, device=dev)
+            mbuf = [torch.empty((mw.k, s.hidden), dtype=torch.float32, device=dev) for _ in range(2)]
+            mnw = torch.zeros((8, 4), dtype=torch.int32, device=dev)
+            for r in range(8):
+                mx_in = torch.from_numpy(gen.hidden_states(mw, rep=r)).to(dev)
+                binding.moe_verify_block(mlayers[r % 4], mx_in, binding.MOE_PRE_RMSNORM | binding.MOE_RESIDUAL,
+                                         mbuf[r % 2], None, None, mnw[r], mws)
+            torch.cuda.synchronize()
+            mU = mnw[:, 0].cpu().numpy().astype(np.int64)
+            del mlayers, mws, mbuf
+            layer_b = {"layer_bytes_mean": float(np.mean([expert_bytes(s, u) for u in Uall])),
+                       "step_bytes_mean": float(np.mean([layer_bytes(s, u, k) for u in Uall])),
+                       "head_bytes": (V + 15) // 16 * 16 * s.hidden * 2 + 16 * s.hidden * 4,
+                       "bexp_gateup_bytes": float(np.mean([gateup_bytes(s, u) for u in bU])),
+                       "bexp_down_bytes": float(np.mean([gateup_bytes(s, u) / 2 for u in bU])),
+                       "mx_layer_bytes_mean": float(np.mean([expert_bytes(mw.shape, u) for u in mU])),
+                       "accept_bytes": NT * V * 4}
         copy_mib = 512
         src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             device.copy_bytes(dst, src)
         torch.cuda.synchronize()
-        print(json.dumps({"profile_run": True, "launches": int(len(Uall)),
-                          "gateup_bytes_mean": float(np.mean([gateup_bytes(s, u) for u in Uall])),
-                          "layer_bytes_mean": float(np.mean([layer_bytes(s, u, k) for u in Uall])),
-                          "head_bytes": (V + 15) // 16 * 16 * s.hidden * 2 + 16 * s.hidden * 4,
-                          "bexp_gateup_bytes": float(np.mean([gateup_bytes(s, u) for u in bU])),
-                          "bexp_down_bytes": float(np.mean([gateup_bytes(s, u) / 2 for u in bU])),
-                          "down_bytes_mean": float(np.mean([down_bytes(s, u) for u in Uall])),
-                          "mx_gateup_bytes_mean": float(np.mean([gateup_bytes(mw.shape, u) for u in mU])),
-                          "mx_down_bytes_mean": float(np.mean([down_bytes(mw.shape, u) for u in mU])),
-                          "copy_bytes": copy_mib << 20, "copy_launches": 3}), flush=True)
+        print(json.dumps({"profile_run": cfg, "launches": int(nsteps), **layer_b, "copy_bytes": copy_mib << 20,
+                          "copy_launches": 3}), flush=True)
         return
 
     # ---- headline: K whole steps bracketed by synchronisations ----
@@ -394,20 +471,19 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     U2 = nw_all[:nsteps, 0].cpu().numpy().astype(np.int64)
-    names = ["router", "gateup", "down", "combine", "accept"]
-    dur = {n: [] for n in names}
+    # events: [0] before the router kernel, [1] after it, [2] = [3] = [4] after the one-launch
+    # layer kernel (gate/up, down, combine), [5] after the acceptance
+    spans = {"router": (0, 1), "experts": (1, 4), "accept": (4, 5)}
+    dur = {n: [] for n in spans}
     for i in range(nsteps):
         e = evs[i]
-        for j, n in enumerate(names):
-            dur[n].append(ev.ms(e[j], e[j + 1]))
+        for n, (j0, j1) in spans.items():
+            dur[n].append(ev.ms(e[j0], e[j1]))
         ev.destroy(e)
-    gu_ms = float(np.mean(dur["gateup"]))
-    gu_bytes = float(np.mean([gateup_bytes(s, u) for u in U2]))
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    lay_ms = float(np.mean(dur["experts"]))
+    lay_bytes = float(np.mean([expert_bytes(s, u) for u in U2]))
+    achieved = lay_bytes / (lay_ms * 1e-3) / 1e9
     kernels_us = {n: round(float(np.mean(v)) * 1e3, 2) for n, v in dur.items()}
-    expert_ms = float(np.mean(np.array(dur["gateup"]) + np.array(dur["down"])))
-    expert_bytes = float(np.mean([layer_bytes(s, u, k) - s.n_experts * s.hidden * 4 - 2 * k * s.hidden * 4
-                                  for u in U2]))
 
     # ---- achievable streaming read (reference kernel, 2 GiB so the LLC cannot hold it) ----
     rd = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
@@ -426,13 +502,14 @@ def main():
     read_ceiling = float(rd.numel() / (np.median(rd_times) * 1e-3) / 1e9)
     del rd
 
-    roofline = {"bound": "hbm", "kernel": "k_gateup", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+    roofline = {"bound": "hbm", "kernel": "k_layer (gate/up, down and combine phases of the layer)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic_from_profile(),
-                "bytes_per_launch": round(gu_bytes), "avg_launch_us": round(gu_ms * 1e3, 2),
+                "bytes_per_launch": round(lay_bytes), "avg_launch_us": round(lay_ms * 1e3, 2),
                 "achievable_read_GBps": round(read_ceiling, 1),
                 "frac_of_achievable": round(achieved / read_ceiling, 4),
-                "expert_kernels_GBps": round(expert_bytes / (expert_ms * 1e-3) / 1e9, 1)}
+                "expert_kernels_GBps": round(achieved, 1)}
 
     # ---- sweeps (same layer; k = 1..16 and correlated blocks at k = 16) ----
     sweep_k, sweep_sigma, fit = [], [], None
@@ -441,8 +518,10 @@ def main():
 
         def time_blocks(blocks):
             nw = torch.zeros((len(blocks) * reps + 1, 4), dtype=torch.int32, device=dev)
+            kb = blocks[0].shape[0]
             for i in range(5):
-                binding.moe_verify_block(layers[i % R], blocks[i % len(blocks)], 0, y, ids, w, nw[0], ws)
+                binding.moe_verify_block(layers[i % R], blocks[i % len(blocks)], 0, y[:kb], ids[:kb], w[:kb], nw[0],
+                                         ws)
             a, b = ev.create(2)
             torch.cuda.synchronize()
             ev.record(a, stream)
@@ -744,6 +823,9 @@ def main():
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {args.cpu_samples} steps", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, args.cpu_samples)
+        if not args.no_stack and args.cpu_stack_layers > 0:
+            print(f"[bench] timing the CPU oracle on {args.cpu_stack_layers} stack layers", file=sys.stderr, flush=True)
+            cpu["stack40_mxfp4"] = cpu_stack_sample(args.cpu_stack_layers, NT, V)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": nsteps,

@@ -153,6 +153,10 @@ size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max);
  *   workspace, ws_bytes: device scratch of at least moe_verify_workspace_size(layer, k) bytes
  *            (k_max = 1024 with bf16 weights: about 104 MB at H 2048, E 256, K 8, I 512);
  *            its contents need no initialisation and are overwritten.
+ * The single-block path (k <= 16) runs its expert phases in one launch whose workgroups wait for
+ * each other's phases through counters in the workspace. The waits are bounded: if a phase is not
+ * complete within seconds (only possible when other work holds the GPU's compute units that
+ * long), the call's outputs are invalid and *n_woken is set to -1.
  * Returns MOE_OK or an MOE_ERR_* code (nothing is enqueued on error). */
 int moe_verify_block(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
                      int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
@@ -162,8 +166,9 @@ int moe_verify_block(const moe_layer* layer, const float* x, int32_t k, uint32_t
  * additionally records events[i] (hipEvent_t created and owned by the caller; any entry may be
  * NULL) on hip_stream at the kernel boundaries: [0] before the router kernel, [1] after it
  * (gathered path: after the router, top-K and permutation kernels), [2] after the gate/up
- * kernel, [3] after the down kernel, [4] after the combine. A failing
- * event record returns MOE_ERR_HIP. */
+ * phase, [3] after the down phase, [4] after the combine. On the single-block path (k <= 16)
+ * gate/up, down and combine are one launch, so [2], [3] and [4] are all recorded after it. A
+ * failing event record returns MOE_ERR_HIP. */
 int moe_verify_block_timed(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
                            int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
                            size_t ws_bytes, void* hip_stream, void* const* events /* [5] */);
@@ -213,6 +218,10 @@ size_t accept_prefix_workspace_size(int32_t n_target, int32_t vocab);
  *   accepted   int32 [1] out: a = the longest prefix with draft_ids[i] == target_ids[i]; the
  *              committed tokens are draft_ids[0..a) followed by target_ids[a] when a < n_target
  * Limits: 1 <= n_target <= 64, 0 <= n_draft <= n_target, 1 <= vocab <= 2^24.
+ * One launch: chunk workgroups publish their maxima as records tagged for this call, and the
+ * last workgroup reduces them once all are valid (the workspace needs no initialisation). That
+ * wait is bounded: past it (seconds; only when other work holds the GPU that long) *accepted is
+ * set to -1 and target_ids are invalid.
  * NaN logits give an unspecified argmax. Returns MOE_OK or an MOE_ERR_* code. */
 int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const int32_t* draft_ids,
                   int32_t n_draft, int32_t* target_ids, int32_t* accepted, void* workspace,
@@ -232,7 +241,8 @@ size_t accept_prefix_batch_workspace_size(int32_t n_seq, int32_t n_target, int32
  *   target_ids  int32 [n_seq][n_target] out: per-row argmax, equal values to the lowest index
  *   accepted    int32 [n_seq] out: each sequence's accepted length
  * Limits: 1 <= n_seq <= 1024, 1 <= n_target <= 64, n_seq * n_target <= 65535,
- * 0 <= n_draft_max <= n_target, 1 <= vocab <= 2^24. Returns MOE_OK or an MOE_ERR_* code. */
+ * 0 <= n_draft_max <= n_target, 1 <= vocab <= 2^24. One launch, as accept_prefix (a sequence
+ * whose wait ran past its bound gets accepted[s] = -1). Returns MOE_OK or an MOE_ERR_* code. */
 int accept_prefix_batch(const float* logits, int32_t n_seq, int32_t n_target, int32_t vocab,
                         const int32_t* draft_ids, int32_t n_draft_max, const int32_t* n_draft,
                         int32_t* target_ids, int32_t* accepted, void* workspace, size_t ws_bytes,

@@ -1,28 +1,26 @@
 // MoE verify-block library for gfx950 (CDNA4). C ABI in include/moe_verify.h.
 //
 // One MoE layer over a speculative block of k <= 16 tokens ("Speculating on a Strix Halo",
-// sections "Speculative decoding", "What the pieces cost", "The verify's own cost") runs as four
+// sections "Speculative decoding", "What the pieces cost", "The verify's own cost") runs as two
 // stream-ordered launches (many sequences at once, up to 1024 tokens: the gathered path further
-// down); the kernel boundaries publish each phase's results to every CU:
+// down):
 //
 //   k_router    (expert tile, H slice) items: fp32 MFMA partial logits and sums of squares; the
 //               block is also packed as the experts' B operands (bf16 hi/lo fragments, or MX-fp8
-//               hi/lo operands for mxfp4 routed experts).
-//   k_gateup    every workgroup first computes the routing in LDS: RMSNorm factor, logits, top-K
-//               per token (ties to the lower expert), softmax over the K, the woken-expert union
-//               (wave ballot + prefix count) and the weight table. Then (woken expert, row tile)
-//               items, assigned statically and balanced, the last rounds claimed: the expert's
-//               gate and up rows are streamed from HBM once (128-bit nontemporal loads, the next
-//               item prefetched) and applied to all 16 token columns on the matrix cores; SwiGLU,
-//               the routing weight and the hi/lo split are fused into the epilogue, which writes
-//               the down B operand.
-//   k_down      (woken expert, row group) items: W_down streamed once, partial rows per (token,
-//               slot).
-//   k_combine   y[t] = sum_j P[t, j] + P[t, shared] (+ x[t]), fixed slot order.
+//               hi/lo operands for mxfp4 routed experts). Zeroes the counters of k_layer.
+//   k_layer     three phases, each starting when the previous one is complete on every workgroup:
+//               (1) the routing in LDS (RMSNorm factor, logits, top-K per token with ties to the
+//               lower expert, softmax over the K, the woken-expert union by wave ballot + prefix
+//               count, the weight table), then (woken expert, row tile) items, assigned statically
+//               and balanced, the last rounds claimed: the expert's gate and up rows are streamed
+//               from HBM once (128-bit nontemporal loads, the next item prefetched) and applied to
+//               all 16 token columns on the matrix cores; SwiGLU, the routing weight and the hi/lo
+//               split are fused into the epilogue, which writes the down B operand; (2) (woken
+//               expert, row group) items: W_down streamed once, partial rows per (token, slot);
+//               (3) the combine y[t] = sum_j P[t, j] + P[t, shared] (+ x[t]), fixed slot order.
 //
-// Kernel boundaries are the cheapest way to publish data across the XCDs' separate L2 caches on
-// this part (a grid barrier needs agent-scope fences, measured several times dearer), so no kernel
-// waits on another workgroup.
+// The router's results reach k_layer through a kernel boundary. Inside k_layer the phases publish
+// through device-coherent stores and counters (no kernel waits on data of a later phase).
 //
 // Tokens are the MFMA N dimension (16 columns; unused columns are explicit zeros written every
 // call), expert rows the M dimension, the hidden / intermediate size the K dimension. MFMA work
@@ -38,7 +36,9 @@
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <mutex>
+#include <random>
 #include <type_traits>
 #include <stdint.h>
 #include <string.h>
@@ -88,6 +88,18 @@ __device__ __forceinline__ uint32_t bld1(rsrc_t r, uint32_t voff, uint32_t soff)
   return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, BUF_NT);
 }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+
+// Device-coherent (sc1) stores and loads: written through to memory and read from it, past the
+// XCD-local L2, so data one workgroup publishes inside a launch is visible to workgroups on every
+// XCD once the writer's stores are complete (s_waitcnt) and a counter says so; no L2 write-back
+// or invalidate fence is needed. A relaxed agent-scope atomic store is exactly such a store.
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+constexpr int BUF_DEV = 16;  // buffer-instruction cache policy bit sc1 (device scope)
 
 __device__ __forceinline__ uint32_t bf16_rne(float f) {  // finite inputs
   uint32_t u = __float_as_uint(f);
@@ -384,6 +396,32 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
 }
+// Wave-wide maximum / minimum of a 32-bit value in every lane: DPP steps inside 16-lane rows, then
+// the gfx950 row and half swaps (no LDS round trips, unlike lane shuffles).
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  x = op(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = op(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = op(x, dpp_u32<0x141>(x));  // row_half_mirror
+  x = op(x, dpp_u32<0x140>(x));  // row_mirror
+  const auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = op((uint32_t)r16[0], (uint32_t)r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op((uint32_t)r32[0], (uint32_t)r32[1]);
+}
+// (value, index) maximum over the wave, equal values to the lower index, in every lane: the
+// largest order-preserving key, then the lowest index among the lanes holding it. The same
+// result as merging the lanes with argmax_merge (-0 and +0 are equal; a NaN never wins over a
+// number), with the value returned as the key's float (+0 for a -0 maximum).
+__device__ __forceinline__ void wave_argmax_dpp(float& v, int& i) {
+  const uint32_t key = okey32(v);
+  const uint32_t km = wave_reduce_u32<true>(key);
+  const uint32_t im = wave_reduce_u32<false>(key == km ? (uint32_t)i : 0xFFFFFFFFu);
+  v = km == 1u ? v : okey32_value(km);  // a wave of NaNs keeps its own value
+  i = (int)im;
+}
+
 // Top-K candidates are (key, expert) composites: the order-preserving logit key in the upper word
 // and the inverted expert id in the lower, so the larger composite is the larger logit and, on
 // equal logits, the lower expert id. Experts are laid out lane-major (lane l holds experts
@@ -673,18 +711,14 @@ __device__ void route(const Args& a, Smem& S, RoutePart rp, int wave, int lane, 
   }
   if (tid < KMAX) S.wcol[U][tid] = (tid < k) ? 1.0f : 0.f;  // shared expert column weights
   __syncthreads();
-  if (blockIdx.x == 0) {  // outputs, and the tables the down kernel reads
+  if (blockIdx.x == 0) {  // outputs
     if (tid < k * K) {
       const int t = tid / K, j = tid % K;
       if (a.out_ids) a.out_ids[t * K + j] = S.ids[t][j];
       if (a.out_w) a.out_w[t * K + j] = S.w[t][j];
     }
-    if (tid == 0) {
-      if (a.out_n) a.out_n[0] = U;
-      a.tab_n[0] = U;
-    }
-    for (int i = tid; i < U; i += NTH) a.tab_woken[i] = S.woken[i];
-    for (int i = tid; i < U * KMAX; i += NTH) a.tab_slot[i] = S.slot[i / KMAX][i % KMAX];
+    // written through to memory, like a later failure report (-1) that must not be overwritten
+    if (tid == 0 && a.out_n) st_dev(reinterpret_cast<uint32_t*>(a.out_n), (uint32_t)U);
   }
 }
 
@@ -785,11 +819,10 @@ __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 
       uint8_t* win = reinterpret_cast<uint8_t*>(a.afrag) + ((size_t)u * (a.I / WIN) + row0 / WIN) * MXW;
       const int blk = (row0 % WIN) / 32 + bb;
       const int L = c + 16 * (2 * (blk & 1) + h), off = 16 * (blk >> 1) + 4 * q;  // the MXW window layout
-      *reinterpret_cast<uint32_t*>(win + L * 32 + off) = hi;
-      *reinterpret_cast<uint32_t*>(win + 2048 + L * 32 + off) = lo;
-      if (g == 0)
-        *reinterpret_cast<uint32_t*>(win + 4096 + (c + 16 * blk) * 4) =
-            (uint32_t)(eh + 127) | ((uint32_t)(el + 127) << 8);
+      const uint32_t sw = (uint32_t)(eh + 127) | ((uint32_t)(el + 127) << 8);
+      st_dev(reinterpret_cast<uint32_t*>(win + L * 32 + off), hi);  // published inside the launch
+      st_dev(reinterpret_cast<uint32_t*>(win + 2048 + L * 32 + off), lo);
+      if (g == 0) st_dev(reinterpret_cast<uint32_t*>(win + 4096 + (c + 16 * blk) * 4), sw);
     }
     return;
   }
@@ -810,8 +843,10 @@ __device__ __forceinline__ void gu_epilogue(const Args& a, Smem& S, const f32x4 
     const int s = w * 4 + j;
     const int I = routed ? a.I : a.Is;
     u32x4* dst = routed ? a.afrag + (size_t)u * (I / 32) * 128 : a.afrag_sh;
-    reinterpret_cast<uint32_t*>(dst + ((size_t)s * 2 + 0) * 64 + c + 16 * q)[m] = h0 | (h1 << 16);
-    reinterpret_cast<uint32_t*>(dst + ((size_t)s * 2 + 1) * 64 + c + 16 * q)[m] = l0 | (l1 << 16);
+    uint32_t* ph = reinterpret_cast<uint32_t*>(dst + ((size_t)s * 2 + 0) * 64 + c + 16 * q) + m;
+    uint32_t* pl = reinterpret_cast<uint32_t*>(dst + ((size_t)s * 2 + 1) * 64 + c + 16 * q) + m;
+    st_dev(ph, h0 | (h1 << 16));  // published inside the launch
+    st_dev(pl, l0 | (l1 << 16));
   }
 }
 
@@ -904,6 +939,14 @@ __device__ __forceinline__ void gu_load_xb(u32x4 (&xb)[WPW][4][2], const u32x4* 
 //    later; it never holds up a load that is needed sooner.
 constexpr int NGRP = 8;          // claim pools
 constexpr int CTR_STRIDE = 64;   // uint32 words between pool counters (256 B)
+// Counters of the one-launch layer kernel, zeroed by the router, each NPC slots 256 B apart:
+// completed gate/up items, then completed down items. Workgroup b adds to slot b mod NPC: adds to
+// one address serialise (about 30 ns each), and 256 workgroups counting into a single word took
+// about 8 us.
+constexpr int NPC = 16;
+constexpr int CT_GU = 2 * NGRP;
+constexpr int CT_DN = CT_GU + NPC;
+constexpr int N_CTR = CT_DN + NPC;
 struct Sched {
   int G, S, f, pool, npool;  // workgroups, static rounds, first item, pool, pools
   bool claims;               // whether the last rounds are claimed
@@ -1172,7 +1215,7 @@ __device__ void dn_epilogue(const Args& a, Smem& S, int ntile, int tpw, int u, b
         float v = 0.f;
 #pragma unroll
         for (int win = 0; win < NWIN; ++win) v += S.red[((win + NWIN * tg) * tpw + lt) * 256 + idx];
-        dst[tl * 16] = v;
+        st_dev(dst + tl * 16, v);  // published inside the launch
       }
     }
   }
@@ -1189,21 +1232,26 @@ __device__ __forceinline__ float quad_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xf, 0xf, false));  // [1,0,3,2]
   return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xf, 0xf, false));  // [2,3,0,1]
 }
-__global__ void __launch_bounds__(256) k_combine(Args a) {
+// Output float4 o of y, thread g of its quad (every lane takes part in the DPP steps; live: o is an
+// output). The partial rows were published inside the same launch and are read past the L2.
+__device__ __forceinline__ void combine_quad(const Args& a, int o, int g, bool live) {
   const int H = a.H, K = a.K, H4 = H / 4;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const int o = idx >> 2, g = idx & 3;
-  const bool live = o < a.k * H4;  // every lane takes part in the DPP steps
   const int oc = live ? o : 0, t = oc / H4, c = oc % H4;
   const int nr = K + (a.Is > 0 ? 1 : 0);   // partial rows of the token
   const int n = nr + (a.residual ? 1 : 0);  // terms
   const float4* p = reinterpret_cast<const float4*>(a.part + (size_t)t * (K + 1) * H) + c;
   const float4* xr = reinterpret_cast<const float4*>(a.x + (size_t)t * H) + c;
+  const rsrc_t rp = buf_rsrc(a.part, (uint32_t)((size_t)a.k * (K + 1) * H * 4));
   float4 v[CMB_T];
 #pragma unroll
   for (int i = 0; i < CMB_T; ++i) {
     const int j = g + 4 * i, jj = j < n ? j : 0;  // terms past n re-read term 0 and are unused
-    v[i] = *(jj < nr ? p + (size_t)jj * H4 : xr);
+    if (jj < nr) {
+      const uint32_t off = (uint32_t)((((size_t)t * (K + 1) + jj) * H + 4 * c) * 4);
+      v[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, BUF_DEV));
+    } else {
+      v[i] = *xr;
+    }
   }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -1214,6 +1262,45 @@ __global__ void __launch_bounds__(256) k_combine(Args a) {
 }
 
 // ------------------------------------------------------------------------------------------
+// phase counters of the one-launch layer kernel
+// ------------------------------------------------------------------------------------------
+// Publishing inside the one-launch layer kernel: the data is written with device-coherent stores,
+// so it is visible everywhere once the stores are complete (s_waitcnt); no L2 write-back is needed
+// before the count that announces it.
+//
+// Adds this workgroup's item count to a phase counter once every wave's stores are complete.
+__device__ __forceinline__ void publish_count(const Args& a, int ct, int n, int tid) {
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores (and loads) are complete
+  __syncthreads();                // and every other wave's
+  if (tid == 0 && n > 0)
+    __hip_atomic_fetch_add(a.ctr + (ct + (int)(blockIdx.x % NPC)) * CTR_STRIDE, (uint32_t)n, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr uint32_t WAIT_POLLS = 1u << 22;
+// Waits until a phase counter's slots sum to `target`: lane i < NPC of wave 0 reads slot i per
+// poll (one round trip), and the workgroup meets at a barrier. Bounded: after WAIT_POLLS polls
+// (seconds) the call is reported failed (n_woken = -1) and the workgroup goes on, so no wave ever
+// hangs.
+__device__ __forceinline__ void wait_count(const Args& a, int ct, uint32_t target, int tid) {
+  if (tid < 64) {
+    uint32_t* slot = a.ctr + (ct + (tid < NPC ? tid : 0)) * CTR_STRIDE;
+    for (uint32_t polls = 0;; ++polls) {
+      uint32_t v = tid < NPC ? __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+#pragma unroll
+      for (int off = NPC / 2; off > 0; off >>= 1) v += __shfl_xor(v, off);  // lanes 0 .. NPC-1 hold the sum
+      if (__builtin_amdgcn_readfirstlane(v) >= target) break;
+      if (polls == WAIT_POLLS) {
+        if (tid == 0 && a.out_n) st_dev(reinterpret_cast<uint32_t*>(a.out_n), 0xFFFFFFFFu);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------
 // kernels
 // ------------------------------------------------------------------------------------------
 template <bool MX>
@@ -1221,15 +1308,16 @@ __global__ void __launch_bounds__(NTH) k_router(Args a) {
   __shared__ RouterSmem S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
-  if (blockIdx.x == 0 && tid < 2 * NGRP) a.ctr[tid * CTR_STRIDE] = 0u;  // this layer's pools start at 0
+  // this layer's claim pools and the counters of the one-launch layer kernel start at 0
+  for (int i = blockIdx.x * NTH + tid; i < N_CTR; i += gridDim.x * NTH) a.ctr[i * CTR_STRIDE] = 0u;
   router_item<MX>(a, S, blockIdx.x, wave, lane, tid);
 }
 
+// The gate/up work of one workgroup: the routing prologue (into LDS), the shared expert's row tile
+// when b < Is/16, then its routed items. Returns the number of items it completed. The activation
+// fragments are published inside the launch (device-coherent stores).
 template <int WPW, bool MX>
-__global__ void __launch_bounds__(NTH) k_gateup(Args a) {
-  __shared__ Smem S;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+__device__ __forceinline__ int gateup_body(const Args& a, Smem& S, int tid, int lane, int wave) {
   const int H = a.H, I = a.I, Is = a.Is;
   const int G = gridDim.x, b = blockIdx.x;
   const int win0 = wave * WPW;
@@ -1271,12 +1359,15 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
 
   const int ipe = I / (16 * (MX ? GU_MX_RT : 1));
   const int n_gu = U * ipe;
+  int n_done = 0;
   if (b < n_sh) {
     f32x4 acc[GU_MX_RT][2];
     gu_math_bf16<WPW>(acc, Ts, xb);
-    gu_epilogue(a, S, acc, 1, U, b * 16, false, wave, lane, tid);
+    gu_epilogue<false>(a, S, acc, 1, U, b * 16, false, wave, lane, tid);
     if (MX) gu_load_xmx<WPW>(xm, a.xfrag, win0, active, lane);
+    n_done = 1;
   }
+
   // Routed items (see make_sched), D items deep: at step h item h is multiplied while the loads
   // of items h + 1 .. h + D - 1 are in flight (those of item h + D - 1 issued at the top of the
   // step). Thread 0 stores the index of item h + D into the LDS ring (static, or claimed two steps
@@ -1287,7 +1378,7 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
   constexpr int D = 2;
   const Sched q = make_sched(n_gu, G, b, n_sh, a.ctr);
   const int r0 = static_item(q, 0);
-  if (r0 >= n_gu) return;  // every later item is past the end too
+  if (r0 >= n_gu) return n_done;  // every later item is past the end too
   const Woken wk = load_woken(S, lane);
   GUItem<WPW> T[D];
   GUDesc dd[D];
@@ -1324,19 +1415,22 @@ __global__ void __launch_bounds__(NTH) k_gateup(Args a) {
           S.claim[(st + D) & 3] = is_static(q, st + D) ? static_item(q, st + D) : pool_item(q, cl[(st + D) & 1]);
         gu_epilogue<MX>(a, S, acc, dd[r].ntile, dd[r].u, dd[r].row0, true, wave, lane, tid, (st + D) & 3, &nload);
       }
+      ++n_done;  // every step's item is inside the list (the loop stops before a step past the end)
       if (nx[(r + 1) % D] >= n_gu) { done = true; break; }  // the next step's item is past the end
     }
     if (done) break;
   }
+  return n_done;
 }
 
+// The down work of one workgroup, after its gate/up items: the shared expert's row group when
+// b < n_sh, then its routed items. The routing tables are in LDS (the routing prologue of the same
+// launch); the activation fragments were published inside the launch, and the partial rows are
+// published the same way. Returns the number of items it completed.
 template <int NWIN, bool MX>
-__global__ void __launch_bounds__(NTH) k_down(Args a) {
+__device__ __forceinline__ int down_body(const Args& a, Smem& S, int tid, int lane, int wave) {
   using SH = DnShape<NWIN>;
   constexpr int TPW = MX ? SH::TPW_MX : SH::TPW_BF;
-  __shared__ Smem S;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int H = a.H, I = a.I, Is = a.Is;
   const int G = gridDim.x, b = blockIdx.x;
 
@@ -1350,16 +1444,37 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
   const rsrc_t raf = buf_rsrc(a.afrag, MX ? (uint32_t)a.umax * (I / WIN) * MXW : (uint32_t)a.umax * (I / 32) * 2048);
   if (b < n_sh) dn_load_bf16<NWIN>(Ts, buf_rsrc(a.shd, H * Is * 2), (uint32_t)(b * 16 * SH::TPI_BF * Is * 2), Is, wave, lane);
 
-  // the routing tables, up to umax entries regardless of U, in one memory round trip
-  static_assert(MAX_U <= NTH && MAX_U * KMAX / 8 <= NTH, "one table load per thread");
-  const int U = __builtin_amdgcn_readfirstlane(a.tab_n[0]);
-  if (tid < a.umax) S.woken[tid] = a.tab_woken[tid];
-  if (tid < a.umax * KMAX / 8)
-    reinterpret_cast<uint2*>(&S.slot[0][0])[tid] = reinterpret_cast<const uint2*>(a.tab_slot)[tid];
-  __syncthreads();
+  const int U = __builtin_amdgcn_readfirstlane(S.nw);
 
   const int ipe = H / (16 * (MX ? SH::TPI_MX : SH::TPI_BF));
   const int n_dn = U * ipe;
+  constexpr int D = 2;
+  const Sched q = make_sched(n_dn, G, b, n_sh, a.ctr + NGRP * CTR_STRIDE, ipe);
+  const int q0 = static_item(q, 0);
+  const Woken wk = load_woken(S, lane);
+  DNItem<NWIN> T[D];
+  DnB<MX> Bf[D];
+  DNDesc dd[D];
+  int nx[D];
+  // The first routed items' weights are requested before the wait for the activations (they do
+  // not depend on them), so the stream goes on while the last gate/up items finish elsewhere:
+  // one item (bf16, 128 KB), or both buffers' items (mxfp4, 34 KB each); two bf16 items would
+  // not fit the registers next to a shared item.
+  constexpr int NPRE = MX ? D : D - 1;
+  if (q0 < n_dn) {
+#pragma unroll
+    for (int j = 0; j < NPRE; ++j) {
+      nx[j] = static_item(q, j);
+      dd[j] = dn_desc<NWIN, MX>(a, wk, nx[j], n_dn, ipe);  // a valid stand-in past the end
+      dn_load<NWIN, MX>(T[j], rw, rs, dd[j], I, wave, lane);
+    }
+  }
+  {  // every gate/up item of the launch (routed and shared) is complete
+    const uint32_t gu_total = (uint32_t)(U * (I / (16 * (MX ? GU_MX_RT : 1))) + Is / 16);
+    wait_count(a, CT_GU, gu_total, tid);
+  }
+
+  int n_done = 0;
   if (b < n_sh) {
     DBF bs;
     dn_load_b<NWIN>(bs.f, buf_rsrc(a.afrag_sh, (Is / 32) * 2048), 0u, wave, lane);
@@ -1367,27 +1482,15 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
     dn_math<NWIN, false>(acc, Ts, bs);
     dn_store_partial<NWIN>(S, acc, SH::TPW_BF, wave, lane);
     dn_epilogue<NWIN>(a, S, SH::TPI_BF, SH::TPW_BF, U, false, b * 16 * SH::TPI_BF, tid);
+    n_done = 1;
   }
   // Routed items, scheduled and pipelined as in the gate/up kernel (D items deep: at step h item
   // h is multiplied while the weights and activation fragments of items h + 1 .. h + D - 1 are in
   // flight). Two in flight for both formats: with the 34 KB mxfp4 items, three or four in flight
   // were measured slower (k = 16: 22.6 and 22.0 us against 19.9).
-  constexpr int D = 2;
-  const Sched q = make_sched(n_dn, G, b, n_sh, a.ctr + NGRP * CTR_STRIDE, ipe);
-  const int q0 = static_item(q, 0);
-  if (q0 >= n_dn) return;  // every later item is past the end too
-  const Woken wk = load_woken(S, lane);
-  DNItem<NWIN> T[D];
-  DnB<MX> Bf[D];
-  DNDesc dd[D];
-  int nx[D];
+  if (q0 >= n_dn) return n_done;  // every later item is past the end too
 #pragma unroll
-  for (int j = 0; j + 1 < D; ++j) {
-    nx[j] = static_item(q, j);
-    dd[j] = dn_desc<NWIN, MX>(a, wk, nx[j], n_dn, ipe);  // a valid stand-in past the end
-    dn_load<NWIN, MX>(T[j], rw, rs, dd[j], I, wave, lane);
-    dn_load_bb<NWIN, MX>(Bf[j], raf, dd[j].u, I, wave, lane);
-  }
+  for (int j = 0; j < NPRE; ++j) dn_load_bb<NWIN, MX>(Bf[j], raf, dd[j].u, I, wave, lane);
   int nload = static_item(q, D - 1);  // item of the next step whose loads are issued
   // Claims (thread 0): the claim for item X sits in cl[X & 1]. It is issued behind the loads of
   // step X - D - 1 (item X - 2 with two in flight), so it returns right after them, and it is read
@@ -1402,10 +1505,12 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
     for (int r = 0; r < D; ++r) {
       const int st = h + r;
       const int jl = (r + D - 1) % D;  // buffer of item st + D - 1
-      nx[jl] = nload;
-      dd[jl] = dn_desc<NWIN, MX>(a, wk, nload, n_dn, ipe);
-      dn_load<NWIN, MX>(T[jl], rw, rs, dd[jl], I, wave, lane);
-      dn_load_bb<NWIN, MX>(Bf[jl], raf, dd[jl].u, I, wave, lane);
+      if (NPRE < D || st > 0) {  // (with NPRE == D the first step's item is already requested)
+        nx[jl] = nload;
+        dd[jl] = dn_desc<NWIN, MX>(a, wk, nload, n_dn, ipe);
+        dn_load<NWIN, MX>(T[jl], rw, rs, dd[jl], I, wave, lane);
+        dn_load_bb<NWIN, MX>(Bf[jl], raf, dd[jl].u, I, wave, lane);
+      }
       if (tid == 0 && !is_static(q, st + D + 1)) cl[(st + D + 1) & 1] = claim_raw(q.ctr);
       __builtin_amdgcn_sched_barrier(0);
       {
@@ -1416,9 +1521,44 @@ __global__ void __launch_bounds__(NTH) k_down(Args a) {
         dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
         dn_epilogue<NWIN>(a, S, dd[r].ntile, TPW, dd[r].u, true, dd[r].row0, tid, (st + D) & 3, &nload);
       }
+      ++n_done;
       if (nx[(r + 1) % D] >= n_dn) { done = true; break; }  // the next step's item is past the end
     }
     if (done) break;
+  }
+  return n_done;
+}
+
+// One MoE layer's expert work in one launch: the routing prologue and the gate/up items, then the
+// down items, then the combine, each phase starting when the previous one is complete on every
+// workgroup. A phase publishes its results with device-coherent stores; each workgroup, once its
+// stores are complete, adds its item count to the phase's counter (zeroed by the router kernel),
+// and the next phase waits for the counter to reach the phase's item total. So no kernel
+// boundary sits between the phases: a workgroup that finishes its gate/up items early already
+// streams its first down items' weights while the last gate/up items finish elsewhere, and the
+// down phase finds the routing tables in LDS. The waits cannot deadlock: a phase's items never
+// wait on anything, and every workgroup runs its items of a phase before it waits for the next;
+// a wait that runs past its bound reports the call as failed.
+template <int WPW, int NWIN, bool MX>
+__global__ void __launch_bounds__(NTH) k_layer(Args a) {
+  using SH = DnShape<NWIN>;
+  __shared__ Smem S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int H = a.H, Is = a.Is;
+  const int n_gu = gateup_body<WPW, MX>(a, S, tid, lane, wave);
+  publish_count(a, CT_GU, n_gu, tid);
+  const int n_dn = down_body<NWIN, MX>(a, S, tid, lane, wave);
+  publish_count(a, CT_DN, n_dn, tid);
+  // the combine: workgroup b < ceil(k H / 512) takes 128 output float4s, four threads each
+  const int n_out = a.k * (H / 4);
+  if ((int)blockIdx.x * 128 < n_out) {
+    const uint32_t U = (uint32_t)__builtin_amdgcn_readfirstlane(S.nw);
+    const uint32_t dn_total = U * (uint32_t)(H / (16 * (MX ? SH::TPI_MX : SH::TPI_BF))) +
+                              (Is > 0 ? (uint32_t)(H / (16 * SH::TPI_BF)) : 0u);
+    wait_count(a, CT_DN, dn_total, tid);
+    const int o = (int)blockIdx.x * 128 + (tid >> 2);
+    combine_quad(a, o, tid & 3, o < n_out);
   }
 }
 
@@ -1457,20 +1597,17 @@ __global__ void __launch_bounds__(256) k_pack_mx(const uint8_t* src, const uint8
 }
 
 // ------------------------------------------------------------------------------------------
-// accept_prefix: chunked argmax, then one workgroup reduces the rows and scans the prefix
+// accept_prefix: chunked argmax and the prefix scan in one launch
 // ------------------------------------------------------------------------------------------
-// Each workgroup takes AM_CHUNK consecutive logits of one row: every thread issues all of its
-// loads before merging any (one memory round trip), then the workgroup reduces.
-__global__ void __launch_bounds__(256) k_argmax_partial(const float* logits, int V, int nchunks,
-                                                        float* pv, int* pi) {
-  __shared__ float sv[4];
-  __shared__ int si[4];
-  const int row = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x;
+// (max, lowest index) of AM_CHUNK consecutive logits of one row by a 256-thread workgroup: every
+// thread issues all of its loads before merging any (one memory round trip). Thread 0 holds the
+// result.
+__device__ __forceinline__ void chunk_argmax(const float* r, int V, int chunk, int tid, float* sv, int* si,
+                                             float& bv, int& bi) {
   const int base = chunk * AM_CHUNK;
   const int end = min(base + AM_CHUNK, V);
-  const float* r = logits + (size_t)row * V;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
+  bv = -INFINITY;
+  bi = 0x7fffffff;
   if ((V & 3) == 0) {
     constexpr int PER = AM_CHUNK / (4 * 256);  // float4 loads per thread
     f32x4 v[PER];
@@ -1492,18 +1629,134 @@ __global__ void __launch_bounds__(256) k_argmax_partial(const float* logits, int
   } else {
     for (int i = base + tid; i < end; i += 256) argmax_merge(bv, bi, r[i], i);
   }
-  wave_argmax(bv, bi);
+  wave_argmax_dpp(bv, bi);
   if ((tid & 63) == 0) { sv[tid >> 6] = bv; si[tid >> 6] = bi; }
   __syncthreads();
-  if (tid == 0) {
+  if (tid == 0)
     for (int w = 1; w < 4; ++w) argmax_merge(bv, bi, sv[w], si[w]);
-    pv[(size_t)row * nchunks + chunk] = bv;
-    pi[(size_t)row * nchunks + chunk] = bi;
+}
+
+// Tag of a published chunk maximum: a 64-bit mix (the splitmix64 finaliser) of the call's epoch
+// and the payload. A record whose tag matches was written by this call with exactly this payload:
+// a record left by an earlier call carries that call's epoch, and a stale, garbage or partly
+// written record fails the check except with probability about 2^-64.
+__device__ __forceinline__ uint64_t acc_tag(uint64_t epoch, float v, int i) {
+  uint64_t z = epoch ^ (((uint64_t)__float_as_uint(v) << 32) | (uint32_t)i);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Workgroup (chunk c, row y) with y = s n_target + t (sequence s, position t) takes AM_CHUNK logits
+// of row y and publishes (max, index, tag) as one 16-byte device-coherent store, and is done. The
+// last workgroup of each sequence (the last chunk of its last row, dispatched after every other
+// workgroup of the sequence) requests all of the sequence's records at once and validates each by
+// its tag, re-requesting the invalid ones until all are valid; so the records carry their own
+// completion, and the workspace needs no initialisation. It then reduces each row (the merge keeps
+// the maximum, ties to the lower index, so the order of the partials does not matter), and wave 0
+// compares the drafts with the targets, one position per lane: the first mismatch (a ballot) is
+// the accepted length. The wait is bounded: past it, accepted = -1 (the call failed). A
+// sequence's draft count is n_draft, or n_draft_seq[s] clamped to [0, n_draft] when given.
+__global__ void __launch_bounds__(256) k_accept(const float* logits, int V, int nchunks, int n_target,
+                                                const int32_t* draft, int n_draft, const int32_t* n_draft_seq,
+                                                int32_t* target_ids, int32_t* accepted, u32x4* rec, uint64_t epoch) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  __shared__ int tgt[64];
+  const int chunk = blockIdx.x, y = blockIdx.y, tid = threadIdx.x;
+  const int sq = y / n_target;
+  const size_t nrec = (size_t)gridDim.y * nchunks;
+  const rsrc_t rr = buf_rsrc(rec, (uint32_t)(nrec * 16));
+  float bv;
+  int bi;
+  chunk_argmax(logits + (size_t)y * V, V, chunk, tid, sv, si, bv, bi);
+  if (tid == 0) {
+    const uint64_t t = acc_tag(epoch, bv, bi);
+    const u32x4 r = {__float_as_uint(bv), (uint32_t)bi, (uint32_t)t, (uint32_t)(t >> 32)};
+    __builtin_amdgcn_raw_buffer_store_b128(r, rr, (uint32_t)(((size_t)y * nchunks + chunk) * 16), 0, BUF_DEV);
+  }
+  if (chunk != nchunks - 1 || y % n_target != n_target - 1) return;
+
+  // The sequence's last workgroup. Its records (row major) are taken in passes of 256 PPT, thread
+  // t owning records t, t + 256, ... of a pass; each staged in LDS once valid, then each wave
+  // merges rows w, w + 4, ... into the rows' running maxima (a row may span passes).
+  const uint32_t r0 = (uint32_t)((size_t)sq * n_target * nchunks * 16);
+  const int nf = n_target * nchunks;
+  constexpr int PPT = 8;
+  __shared__ float stv[256 * PPT];
+  __shared__ int sti[256 * PPT];
+  __shared__ float rowv[64];
+  const int lane = tid & 63, wave = tid >> 6;
+  int nd = n_draft;
+  if (n_draft_seq) nd = min(max(n_draft_seq[sq], 0), n_draft);
+  const int32_t d = (tid < nd) ? draft[(size_t)sq * n_draft + tid] : 0;  // nd <= n_target <= 64
+  if (tid < 64) {
+    rowv[tid] = -INFINITY;
+    tgt[tid] = 0x7fffffff;
+  }
+  bool ok = true;
+  for (int base = 0; base < nf && ok; base += 256 * PPT) {
+    uint32_t seen = 0;  // bit m: record base + tid + 256 m is valid and staged
+    for (uint32_t polls = 0;; ++polls) {
+      u32x4 r[PPT];
+#pragma unroll
+      for (int m = 0; m < PPT; ++m) {
+        const int i = base + tid + 256 * m;
+        r[m] = (i < nf && !((seen >> m) & 1u))
+                   ? __builtin_amdgcn_raw_buffer_load_b128(rr, (uint32_t)i * 16u, r0, BUF_DEV)
+                   : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int m = 0; m < PPT; ++m) {
+        const int i = base + tid + 256 * m;
+        if (i >= nf) {
+          seen |= 1u << m;
+        } else if (!((seen >> m) & 1u)) {
+          const float v = __uint_as_float(r[m].x);
+          const uint64_t t = (uint64_t)r[m].z | ((uint64_t)r[m].w << 32);
+          if (t == acc_tag(epoch, v, (int)r[m].y)) {
+            stv[tid + 256 * m] = v;
+            sti[tid + 256 * m] = (int)r[m].y;
+            seen |= 1u << m;
+          }
+        }
+      }
+      if (__syncthreads_and(seen == (1u << PPT) - 1u)) break;
+      if (polls == WAIT_POLLS) { ok = false; break; }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (!ok) break;
+    const int end = min(nf, base + 256 * PPT);
+    const int r_lo = base / nchunks, r_hi = (end - 1) / nchunks;
+    for (int row = r_lo + wave; row <= r_hi; row += 4) {
+      float v = rowv[row];
+      int vi = tgt[row];
+      const int p_lo = max(base, row * nchunks), p_hi = min(end, (row + 1) * nchunks);
+      for (int i = p_lo + lane; i < p_hi; i += 64) argmax_merge(v, vi, stv[i - base], sti[i - base]);
+      wave_argmax_dpp(v, vi);
+      if (lane == 0) {
+        rowv[row] = v;
+        tgt[row] = vi;
+      }
+    }
+    __syncthreads();  // the stage is reused by the next pass
+  }
+  if (!ok) {
+    if (tid == 0) accepted[sq] = -1;
+    return;
+  }
+  if (wave == 0) {  // the rows' results are in LDS (the last pass ended with a barrier)
+    const int t = tgt[lane];
+    const bool miss = lane < nd && d != t;
+    const unsigned long long m = __ballot(miss);
+    if (lane == 0) accepted[sq] = m ? __builtin_ctzll(m) : nd;
+    if (lane < n_target) target_ids[(size_t)sq * n_target + lane] = t;
   }
 }
 
-// One workgroup of 16 waves per sequence (workgroup s: sequence s, its rows, drafts and results
-// at s times the strides): wave w reduces rows w, w + 16, ... (lane l takes chunks l, l + 64,
+// The output head's final pass. One workgroup of 16 waves per sequence (workgroup s: sequence s,
+// its rows, drafts and results at s times the strides): wave w reduces rows w, w + 16, ... (lane l
+// takes chunks l, l + 64,
 // ...); then wave 0 compares the drafts with the targets, one position per lane, and the first
 // mismatch (a ballot) is the accepted length. The draft ids are requested before the partials.
 // A sequence's draft count is n_draft, or n_draft_seq[s] clamped to [0, n_draft] when given.
@@ -3076,7 +3329,7 @@ __global__ void __launch_bounds__(256) k_bcombine(BArgs a) {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t ctr, tab_n, tab_woken, tab_slot, xfrag, xfrag_sh, plog, psq, afrag, afrag_sh, part, total;
+  size_t ctr, xfrag, xfrag_sh, plog, psq, afrag, afrag_sh, part, total;
   int umax, hs;
 };
 
@@ -3088,10 +3341,7 @@ Layout make_layout(const moe_layer* L, int k) {
   o.umax = (int)((E < (size_t)KMAX * K) ? E : (size_t)KMAX * K);
   o.hs = router_splits(L->hidden);
   size_t off = 0;
-  o.ctr = off;       off = align256(off + (size_t)2 * NGRP * CTR_STRIDE * 4);
-  o.tab_n = off;     off = align256(off + 16);
-  o.tab_woken = off; off = align256(off + (size_t)o.umax * 4);
-  o.tab_slot = off;  off = align256(off + (size_t)o.umax * KMAX);
+  o.ctr = off;       off = align256(off + (size_t)N_CTR * CTR_STRIDE * 4);
   o.xfrag = off;    off = align256(off + H * 64);
   o.xfrag_sh = off; off = align256(off + H * 64);
   o.plog = off;     off = align256(off + (size_t)o.hs * KMAX * E * 4);
@@ -3169,6 +3419,22 @@ int check_layer(const moe_layer* L) {
 // MOE_ERR_HIP and leaves the error pending for the caller to read.
 bool error_pending() { return hipPeekAtLastError() != hipSuccess; }
 
+// A 64-bit value unique to each call in this process (a Weyl sequence from a random start), never
+// zero: the tag of that call's completion flags, so flags left in a workspace by earlier calls, or
+// any other stale contents, are not taken for this call's.
+uint64_t next_epoch() {
+  static const uint64_t base = [] {
+    std::random_device rd;
+    return ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+  }();
+  static std::atomic<uint64_t> n{0};
+  uint64_t e;
+  do {
+    e = base + 0x9E3779B97F4A7C15ull * (n.fetch_add(1, std::memory_order_relaxed) + 1);
+  } while (e == 0);
+  return e;
+}
+
 int num_cus() {
   static int cached[64] = {0};
   int dev = 0;
@@ -3186,19 +3452,20 @@ bool mark(void* const* events, int i, hipStream_t s) {
   return !events || !events[i] || hipEventRecord((hipEvent_t)events[i], s) == hipSuccess;
 }
 
+// Workgroups of the expert kernels: one per CU; never fewer than shared-expert items (one each),
+// nor than combine slices of the one-launch kernel (128 output float4s each).
+int layer_grid(const Args& a) {
+  return std::max(std::max(num_cus(), (a.k * a.H / 4 + 127) / 128), std::max(a.Is / 16, a.H / 64));
+}
+
 template <int WPW, int NWIN, bool MX>
 bool launch_layer(const Args& a, hipStream_t s, void* const* ev) {
-  // one workgroup per CU; never fewer workgroups than shared-expert items (one each)
-  const int cus = std::max(num_cus(), std::max(a.Is / 16, a.H / 64));
+  const int cus = layer_grid(a);
   if (!mark(ev, 0, s)) return false;
   k_router<MX><<<a.ntile_e * a.hs, NTH, 0, s>>>(a);
   if (!mark(ev, 1, s)) return false;
-  k_gateup<WPW, MX><<<cus, NTH, 0, s>>>(a);
-  if (!mark(ev, 2, s)) return false;
-  k_down<NWIN, MX><<<cus, NTH, 0, s>>>(a);
-  if (!mark(ev, 3, s)) return false;
-  k_combine<<<(a.k * a.H + 255) / 256, 256, 0, s>>>(a);  // four threads per float4 of y
-  return mark(ev, 4, s);
+  k_layer<WPW, NWIN, MX><<<cus, NTH, 0, s>>>(a);
+  return mark(ev, 2, s) && mark(ev, 3, s) && mark(ev, 4, s);
 }
 
 template <int WPW, bool MX>
@@ -3369,8 +3636,7 @@ static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint
   a.wg = (const uint8_t*)L->w_gate; a.wu = (const uint8_t*)L->w_up; a.wd = (const uint8_t*)L->w_down;
   a.sg = L->s_gate; a.su = L->s_up; a.sd = L->s_down;
   a.shg = (const uint8_t*)L->sh_gate; a.shu = (const uint8_t*)L->sh_up; a.shd = (const uint8_t*)L->sh_down;
-  a.tab_n = (int32_t*)(ws + lay.tab_n); a.ctr = (uint32_t*)(ws + lay.ctr); a.tab_woken = (int32_t*)(ws + lay.tab_woken);
-  a.tab_slot = (int8_t*)(ws + lay.tab_slot);
+  a.ctr = (uint32_t*)(ws + lay.ctr);
   a.xfrag = (u32x4*)(ws + lay.xfrag); a.xfrag_sh = (u32x4*)(ws + lay.xfrag_sh); a.plog = (float*)(ws + lay.plog); a.psq = (float*)(ws + lay.psq);
   a.afrag = (u32x4*)(ws + lay.afrag); a.afrag_sh = (u32x4*)(ws + lay.afrag_sh); a.part = (float*)(ws + lay.part);
   a.H = L->hidden; a.E = L->n_experts; a.K = L->top_k; a.I = L->inter; a.Is = L->shared_inter; a.k = k;
@@ -3446,10 +3712,13 @@ int moe_pack_weights(int32_t wdtype, int32_t n_mats, int32_t rows, int32_t cols,
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
+// workspace of the acceptance: one 16-byte record (max, index, tag) per row and chunk
+size_t accept_ws_bytes(size_t rows, size_t nchunks) { return align256(rows * nchunks * 16); }
+
 size_t accept_prefix_workspace_size(int32_t n_target, int32_t vocab) {
   if (n_target < 1 || n_target > 64 || vocab < 1 || vocab > (1 << 24)) return 0;
   const size_t nchunks = ((size_t)vocab + AM_CHUNK - 1) / AM_CHUNK;
-  return align256((size_t)n_target * nchunks * 4) * 2;
+  return accept_ws_bytes((size_t)n_target, nchunks);
 }
 
 size_t accept_prefix_batch_workspace_size(int32_t n_seq, int32_t n_target, int32_t vocab) {
@@ -3457,7 +3726,7 @@ size_t accept_prefix_batch_workspace_size(int32_t n_seq, int32_t n_target, int32
       vocab > (1 << 24))
     return 0;
   const size_t nchunks = ((size_t)vocab + AM_CHUNK - 1) / AM_CHUNK;
-  return align256((size_t)n_seq * n_target * nchunks * 4) * 2;
+  return accept_ws_bytes((size_t)n_seq * n_target, nchunks);
 }
 
 int accept_prefix_batch(const float* logits, int32_t n_seq, int32_t n_target, int32_t vocab,
@@ -3480,13 +3749,11 @@ int accept_prefix_batch(const float* logits, int32_t n_seq, int32_t n_target, in
       overlaps(accepted, abytes, target_ids, tbytes))
     return MOE_ERR_ALIAS;
   const int nchunks = (vocab + AM_CHUNK - 1) / AM_CHUNK;
-  float* pv = (float*)workspace;
-  int* pi = (int*)((uint8_t*)workspace + need / 2);
   hipStream_t s = (hipStream_t)hip_stream;
   if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
-  k_argmax_partial<<<dim3(nchunks, n_seq * n_target), 256, 0, s>>>(logits, vocab, nchunks, pv, pi);
-  k_accept_final<<<n_seq, 1024, 0, s>>>(pv, pi, nchunks, n_target, n_draft_max > 0 ? draft_ids : nullptr,
-                                        n_draft_max, target_ids, accepted, n_draft);
+  k_accept<<<dim3(nchunks, n_seq * n_target), 256, 0, s>>>(logits, vocab, nchunks, n_target,
+                                                           n_draft_max > 0 ? draft_ids : nullptr, n_draft_max, n_draft,
+                                                           target_ids, accepted, (u32x4*)workspace, next_epoch());
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -3507,12 +3774,11 @@ int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const in
       overlaps(accepted, 4, target_ids, (size_t)n_target * 4))
     return MOE_ERR_ALIAS;
   const int nchunks = (vocab + AM_CHUNK - 1) / AM_CHUNK;
-  float* pv = (float*)workspace;
-  int* pi = (int*)((uint8_t*)workspace + need / 2);
   hipStream_t s = (hipStream_t)hip_stream;
   if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
-  k_argmax_partial<<<dim3(nchunks, n_target), 256, 0, s>>>(logits, vocab, nchunks, pv, pi);
-  k_accept_final<<<1, 1024, 0, s>>>(pv, pi, nchunks, n_target, draft_ids, n_draft, target_ids, accepted);
+  k_accept<<<dim3(nchunks, n_target), 256, 0, s>>>(logits, vocab, nchunks, n_target, n_draft > 0 ? draft_ids : nullptr,
+                                                   n_draft, nullptr, target_ids, accepted, (u32x4*)workspace,
+                                                   next_epoch());
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

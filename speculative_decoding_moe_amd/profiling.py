@@ -91,7 +91,7 @@ def traffic(fetch_dir, write_dir, run_json, cmd_fetch, cmd_write, kernel, source
         f, c = fetch[n]
         w = write.get(n, (float("nan"), 0))[0]
         out.append(f"{n[:40]:40s} {c:6d} {f:12.1f} {w:12.1f} {f * fscale / 1e6:10.2f} {w * wscale / 1e6:10.2f}")
-    name = [n for n in fetch if kernel in n]
+    name = [n for n in fetch if n == kernel] or [n for n in fetch if kernel in n]  # an exact name first
     if len(name) != 1:
         raise ValueError(f"kernel substring {kernel!r} matches {name}")
     name = name[0]
@@ -102,9 +102,8 @@ def traffic(fetch_dir, write_dir, run_json, cmd_fetch, cmd_write, kernel, source
             f"traffic_bytes_per_launch: {fb + wb:.0f}"]
     # algorithmic bytes per launch that the profiled program reports for each kernel
     keys = [("k_bexp<true", "bexp_gateup_bytes"), ("k_bexp<false", "bexp_down_bytes"),
-            ("k_gateup<2, true>", "mx_gateup_bytes_mean"), ("k_down<4, true>", "mx_down_bytes_mean"),
-            ("k_gateup<2, false>", "gateup_bytes_mean"), ("k_down<4, false>", "down_bytes_mean"),
-            ("k_head", "head_bytes")]
+            ("k_layer<2, 4, true>", "mx_layer_bytes_mean"), ("k_layer<2, 4, false>", "layer_bytes_mean"),
+            ("k_accept", "accept_bytes"), ("k_head", "head_bytes")]
     alg = next((float(run[key]) for sub, key in keys if sub in name and key in run), None)
     if alg:
         out += [f"algorithmic_bytes_per_launch: {alg:.0f}", f"traffic_over_algorithmic: {(fb + wb) / alg:.4f}"]
