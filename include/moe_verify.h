@@ -154,9 +154,11 @@ size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max);
  *            (k_max = 1024 with bf16 weights: about 104 MB at H 2048, E 256, K 8, I 512);
  *            its contents need no initialisation and are overwritten.
  * The single-block path (k <= 16) runs its expert phases in one launch whose workgroups wait for
- * each other's phases through counters in the workspace. The waits are bounded: if a phase is not
- * complete within seconds (only possible when other work holds the GPU's compute units that
- * long), the call's outputs are invalid and *n_woken is set to -1.
+ * each other's phases through counters in the workspace, one workgroup per compute unit, so every
+ * workgroup must be resident at once: a device with fewer compute units than the launch needs
+ * (max(k H / 512, Is / 16, H / 64), at most 64 here) gets MOE_ERR_SHAPE. The waits are bounded: if
+ * a phase is not complete within seconds (only possible when other work holds the GPU's compute
+ * units that long), the call's outputs are invalid and *n_woken is set to -1.
  * Returns MOE_OK or an MOE_ERR_* code (nothing is enqueued on error). */
 int moe_verify_block(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
                      int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,

@@ -3646,6 +3646,8 @@ static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint
 
   hipStream_t s = (hipStream_t)hip_stream;
   if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
+  // the one-launch layer kernel's phases wait for each other: every workgroup must be resident
+  if (layer_grid(a) > num_cus()) return MOE_ERR_SHAPE;
   const bool mx = L->wdtype == MOE_W_MXFP4;
   bool ok;
   if (L->hidden > 1024) ok = mx ? launch_nwin<2, true>(a, s, events) : launch_nwin<2, false>(a, s, events);

@@ -602,15 +602,19 @@ def test_geometric_acceptance_reproduces_printed_values(row):
 
 
 def test_signed_zero_worked_example():
-    """The part-2 page's 16x16 example: D = A B is -(j+1)/16 exactly with +0 or -0 padding."""
+    """The part-2 page's 16x16 example, D = A B with D[i, j] = -(j+1)/16 whether B's zeros are +0
+    or -0, run through the oracle's own product: the router logits of 16 tokens (B's columns,
+    padded with signed zeros) against 16 experts (A's rows), l[t, e] = D[e, t]. A dropped term, a
+    transposed operand or a sign slip in router_logits moves a printed value or its bits."""
     rows = _read_golden("signed_zero_mma.txt")
+    A = np.zeros((16, 16), dtype=np.float32)
+    A[:, 12] = -1.0
     for neg in (False, True):
-        A = np.zeros((16, 16), dtype=np.float32)
         B = np.full((16, 16), -0.0 if neg else 0.0, dtype=np.float32)
-        A[:, 12] = -1.0
         B[12, :] = (np.arange(16) + 1) / 16.0
-        D = (A.astype(np.float64) @ B.astype(np.float64)).astype(np.float32)
-        assert np.array_equal(D, np.tile(-(np.arange(16) + 1) / 16.0, (16, 1)).astype(np.float32))
+        tokens = B.T.copy()  # token j is column j of B
+        logits = oracle.router_logits(tokens, A).astype(np.float32)
+        D = logits.T
         for i, j, v, bits in rows:
             assert D[int(i), int(j)] == float(v)
             assert struct.unpack("<I", struct.pack("<f", D[int(i), int(j)]))[0] == int(bits, 16)
