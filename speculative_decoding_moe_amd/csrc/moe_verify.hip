@@ -1499,32 +1499,38 @@ __device__ __forceinline__ int down_body(const Args& a, Smem& S, int tid, int la
   static_assert(D == 2, "the claim timing assumes two items in flight");
   uint32_t cl[2] = {0u, 0u};
   if (tid == 0 && !is_static(q, D)) cl[D & 1] = claim_raw(q.ctr);
-  for (int h = 0;; h += D) {
-    bool done = false;
-#pragma unroll
-    for (int r = 0; r < D; ++r) {
-      const int st = h + r;
-      const int jl = (r + D - 1) % D;  // buffer of item st + D - 1
-      if (NPRE < D || st > 0) {  // (with NPRE == D the first step's item is already requested)
-        nx[jl] = nload;
-        dd[jl] = dn_desc<NWIN, MX>(a, wk, nload, n_dn, ipe);
-        dn_load<NWIN, MX>(T[jl], rw, rs, dd[jl], I, wave, lane);
-        dn_load_bb<NWIN, MX>(Bf[jl], raf, dd[jl].u, I, wave, lane);
-      }
-      if (tid == 0 && !is_static(q, st + D + 1)) cl[(st + D + 1) & 1] = claim_raw(q.ctr);
-      __builtin_amdgcn_sched_barrier(0);
-      {
-        f32x4 acc[SH::TPW_MX];
-        dn_math<NWIN, MX>(acc, T[r], Bf[r]);
-        if (tid == 0)  // item st + D, read back by this step's epilogue after its barrier
-          S.claim[(st + D) & 3] = is_static(q, st + D) ? static_item(q, st + D) : pool_item(q, cl[(st + D) & 1]);
-        dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
-        dn_epilogue<NWIN>(a, S, dd[r].ntile, TPW, dd[r].u, true, dd[r].row0, tid, (st + D) & 3, &nload);
-      }
-      ++n_done;
-      if (nx[(r + 1) % D] >= n_dn) { done = true; break; }  // the next step's item is past the end
+  // Step st: request item st + D - 1 (unless already requested), multiply item st, publish it.
+  // Returns whether the next step's item is past the end.
+  auto step = [&](const int st, const int r, const bool load) __attribute__((always_inline)) {
+    const int jl = (r + D - 1) % D;  // buffer of item st + D - 1
+    if (load) {
+      nx[jl] = nload;
+      dd[jl] = dn_desc<NWIN, MX>(a, wk, nload, n_dn, ipe);
+      dn_load<NWIN, MX>(T[jl], rw, rs, dd[jl], I, wave, lane);
+      dn_load_bb<NWIN, MX>(Bf[jl], raf, dd[jl].u, I, wave, lane);
     }
-    if (done) break;
+    if (tid == 0 && !is_static(q, st + D + 1)) cl[(st + D + 1) & 1] = claim_raw(q.ctr);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      f32x4 acc[SH::TPW_MX];
+      dn_math<NWIN, MX>(acc, T[r], Bf[r]);
+      if (tid == 0)  // item st + D, read back by this step's epilogue after its barrier
+        S.claim[(st + D) & 3] = is_static(q, st + D) ? static_item(q, st + D) : pool_item(q, cl[(st + D) & 1]);
+      dn_store_partial<NWIN>(S, acc, TPW, wave, lane);
+      dn_epilogue<NWIN>(a, S, dd[r].ntile, TPW, dd[r].u, true, dd[r].row0, tid, (st + D) & 3, &nload);
+    }
+    ++n_done;
+    return nx[(r + 1) % D] >= n_dn;
+  };
+  // The first round is peeled off: with NPRE == D its first step requests nothing. A step whose
+  // loads depend on the iteration made the compiler wait for every load in flight (the next
+  // item's too) before that step's products, once per round.
+  bool done = false;
+#pragma unroll
+  for (int r = 0; r < D && !done; ++r) done = step(r, r, NPRE < D || r > 0);
+  for (int h = D; !done; h += D) {
+#pragma unroll
+    for (int r = 0; r < D && !done; ++r) done = step(h + r, r, true);
   }
   return n_done;
 }
