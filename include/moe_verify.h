@@ -220,10 +220,12 @@ size_t accept_prefix_workspace_size(int32_t n_target, int32_t vocab);
  *   accepted   int32 [1] out: a = the longest prefix with draft_ids[i] == target_ids[i]; the
  *              committed tokens are draft_ids[0..a) followed by target_ids[a] when a < n_target
  * Limits: 1 <= n_target <= 64, 0 <= n_draft <= n_target, 1 <= vocab <= 2^24.
- * One launch: chunk workgroups publish their maxima as records tagged for this call, and the
- * last workgroup reduces them once all are valid (the workspace needs no initialisation). That
- * wait is bounded: past it (seconds; only when other work holds the GPU that long) *accepted is
- * set to -1 and target_ids are invalid.
+ * One launch: chunk workgroups publish their maxima as records tagged for this execution, and
+ * the last workgroup reduces them once all are valid (the workspace needs no initialisation).
+ * The tags mix a per-call value with a generation word in the workspace that every execution
+ * advances, so the call may be captured in a HIP graph and replayed. That wait is bounded: past
+ * it (seconds; only when other work holds the GPU that long) *accepted is set to -1 and
+ * target_ids are invalid.
  * NaN logits give an unspecified argmax. Returns MOE_OK or an MOE_ERR_* code. */
 int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const int32_t* draft_ids,
                   int32_t n_draft, int32_t* target_ids, int32_t* accepted, void* workspace,
@@ -234,7 +236,7 @@ size_t accept_prefix_batch_workspace_size(int32_t n_seq, int32_t n_target, int32
 
 /* accept_prefix for many sequences verified together (the blocks of one moe_verify_block call
  * over several sequences): sequence s is judged exactly as accept_prefix judges one block, in
- * two launches for all of them. Draft counts may differ per sequence: a cycle need not draft a
+ * one launch for all of them. Draft counts may differ per sequence: a cycle need not draft a
  * full block ("Speculating on a Strix Halo (part 2)", section "llama curiosities").
  *   logits      fp32 [n_seq][n_target][vocab]
  *   draft_ids   int32 [n_seq][n_draft_max] (may be NULL when n_draft_max == 0)

@@ -1663,14 +1663,22 @@ __device__ __forceinline__ uint64_t acc_tag(uint64_t epoch, float v, int i) {
 // compares the drafts with the targets, one position per lane: the first mismatch (a ballot) is
 // the accepted length. The wait is bounded: past it, accepted = -1 (the call failed). A
 // sequence's draft count is n_draft, or n_draft_seq[s] clamped to [0, n_draft] when given.
+// The tags mix the host's per-call epoch with a per-sequence generation word in the workspace,
+// read by every workgroup at its start and advanced by the sequence's last workgroup at its end
+// (after every other workgroup of the sequence has published): a launch replayed from a captured
+// graph keeps its epoch argument, and the generation is what keeps an earlier replay's records
+// from validating.
 __global__ void __launch_bounds__(256) k_accept(const float* logits, int V, int nchunks, int n_target,
                                                 const int32_t* draft, int n_draft, const int32_t* n_draft_seq,
-                                                int32_t* target_ids, int32_t* accepted, u32x4* rec, uint64_t epoch) {
+                                                int32_t* target_ids, int32_t* accepted, u32x4* rec, uint32_t* gen,
+                                                uint64_t host_epoch) {
   __shared__ float sv[4];
   __shared__ int si[4];
   __shared__ int tgt[64];
   const int chunk = blockIdx.x, y = blockIdx.y, tid = threadIdx.x;
   const int sq = y / n_target;
+  const uint32_t g = gen[sq];
+  const uint64_t epoch = host_epoch ^ ((uint64_t)g * 0x9E3779B97F4A7C15ull);
   const size_t nrec = (size_t)gridDim.y * nchunks;
   const rsrc_t rr = buf_rsrc(rec, (uint32_t)(nrec * 16));
   float bv;
@@ -1748,14 +1756,20 @@ __global__ void __launch_bounds__(256) k_accept(const float* logits, int V, int 
     __syncthreads();  // the stage is reused by the next pass
   }
   if (!ok) {
-    if (tid == 0) accepted[sq] = -1;
+    if (tid == 0) {
+      accepted[sq] = -1;
+      gen[sq] = g + 1u;
+    }
     return;
   }
   if (wave == 0) {  // the rows' results are in LDS (the last pass ended with a barrier)
     const int t = tgt[lane];
     const bool miss = lane < nd && d != t;
     const unsigned long long m = __ballot(miss);
-    if (lane == 0) accepted[sq] = m ? __builtin_ctzll(m) : nd;
+    if (lane == 0) {
+      accepted[sq] = m ? __builtin_ctzll(m) : nd;
+      gen[sq] = g + 1u;
+    }
     if (lane < n_target) target_ids[(size_t)sq * n_target + lane] = t;
   }
 }
@@ -3721,12 +3735,16 @@ int moe_pack_weights(int32_t wdtype, int32_t n_mats, int32_t rows, int32_t cols,
 }
 
 // workspace of the acceptance: one 16-byte record (max, index, tag) per row and chunk
-size_t accept_ws_bytes(size_t rows, size_t nchunks) { return align256(rows * nchunks * 16); }
+// records [rows][nchunks] of 16 bytes, then a generation word per sequence
+size_t accept_rec_bytes(size_t rows, size_t nchunks) { return align256(rows * nchunks * 16); }
+size_t accept_ws_bytes(size_t rows, size_t nchunks, size_t nseq) {
+  return accept_rec_bytes(rows, nchunks) + align256(nseq * 4);
+}
 
 size_t accept_prefix_workspace_size(int32_t n_target, int32_t vocab) {
   if (n_target < 1 || n_target > 64 || vocab < 1 || vocab > (1 << 24)) return 0;
   const size_t nchunks = ((size_t)vocab + AM_CHUNK - 1) / AM_CHUNK;
-  return accept_ws_bytes((size_t)n_target, nchunks);
+  return accept_ws_bytes((size_t)n_target, nchunks, 1);
 }
 
 size_t accept_prefix_batch_workspace_size(int32_t n_seq, int32_t n_target, int32_t vocab) {
@@ -3734,7 +3752,7 @@ size_t accept_prefix_batch_workspace_size(int32_t n_seq, int32_t n_target, int32
       vocab > (1 << 24))
     return 0;
   const size_t nchunks = ((size_t)vocab + AM_CHUNK - 1) / AM_CHUNK;
-  return accept_ws_bytes((size_t)n_seq * n_target, nchunks);
+  return accept_ws_bytes((size_t)n_seq * n_target, nchunks, (size_t)n_seq);
 }
 
 int accept_prefix_batch(const float* logits, int32_t n_seq, int32_t n_target, int32_t vocab,
@@ -3759,9 +3777,10 @@ int accept_prefix_batch(const float* logits, int32_t n_seq, int32_t n_target, in
   const int nchunks = (vocab + AM_CHUNK - 1) / AM_CHUNK;
   hipStream_t s = (hipStream_t)hip_stream;
   if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
+  uint32_t* gen = (uint32_t*)((uint8_t*)workspace + accept_rec_bytes((size_t)n_seq * n_target, nchunks));
   k_accept<<<dim3(nchunks, n_seq * n_target), 256, 0, s>>>(logits, vocab, nchunks, n_target,
                                                            n_draft_max > 0 ? draft_ids : nullptr, n_draft_max, n_draft,
-                                                           target_ids, accepted, (u32x4*)workspace, next_epoch());
+                                                           target_ids, accepted, (u32x4*)workspace, gen, next_epoch());
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -3784,8 +3803,9 @@ int accept_prefix(const float* logits, int32_t n_target, int32_t vocab, const in
   const int nchunks = (vocab + AM_CHUNK - 1) / AM_CHUNK;
   hipStream_t s = (hipStream_t)hip_stream;
   if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
+  uint32_t* gen = (uint32_t*)((uint8_t*)workspace + accept_rec_bytes((size_t)n_target, nchunks));
   k_accept<<<dim3(nchunks, n_target), 256, 0, s>>>(logits, vocab, nchunks, n_target, n_draft > 0 ? draft_ids : nullptr,
-                                                   n_draft, nullptr, target_ids, accepted, (u32x4*)workspace,
+                                                   n_draft, nullptr, target_ids, accepted, (u32x4*)workspace, gen,
                                                    next_epoch());
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
