@@ -151,7 +151,7 @@ size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max);
  *   n_woken  int32 [1]    or NULL: size of the union of the block's routed experts (shared
  *            expert not counted)
  *   workspace, ws_bytes: device scratch of at least moe_verify_workspace_size(layer, k) bytes
- *            (k_max = 1024 with bf16 weights: about 104 MB at H 2048, E 256, K 8, I 512);
+ *            (k_max = 1024 with bf16 weights: about 106 MB at H 2048, E 256, K 8, I 512);
  *            its contents need no initialisation and are overwritten.
  * The single-block path (k <= 16) runs its expert phases in one launch whose workgroups wait for
  * each other's phases through counters in the workspace, one workgroup per compute unit, so every

@@ -2443,9 +2443,11 @@ __global__ void __launch_bounds__(1024) k_accept_hist(const int32_t* acc, int n_
 // experts' B operands become per-expert token gathers (tokens sorted by expert, "Speculating on
 // a Strix Halo", section "The verify's own cost"):
 //
-//   k_brouter   (16-token tile, 16-expert tile) items, fp32 MFMA over the full H: raw logits,
-//               the RMSNorm factor, and each token's bf16 hi/lo B fragments (token-major).
-//   k_btopk     one wave per token: top-K (ties to the lower expert), softmax over the K.
+//   k_brouter   (64-token, 64-expert, column slice) workgroups, fp32 MFMA over LDS-staged rows:
+//               partial logits and sums of squares per slice, and each token's bf16 hi/lo B
+//               fragments (token-major).
+//   k_btopk     one wave per token: the slice partials added in slice order, the RMSNorm factor,
+//               top-K (ties to the lower expert), softmax over the K.
 //   k_bperm     eight workgroups, each: per-expert token bitmasks (LDS), counts, a scan over
 //               experts for the list offsets and item counts, then the list position of each
 //               (token, slot) pair of one eighth of the experts = expert offset + number of the
@@ -2485,7 +2487,8 @@ struct BArgs {
   const uint8_t* sg;  // mxfp4 scales of the routed experts (NULL for bf16 layers)
   const uint8_t* su;
   const uint8_t* sd;
-  float* logits;    // [T][E] raw router logits (un-normalised input)
+  float* logits;    // [H / gr_slice(H)][T][E] partial raw router logits of each column slice
+  float* psq;       // [H / gr_slice(H)][T] partial sums of squares of each column slice
   float* rinv;      // [T] RMSNorm factor (1 without pre-norm)
   uint8_t* xg;      // [T][H/128][512 B] bf16 hi/lo B fragments of each token, k-step j, half hl,
                     // lane quad q at ((j * 2 + hl) * 4 + q) * 16
@@ -2523,134 +2526,131 @@ __device__ __forceinline__ void mx8_store16_tok(uint8_t* tw, int blk, int h, con
     *reinterpret_cast<uint32_t*>(tw + 256 + 4 * blk) = (uint32_t)(eh + 127) | ((uint32_t)(el + 127) << 8);
 }
 
-// The many-token router is an fp32 [T x H] x [H x E] product on fp32 MFMA (16 x 16 x 4). One
-// workgroup takes 16 tokens x ET 16-expert tiles; its BR_NW waves split H (wave w takes the
-// 16-column steps w n / BR_NW .. (w + 1) n / BR_NW - 1 of the n = H / 16), so a token's logits
-// are summed in the same order whatever the call. Lane (row r = lane % 16, quad q = lane / 16)
-// holds, for each step h, columns h + 4 q .. h + 4 q + 3 of token row r and of expert row r of
-// every tile (the same k order for both operands): one token load feeds ET MFMAs. With one tile
-// per wave each MFMA needs two fresh operands from the cache and the loads, not the MFMAs, set the
-// pace; four tiles cut the bytes per MFMA to 5/8 of that, but a workgroup then holds four times
-// the MFMA work, so the launch takes the widest ET (4, 2, 1) that still gives every CU a
-// workgroup. A group's loads are all issued before its first MFMA (one round trip per group).
+// The many-token router is an fp32 [T x H] x [H x E] product on fp32 MFMA (16 x 16 x 4), split
+// over the columns: workgroup (64-token group, 64-expert group, column slice of gr_slice(H)) stages
+// its slice of the token rows and router rows in LDS, each row in contiguous 256-byte pieces (64
+// columns per chunk, every load of the slice issued at once), and each of its 16 waves takes one
+// 16 x 16 (expert, token) tile over the slice, lane (row r = lane % 16, quad q = lane / 16) reading
+// columns 16 g + 4 q .. 16 g + 4 q + 3 of expert row r and of token row r (the same k order for both
+// operands). Reading each operand piece from the cache once per workgroup, instead of once per
+// wave and tile, is what lets the matrix cores set the pace. The partial logits [slice][T][E] and
+// partial sums of squares [slice][T] are added by k_btopk in slice order, and the slice width
+// depends only on H, so a token's logits are summed in the same order whatever the call. The same
+// LDS rows give the tokens' bf16 hi/lo B fragments and (mxfp4 layers) MX-fp8 windows.
 constexpr int BR_NW = 16, BR_NTH = 64 * BR_NW;
+constexpr int GR_T = 64, GR_E = 64, GR_KC = 64, GR_LD = GR_KC + 4;  // LDS rows padded by 16 bytes
+__host__ __device__ constexpr int gr_slice(int H) { return H % 256 == 0 ? 256 : 128; }
+constexpr int GR_MS = 8;  // slices at most: H <= 2048 in 256-column slices, or H <= 896 in 128-column ones
 
-template <int NG, int ET>
-__device__ __forceinline__ void brouter_steps(const float* const (&wrow)[ET], const bool (&wz)[ET],
-                                              const float* xrow, bool xz, int h, f32x4 (&acc)[ET],
-                                              float& ss) {
-  f32x4 xv[NG], wv[NG][ET];
-#pragma unroll
-  for (int u = 0; u < NG; ++u) {
-    xv[u] = *reinterpret_cast<const f32x4*>(xrow + h + 16 * u);
-#pragma unroll
-    for (int i = 0; i < ET; ++i) wv[u][i] = *reinterpret_cast<const f32x4*>(wrow[i] + h + 16 * u);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // keep the scheduler from moving loads down to their uses
-#pragma unroll
-  for (int u = 0; u < NG; ++u) {
-    if (xz) xv[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    ss += xv[u][0] * xv[u][0] + xv[u][1] * xv[u][1] + xv[u][2] * xv[u][2] + xv[u][3] * xv[u][3];
-#pragma unroll
-    for (int i = 0; i < ET; ++i) {
-      if (wz[i]) wv[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(wv[u][i][j], xv[u][j], acc[i], 0, 0, 0);
-    }
-  }
-}
-
-template <int ET>
-struct BRouterSmem {
-  float red[BR_NW][ET * 256];
-  float rsq[BR_NW][64];
+template <int NCH>
+struct alignas(16) BRouterSmem {
+  float x[NCH][GR_T][GR_LD];
+  float w[NCH][GR_E][GR_LD];
 };
 
-template <int ET>
+template <int NCH>
 __global__ void __launch_bounds__(BR_NTH) k_brouter(BArgs a) {
-  __shared__ BRouterSmem<ET> S;
+  __shared__ BRouterSmem<NCH> S;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H, E = a.E, T = a.T;
-  const int nte = (E + 16 * ET - 1) / (16 * ET);
-  const int tt = blockIdx.x / nte, et = blockIdx.x % nte;
-  const int row = lane & 15, q = lane >> 4;
-  const int t = tt * 16 + row;
-  const float* xrow = a.x + (size_t)(t < T ? t : 0) * H + 4 * q;
-  const float* wrow[ET];
-  bool wz[ET];
+  constexpr int SW = NCH * GR_KC;
+  const int ns = H / SW, neg = (E + GR_E - 1) / GR_E;
+  const int b = blockIdx.x;
+  const int sl = b % ns, eg = (b / ns) % neg, tg = b / (ns * neg);
+  const int t0 = tg * GR_T, e0 = eg * GR_E, c0 = sl * SW;
+  // thread: row tid / 16 of the chunk's token rows and router rows, 16-byte piece tid % 16;
+  // rows past T or E read the last row (their results are never stored)
+  const int lr = tid >> 4, lc = (tid & 15) * 4;
+  const float* xr = a.x + (size_t)min(t0 + lr, T - 1) * H + c0 + lc;
+  const float* wr = a.wr + (size_t)min(e0 + lr, E - 1) * H + c0 + lc;
+  f32x4 vx[NCH], vw[NCH];
 #pragma unroll
-  for (int i = 0; i < ET; ++i) {
-    const int e = et * 16 * ET + 16 * i + row;
-    wz[i] = e >= E;
-    wrow[i] = a.wr + (size_t)(e < E ? e : 0) * H + 4 * q;
+  for (int c = 0; c < NCH; ++c) {
+    vx[c] = *reinterpret_cast<const f32x4*>(xr + c * GR_KC);
+    vw[c] = *reinterpret_cast<const f32x4*>(wr + c * GR_KC);
   }
-  f32x4 acc[ET];
-#pragma unroll
-  for (int i = 0; i < ET; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int tt = wave & 3, et = wave >> 2, r = lane & 15, q = lane >> 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
-  const int n = H / 16, s0 = wave * n / BR_NW, s1 = (wave + 1) * n / BR_NW;
-  int m = s0;
-  for (; m + 4 <= s1; m += 4) brouter_steps<4, ET>(wrow, wz, xrow, t >= T, 16 * m, acc, ss);
-  for (; m < s1; ++m) brouter_steps<1, ET>(wrow, wz, xrow, t >= T, 16 * m, acc, ss);
 #pragma unroll
-  for (int i = 0; i < ET; ++i) *reinterpret_cast<f32x4*>(&S.red[wave][i * 256 + lane * 4]) = acc[i];
-  S.rsq[wave][lane] = ss;
-  __syncthreads();
-  if (tid < ET * 256) {  // one output per thread: tile i, D[ei][j] in lane j + 16 (ei / 4), element ei % 4
-    float d = 0.f;
+  for (int c = 0; c < NCH; ++c) {
+    *reinterpret_cast<f32x4*>(&S.x[c][lr][lc]) = vx[c];
+    *reinterpret_cast<f32x4*>(&S.w[c][lr][lc]) = vw[c];
+    __syncthreads();  // chunk c is complete; later chunks use other rows of LDS
+    f32x4 av[GR_KC / 16], bv[GR_KC / 16];  // the chunk's operands, read before its first MFMA
 #pragma unroll
-    for (int w = 0; w < BR_NW; ++w) d += S.red[w][tid];
-    const int i = tid >> 8, l = (tid >> 2) & 63, v = tid & 3;
-    const int tok = tt * 16 + (l & 15), ei = et * 16 * ET + 16 * i + 4 * (l >> 4) + v;
-    if (tok < T && ei < E) a.logits[(size_t)tok * E + ei] = d;
+    for (int g = 0; g < GR_KC / 16; ++g) {
+      av[g] = *reinterpret_cast<const f32x4*>(&S.w[c][et * 16 + r][16 * g + 4 * q]);
+      bv[g] = *reinterpret_cast<const f32x4*>(&S.x[c][tt * 16 + r][16 * g + 4 * q]);
+    }
+#pragma unroll
+    for (int g = 0; g < GR_KC / 16; ++g) {
+      ss += bv[g][0] * bv[g][0] + bv[g][1] * bv[g][1] + bv[g][2] * bv[g][2] + bv[g][3] * bv[g][3];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[g][j], bv[g][j], acc, 0, 0, 0);
+    }
   }
-  if (et == 0 && tid < 16) {
-    float s = 0.f;
-    for (int w = 0; w < BR_NW; ++w)
-      for (int qq = 0; qq < 4; ++qq) s += S.rsq[w][tid + 16 * qq];
-    const int tok = tt * 16 + tid;
-    if (tok < T) a.rinv[tok] = a.pre_norm ? 1.0f / sqrtf(s / (float)H + a.eps) : 1.0f;
+  {  // D[i][j] in lane j + 16 (i / 4), element i % 4: expert e0 + 16 et + i, token t0 + 16 tt + j
+    const int t = t0 + tt * 16 + r, e = e0 + et * 16 + 4 * q;
+    float* pl = a.logits + ((size_t)sl * T + (t < T ? t : 0)) * E + e;
+    if (E % 4 == 0) {
+      if (t < T && e < E) *reinterpret_cast<f32x4*>(pl) = acc;
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (t < T && e + v < E) pl[v] = acc[v];
+    }
   }
-  // B fragments of the tile's tokens, windows et, et + nte, ... (256 threads per window)
-  const int nwt = H / WIN;
-  for (int w = et + nte * (tid >> 8); w < nwt; w += (BR_NTH / 256) * nte) {
-    const int r = tid & 255, c = r & 15, j = (r >> 4) & 3, qq = r >> 6;
-    const int tok = tt * 16 + c;
+  if (eg == 0 && et == 0) {  // the slice's sum of squares of token 16 tt + r: its four quads' sums
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const int t = t0 + tt * 16 + r;
+    if (q == 0 && t < T) a.psq[(size_t)sl * T + t] = ss;
+  }
+  // B fragments of the group's tokens in the slice: units (window wi, token tile tt) = u, wi = u / 4,
+  // dealt over the token group's expert-group workgroups (unit u to eg = u mod neg), 256 threads
+  // per unit (token, k-step and lane quad of tid % 256)
+  const int nwt = H / WIN, nws = SW / WIN;
+  for (int u = eg + neg * (tid >> 8); u < 4 * nws; u += neg * (BR_NTH / 256)) {
+    const int wi = u >> 2, rr = tid & 255, tc = (u & 3) * 16 + (rr & 15), j = (rr >> 4) & 3, qq = rr >> 6;
+    const int tok = t0 + tc;
+    const int col = wi * WIN + kofs(j, qq);  // within the slice: chunk col / 64, 8 values
+    const float* src = &S.x[col / GR_KC][tc][col % GR_KC];
+    const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+    const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+    const float f[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    uint32_t hi[8], lo[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split_bf16(f[i], hi[i], lo[i]);
+    u32x4 hv, lv;
+    pack8(hi, hv);
+    pack8(lo, lv);
     if (tok < T) {
-      const float* src = a.x + (size_t)tok * H + w * WIN + kofs(j, qq);
-      const float4 v0 = *reinterpret_cast<const float4*>(src);
-      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-      const float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      uint32_t hi[8], lo[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) split_bf16(f[i], hi[i], lo[i]);
-      u32x4 hv, lv;
-      pack8(hi, hv);
-      pack8(lo, lv);
-      uint8_t* dst = a.xg + ((size_t)tok * nwt + w) * 512;
+      uint8_t* dst = a.xg + ((size_t)tok * nwt + sl * nws + wi) * 512;
       *reinterpret_cast<u32x4*>(dst + ((j * 2 + 0) * 4 + qq) * 16) = hv;
       *reinterpret_cast<u32x4*>(dst + ((j * 2 + 1) * 4 + qq) * 16) = lv;
     }
   }
-  // mxfp4 layers: the MX-fp8 windows of the routed experts' B operands, one wave per window,
-  // lane (column c, 32-block blk)
+  // mxfp4 layers: the MX-fp8 windows of the routed experts' B operands, one wave per unit (window
+  // wi, token tile tt) = u as above, lane (column c, 32-block blk)
   if (a.xgm) {
-    const int c = lane & 15, blk = lane >> 4, tok = tt * 16 + c;
-    for (int w = et + nte * wave; w < nwt; w += nte * BR_NW) {
+    const int c = lane & 15, blk = lane >> 4;
+    for (int u = eg + neg * wave; u < 4 * nws; u += neg * BR_NW) {
+      const int wi = u >> 2, tc = (u & 3) * 16 + c, tok = t0 + tc;
+      const int col = wi * WIN + 32 * blk;
+      const float* src = &S.x[col / GR_KC][tc][col % GR_KC];
       float v[32];
-      const float* src = a.x + (size_t)(tok < T ? tok : 0) * H + w * WIN + 32 * blk;
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
-        const float4 f = *reinterpret_cast<const float4*>(src + 4 * g);
-        v[4 * g + 0] = f.x; v[4 * g + 1] = f.y; v[4 * g + 2] = f.z; v[4 * g + 3] = f.w;
+        const f32x4 f = *reinterpret_cast<const f32x4*>(src + 4 * g);
+        v[4 * g + 0] = f[0]; v[4 * g + 1] = f[1]; v[4 * g + 2] = f[2]; v[4 * g + 3] = f[3];
       }
       uint32_t hi[8], lo[8];
       int eh, el;
       mx8_quant<32, false>(v, hi, lo, eh, el);
       if (tok < T) {
-        uint8_t* tw = a.xgm + ((size_t)tok * nwt + w) * MXT;
+        uint8_t* tw = a.xgm + ((size_t)tok * nwt + sl * nws + wi) * MXT;
         const uint32_t h0[4] = {hi[0], hi[1], hi[2], hi[3]}, h1[4] = {hi[4], hi[5], hi[6], hi[7]};
         const uint32_t l0[4] = {lo[0], lo[1], lo[2], lo[3]}, l1[4] = {lo[4], lo[5], lo[6], lo[7]};
         mx8_store16_tok(tw, blk, 0, h0, l0, eh, el);
@@ -2660,19 +2660,46 @@ __global__ void __launch_bounds__(BR_NTH) k_brouter(BArgs a) {
   }
 }
 
-// one wave per token: top-K over the scaled logits, softmax over the K
+// A lane's NS logits (experts e0 ..) as the sum of the router's ns slice partials, slice 0 first;
+// every slice's loads are issued before the first add
+template <int NS>
+__device__ __forceinline__ void slice_logits(const float* row, size_t stride, int ns, int e0, int E, float (&v)[NS]) {
+  float p[GR_MS][NS];
+#pragma unroll
+  for (int sl = 0; sl < GR_MS; ++sl) lane_logits<NS>(row + (sl < ns ? sl : ns - 1) * stride, e0, E, p[sl]);
+#pragma unroll
+  for (int m = 0; m < NS; ++m) v[m] = p[0][m];
+#pragma unroll
+  for (int sl = 1; sl < GR_MS; ++sl)
+    if (sl < ns)
+#pragma unroll
+      for (int m = 0; m < NS; ++m) v[m] += p[sl][m];
+}
+
+// one wave per token: its logits and sum of squares from the router's slice partials (slice
+// order), the RMSNorm factor, top-K over the scaled logits, softmax over the K
 __global__ void __launch_bounds__(NTH) k_btopk(BArgs a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * NW + (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (t >= a.T) return;
-  const int E = a.E, K = a.K;
-  const float rv = a.rinv[t];
+  const int E = a.E, K = a.K, T = a.T;
+  const int ns = a.H / gr_slice(a.H);  // the router's column slices, added in slice order
+  float pq[GR_MS];
+#pragma unroll
+  for (int sl = 0; sl < GR_MS; ++sl) pq[sl] = a.psq[(size_t)(sl < ns ? sl : ns - 1) * T + t];
+  float sq = pq[0];
+#pragma unroll
+  for (int sl = 1; sl < GR_MS; ++sl)
+    if (sl < ns) sq += pq[sl];
+  const float rv = a.pre_norm ? 1.0f / sqrtf(sq / (float)a.H + a.eps) : 1.0f;
+  if (lane == 0) a.rinv[t] = rv;
   const float* lg = a.logits + (size_t)t * E;
+  const size_t lst = (size_t)T * E;  // between the slices' partial rows
   int my_e = 0;
   uint32_t my_key = 0;
   if (E <= 256) {  // experts 4 lane + m
     float v[4];
-    lane_logits<4>(lg, 4 * lane, E, v);
+    slice_logits<4>(lg, lst, ns, 4 * lane, E, v);
     uint64_t c[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -2683,7 +2710,7 @@ __global__ void __launch_bounds__(NTH) k_btopk(BArgs a) {
     topk_sorted<4, false>(c, K, lane, my_e, my_key);
   } else {  // experts 8 lane + m
     float v[8];
-    lane_logits<8>(lg, 8 * lane, E, v);
+    slice_logits<8>(lg, lst, ns, 8 * lane, E, v);
     uint64_t c[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -3375,7 +3402,7 @@ Layout make_layout(const moe_layer* L, int k) {
 
 // workspace of the gathered path for T tokens
 struct BLayout {
-  size_t tab, ut, logits, rinv, xg, ids, wts, blist, bw, brv, bpos, af, part, xgm, afm, total;
+  size_t tab, ut, logits, psq, rinv, xg, ids, wts, blist, bw, brv, bpos, af, part, xgm, afm, total;
 };
 
 BLayout make_blayout(const moe_layer* L, int T) {
@@ -3385,7 +3412,9 @@ BLayout make_blayout(const moe_layer* L, int T) {
   size_t off = 0;
   o.tab = off;    off = align256(off + 16);
   o.ut = off;     off = align256(off + 5 * (E + 2) * 4);
-  o.logits = off; off = align256(off + (size_t)T * E * 4);
+  const size_t ns = H / gr_slice((int)H);  // router column slices
+  o.logits = off; off = align256(off + ns * T * E * 4);
+  o.psq = off;    off = align256(off + ns * T * 4);
   o.rinv = off;   off = align256(off + (size_t)T * 4);
   o.xg = off;     off = align256(off + (size_t)T * H * 4);
   o.ids = off;    off = align256(off + (size_t)T * K * 4);
@@ -3580,7 +3609,8 @@ static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t f
   a.wr = L->router_w;
   a.wg = (const uint8_t*)L->w_gate; a.wu = (const uint8_t*)L->w_up; a.wd = (const uint8_t*)L->w_down;
   a.shg = (const uint8_t*)L->sh_gate; a.shu = (const uint8_t*)L->sh_up; a.shd = (const uint8_t*)L->sh_down;
-  a.logits = (float*)(ws + lay.logits); a.rinv = (float*)(ws + lay.rinv); a.xg = ws + lay.xg;
+  a.logits = (float*)(ws + lay.logits); a.psq = (float*)(ws + lay.psq); a.rinv = (float*)(ws + lay.rinv);
+  a.xg = ws + lay.xg;
   a.ids = (int32_t*)(ws + lay.ids); a.wts = (float*)(ws + lay.wts); a.tab = (int32_t*)(ws + lay.tab);
   a.ut = (int32_t*)(ws + lay.ut); a.blist = (int32_t*)(ws + lay.blist); a.bw = (float*)(ws + lay.bw);
   a.brv = (float*)(ws + lay.brv); a.bpos = (int32_t*)(ws + lay.bpos); a.af = ws + lay.af;
@@ -3595,13 +3625,11 @@ static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t f
   hipStream_t s = (hipStream_t)hip_stream;
   if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   const int cus = num_cus();
-  const int ntt = (T + 15) / 16;
-  auto nte = [&](int et) { return (a.E + 16 * et - 1) / (16 * et); };
+  const int n_rt = ((T + GR_T - 1) / GR_T) * ((a.E + GR_E - 1) / GR_E) * (a.H / gr_slice(a.H));
   bool ok = mark(events, 0, s);
   if (ok) {
-    if (ntt * nte(4) >= cus) k_brouter<4><<<ntt * nte(4), BR_NTH, 0, s>>>(a);
-    else if (ntt * nte(2) >= cus) k_brouter<2><<<ntt * nte(2), BR_NTH, 0, s>>>(a);
-    else k_brouter<1><<<ntt * nte(1), BR_NTH, 0, s>>>(a);
+    if (gr_slice(a.H) == 256) k_brouter<4><<<n_rt, BR_NTH, 0, s>>>(a);
+    else                      k_brouter<2><<<n_rt, BR_NTH, 0, s>>>(a);
     k_btopk<<<(T + NW - 1) / NW, NTH, 0, s>>>(a);
     k_bperm<<<BPERM_G, BPERM_NTH, 0, s>>>(a);
     ok = mark(events, 1, s);
