@@ -2950,15 +2950,23 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
 // XCD take consecutive items, which share their gathered columns and repeated weights in that
 // XCD's L2) rotated by rot, so a phase that follows another starts its deal after the
 // workgroups the first one loaded.
+// With rfull >= 0, only rounds 0 .. rfull - 1 go to every workgroup; the items after them are dealt
+// over the workgroups at positions 0 .. nfree - 1 only (item rfull G + (m - rfull) nfree + position).
 template <bool GU, bool MX>
 __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_items, int rot, int tid,
-                         int lane, int wave) {
+                         int lane, int wave, int rfull = -1, int nfree = 0) {
   using GE = BGeo<GU, MX>;
   const int G = gridDim.x, b = blockIdx.x;
   const int slotb = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
   const int pos = (slotb - rot % G + G) % G;
-  const int n_my = pos < n_items ? (n_items - pos + G - 1) / G : 0;
+  const bool split = rfull >= 0 && nfree > 0 && rfull * G <= n_items;
+  const int rest = split ? n_items - rfull * G : 0;
+  const int n_my = !split ? (pos < n_items ? (n_items - pos + G - 1) / G : 0)
+                          : rfull + ((pos < nfree && pos < rest) ? (rest - pos + nfree - 1) / nfree : 0);
   if (n_my == 0) return;  // uniform over the workgroup
+  auto gidx = [&](int m) {
+    return (!split || m < rfull) ? m * G + pos : rfull * G + (m - rfull) * nfree + pos;
+  };
 
   const int H = a.H, I = a.I;
   const int nwt = H / WIN;                     // windows of a token row (gate/up B source)
@@ -2992,7 +3000,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
 
   auto item_of = [&](int m) {
     const int mm = m < n_my ? m : n_my - 1;  // past the end: the last item again (valid loads)
-    return b_item<GU, MX>(a, S, U, base + mm * G + pos, wave);
+    return b_item<GU, MX>(a, S, U, base + gidx(mm), wave);
   };
   // window of B window-slot (K half h, tick window v) at tick step, and whether it exists
   auto win_of = [&](int h, int v, int step, bool& ok) {
@@ -3322,6 +3330,29 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   }
 }
 
+// The routed phase's deal in mxfp4 layers. With n1 < G shared items (bf16, one each on n1
+// workgroups, which the routed deal's rotation puts last), a plain deal of the n2 routed items
+// leaves those workgroups a whole shared item behind: at 512 tokens 128 of 256 workgroups took
+// one shared item and four routed items and ended 22 us (gate/up) and 13 us (down) after the rest.
+// So the routed rounds r0, r0 + 1, ... go only to the G - n1 workgroups without a shared item, r0
+// chosen to minimise the larger of the two loads, a shared item counted as SC / 2 routed items
+// (gate/up 3 / 2, down 5 / 2: the per-item times measured at 512 tokens). Returns (r0, G - n1), or
+// (-1, 0) for the plain deal. The deal stays a bijection onto the items whatever the counts.
+__device__ __forceinline__ int2 mx_tail_deal(int n2, int n1, int G, bool gu) {
+  if (n1 <= 0 || n1 >= G || n2 < G) return int2{-1, 0};
+  const int SC = gu ? 3 : 5, nf = G - n1;
+  // loads in half routed items: shared workgroups SC + 2 r0; the others 2 (r0 + ceil((n2 - r0 G) / nf))
+  auto load = [&](int x) {
+    const int rest = n2 - x * G;
+    return max(SC + 2 * x, 2 * (x + (rest + nf - 1) / nf));
+  };
+  const int plain = max(SC + 2 * ((n2 - nf + G - 1) / G), 2 * ((n2 + G - 1) / G));
+  int best = 0, bl = load(0);
+  for (int x = 1; x * G <= n2; ++x)  // the most full rounds among the lightest deals
+    if (load(x) <= bl) { bl = load(x); best = x; }
+  return bl < plain ? int2{best, nf} : int2{-1, 0};
+}
+
 // Gathered gate/up (GU) or down items. bf16 layers: one phase over every item. mxfp4 layers: the
 // shared expert's items (bf16) first, then the routed experts' (mxfp4), in one launch.
 template <bool GU, bool MXL>
@@ -3342,9 +3373,11 @@ __global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
   if constexpr (!MXL) {
     bexp_run<GU, false>(a, S, U, 0, total, 0, tid, lane, wave);
   } else {
-    bexp_run<GU, false>(a, S, U, routed, total - routed, 0, tid, lane, wave);
+    const int n1 = total - routed;
+    bexp_run<GU, false>(a, S, U, routed, n1, 0, tid, lane, wave);
     __syncthreads();  // the next phase reuses the LDS ring
-    bexp_run<GU, true>(a, S, U, 0, routed, total - routed, tid, lane, wave);
+    const int2 d = mx_tail_deal(routed, n1, gridDim.x, GU);
+    bexp_run<GU, true>(a, S, U, 0, routed, n1, tid, lane, wave, d.x, d.y);
   }
 }
 
