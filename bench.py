@@ -416,13 +416,25 @@ def main():
                                          mbuf[r % 2], None, None, mnw[r], mws)
             torch.cuda.synchronize()
             mU = mnw[:, 0].cpu().numpy().astype(np.int64)
-            del mlayers, mws, mbuf
+            del mws, mbuf
+            # the gathered path on that mxfp4 layer: 4 calls of 512 tokens
+            mbws = torch.empty(mlayers[0].workspace_size(bt), dtype=torch.uint8, device=dev)
+            mby = torch.empty((bt, s.hidden), dtype=torch.float32, device=dev)
+            mbnw = torch.zeros((4, 4), dtype=torch.int32, device=dev)
+            for r in range(4):
+                binding.moe_verify_block(mlayers[r % 4], bx, binding.MOE_PRE_RMSNORM | binding.MOE_RESIDUAL, mby,
+                                         None, None, mbnw[r], mbws)
+            torch.cuda.synchronize()
+            mbU = mbnw[:, 0].cpu().numpy().astype(np.int64)
+            del mlayers, mbws, mby
             layer_b = {"layer_bytes_mean": float(np.mean([expert_bytes(s, u) for u in Uall])),
                        "step_bytes_mean": float(np.mean([layer_bytes(s, u, k) for u in Uall])),
                        "head_bytes": (V + 15) // 16 * 16 * s.hidden * 2 + 16 * s.hidden * 4,
                        "bexp_gateup_bytes": float(np.mean([gateup_bytes(s, u) for u in bU])),
                        "bexp_down_bytes": float(np.mean([gateup_bytes(s, u) / 2 for u in bU])),
                        "mx_layer_bytes_mean": float(np.mean([expert_bytes(mw.shape, u) for u in mU])),
+                       "mx_bexp_gateup_bytes": float(np.mean([gateup_bytes(mw.shape, u) for u in mbU])),
+                       "mx_bexp_down_bytes": float(np.mean([down_bytes(mw.shape, u) for u in mbU])),
                        "accept_bytes": NT * V * 4}
         copy_mib = 512
         src = torch.empty(copy_mib << 20, dtype=torch.uint8, device=dev)

@@ -101,7 +101,8 @@ def traffic(fetch_dir, write_dir, run_json, cmd_fetch, cmd_write, kernel, source
             f"fetch_bytes_per_launch: {fb:.0f}", f"write_bytes_per_launch: {wb:.0f}",
             f"traffic_bytes_per_launch: {fb + wb:.0f}"]
     # algorithmic bytes per launch that the profiled program reports for each kernel
-    keys = [("k_bexp<true", "bexp_gateup_bytes"), ("k_bexp<false", "bexp_down_bytes"),
+    keys = [("k_bexp<true, false>", "bexp_gateup_bytes"), ("k_bexp<false, false>", "bexp_down_bytes"),
+            ("k_bexp<true, true>", "mx_bexp_gateup_bytes"), ("k_bexp<false, true>", "mx_bexp_down_bytes"),
             ("k_layer<2, 4, true>", "mx_layer_bytes_mean"), ("k_layer<2, 4, false>", "layer_bytes_mean"),
             ("k_accept", "accept_bytes"), ("k_head", "head_bytes")]
     alg = next((float(run[key]) for sub, key in keys if sub in name and key in run), None)
