@@ -103,8 +103,10 @@ enum {
  *   sh_gate, sh_up bf16 [Is][H];  sh_down bf16 [H][Is]    (NULL when shared_inter == 0)
  * Expert FFN: y_e = W_down (silu(W_gate x) * (W_up x)), silu(z) = z / (1 + e^-z).
  * Supported sizes: H a multiple of 128 in [128, 1024] or of 256 in [1280, 2048] (mxfp4: a
- * multiple of 256); I in {128, 256, 512, 1024}; Is = I, or 0 for no shared expert;
- * 1 <= top_k <= min(E, 16); E <= 512. */
+ * multiple of 256); I a multiple of 128 in [128, 1024]; Is a multiple of 128 in [128, 1024], or 0
+ * for no shared expert; 1 <= top_k <= min(E, 16); E <= 512. Layers with I in {128, 256, 512, 1024}
+ * and Is in {0, I} run blocks of up to 16 tokens on the single-block kernels; every other layer
+ * takes the gathered path at every k (moe_verify_block). */
 typedef struct moe_layer {
   int32_t hidden;       /* H */
   int32_t n_experts;    /* E */
@@ -136,7 +138,9 @@ size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max);
  *   k        1 <= k <= 1024 tokens. One sequence's block carries 1 known token and up to 15
  *            drafted ones ("Speculating on a Strix Halo", section "Speculative decoding"); the
  *            blocks of several sequences may be stacked into one call, since every token routes
- *            on its own. With k > 16 (or MOE_GATHER) the call takes the gathered path: the
+ *            on its own. With k > 16, MOE_GATHER, or a layer outside the single-block sizes
+ *            (I not in {128, 256, 512, 1024}, or a shared expert of another size than I), the
+ *            call takes the gathered path: the
  *            tokens are sorted by expert (a deterministic counting sort) and each woken expert
  *            is applied to its own tokens only, 32 token columns per weight pass. That is the
  *            regime of batched serving, where the verify step becomes compute-heavy

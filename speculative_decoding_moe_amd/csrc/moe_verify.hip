@@ -2798,6 +2798,7 @@ __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
   // row blocks per column group: gate/up 64 rows (bf16, and the shared expert) or 128 rows
   // (mxfp4 routed experts); down 256 rows
   const int nrb_gu = a.I / 64, nrb_gr = a.xgm ? a.I / 128 : nrb_gu, nrb_dn = (H + 255) / 256;
+  const int nrb_sh = a.Is / 64;  // the shared expert's gate/up items (bf16, 64 rows of Is)
   int4 tot;
   const int4 pre = block_excl_scan4(int4{cnt, cnt > 0 ? 1 : 0, ncg * nrb_gr, ncg * nrb_dn}, S.wsum, tid, tot);
   const int U = tot.y;
@@ -2817,7 +2818,7 @@ __global__ void __launch_bounds__(BPERM_NTH) k_bperm(BArgs a) {
     const int ncs = a.Is ? (T + 16 * BCG - 1) / (16 * BCG) : 0;
     ue[U] = -1; uoff[U] = n; ucnt[U] = a.Is ? T : 0; gpre[U] = tot.z; dpre[U] = tot.w;
     ue[U + 1] = -1; uoff[U + 1] = n + T; ucnt[U + 1] = 0;
-    gpre[U + 1] = tot.z + ncs * nrb_gu;
+    gpre[U + 1] = tot.z + ncs * nrb_sh;
     dpre[U + 1] = tot.w + ncs * nrb_dn;
     a.tab[0] = U; a.tab[1] = gpre[U + 1]; a.tab[2] = dpre[U + 1];
     if (a.out_n) a.out_n[0] = U;
@@ -2890,6 +2891,8 @@ struct BItem {
   bool cached;            // the slot's weights are read by several column groups
   uint32_t aoff;          // byte offset of the wave's first A band (codes for mxfp4) in its tensor
   uint32_t soff;          // byte offset of its scales (mxfp4)
+  int nwk;                // 128-wide windows of its rows' reduction (down: I, or Is for the shared expert)
+  uint32_t band2;         // bf16 down: byte offset of its second row tile from the first
 };
 
 template <bool GU>
@@ -2930,9 +2933,11 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
   // (mxfp4); down wave w: row tiles rb 256 + 32 w (+ 16)
   const uint32_t row = GU ? eb * (uint32_t)a.I + (uint32_t)(d.rb * BGeo<GU, MX>::RBR + 16 * (MX ? wave : (wave & 3)))
                           : eb * (uint32_t)a.H + (uint32_t)(d.rb * 256 + 32 * wave);
-  const uint32_t K = GU ? (uint32_t)a.H : (uint32_t)a.I;  // reduction length of a row
+  const uint32_t K = GU ? (uint32_t)a.H : (uint32_t)(d.shared ? a.Is : a.I);  // reduction length of a row
   d.aoff = MX ? row * (K / 2) : row * (K * 2);
   d.soff = MX ? row * (K / 32) : 0u;
+  d.nwk = (int)K / WIN;
+  d.band2 = 16u * K * 2u;
   d.u = __builtin_amdgcn_readfirstlane(d.u);
   d.off = __builtin_amdgcn_readfirstlane(d.off);
   d.cnt = __builtin_amdgcn_readfirstlane(d.cnt);
@@ -2942,6 +2947,8 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
   d.soff = __builtin_amdgcn_readfirstlane(d.soff);
   d.cached = __builtin_amdgcn_readfirstlane((int)d.cached) != 0;
   d.shared = __builtin_amdgcn_readfirstlane((int)d.shared) != 0;
+  d.nwk = __builtin_amdgcn_readfirstlane(d.nwk);
+  d.band2 = __builtin_amdgcn_readfirstlane(d.band2);
   return d;
 }
 
@@ -2952,9 +2959,12 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
 // workgroups the first one loaded.
 // With rfull >= 0, only rounds 0 .. rfull - 1 go to every workgroup; the items after them are dealt
 // over the workgroups at positions 0 .. nfree - 1 only (item rfull G + (m - rfull) nfree + position).
+// kwin: windows of the down reduction of the phase's longest items (the layer's I, or Is when the
+// phase holds shared items of a larger size); an item with a shorter reduction treats the windows
+// past it as zero.
 template <bool GU, bool MX>
 __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_items, int rot, int tid,
-                         int lane, int wave, int rfull = -1, int nfree = 0) {
+                         int lane, int wave, int kwin, int rfull = -1, int nfree = 0) {
   using GE = BGeo<GU, MX>;
   const int G = gridDim.x, b = blockIdx.x;
   const int slotb = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
@@ -2970,7 +2980,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
 
   const int H = a.H, I = a.I;
   const int nwt = H / WIN;                     // windows of a token row (gate/up B source)
-  const int nwk = GU ? nwt : I / WIN;          // windows of the A reduction
+  const int nwk = GU ? nwt : kwin;             // windows of the A reduction (the phase's longest)
   const int nwh = GE::NKH == 2 ? (nwk + 1) / 2 : nwk;  // windows per K half
   const int ns = (nwh + GE::NWT - 1) / GE::NWT;        // ticks per item
   const int ticks = n_my * ns;
@@ -2985,7 +2995,8 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   const rsrc_t s0 = buf_rsrc(GU ? a.shg : a.shd, snum * 2), s1 = buf_rsrc(a.shu, GU ? snum * 2 : 0);
   const uint32_t vl = (uint32_t)lane * 16u;
   const int npos = a.T * a.K + a.T;
-  const int bwr = GU ? nwt : I / WIN;  // windows per B source row
+  const int nwa = max(I, a.Is) / WIN;  // windows per list position of the bf16 down operands
+  const int bwr = GU ? nwt : (MX ? I / WIN : nwa);  // windows per B source row
   const uint8_t* bsrc = MX ? (GU ? a.xgm : a.afm) : (GU ? a.xg : a.af);
   const rsrc_t rx = buf_rsrc(bsrc, (uint32_t)(GU ? a.T : npos + 16) * (uint32_t)bwr * (MX ? MXT : 512));
   // B staging. bf16: thread tid holds 16-byte piece tid % 32 of column tid / 32 for every (K
@@ -3002,19 +3013,22 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
     const int mm = m < n_my ? m : n_my - 1;  // past the end: the last item again (valid loads)
     return b_item<GU, MX>(a, S, U, base + gidx(mm), wave);
   };
-  // window of B window-slot (K half h, tick window v) at tick step, and whether it exists
-  auto win_of = [&](int h, int v, int step, bool& ok) {
+  // window of B window-slot (K half h, tick window v) at tick step, and whether it exists in a
+  // reduction of inwk windows (an item's own; windows past it take zero B operands)
+  auto win_of = [&](int h, int v, int step, int inwk, bool& ok) {
     const int wl = step * GE::NWT + v;
     const int w = h * nwh + wl;
-    ok = wl < nwh && w < nwk;
+    ok = wl < nwh && w < inwk;
     return w;
   };
   auto load_a = [&](BWin& W, const BItem& d, int step) {
     if constexpr (!MX) {
       const int w = GU ? kh * ns + step : step;
       const uint32_t so = d.aoff + (uint32_t)w * 4096u;
+      // a window past the item's reduction reads on into the tensor (finite values, or zeros past
+      // its end) and meets zero B operands
       const rsrc_t ra = d.shared ? s0 : r0, rb2 = d.shared ? s1 : r1;
-      const uint32_t band2 = (uint32_t)(16 * I * 2);  // down: the second tile, 16 rows below
+      const uint32_t band2 = d.band2;  // down: the second tile, 16 rows below
       if (d.cached) {  // read again by the slot's other column groups: keep in L2
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -3035,7 +3049,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
 #pragma unroll
       for (int v = 0; v < GE::NWT; ++v) {
         bool ok;
-        int w = win_of(kh, v, step, ok);
+        int w = win_of(kh, v, step, d.nwk, ok);
         if (!ok) w = kh * nwh;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -3055,12 +3069,12 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   };
   // gathered B pieces of one tick; padding columns and missing windows read past the resource
   // (zeros, with no memory access: every real offset is far below 2^31)
-  auto load_b = [&](BReg& R, const int (&src)[2], int step) {
+  auto load_b = [&](BReg& R, const int (&src)[2], int step, int inwk) {
     if constexpr (!MX) {
 #pragma unroll
       for (int h = 0; h < GE::NKH; ++h) {
         bool okw;
-        const int w = win_of(h, 0, step, okw);
+        const int w = win_of(h, 0, step, inwk, okw);
 #pragma unroll
         for (int ct = 0; ct < BCG; ++ct) {
           const bool ok = src[ct] >= 0 && okw;
@@ -3073,7 +3087,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
       for (int m = 0; m < GE::NCH; ++m) {
         const int hv = ((tid >> 8) + 2 * m) >> 1;  // B window index / BCG
         bool okw;
-        const int w = win_of(hv / GE::NWT, hv % GE::NWT, step, okw);
+        const int w = win_of(hv / GE::NWT, hv % GE::NWT, step, inwk, okw);
         const bool ok = src[0] >= 0 && okw;
         const uint32_t o = ok ? (uint32_t)((src[0] * bwr + w) * MXT + mch * 16) : 0x80000000u;
         R.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
@@ -3081,7 +3095,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
       {
         const int hv = scb >> 1;
         bool okw;
-        const int w = win_of(hv / GE::NWT, hv % GE::NWT, step, okw);
+        const int w = win_of(hv / GE::NWT, hv % GE::NWT, step, inwk, okw);
         const bool ok = tid < GE::NCB * 64 && src[1] >= 0 && okw;
         const uint32_t o = ok ? (uint32_t)((src[1] * bwr + w) * MXT + 256 + sblk * 4) : 0x80000000u;
         R.s = __builtin_amdgcn_raw_buffer_load_b32(rx, o, 0, 0);
@@ -3150,7 +3164,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
 #pragma unroll
   for (int j = 0; j < GE::DEPTH - 1; ++j) {
     load_a(W[j], da, sa);
-    load_b(R[j], srca, sa);
+    load_b(R[j], srca, sa, da.nwk);
     advance();
   }
   store_b(R[0], 0);
@@ -3184,7 +3198,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
       const int t = t0 + r;
       const int ib = (r + GE::DEPTH - 1) % GE::DEPTH;  // buffers of tick t + DEPTH - 1
       load_a(W[ib], da, sa);
-      load_b(R[ib], srca, sa);
+      load_b(R[ib], srca, sa, da.nwk);
       advance();
       __builtin_amdgcn_sched_barrier(0);
       // math of tick t
@@ -3263,7 +3277,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
               pack8(lo, lv);
               const int R0 = dc.rb * 64 + 16 * rt2 + 8 * half;  // intermediate row
               const int w = R0 / WIN, o = R0 % WIN, j = o / 32, qd = (o % 32) / 8;
-              uint8_t* dst = a.af + ((size_t)(dc.off + rnk) * (I / WIN) + w) * 512;
+              uint8_t* dst = a.af + ((size_t)(dc.off + rnk) * nwa + w) * 512;
               *reinterpret_cast<u32x4*>(dst + ((j * 2 + 0) * 4 + qd) * 16) = hv;
               *reinterpret_cast<u32x4*>(dst + ((j * 2 + 1) * 4 + qd) * 16) = lv;
             }
@@ -3371,13 +3385,13 @@ __global__ void __launch_bounds__(NTH) k_bexp(BArgs a) {
   const int routed = __builtin_amdgcn_readfirstlane(S.pre[U]);
   const int total = __builtin_amdgcn_readfirstlane(S.pre[U + 1]);
   if constexpr (!MXL) {
-    bexp_run<GU, false>(a, S, U, 0, total, 0, tid, lane, wave);
+    bexp_run<GU, false>(a, S, U, 0, total, 0, tid, lane, wave, max(a.I, a.Is) / WIN);
   } else {
     const int n1 = total - routed;
-    bexp_run<GU, false>(a, S, U, routed, n1, 0, tid, lane, wave);
+    bexp_run<GU, false>(a, S, U, routed, n1, 0, tid, lane, wave, max(a.Is, WIN) / WIN);
     __syncthreads();  // the next phase reuses the LDS ring
     const int2 d = mx_tail_deal(routed, n1, gridDim.x, GU);
-    bexp_run<GU, true>(a, S, U, 0, routed, n1, tid, lane, wave, d.x, d.y);
+    bexp_run<GU, true>(a, S, U, 0, routed, n1, tid, lane, wave, a.I / WIN, d.x, d.y);
   }
 }
 
@@ -3456,7 +3470,7 @@ BLayout make_blayout(const moe_layer* L, int T) {
   o.bw = off;     off = align256(off + n * 4);
   o.brv = off;    off = align256(off + n * 4);
   o.bpos = off;   off = align256(off + (size_t)T * K * 4);
-  o.af = off;     off = align256(off + (n + 16) * I * 4);
+  o.af = off;     off = align256(off + (n + 16) * std::max(I, (size_t)L->shared_inter) * 4);
   o.part = off;   off = align256(off + n * H * 4);
   const bool mx = L->wdtype == MOE_W_MXFP4;  // MX-fp8 B windows of the routed experts
   o.xgm = off;    off = align256(off + (mx ? (size_t)T * (H / WIN) * MXT : 0));
@@ -3480,8 +3494,8 @@ int check_layer(const moe_layer* L) {
   if (H < 128 || H > 2048 || H % 128 || (H > 1024 && H % 256)) return MOE_ERR_SHAPE;
   if (E < 1 || E > MAX_E) return MOE_ERR_SHAPE;
   if (K < 1 || K > MAX_K || K > E) return MOE_ERR_SHAPE;
-  if (I != 128 && I != 256 && I != 512 && I != 1024) return MOE_ERR_SHAPE;
-  if (Is != 0 && Is != I) return MOE_ERR_SHAPE;
+  if (I < 128 || I > 1024 || I % 128) return MOE_ERR_SHAPE;
+  if (Is != 0 && (Is < 128 || Is > 1024 || Is % 128)) return MOE_ERR_SHAPE;
   if (L->wdtype != MOE_W_BF16 && L->wdtype != MOE_W_MXFP4) return MOE_ERR_DTYPE;
   if (L->layout != MOE_LAYOUT_TILED) return MOE_ERR_DTYPE;
   if (L->wdtype == MOE_W_MXFP4 && H % 256) return MOE_ERR_SHAPE;  // mxfp4 kernels take whole 256-row down blocks
@@ -3494,6 +3508,17 @@ int check_layer(const moe_layer* L) {
     if (p && !aligned16(p)) return MOE_ERR_ALIGN;
   if (!(L->rms_eps >= 0.0f) || L->rms_eps > 3.0e38f) return MOE_ERR_ARG;
   return MOE_OK;
+}
+
+// The single-block kernels give each wave whole 128-column windows of the down reduction (I / 128
+// must divide the eight waves) and lay the shared expert's items out like the routed ones (Is = I).
+// Layers outside that set take the gathered path for every k, which handles any multiple of 128.
+bool block_shape_ok(const moe_layer* L) {
+  const int I = L->inter, Is = L->shared_inter;
+  return (I == 128 || I == 256 || I == 512 || I == 1024) && (Is == 0 || Is == I);
+}
+bool use_gather(const moe_layer* L, int k, uint32_t flags) {
+  return k > KMAX || (flags & MOE_GATHER) || !block_shape_ok(L);
 }
 
 // A HIP error left pending by the caller's earlier work would be reported (and cleared) by the
@@ -3611,11 +3636,12 @@ const char* moe_status_string(int status) {
 
 size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max) {
   if (check_layer(layer) != MOE_OK || k_max < 1 || k_max > BT_MAX) return 0;
+  if (!block_shape_ok(layer)) return make_blayout(layer, k_max).total;
   const size_t small = make_layout(layer, std::min(k_max, (int32_t)KMAX)).total;
   return std::max(small, make_blayout(layer, k_max).total);
 }
 
-// the gathered path (k > 16 tokens, or MOE_GATHER)
+// the gathered path (k > 16 tokens, MOE_GATHER, or a layer outside the single-block shapes)
 static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t flags, float* y,
                        int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace, size_t ws_bytes,
                        void* hip_stream, void* const* events) {
@@ -3692,7 +3718,7 @@ static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint
   if (!x || !y || !workspace) return MOE_ERR_NULL;
   if (k < 1 || k > BT_MAX) return MOE_ERR_SHAPE;
   if (flags & ~(uint32_t)(MOE_PRE_RMSNORM | MOE_RESIDUAL | MOE_GATHER)) return MOE_ERR_ARG;
-  if (k > KMAX || (flags & MOE_GATHER))
+  if (use_gather(L, k, flags))
     return gather_impl(L, x, k, flags, y, topk_ids, topk_w, n_woken, workspace, ws_bytes, hip_stream, events);
   if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || (topk_ids && !aligned16(topk_ids)) ||
       (topk_w && !aligned16(topk_w)) || (n_woken && !aligned16(n_woken)))
@@ -3757,7 +3783,7 @@ int moe_verify_block_noalloc(const moe_layer* L, const float* x, int32_t k, uint
   if (!x || !y) return MOE_ERR_NULL;
   if (k < 1 || k > BT_MAX) return MOE_ERR_SHAPE;
   if (flags & ~(uint32_t)(MOE_PRE_RMSNORM | MOE_RESIDUAL | MOE_GATHER)) return MOE_ERR_ARG;
-  const size_t need = (k > KMAX || (flags & MOE_GATHER)) ? make_blayout(L, k).total : make_layout(L, k).total;
+  const size_t need = use_gather(L, k, flags) ? make_blayout(L, k).total : make_layout(L, k).total;
   if (need > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
   if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
   int lookup = MOE_OK;

@@ -84,13 +84,32 @@ def test_workspace_size(b):
 @pytest.mark.parametrize("over,status", [
     (dict(hidden=100), -2), (dict(hidden=64), -2), (dict(hidden=4096), -2), (dict(hidden=1152), -2),
     (dict(n_experts=0), -2), (dict(n_experts=513), -2), (dict(top_k=0), -2), (dict(top_k=17), -2),
-    (dict(n_experts=4, top_k=5), -2), (dict(inter=384), -2), (dict(inter=2048), -2),
-    (dict(shared_inter=256), -2), (dict(wdtype=2), -3), (dict(wdtype=1), -3), (dict(layout=0), -3),
+    (dict(n_experts=4, top_k=5), -2), (dict(inter=192), -2), (dict(inter=1152), -2), (dict(inter=2048), -2),
+    (dict(inter=0), -2), (dict(shared_inter=64), -2), (dict(shared_inter=1280), -2), (dict(shared_inter=-128), -2),
+    (dict(wdtype=2), -3), (dict(wdtype=1), -3), (dict(layout=0), -3),
     (dict(router_w=None), -1), (dict(w_down=None), -1), (dict(sh_up=None), -1),
     (dict(w_gate=FAKE + 8), -4), (dict(rms_eps=-1.0), -8), (dict(rms_eps=float("nan")), -8),
 ])
 def test_bad_layer_rejected(b, over, status):
     assert _call(b, _layer(b, **over), ws_bytes=1 << 30) == status
+
+
+@pytest.mark.parametrize("over", [dict(inter=384), dict(inter=640, shared_inter=128), dict(shared_inter=256),
+                                  dict(inter=256, shared_inter=1024), dict(inter=768, shared_inter=0)])
+def test_general_sizes_take_the_gathered_workspace(b, over):
+    """Layers outside the single-block shapes (I / 128 not dividing eight, or a shared expert of
+    another size) are accepted and take the gathered path at every k: their workspace for a
+    16-token block is the gathered path's, which grows with the token count, and one byte less
+    is refused before anything is launched."""
+    L = _layer(b, **over)
+    n1 = b.lib.moe_verify_workspace_size(ctypes.byref(L), 1)
+    n16 = b.lib.moe_verify_workspace_size(ctypes.byref(L), 16)
+    n17 = b.lib.moe_verify_workspace_size(ctypes.byref(L), 17)
+    assert 0 < n1 < n16 < n17
+    for k in (1, 16):
+        need = b.lib.moe_verify_workspace_size(ctypes.byref(L), k)
+        assert _call(b, L, k=k, ws_bytes=need - 1) == b.MOE_ERR_WORKSPACE
+        assert _call(b, L, k=k, flags=4, ws_bytes=need - 1) == b.MOE_ERR_WORKSPACE
 
 
 def test_bad_call_arguments_rejected(b):
@@ -335,7 +354,7 @@ def test_noalloc_rejects_calls_beyond_its_scratch_and_bad_arguments(b):
     assert call(L, 16, flags=8) == b.MOE_ERR_ARG
     assert call(L, 16, x=None) == b.MOE_ERR_NULL
     assert call(L, 16, y=None) == b.MOE_ERR_NULL
-    assert call(_layer(b, inter=384), 16) == b.MOE_ERR_SHAPE
+    assert call(_layer(b, inter=192), 16) == b.MOE_ERR_SHAPE
     # the largest layer's 16-token block fits: its workspace is below the scratch size
     big = _layer(b, n_experts=512, top_k=16, inter=1024, shared_inter=1024)
     assert 0 < b.lib.moe_verify_workspace_size(ctypes.byref(big), 16) <= b.NOALLOC_SCRATCH_BYTES

@@ -386,6 +386,37 @@ def test_gather_mxfp4_edge_shapes(B, shape):
         check_outputs_tol(g, x, wl, np.arange(k) if k < 40 else [0, k - 1], 0, MX_TOL, False)
 
 
+@pytest.mark.parametrize("shape", [
+    gen.LayerShape(hidden=512, n_experts=32, top_k=4, inter=384, shared_inter=384),   # I / 128 = 3 windows
+    gen.LayerShape(hidden=512, n_experts=32, top_k=4, inter=512, shared_inter=256),   # shared expert smaller than I
+    gen.LayerShape(hidden=384, n_experts=40, top_k=6, inter=640, shared_inter=128),   # 5 windows, 3 windows of H
+    gen.LayerShape(hidden=256, n_experts=16, top_k=2, inter=256, shared_inter=768),   # shared expert larger than I
+    gen.LayerShape(hidden=512, n_experts=32, top_k=4, inter=384, shared_inter=256, wdtype="mxfp4"),
+    gen.LayerShape(hidden=256, n_experts=16, top_k=4, inter=768, shared_inter=1024, wdtype="mxfp4"),
+])
+def test_general_shapes(B, shape):
+    """Layers outside the single-block shapes (I / 128 not dividing eight, or a shared expert of its
+    own size) take the gathered path at every k: blocks of 1, 16 (without MOE_GATHER) and 70 tokens
+    against the oracle, and the 16-token call equal, bit for bit, to the same call with MOE_GATHER."""
+    from speculative_decoding_moe_amd.workloads import device
+    wl = gen.Workload("general", shape, k=16, seed=5150)
+    layer = device.make_layer(wl, 0, "cuda")
+    mx = shape.wdtype == "mxfp4"
+    for k, flags in ((1, 0), (16, 0), (70, PRE | RES)):
+        x = gen.hidden_states(wl, rep=k, k=k)
+        g = run(B, layer, x, flags)
+        check_routing(g, x, wl, flags=flags & PRE)
+        rows = np.arange(k) if k <= 16 else [0, 33, k - 1]
+        if mx:
+            check_outputs_tol(g, x, wl, rows, flags, MX_TOL, bool(flags & RES))
+        else:
+            check_outputs(g, x, wl, rows, flags, compare_delta=bool(flags & RES))
+        if k == 16:
+            h = run(B, layer, x, flags | GATHER)
+            for key in ("y", "ids", "w"):
+                assert np.array_equal(g[key], h[key]), key
+
+
 def test_gather_largest_lists(B):
     """1024 tokens x top-16 of 512 experts (16384 routed pairs, every pair slot of the permutation
     kernel's threads in use), with and without the shared expert: routing of every token, sampled
