@@ -2936,8 +2936,13 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
   const uint32_t K = GU ? (uint32_t)a.H : (uint32_t)(d.shared ? a.Is : a.I);  // reduction length of a row
   d.aoff = MX ? row * (K / 2) : row * (K * 2);
   d.soff = MX ? row * (K / 32) : 0u;
-  d.nwk = (int)K / WIN;
-  d.band2 = 16u * K * 2u;
+  if constexpr (!GU) {  // gate/up items all reduce over H
+    d.nwk = (int)K / WIN;
+    d.band2 = 16u * K * 2u;
+  } else {
+    d.nwk = a.H / WIN;
+    d.band2 = 0u;
+  }
   d.u = __builtin_amdgcn_readfirstlane(d.u);
   d.off = __builtin_amdgcn_readfirstlane(d.off);
   d.cnt = __builtin_amdgcn_readfirstlane(d.cnt);
@@ -2947,8 +2952,10 @@ __device__ __forceinline__ BItem b_item(const BArgs& a, const BSmem<GU>& S, int 
   d.soff = __builtin_amdgcn_readfirstlane(d.soff);
   d.cached = __builtin_amdgcn_readfirstlane((int)d.cached) != 0;
   d.shared = __builtin_amdgcn_readfirstlane((int)d.shared) != 0;
-  d.nwk = __builtin_amdgcn_readfirstlane(d.nwk);
-  d.band2 = __builtin_amdgcn_readfirstlane(d.band2);
+  if constexpr (!GU) {
+    d.nwk = __builtin_amdgcn_readfirstlane(d.nwk);
+    d.band2 = __builtin_amdgcn_readfirstlane(d.band2);
+  }
   return d;
 }
 
@@ -2997,6 +3004,9 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   const int npos = a.T * a.K + a.T;
   const int nwa = max(I, a.Is) / WIN;  // windows per list position of the bf16 down operands
   const int bwr = GU ? nwt : (MX ? I / WIN : nwa);  // windows per B source row
+  // items of one length (every gate/up item; down unless a shared expert of another size shares
+  // the phase) keep the phase's window count, a loop invariant, in their window checks
+  const bool mixed = !GU && !MX && a.Is != 0 && a.Is != I;
   const uint8_t* bsrc = MX ? (GU ? a.xgm : a.afm) : (GU ? a.xg : a.af);
   const rsrc_t rx = buf_rsrc(bsrc, (uint32_t)(GU ? a.T : npos + 16) * (uint32_t)bwr * (MX ? MXT : 512));
   // B staging. bf16: thread tid holds 16-byte piece tid % 32 of column tid / 32 for every (K
@@ -3013,12 +3023,11 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
     const int mm = m < n_my ? m : n_my - 1;  // past the end: the last item again (valid loads)
     return b_item<GU, MX>(a, S, U, base + gidx(mm), wave);
   };
-  // window of B window-slot (K half h, tick window v) at tick step, and whether it exists in a
-  // reduction of inwk windows (an item's own; windows past it take zero B operands)
-  auto win_of = [&](int h, int v, int step, int inwk, bool& ok) {
+  // window of B window-slot (K half h, tick window v) at tick step, and whether it exists
+  auto win_of = [&](int h, int v, int step, bool& ok) {
     const int wl = step * GE::NWT + v;
     const int w = h * nwh + wl;
-    ok = wl < nwh && w < inwk;
+    ok = wl < nwh && w < nwk;
     return w;
   };
   auto load_a = [&](BWin& W, const BItem& d, int step) {
@@ -3028,7 +3037,8 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
       // a window past the item's reduction reads on into the tensor (finite values, or zeros past
       // its end) and meets zero B operands
       const rsrc_t ra = d.shared ? s0 : r0, rb2 = d.shared ? s1 : r1;
-      const uint32_t band2 = d.band2;  // down: the second tile, 16 rows below
+      // down: the second tile, 16 rows below (gate/up keeps the expression its schedule was tuned with)
+      const uint32_t band2 = GU ? (uint32_t)(16 * I * 2) : d.band2;
       if (d.cached) {  // read again by the slot's other column groups: keep in L2
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -3049,7 +3059,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
 #pragma unroll
       for (int v = 0; v < GE::NWT; ++v) {
         bool ok;
-        int w = win_of(kh, v, step, d.nwk, ok);
+        int w = win_of(kh, v, step, ok);
         if (!ok) w = kh * nwh;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -3069,12 +3079,16 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   };
   // gathered B pieces of one tick; padding columns and missing windows read past the resource
   // (zeros, with no memory access: every real offset is far below 2^31)
-  auto load_b = [&](BReg& R, const int (&src)[2], int step, int inwk) {
+  int ld_nwk = nwk;  // windows of the load cursor's item (read by down loads of mixed lengths)
+  auto load_b = [&](BReg& R, const int (&src)[2], int step) {
     if constexpr (!MX) {
 #pragma unroll
       for (int h = 0; h < GE::NKH; ++h) {
         bool okw;
-        const int w = win_of(h, 0, step, inwk, okw);
+        const int w = win_of(h, 0, step, okw);
+        // down items shorter than the phase's longest (a shared expert of another size): their
+        // windows past their own reduction take zero B operands
+        if constexpr (!GU) okw = okw && (!mixed || w < ld_nwk);
 #pragma unroll
         for (int ct = 0; ct < BCG; ++ct) {
           const bool ok = src[ct] >= 0 && okw;
@@ -3087,7 +3101,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
       for (int m = 0; m < GE::NCH; ++m) {
         const int hv = ((tid >> 8) + 2 * m) >> 1;  // B window index / BCG
         bool okw;
-        const int w = win_of(hv / GE::NWT, hv % GE::NWT, step, inwk, okw);
+        const int w = win_of(hv / GE::NWT, hv % GE::NWT, step, okw);
         const bool ok = src[0] >= 0 && okw;
         const uint32_t o = ok ? (uint32_t)((src[0] * bwr + w) * MXT + mch * 16) : 0x80000000u;
         R.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
@@ -3095,7 +3109,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
       {
         const int hv = scb >> 1;
         bool okw;
-        const int w = win_of(hv / GE::NWT, hv % GE::NWT, step, inwk, okw);
+        const int w = win_of(hv / GE::NWT, hv % GE::NWT, step, okw);
         const bool ok = tid < GE::NCB * 64 && src[1] >= 0 && okw;
         const uint32_t o = ok ? (uint32_t)((src[1] * bwr + w) * MXT + 256 + sblk * 4) : 0x80000000u;
         R.s = __builtin_amdgcn_raw_buffer_load_b32(rx, o, 0, 0);
@@ -3148,6 +3162,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
   BReg R[GE::DEPTH];
   int ma = 0, sa = 0;  // load cursor (item, step)
   BItem da = item_of(0);
+  if constexpr (!GU) ld_nwk = da.nwk;
   int srca[2], srcn[2];
   src_of(da, srca);
   src_of(item_of(1), srcn);
@@ -3156,6 +3171,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
       sa = 0;
       ++ma;
       da = item_of(ma);
+      if constexpr (!GU) ld_nwk = da.nwk;
       srca[0] = srcn[0];
       srca[1] = srcn[1];
       src_of(item_of(ma + 1), srcn);
@@ -3164,7 +3180,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
 #pragma unroll
   for (int j = 0; j < GE::DEPTH - 1; ++j) {
     load_a(W[j], da, sa);
-    load_b(R[j], srca, sa, da.nwk);
+    load_b(R[j], srca, sa);
     advance();
   }
   store_b(R[0], 0);
@@ -3198,7 +3214,7 @@ __device__ void bexp_run(const BArgs& a, BSmem<GU>& S, int U, int base, int n_it
       const int t = t0 + r;
       const int ib = (r + GE::DEPTH - 1) % GE::DEPTH;  // buffers of tick t + DEPTH - 1
       load_a(W[ib], da, sa);
-      load_b(R[ib], srca, sa, da.nwk);
+      load_b(R[ib], srca, sa);
       advance();
       __builtin_amdgcn_sched_barrier(0);
       // math of tick t
