@@ -410,6 +410,22 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t x) {
   const auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   return op((uint32_t)r32[0], (uint32_t)r32[1]);
 }
+// The same maximum over each 16-lane row of the wave (DPP steps that stay inside a row), in every
+// lane of the row.
+__device__ __forceinline__ void row16_argmax_dpp(float& v, int& i) {
+  auto red = [](uint32_t x, bool mx) {
+    auto op = [mx](uint32_t a, uint32_t b) { return mx ? max(a, b) : min(a, b); };
+    x = op(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
+    x = op(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
+    x = op(x, dpp_u32<0x141>(x));  // row_half_mirror
+    return op(x, dpp_u32<0x140>(x));  // row_mirror
+  };
+  const uint32_t key = okey32(v);
+  const uint32_t km = red(key, true);
+  const uint32_t im = red(key == km ? (uint32_t)i : 0xFFFFFFFFu, false);
+  v = km == 1u ? v : okey32_value(km);  // a row of NaNs keeps its own value
+  i = (int)im;
+}
 // (value, index) maximum over the wave, equal values to the lower index, in every lane: the
 // largest order-preserving key, then the lowest index among the lanes holding it. The same
 // result as merging the lanes with argmax_merge (-0 and +0 are equal; a NaN never wins over a
@@ -1741,6 +1757,24 @@ __global__ void __launch_bounds__(256) k_accept(const float* logits, int V, int 
     }
     if (!ok) break;
     const int end = min(nf, base + 256 * PPT);
+    if (nf <= 256 * PPT && nchunks <= 32) {
+      // every record in one pass: 16 lanes per row (lane c of the row's group takes chunks c and
+      // c + 16), so each wave merges four rows at once; the merge order does not change the result
+      for (int rb = wave * 4; rb < n_target; rb += 16) {  // uniform over the wave
+        const int row = rb + (lane >> 4), c = lane & 15;
+        float v = -INFINITY;
+        int vi = 0x7fffffff;
+        if (row < n_target)
+          for (int cc = c; cc < nchunks; cc += 16) argmax_merge(v, vi, stv[row * nchunks + cc], sti[row * nchunks + cc]);
+        row16_argmax_dpp(v, vi);
+        if (c == 0 && row < n_target) {
+          rowv[row] = v;
+          tgt[row] = vi;
+        }
+      }
+      __syncthreads();
+      break;
+    }
     const int r_lo = base / nchunks, r_hi = (end - 1) / nchunks;
     for (int row = r_lo + wave; row <= r_hi; row += 4) {
       float v = rowv[row];
