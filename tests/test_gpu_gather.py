@@ -447,8 +447,7 @@ class _PeriodicRouterLayer(GenLayer):
 @pytest.mark.parametrize("shape,period,k", [
     (gen.LayerShape(hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512), 5, 300),
     (gen.LayerShape(hidden=256, n_experts=200, top_k=6, inter=256, shared_inter=0), 3, 77),   # E not a multiple of 16
-    # the many-token router's wider tiles (2 and 4 sixteen-expert tiles per wave on 256 CUs) with
-    # a last tile group that runs past E
+    # many token groups with a last 64-expert group of the router that runs past E
     (gen.LayerShape(hidden=256, n_experts=200, top_k=6, inter=256, shared_inter=0), 3, 600),
     (gen.LayerShape(hidden=256, n_experts=200, top_k=6, inter=256, shared_inter=0), 3, 1024),
     (gen.LayerShape(hidden=256, n_experts=512, top_k=16, inter=256, shared_inter=256), 7, 40),
