@@ -162,7 +162,10 @@ size_t moe_verify_workspace_size(const moe_layer* layer, int32_t k_max);
  * workgroup must be resident at once: a device with fewer compute units than the launch needs
  * (max(k H / 512, Is / 16, H / 64), at most 64 here) gets MOE_ERR_SHAPE. The waits are bounded: if
  * a phase is not complete within seconds (only possible when other work holds the GPU's compute
- * units that long), the call's outputs are invalid and *n_woken is set to -1.
+ * units that long), the call's outputs are invalid and *n_woken is set to -1. Two single-block
+ * calls that run at the same time (on different streams) can each hold compute units the other's
+ * waiting workgroups need, so both would reach that bound: order such calls on one stream (or
+ * with events). The gathered path and the other entry points have no such waits.
  * Returns MOE_OK or an MOE_ERR_* code (nothing is enqueued on error). */
 int moe_verify_block(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
                      int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
