@@ -201,6 +201,38 @@ int moe_verify_block_timed(const moe_layer* layer, const float* x, int32_t k, ui
 int moe_verify_block_noalloc(const moe_layer* layer, const float* x, int32_t k, uint32_t flags, float* y,
                              int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* hip_stream);
 
+/* Largest number of layers one moe_verify_stack call takes. */
+#define MOE_STACK_MAX_LAYERS 4096
+
+/* Bytes of device workspace moe_verify_stack needs for blocks of up to k_max tokens of layers of
+ * this shape (0 if the layer is invalid, k_max is outside 1..16, or the layer's sizes take the
+ * gathered path: see moe_verify_block's supported sizes). Host only. */
+size_t moe_verify_stack_workspace_size(const moe_layer* layer, int32_t k_max);
+
+/* A stack of n_layers MoE layers over one block in one call: y = L_{n-1}(... L_1(L_0(x))), each
+ * layer as moe_verify_block computes it with the same flags, so with MOE_PRE_RMSNORM |
+ * MOE_RESIDUAL the layers form a pre-norm residual stream (the target's MoE layers run back to
+ * back in a verify pass: "Speculating on a Strix Halo", section "The verify's own cost"). The
+ * result equals, bit for bit, n_layers moe_verify_block calls chained through their outputs: the
+ * same two launches per layer, with the intermediate rows in the workspace.
+ *   layers    moe_layer [n_layers]: every layer of one shape (hidden, n_experts, top_k, inter,
+ *             shared_inter, wdtype, layout); rms_eps and the weights may differ
+ *   x, y      fp32 [k][H] input and output (must not overlap each other or the workspace)
+ *   k         1..16; the layers' sizes must take the single-block path (I in {128, 256, 512,
+ *             1024}, shared_inter 0 or I); other stacks are run with one moe_verify_block call
+ *             per layer
+ *   flags     MOE_PRE_RMSNORM | MOE_RESIDUAL (MOE_GATHER is not accepted)
+ *   n_woken   int32 [n_layers] or NULL: each layer's woken-expert count (-1: that layer's wait
+ *             ran past its bound, as in moe_verify_block)
+ *   workspace, ws_bytes: at least moe_verify_stack_workspace_size(&layers[0], k) bytes, no
+ *             initialisation needed
+ * Limits: 1 <= n_layers <= MOE_STACK_MAX_LAYERS. x, y, n_woken and workspace 16-byte aligned.
+ * Each layer's launches wait for each other as moe_verify_block's single-block launch does (every
+ * workgroup resident; overlapping calls on two streams can exhaust the bound). Returns MOE_OK or
+ * an MOE_ERR_* code (nothing is enqueued on an argument error). */
+int moe_verify_stack(const moe_layer* layers, int32_t n_layers, const float* x, int32_t k, uint32_t flags, float* y,
+                     int32_t* n_woken, void* workspace, size_t ws_bytes, void* hip_stream);
+
 /* Rearranges n_mats row-major matrices of rows x cols into MOE_LAYOUT_TILED (a permutation of
  * 16-byte chunks and, for mxfp4, of scale bytes; output sizes equal input sizes).
  *   wdtype      MOE_W_BF16: src, dst bf16 [n_mats][rows][cols]

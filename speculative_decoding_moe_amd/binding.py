@@ -20,9 +20,10 @@ MOE_LAYOUT_TILED = 1
 MOE_PRE_RMSNORM, MOE_RESIDUAL, MOE_GATHER = 1, 2, 4
 
 NOALLOC_SCRATCH_BYTES = 24 << 20  # MOE_NOALLOC_SCRATCH_BYTES
+STACK_MAX_LAYERS = 4096  # MOE_STACK_MAX_LAYERS
 
 EXPORTS = ("moe_verify_workspace_size", "moe_verify_block", "moe_verify_block_timed", "moe_verify_block_noalloc",
-           "moe_pack_weights", "accept_prefix_workspace_size", "accept_prefix",
+           "moe_verify_stack_workspace_size", "moe_verify_stack", "moe_pack_weights", "accept_prefix_workspace_size", "accept_prefix",
            "accept_prefix_batch_workspace_size", "accept_prefix_batch",
            "lm_head_accept_workspace_size", "lm_head_accept", "accept_sample_workspace_size",
            "accept_sample", "accept_sample_batch_workspace_size", "accept_sample_batch",
@@ -61,6 +62,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_block_timed.restype = ctypes.c_int
     lib.moe_verify_block_noalloc.argtypes = [ctypes.POINTER(MoeLayerStruct), vp, i32, u32, vp, vp, vp, vp, vp]
     lib.moe_verify_block_noalloc.restype = ctypes.c_int
+    lib.moe_verify_stack_workspace_size.argtypes = [ctypes.POINTER(MoeLayerStruct), i32]
+    lib.moe_verify_stack_workspace_size.restype = sz
+    lib.moe_verify_stack.argtypes = [ctypes.POINTER(MoeLayerStruct), i32, vp, i32, u32, vp, vp, vp, sz, vp]
+    lib.moe_verify_stack.restype = ctypes.c_int
     lib.moe_pack_weights.argtypes = [i32, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.moe_pack_weights.restype = ctypes.c_int
     lib.accept_prefix_workspace_size.argtypes = [i32, i32]
@@ -274,6 +279,29 @@ def moe_verify_block_noalloc(layer: MoeLayer, x, flags: int, y, topk_ids=None, t
     k = _check_block_args(layer, x, y, topk_ids, topk_w, n_woken, None)
     st = lib.moe_verify_block_noalloc(ctypes.byref(layer.struct), _ptr(x), k, int(flags), _ptr(y), _ptr(topk_ids),
                                       _ptr(topk_w), _ptr(n_woken), _stream_handle() if stream is None else stream)
+    _check(st)
+
+
+def moe_verify_stack_workspace_size(layer: MoeLayer, k_max: int) -> int:
+    return int(lib.moe_verify_stack_workspace_size(ctypes.byref(layer.struct), int(k_max)))
+
+
+def moe_verify_stack(layers, x, flags: int, y, n_woken=None, workspace=None, stream=None) -> None:
+    """y = L_{n-1}(... L_0(x)) over a block of k = x.shape[0] tokens, layers of one shape, in
+    one library call: equal to chained moe_verify_block calls."""
+    layers = list(layers)
+    if not layers or len(layers) > STACK_MAX_LAYERS:
+        raise ValueError(f"layers must hold 1..{STACK_MAX_LAYERS} MoeLayer objects")
+    for i, L in enumerate(layers):
+        if not isinstance(L, MoeLayer):
+            raise ValueError(f"layers[{i}] must be a MoeLayer")
+    k = _check_block_args(layers[0], x, y, None, None, None, workspace)
+    _req("n_woken", n_woken, I32, min_numel=len(layers), optional=True)
+    _on_gpu(n_woken=n_woken)
+    arr = (MoeLayerStruct * len(layers))(*[L.struct for L in layers])
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.moe_verify_stack(arr, len(layers), _ptr(x), k, int(flags), _ptr(y), _ptr(n_woken), _ptr(workspace),
+                              ws_bytes, _stream_handle() if stream is None else stream)
     _check(st)
 
 

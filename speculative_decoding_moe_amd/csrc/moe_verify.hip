@@ -3760,6 +3760,25 @@ static int gather_impl(const moe_layer* L, const float* x, int32_t T, uint32_t f
   return (ok && hipGetLastError() == hipSuccess) ? MOE_OK : MOE_ERR_HIP;
 }
 
+// The single-block path's kernel arguments for one layer call on workspace ws (layout lay).
+static Args block_args(const moe_layer* L, const float* x, int32_t k, uint32_t flags, float* y, int32_t* topk_ids,
+                       float* topk_w, int32_t* n_woken, uint8_t* ws, const Layout& lay) {
+  Args a;
+  a.x = x; a.y = y; a.out_ids = topk_ids; a.out_w = topk_w; a.out_n = n_woken;
+  a.wr = L->router_w;
+  a.wg = (const uint8_t*)L->w_gate; a.wu = (const uint8_t*)L->w_up; a.wd = (const uint8_t*)L->w_down;
+  a.sg = L->s_gate; a.su = L->s_up; a.sd = L->s_down;
+  a.shg = (const uint8_t*)L->sh_gate; a.shu = (const uint8_t*)L->sh_up; a.shd = (const uint8_t*)L->sh_down;
+  a.ctr = (uint32_t*)(ws + lay.ctr);
+  a.xfrag = (u32x4*)(ws + lay.xfrag); a.xfrag_sh = (u32x4*)(ws + lay.xfrag_sh); a.plog = (float*)(ws + lay.plog); a.psq = (float*)(ws + lay.psq);
+  a.afrag = (u32x4*)(ws + lay.afrag); a.afrag_sh = (u32x4*)(ws + lay.afrag_sh); a.part = (float*)(ws + lay.part);
+  a.H = L->hidden; a.E = L->n_experts; a.K = L->top_k; a.I = L->inter; a.Is = L->shared_inter; a.k = k;
+  a.hs = lay.hs; a.ntile_e = (L->n_experts + 15) / 16; a.umax = lay.umax;
+  a.pre_norm = (flags & MOE_PRE_RMSNORM) ? 1 : 0; a.residual = (flags & MOE_RESIDUAL) ? 1 : 0;
+  a.eps = L->rms_eps;
+  return a;
+}
+
 static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint32_t flags, float* y,
                              int32_t* topk_ids, float* topk_w, int32_t* n_woken, void* workspace,
                              size_t ws_bytes, void* hip_stream, void* const* events) {
@@ -3786,20 +3805,7 @@ static int verify_block_impl(const moe_layer* L, const float* x, int32_t k, uint
   if (n_woken && (overlaps(n_woken, 4, workspace, lay.total) || overlaps(n_woken, 4, y, xy_bytes)))
     return MOE_ERR_ALIAS;
 
-  uint8_t* ws = (uint8_t*)workspace;
-  Args a;
-  a.x = x; a.y = y; a.out_ids = topk_ids; a.out_w = topk_w; a.out_n = n_woken;
-  a.wr = L->router_w;
-  a.wg = (const uint8_t*)L->w_gate; a.wu = (const uint8_t*)L->w_up; a.wd = (const uint8_t*)L->w_down;
-  a.sg = L->s_gate; a.su = L->s_up; a.sd = L->s_down;
-  a.shg = (const uint8_t*)L->sh_gate; a.shu = (const uint8_t*)L->sh_up; a.shd = (const uint8_t*)L->sh_down;
-  a.ctr = (uint32_t*)(ws + lay.ctr);
-  a.xfrag = (u32x4*)(ws + lay.xfrag); a.xfrag_sh = (u32x4*)(ws + lay.xfrag_sh); a.plog = (float*)(ws + lay.plog); a.psq = (float*)(ws + lay.psq);
-  a.afrag = (u32x4*)(ws + lay.afrag); a.afrag_sh = (u32x4*)(ws + lay.afrag_sh); a.part = (float*)(ws + lay.part);
-  a.H = L->hidden; a.E = L->n_experts; a.K = L->top_k; a.I = L->inter; a.Is = L->shared_inter; a.k = k;
-  a.hs = lay.hs; a.ntile_e = (L->n_experts + 15) / 16; a.umax = lay.umax;
-  a.pre_norm = (flags & MOE_PRE_RMSNORM) ? 1 : 0; a.residual = (flags & MOE_RESIDUAL) ? 1 : 0;
-  a.eps = L->rms_eps;
+  const Args a = block_args(L, x, k, flags, y, topk_ids, topk_w, n_woken, (uint8_t*)workspace, lay);
 
   hipStream_t s = (hipStream_t)hip_stream;
   if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
@@ -3841,6 +3847,71 @@ int moe_verify_block_noalloc(const moe_layer* L, const float* x, int32_t k, uint
   if (!ws) return lookup;
   return verify_block_impl(L, x, k, flags, y, topk_ids, topk_w, n_woken, ws, MOE_NOALLOC_SCRATCH_BYTES, hip_stream,
                            nullptr);
+}
+
+// Stack workspace: the single-block layout, then two ping-pong activation buffers.
+struct StackLayout {
+  Layout base;
+  size_t pp0, pp1, total;
+};
+static StackLayout make_stack_layout(const moe_layer* L, int k) {
+  StackLayout o;
+  o.base = make_layout(L, k);
+  size_t off = o.base.total;
+  o.pp0 = off; off = align256(off + (size_t)k * L->hidden * 4);
+  o.pp1 = off; off = align256(off + (size_t)k * L->hidden * 4);
+  o.total = off;
+  return o;
+}
+static bool same_shape(const moe_layer* a, const moe_layer* b) {
+  return a->hidden == b->hidden && a->n_experts == b->n_experts && a->top_k == b->top_k && a->inter == b->inter &&
+         a->shared_inter == b->shared_inter && a->wdtype == b->wdtype && a->layout == b->layout;
+}
+
+size_t moe_verify_stack_workspace_size(const moe_layer* layer, int32_t k_max) {
+  if (check_layer(layer) != MOE_OK || k_max < 1 || k_max > KMAX || !block_shape_ok(layer)) return 0;
+  return make_stack_layout(layer, k_max).total;
+}
+
+int moe_verify_stack(const moe_layer* layers, int32_t n_layers, const float* x, int32_t k, uint32_t flags, float* y,
+                     int32_t* n_woken, void* workspace, size_t ws_bytes, void* hip_stream) {
+  if (!layers || !x || !y || !workspace) return MOE_ERR_NULL;
+  if (n_layers < 1 || n_layers > MOE_STACK_MAX_LAYERS) return MOE_ERR_SHAPE;
+  for (int l = 0; l < n_layers; ++l) {
+    const int st = check_layer(&layers[l]);
+    if (st != MOE_OK) return st;
+    if (!same_shape(&layers[0], &layers[l])) return MOE_ERR_SHAPE;
+  }
+  if (flags & ~(uint32_t)(MOE_PRE_RMSNORM | MOE_RESIDUAL)) return MOE_ERR_ARG;
+  if (k < 1 || k > KMAX || !block_shape_ok(&layers[0])) return MOE_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(workspace) || (n_woken && !aligned16(n_woken)))
+    return MOE_ERR_ALIGN;
+  const StackLayout lay = make_stack_layout(&layers[0], k);
+  if (ws_bytes < lay.total) return MOE_ERR_WORKSPACE;
+  const size_t xy_bytes = (size_t)k * layers[0].hidden * 4, nw_bytes = (size_t)n_layers * 4;
+  if (overlaps(x, xy_bytes, y, xy_bytes) || overlaps(x, xy_bytes, workspace, lay.total) ||
+      overlaps(y, xy_bytes, workspace, lay.total))
+    return MOE_ERR_ALIAS;
+  if (n_woken && (overlaps(n_woken, nw_bytes, workspace, lay.total) || overlaps(n_woken, nw_bytes, y, xy_bytes) ||
+                  overlaps(n_woken, nw_bytes, x, xy_bytes)))
+    return MOE_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)hip_stream;
+  if (error_pending()) return MOE_ERR_HIP;  // the caller's own error stays pending
+  uint8_t* ws = (uint8_t*)workspace;
+  float* pp[2] = {(float*)(ws + lay.pp0), (float*)(ws + lay.pp1)};
+  const bool mx = layers[0].wdtype == MOE_W_MXFP4;
+  for (int l = 0; l < n_layers; ++l) {
+    const float* in = l == 0 ? x : pp[(l - 1) & 1];
+    float* out = l == n_layers - 1 ? y : pp[l & 1];
+    const Args a = block_args(&layers[l], in, k, flags, out, nullptr, nullptr, n_woken ? n_woken + l : nullptr, ws,
+                              lay.base);
+    if (layer_grid(a) > num_cus()) return MOE_ERR_SHAPE;  // every workgroup resident (see moe_verify_block)
+    bool ok;
+    if (layers[0].hidden > 1024) ok = mx ? launch_nwin<2, true>(a, s, nullptr) : launch_nwin<2, false>(a, s, nullptr);
+    else                         ok = mx ? launch_nwin<1, true>(a, s, nullptr) : launch_nwin<1, false>(a, s, nullptr);
+    if (!ok) return MOE_ERR_HIP;
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int moe_pack_weights(int32_t wdtype, int32_t n_mats, int32_t rows, int32_t cols, const void* src,

@@ -358,3 +358,53 @@ def test_noalloc_rejects_calls_beyond_its_scratch_and_bad_arguments(b):
     # the largest layer's 16-token block fits: its workspace is below the scratch size
     big = _layer(b, n_experts=512, top_k=16, inter=1024, shared_inter=1024)
     assert 0 < b.lib.moe_verify_workspace_size(ctypes.byref(big), 16) <= b.NOALLOC_SCRATCH_BYTES
+
+
+def _stack(b, layers, k=16, flags=3, x=FAKE + 0x10000000, y=FAKE + 0x20000000, n=None, ws=FAKE + 0x40000000,
+           ws_bytes=None):
+    arr = (b.MoeLayerStruct * max(1, len(layers)))(*layers)
+    if ws_bytes is None:
+        ws_bytes = 1 << 30
+    return b.lib.moe_verify_stack(arr if layers else None, len(layers), x, k, flags, y, n, ws, ws_bytes, None)
+
+
+def test_stack_workspace_size(b):
+    """A stack's workspace is one layer's single-block workspace plus a second counter set and two
+    activation buffers; 0 for blocks or layer sizes that take the gathered path."""
+    L = _layer(b)
+    s1 = b.lib.moe_verify_stack_workspace_size(ctypes.byref(L), 1)
+    s16 = b.lib.moe_verify_stack_workspace_size(ctypes.byref(L), 16)
+    assert 0 < s1 < s16 and s16 % 256 == 0
+    assert s16 >= 16 * 2048 * 4 * 2  # the two activation buffers
+    assert b.lib.moe_verify_stack_workspace_size(ctypes.byref(L), 0) == 0
+    assert b.lib.moe_verify_stack_workspace_size(ctypes.byref(L), 17) == 0
+    assert b.lib.moe_verify_stack_workspace_size(ctypes.byref(_layer(b, inter=384)), 16) == 0
+    assert b.lib.moe_verify_stack_workspace_size(None, 16) == 0
+
+
+def test_stack_arguments_rejected(b):
+    """moe_verify_stack validates everything on the host before any launch."""
+    L = _layer(b)
+    need = b.lib.moe_verify_stack_workspace_size(ctypes.byref(L), 16)
+    assert _stack(b, []) == b.MOE_ERR_NULL
+    assert _stack(b, [L], x=None) == b.MOE_ERR_NULL
+    assert _stack(b, [L], y=None) == b.MOE_ERR_NULL
+    assert _stack(b, [L], ws=None) == b.MOE_ERR_NULL
+    assert _stack(b, [L, _layer(b, hidden=100)]) == b.MOE_ERR_SHAPE           # an invalid layer
+    assert _stack(b, [L, _layer(b, n_experts=128)]) == b.MOE_ERR_SHAPE         # shapes differ
+    mx = _layer(b, wdtype=1, s_gate=FAKE + 0x7000, s_up=FAKE + 0x8000, s_down=FAKE + 0x9000)
+    assert _stack(b, [L, mx]) == b.MOE_ERR_SHAPE                                # formats differ
+    assert _stack(b, [L], k=0) == b.MOE_ERR_SHAPE
+    assert _stack(b, [L], k=17) == b.MOE_ERR_SHAPE
+    assert _stack(b, [_layer(b, inter=384)]) == b.MOE_ERR_SHAPE                # a gathered-path layer
+    assert _stack(b, [L], flags=4) == b.MOE_ERR_ARG                             # MOE_GATHER
+    assert _stack(b, [L], flags=8) == b.MOE_ERR_ARG
+    assert _stack(b, [L], x=FAKE + 8) == b.MOE_ERR_ALIGN
+    assert _stack(b, [L], n=FAKE + 0x30000004) == b.MOE_ERR_ALIGN
+    assert _stack(b, [L], ws_bytes=need - 1) == b.MOE_ERR_WORKSPACE
+    assert _stack(b, [L], y=FAKE + 0x10000000 + 256) == b.MOE_ERR_ALIAS         # y overlaps x
+    assert _stack(b, [L], y=FAKE + 0x40000000 + 4096) == b.MOE_ERR_ALIAS        # y inside the workspace
+    assert _stack(b, [L, L], n=FAKE + 0x40000000) == b.MOE_ERR_ALIAS            # n_woken inside the workspace
+    many = [L] * (b.STACK_MAX_LAYERS + 1)
+    assert b.lib.moe_verify_stack((b.MoeLayerStruct * len(many))(*many), len(many), FAKE + 0x10000000, 16, 3,
+                                  FAKE + 0x20000000, None, FAKE + 0x40000000, 1 << 30, None) == b.MOE_ERR_SHAPE
