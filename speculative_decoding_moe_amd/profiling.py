@@ -8,6 +8,10 @@ usage:
       HBM bytes per dispatch from one `--pmc FETCH_SIZE` run and one `--pmc WRITE_SIZE` run (csv output),
       each scaled by what the same counter reads for the plain copy kernel of known size that the
       profiled program runs last (`bench.py --profile-run` prints its size as JSON).
+  python -m speculative_decoding_moe_amd.profiling counters "<command>" <pmc_dir> [<pmc_dir> ...]
+      per-kernel means of the SQ counters of one or more `--pmc` runs (csv output) that each
+      include SQ_WAVE_CYCLES: every other wave-cycle counter as a fraction of it, and the other
+      counters per dispatch
 """
 import csv
 import glob
@@ -111,11 +115,59 @@ def traffic(fetch_dir, write_dir, run_json, cmd_fetch, cmd_write, kernel, source
     return "\n".join(out)
 
 
+def _counter_means(d):
+    """{kernel: {counter: (mean per dispatch, dispatches)}} of one counter_collection csv directory."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *counter_collection.csv under {d}")
+    by_dispatch = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                key = (int(r["Dispatch_Id"]), _short(r["Kernel_Name"]), r["Counter_Name"])
+                by_dispatch[key] = by_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+    per = {}
+    for (_, name, ctr), v in by_dispatch.items():
+        per.setdefault(name, {}).setdefault(ctr, []).append(v)
+    return {n: {c: (sum(v) / len(v), len(v)) for c, v in cs.items()} for n, cs in per.items()}
+
+
+# counters in wave-cycles (quad-cycles), shown as fractions of SQ_WAVE_CYCLES
+_WAVE_CYCLE_COUNTERS = ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                        "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_MISC")
+
+
+def counters(cmd, *dirs):
+    runs = [_counter_means(d) for d in dirs]
+    kernels = sorted(set().union(*runs), key=lambda n: -max(r.get(n, {}).get("SQ_WAVE_CYCLES", (0, 0))[0]
+                                                             for r in runs))
+    out = ["# SQ counters per kernel from rocprofv3 --pmc runs (csv output), one run per counter set;",
+           "# wave-cycle counters as fractions of the same run's SQ_WAVE_CYCLES, others per dispatch",
+           f"# command: {cmd}", "# runs: " + " ".join(os.path.basename(d.rstrip('/')) for d in dirs)]
+    for n in kernels:
+        cols = []
+        for r in runs:
+            cs = r.get(n)
+            if not cs or "SQ_WAVE_CYCLES" not in cs:
+                continue
+            wc = cs["SQ_WAVE_CYCLES"][0]
+            for c, (v, _) in sorted(cs.items()):
+                if c == "SQ_WAVE_CYCLES":
+                    continue
+                cols.append(f"{c[3:]}={v / wc:.3f}" if c in _WAVE_CYCLE_COUNTERS else f"{c[3:]}={v:.4g}")
+            cols.append(f"WAVE_CYCLES={wc:.4g}")
+        calls = max(r.get(n, {}).get("SQ_WAVE_CYCLES", (0, 0))[1] for r in runs)
+        out.append(f"{n[:28]:28s} calls {calls:3d}  " + " ".join(cols))
+    return "\n".join(out)
+
+
 def main(argv):
     if argv[0] == "trace":
         print(trace(argv[1], argv[2], int(argv[3]) if len(argv) > 3 else 0))
     elif argv[0] == "traffic":
         print(traffic(*argv[1:8]))
+    elif argv[0] == "counters":
+        print(counters(argv[1], *argv[2:]))
     else:
         raise SystemExit(__doc__)
 
