@@ -473,12 +473,23 @@ __device__ __forceinline__ void sort_desc(uint64_t (&c)[NS]) {
 // equals it (one ballot) and pops that lane's head. HALF: the wave serves two tokens, lanes 0-31
 // and 32-63; no step crosses a half, so each half picks its own token's next expert. Lane j of a
 // half records pick j (expert and key).
+// The sorted list is split into its 32-bit keys and the candidates' positions m inside the lane
+// (4 bits each, head in the low bits): the expert of the winning head is NS (lane - first lane of
+// the half) + m, so a pop shifts NS keys and one word instead of NS 64-bit composites.
 template <int NS, bool HALF>
-__device__ __forceinline__ void topk_sorted(uint64_t (&c)[NS], int K, int lane, int& my_e, uint32_t& my_key) {
+__device__ __forceinline__ void topk_sorted(const uint64_t (&c)[NS], int K, int lane, int& my_e, uint32_t& my_key) {
+  static_assert(NS <= 8, "4-bit positions, 8 per word");
   const bool hi = HALF && lane >= 32;
   const int jl = HALF ? (lane & 31) : lane;
+  uint32_t kk[NS];
+  uint32_t pk = 0;
+#pragma unroll
+  for (int m = 0; m < NS; ++m) {
+    kk[m] = (uint32_t)(c[m] >> 32);
+    pk |= ((~(uint32_t)c[m]) & (uint32_t)(NS - 1)) << (4 * m);  // expert NS l + position
+  }
   for (int j = 0; j < K; ++j) {
-    const uint32_t h = (uint32_t)(c[0] >> 32);
+    const uint32_t h = kk[0];
     uint32_t x = h;
     x = max(x, dpp_u32<0xB1>(x));   // quad_perm [1,0,3,2]
     x = max(x, dpp_u32<0x4E>(x));   // quad_perm [2,3,0,1]
@@ -491,25 +502,28 @@ __device__ __forceinline__ void topk_sorted(uint64_t (&c)[NS], int K, int lane, 
       const auto r32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
       w = max((uint32_t)r32[0], (uint32_t)r32[1]);
     }
-    const uint32_t lo = (uint32_t)c[0];
-    uint32_t e;
-    int sl;
+    int e, sl;
     if constexpr (HALF) {
       const uint64_t bm = __ballot(h == w);  // each half holds its own maximum
       const int sla = __builtin_ctz((uint32_t)bm), slb = 32 + __builtin_ctz((uint32_t)(bm >> 32));
-      const uint32_t ea = (uint32_t)__builtin_amdgcn_readlane((int)lo, sla);
-      const uint32_t eb = (uint32_t)__builtin_amdgcn_readlane((int)lo, slb);
+      const int ea = NS * sla + (int)((uint32_t)__builtin_amdgcn_readlane((int)pk, sla) & 15u);
+      const int eb = NS * (slb - 32) + (int)((uint32_t)__builtin_amdgcn_readlane((int)pk, slb) & 15u);
       sl = hi ? slb : sla;
       e = hi ? eb : ea;
     } else {
       sl = __builtin_ctzll(__ballot(h == w));
-      e = (uint32_t)__builtin_amdgcn_readlane((int)lo, sl);
+      e = NS * sl + (int)((uint32_t)__builtin_amdgcn_readlane((int)pk, sl) & 15u);
     }
-    if (jl == j) { my_e = (int)~e; my_key = w; }
-    const bool pop = lane == sl;
+    if (jl == j) { my_e = e; my_key = w; }
+    // the pop as bit selects under an all-ones / zero mask that the optimizer cannot see through:
+    // written as selects on the lane test, the shifts were turned into per-key position tracking
+    // with compare chains, three times the instructions
+    uint32_t pm = lane == sl ? ~0u : 0u;
+    asm volatile("" : "+v"(pm));
 #pragma unroll
-    for (int m = 0; m + 1 < NS; ++m) c[m] = pop ? c[m + 1] : c[m];
-    c[NS - 1] = pop ? 0ull : c[NS - 1];
+    for (int m = 0; m + 1 < NS; ++m) kk[m] = (kk[m] & ~pm) | (kk[m + 1] & pm);
+    kk[NS - 1] &= ~pm;
+    pk = (pk & ~pm) | ((pk >> 4) & pm);
   }
 }
 
